@@ -1,0 +1,32 @@
+"""Float64 CPU oracle for the diagonal linear RNN / diagonal SSM forward map.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package: only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code,
+tables, constants or helpers with the HIP library; the two meet only through
+the seeded input generators, which hold none of the method's arithmetic.
+
+Every function here is a plain, slow, obviously correct restatement of what the
+pages define, in float64, from the float32 input values promoted exactly:
+
+* ``dlr``  -- the diagonal linear RNN (DLR) of "Simplifying and Understanding
+  State Space Models with Diagonal Linear RNNs", section 2: the parameterisation
+  of Lambda, the kernel K_j = sum_n w_n lambda_n^j, the real cast, the causal
+  convolution and the bidirectional sum; computed twice, as an O(L^2) direct sum
+  and as a sequential recurrence.
+* ``s5``   -- the multi-input multi-output diagonal SSM of "Simplified State
+  Space Layers for Sequence Modeling", section 3, computed as a sequential
+  recurrence and as a direct causal sum over a prefix.
+
+Parity status: every function is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` (closed forms, a library DFT, brute-force
+Toeplitz/circulant matrices and invariants).  No function is "parity unpinned".
+"""
+
+from .dlr import (  # noqa: F401
+    dlr_lambda,
+    dlr_kernel,
+    dlr_direct,
+    dlr_recurrence,
+)
+from .s5 import s5_recurrence, s5_direct_prefix  # noqa: F401

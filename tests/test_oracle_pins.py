@@ -1,0 +1,419 @@
+"""Pins of the float64 oracle to facts the pages and mathematics fix (CPU only).
+
+Each pin is written as a function of an oracle implementation ``impl`` (an
+object with dlr_kernel / dlr_direct / dlr_recurrence), so the same pins are run
+on the real oracle (all must hold) and on deliberately broken copies of it
+(at least one must fail) -- a check that the pins are strong enough to catch a
+dropped term, a wrong sign, a wrong index or a wrong direction.
+
+Sources cited per pin: "Simplifying and Understanding State Space Models with
+Diagonal Linear RNNs" (DLR page), "The Annotated S4" (S4 page) and
+"Simplified State Space Layers for Sequence Modeling" (S5 page).
+"""
+
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from long_convolution_sequence_amd import inputs
+
+RTOL = 1e-11
+
+
+def _rel(a, b):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    return np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(np.asarray(b).ravel()), 1e-300)
+
+
+def _params(H, N, ndir=1, seed=0, re_scale=1.0):
+    x = inputs.dlr_inputs(1, H, N, 8, bidirectional=(ndir == 2), seed=seed, re_scale=re_scale)
+    return x["log_re"], x["log_im"], x["W"], x["D"]
+
+
+# ----------------------------------------------------------------------------
+# Pins as functions of an implementation
+# ----------------------------------------------------------------------------
+
+def pin_dft_identity(impl):
+    """DLR page, section 2: with (log L)_re = 0, (log L)_im = 2 pi n / N and
+    L = N, K = DFT . w.  The DFT with kernel e^{+2 pi i n k / N} is N*ifft."""
+    for N in (8, 16, 64):
+        rng = np.random.default_rng(N)
+        w = rng.normal(size=N) + 1j * rng.normal(size=N)
+        re = np.zeros(N)
+        im = 2 * np.pi * np.arange(N) / N
+        K = impl.dlr_kernel(re, im, w, N)
+        if _rel(K, N * np.fft.ifft(w)) > 1e-12:
+            return False
+    return True
+
+
+def pin_shift_one_hot(impl):
+    """DLR page, section 3.1 (Shift): a one-hot kernel at r shifts by r.  With
+    re = 0, im = 2 pi n/N and w_n = e^{-2 pi i n r/N}/N, K_k = 1 when
+    k = r (mod N) and 0 otherwise, so y_k = sum_{m>=0} u_{k-r-mN} + D u_k."""
+    N, L, r = 8, 40, 3
+    n = np.arange(N)
+    re = np.zeros((1, 1, N))
+    im = (2 * np.pi * n / N)[None, None, :]
+    w = (np.exp(-2j * np.pi * n * r / N) / N)[None, None, :]
+    D = np.array([[0.75]])
+    u = np.random.default_rng(1).integers(-5, 6, size=(1, 1, L)).astype(np.float64)
+    expect = 0.75 * u[0, 0].copy()
+    for k in range(L):
+        j = k - r
+        while j >= 0:
+            expect[k] += u[0, 0, j]
+            j -= N
+    ok = True
+    for f in (impl.dlr_direct, impl.dlr_recurrence):
+        ok &= _rel(f(u, re, im, w, D)[0, 0], expect) < 1e-12
+    return bool(ok)
+
+
+def pin_cumsum_all_ones(impl):
+    """DLR page, section 3.1 (CumSum): the all-ones kernel gives the prefix
+    sum.  w = delta_{n,0} with lambda_0 = 1 makes K identically 1."""
+    N, L = 4, 50
+    re = np.zeros((1, 1, N))
+    im = (2 * np.pi * np.arange(N) / N)[None, None, :]
+    w = np.zeros((1, 1, N), dtype=complex)
+    w[..., 0] = 1.0
+    D = np.array([[-0.5]])
+    u = np.random.default_rng(2).normal(size=(2, 1, L))
+    expect = np.cumsum(u, axis=-1) - 0.5 * u
+    return all(_rel(f(u, re, im, w, D), expect) < 1e-12
+               for f in (impl.dlr_direct, impl.dlr_recurrence))
+
+
+def pin_impulse_response(impl):
+    """DLR page, section 2: dy_k/du_{k-j} = K_j -- the response to a unit
+    impulse at position p is Re K shifted by p (D = 0)."""
+    lr, li, W, _ = _params(3, 16, seed=3)
+    L, p = 64, 5
+    u = np.zeros((1, 3, L))
+    u[0, :, p] = 1.0
+    D0 = np.zeros((1, 3))
+    K = impl.dlr_kernel(lr[0], li[0], W[0], L).real
+    expect = np.zeros((3, L))
+    expect[:, p:] = K[:, : L - p]
+    return all(_rel(f(u, lr, li, W, D0)[0], expect) < RTOL
+               for f in (impl.dlr_direct, impl.dlr_recurrence))
+
+
+def pin_two_forms_agree(impl):
+    """S4 page, Part 1 ("the CNN and RNN modes give the same result"): the
+    convolution view and the recurrence view are the same map."""
+    ok = True
+    for bi in (False, True):
+        x = inputs.dlr_inputs(2, 3, 16, 96, bidirectional=bi, seed=4)
+        a = impl.dlr_direct(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], bi)
+        b = impl.dlr_recurrence(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], bi)
+        ok &= _rel(a, b) < RTOL
+    return bool(ok)
+
+
+def _toeplitz_bruteforce(Kf, Kb, Dsum, u):
+    L = u.shape[-1]
+    T = np.zeros((L, L))
+    for k in range(L):
+        for j in range(L):
+            if k >= j:
+                T[k, j] += Kf[k - j]
+            if Kb is not None and j >= k:
+                T[k, j] += Kb[j - k]
+    return T @ u + Dsum * u
+
+
+def pin_toeplitz_and_circulant(impl):
+    """DLR page, section 2: the causal convolution is a Toeplitz mat-vec that
+    equals the first L rows of a 2L circulant mat-vec on zero-padded operands.
+    Both explicit matrices are built element by element (tiny L)."""
+    ok = True
+    for L in (1, 2, 7, 16):
+        lr, li, W, D = _params(2, 8, seed=5 + L)
+        u = np.random.default_rng(L).normal(size=(1, 2, L))
+        y = impl.dlr_direct(u, lr, li, W, D)
+        for h in range(2):
+            K = impl.dlr_kernel(lr[0, h], li[0, h], W[0, h], L).real
+            t = _toeplitz_bruteforce(K, None, float(D[0, h]), u[0, h])
+            kp = np.concatenate([K, np.zeros(L)])
+            up = np.concatenate([u[0, h], np.zeros(L)])
+            C = np.array([[kp[(i - j) % (2 * L)] for j in range(2 * L)] for i in range(2 * L)])
+            c = (C @ up)[:L] + float(D[0, h]) * u[0, h]
+            ok &= _rel(y[0, h], t) < RTOL and _rel(y[0, h], c) < RTOL
+    return bool(ok)
+
+
+def pin_bidirectional_toeplitz(impl):
+    """DLR page, section 2 (bidirectional DLR = sum of two independent DLRs,
+    one per direction): a full Toeplitz matrix with Re K_f below, Re K_b above
+    and Re K_f[0] + Re K_b[0] + D_f + D_b on the diagonal (tiny L)."""
+    ok = True
+    lr, li, W, D = _params(2, 8, ndir=2, seed=9)
+    for L in (1, 5, 12):
+        u = np.random.default_rng(L + 100).normal(size=(1, 2, L))
+        for f in (impl.dlr_direct, impl.dlr_recurrence):
+            y = f(u, lr, li, W, D, True)
+            for h in range(2):
+                Kf = impl.dlr_kernel(lr[0, h], li[0, h], W[0, h], L).real
+                Kb = impl.dlr_kernel(lr[1, h], li[1, h], W[1, h], L).real
+                t = _toeplitz_bruteforce(Kf, Kb, float(D[0, h]) + float(D[1, h]), u[0, h])
+                ok &= _rel(y[0, h], t) < RTOL
+    return bool(ok)
+
+
+def pin_bidirectional_reductions(impl):
+    """Bidirectional reductions: W_b = 0, D_b = 0 gives the unidirectional map;
+    swapping the two parameter sets and reversing the input reverses y."""
+    x = inputs.dlr_inputs(2, 3, 8, 33, bidirectional=True, seed=11)
+    u, lr, li, W, D = x["u"], x["log_re"], x["log_im"], x["W"], x["D"]
+    ok = True
+    W0 = W.astype(np.complex128).copy()
+    W0[1] = 0
+    D0 = D.astype(np.float64).copy()
+    D0[1] = 0
+    for f in (impl.dlr_direct, impl.dlr_recurrence):
+        a = f(u, lr, li, W0, D0, True)
+        b = f(u, lr[:1], li[:1], W[:1], D[:1], False)
+        ok &= _rel(a, b) < RTOL
+        y = f(u, lr, li, W, D, True)
+        ys = f(u[..., ::-1], lr[::-1], li[::-1], W[::-1], D[::-1], True)
+        ok &= _rel(ys[..., ::-1], y) < RTOL
+    return bool(ok)
+
+
+def pin_generating_function(impl):
+    """S4 page, Part 2, step 1 and step 2: the length-L truncated generating
+    function at the L-th roots of unity omega_m = exp(-2 pi i m / L) is the DFT
+    of K, and for a diagonal state it is the weighted sum
+    sum_n w_n (1 - lambda_n^L) / (1 - lambda_n omega_m)."""
+    lr, li, W, _ = _params(2, 16, seed=12)
+    ok = True
+    for L in (16, 64, 256):
+        for h in range(2):
+            K = impl.dlr_kernel(lr[0, h], li[0, h], W[0, h], L)
+            lam = oracle.dlr_lambda(lr[0, h], li[0, h]).astype(np.complex128)
+            om = np.exp(-2j * np.pi * np.arange(L) / L)
+            gen = ((W[0, h].astype(np.complex128) * (1 - np.power(lam, L)))[None, :]
+                   / (1 - lam[None, :] * om[:, None])).sum(axis=1)
+            ok &= _rel(np.fft.fft(K), gen) < 1e-10
+    return bool(ok)
+
+
+def pin_step_input(impl):
+    """Step input u = 1: y_k = Re sum_n w_n (1 - lambda_n^{k+1}) / (1 - lambda_n)
+    + D, the geometric sum of the kernel (a closed form at full length)."""
+    lr, li, W, D = _params(3, 16, seed=13, re_scale=0.1)
+    L = 4096
+    u = np.ones((1, 3, L))
+    y = impl.dlr_direct(u, lr, li, W, D)
+    y2 = impl.dlr_recurrence(u, lr, li, W, D)
+    lam = oracle.dlr_lambda(lr[0], li[0])
+    k = np.arange(L)
+    ok = True
+    for h in range(3):
+        geo = (W[0, h].astype(np.complex128)[None, :]
+               * (1 - np.power(lam[h][None, :], (k + 1)[:, None])) / (1 - lam[h][None, :])).sum(1)
+        expect = geo.real + float(D[0, h])
+        ok &= _rel(y[0, h], expect) < 1e-10 and _rel(y2[0, h], expect) < 1e-10
+    return bool(ok)
+
+
+def pin_lambda_modulus(impl):
+    """DLR page, section 2: |lambda| = exp(-re^2) <= 1, decreasing in re, equal
+    to 1 at re = 0, periodic in the imaginary log with period 2 pi.  Pinned as
+    properties: |lambda(2 re)| = |lambda(re)|^4 fixes the square in the
+    exponent and its sign; the phase is the imaginary log mod 2 pi."""
+    re = np.linspace(0, 2, 41)
+    im = np.linspace(-7, 7, 41)
+    K1 = impl.dlr_kernel(re[:, None], im[:, None], np.ones((41, 1)), 2)[:, 1]
+    K2 = impl.dlr_kernel(2 * re[:, None], im[:, None], np.ones((41, 1)), 2)[:, 1]
+    Kp = impl.dlr_kernel(re[:, None], im[:, None] + 2 * np.pi, np.ones((41, 1)), 2)[:, 1]
+    mag = np.abs(K1)
+    ok = np.all(mag <= 1 + 1e-15) and abs(mag[0] - 1) < 1e-15
+    ok &= np.all(np.diff(mag) < 0)
+    ok &= np.allclose(np.abs(K2), mag ** 4, rtol=1e-12, atol=0)
+    ok &= np.allclose(Kp, K1, rtol=1e-12, atol=1e-15)
+    ok &= np.allclose(np.angle(K1 / mag), np.angle(np.exp(1j * im)), atol=1e-12)
+    return bool(ok)
+
+
+def pin_invariants(impl):
+    """Linearity in u, causality, time-shift equivariance and independence of
+    channels (S5 page, section 2.3: a bank of independent SISO SSMs)."""
+    x = inputs.dlr_inputs(2, 4, 8, 48, seed=14)
+    lr, li, W, D = x["log_re"], x["log_im"], x["W"], x["D"]
+    rng = np.random.default_rng(3)
+    u = rng.normal(size=(2, 4, 48))
+    v = rng.normal(size=(2, 4, 48))
+    f = impl.dlr_direct
+    ok = _rel(f(2 * u - 3 * v, lr, li, W, D), 2 * f(u, lr, li, W, D) - 3 * f(v, lr, li, W, D)) < RTOL
+    w = u.copy()
+    w[..., 30:] = rng.normal(size=(2, 4, 18))
+    ok &= np.allclose(f(w, lr, li, W, D)[..., :30], f(u, lr, li, W, D)[..., :30], rtol=0, atol=1e-12)
+    s = 7
+    us = np.zeros_like(u)
+    us[..., s:] = u[..., :-s]
+    ok &= _rel(f(us, lr, li, W, D)[..., s:], f(u, lr, li, W, D)[..., :-s]) < RTOL
+    perm = np.array([2, 0, 3, 1])
+    ok &= _rel(f(u[:, perm], lr[:, perm], li[:, perm], W[:, perm], D[:, perm]),
+               f(u, lr, li, W, D)[:, perm]) < RTOL
+    return bool(ok)
+
+
+PINS = [
+    pin_dft_identity, pin_shift_one_hot, pin_cumsum_all_ones, pin_impulse_response,
+    pin_two_forms_agree, pin_toeplitz_and_circulant, pin_bidirectional_toeplitz,
+    pin_bidirectional_reductions, pin_generating_function, pin_step_input,
+    pin_lambda_modulus, pin_invariants,
+]
+
+REAL = types.SimpleNamespace(dlr_kernel=oracle.dlr_kernel, dlr_direct=oracle.dlr_direct,
+                             dlr_recurrence=oracle.dlr_recurrence)
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    assert pin(REAL)
+
+
+# ----------------------------------------------------------------------------
+# Planted mistakes: broken copies of the oracle that the pins must reject.
+# ----------------------------------------------------------------------------
+
+def _mutant_kernel(kind):
+    def kernel(log_re, log_im, W, L):
+        re = np.asarray(log_re, dtype=np.float64)
+        im = np.asarray(log_im, dtype=np.float64)
+        w = np.asarray(W).astype(np.complex128)
+        if kind == "sign":
+            ll = re * re + 1j * im
+        elif kind == "abs":
+            ll = -np.abs(re) + 1j * im
+        elif kind == "conj_im":
+            ll = -re * re - 1j * im
+        else:
+            ll = -re * re + 1j * im
+        if kind == "conj_w":
+            w = np.conj(w)
+        j = np.arange(L, dtype=np.float64) + (1.0 if kind == "offbyone" else 0.0)
+        lead = re.shape[:-1]
+        n = re.shape[-1]
+        ll2 = ll.reshape(-1, n)
+        w2 = np.broadcast_to(w, ll.shape).reshape(-1, n)
+        out = np.stack([np.exp(j[:, None] * ll2[c][None, :]) @ w2[c] for c in range(ll2.shape[0])])
+        return out.reshape(lead + (L,))
+    return kernel
+
+
+def _mutant(kind):
+    """An oracle with one planted mistake."""
+    kern = _mutant_kernel(kind)
+
+    def direct(u, log_re, log_im, W, D, bidirectional=False):
+        u = np.asarray(u, dtype=np.float64)
+        Bsz, H, L = u.shape
+        ndir = 2 if bidirectional else 1
+        D = np.asarray(D, dtype=np.float64)
+        y = u * (D[0] if kind == "one_d" else D.sum(0))[None, :, None]
+        if kind == "no_d":
+            y = np.zeros_like(u)
+        for d in range(ndir):
+            for h in range(H):
+                K = kern(log_re[d, h], log_im[d, h], W[d, h], L)
+                K = K.imag if kind == "imag" else K.real
+                for b in range(Bsz):
+                    if d == 0 or kind == "no_flip":
+                        y[b, h] += np.convolve(u[b, h], K)[:L]
+                    else:
+                        y[b, h] += np.convolve(u[b, h][::-1], K)[:L][::-1]
+        return y
+
+    def recurrence(u, log_re, log_im, W, D, bidirectional=False):
+        # The planted mistakes sit in the kernel or the direct sum; the second
+        # form repeats the first so that "two forms agree" cannot hide them.
+        return direct(u, log_re, log_im, W, D, bidirectional)
+
+    return types.SimpleNamespace(dlr_kernel=kern, dlr_direct=direct, dlr_recurrence=recurrence)
+
+
+@pytest.mark.parametrize("kind", ["sign", "abs", "conj_im", "conj_w", "offbyone", "imag",
+                                  "no_d", "one_d", "no_flip"])
+def test_pins_reject_planted_mistake(kind):
+    m = _mutant(kind)
+    failed = [p.__name__ for p in PINS if not p(m)]
+    assert failed, f"no pin caught the planted mistake '{kind}'"
+
+
+def test_mutant_harness_is_faithful():
+    """The unmutated copy used for planting passes every pin (so a failure
+    above is caused by the planted mistake, not by the copy)."""
+    m = _mutant("none")
+    assert all(p(m) for p in PINS)
+
+
+# ----------------------------------------------------------------------------
+# S5 oracle pins
+# ----------------------------------------------------------------------------
+
+def test_s5_reduces_to_bank_of_dlrs():
+    """S5 page, section 3 vs the S4 bank of SISO SSMs (section 2.3): with
+    P = H, Bbar = I and C = diag(w) the MIMO system is H scalar DLRs (N = 1)
+    whose eigenvalue is lambda_h and whose output weight is w_h."""
+    H, L = 3, 64
+    rng = np.random.default_rng(5)
+    lam = np.exp(-rng.uniform(0.01, 0.3, H) + 1j * rng.uniform(-3, 3, H))
+    w = rng.normal(size=H) + 1j * rng.normal(size=H)
+    D = rng.normal(size=H)
+    u = rng.normal(size=(2, H, L))
+    y = oracle.s5_recurrence(u, lam, np.eye(H), np.diag(w), D)
+    log_re = np.sqrt(-np.log(np.abs(lam)))[None, :, None]
+    log_im = np.angle(lam)[None, :, None]
+    yd = oracle.dlr_direct(u, log_re, log_im, w[None, :, None], D[None, :])
+    assert _rel(y, yd) < 1e-10
+
+
+def test_s5_mixing_matches_dlr_superposition():
+    """P = 1, H = 2 with general Bbar [1,2] and C [2,1]: by linearity
+    y_h = sum_g DLR(u_g; w = C[h] Bbar[g]) + D_h u_h.  Catches a transposed
+    input or output matrix."""
+    L = 40
+    rng = np.random.default_rng(6)
+    lam = np.array([np.exp(-0.05 + 0.7j)])
+    Bb = rng.normal(size=(1, 2)) + 1j * rng.normal(size=(1, 2))
+    C = rng.normal(size=(2, 1)) + 1j * rng.normal(size=(2, 1))
+    D = rng.normal(size=2)
+    u = rng.normal(size=(1, 2, L))
+    y = oracle.s5_recurrence(u, lam, Bb, C, D)
+    lr = np.array([[[np.sqrt(0.05)]]])
+    li = np.array([[[0.7]]])
+    for h in range(2):
+        acc = D[h] * u[0, h]
+        for g in range(2):
+            acc = acc + oracle.dlr_direct(u[:, g:g + 1], lr, li,
+                                          np.array([[[C[h, 0] * Bb[0, g]]]]), np.zeros((1, 1)))[0, 0]
+        assert _rel(y[0, h], acc) < 1e-11
+
+
+def test_s5_recurrence_equals_direct_prefix():
+    """The scan (S5 page, section 2.2) and the direct causal sum agree."""
+    x = inputs.s5_inputs(2, 6, 5, 80, seed=7)
+    a = oracle.s5_recurrence(x["u"], x["lam"], x["Bbar"], x["C"], x["D"])
+    b = oracle.s5_direct_prefix(x["u"], x["lam"], x["Bbar"], x["C"], x["D"], 80)
+    assert _rel(a, b) < 1e-11
+    c = oracle.s5_direct_prefix(x["u"], x["lam"], x["Bbar"], x["C"], x["D"], 33)
+    assert _rel(a[..., :33], c) < 1e-11
+
+
+def test_inputs_are_seeded_and_float32():
+    a = inputs.inputs_for(inputs.config(0))
+    b = inputs.inputs_for(inputs.config("tiny"))
+    for k in a:
+        assert a[k].dtype in (np.float32, np.complex64)
+        assert np.array_equal(a[k], b[k])
+    c2 = inputs.dlr_inputs(1, 2, 4, 8, bidirectional=True, seed=2)
+    assert c2["log_re"].shape == (2, 2, 4) and c2["D"].shape == (2, 2)
