@@ -1,0 +1,138 @@
+/*
+ * dssm.h -- C ABI of libdssm.so: the forward map of a bank of H independent
+ * diagonal linear RNN / diagonal state-space channels on AMD MI355X (gfx950).
+ *
+ * The map (DLR = "Simplifying and Understanding State Space Models with
+ * Diagonal Linear RNNs", section 2):
+ *
+ *   lambda[h,n] = exp(-log_re[h,n]^2 + i*log_im[h,n])        (parameterisation)
+ *   K[h,j]      = sum_n W[h,n] * lambda[h,n]^j,  0 <= j < L    (kernel)
+ *   y[b,h,k]    = sum_{j=0}^{k} Re(K[h,j]) u[b,h,k-j] + D[h] u[b,h,k]
+ *
+ * The real cast of the kernel is the DLR page's (section 2, first paragraph);
+ * the D feed-through is the SSM layer of "The Annotated S4" (Part 1, "An SSM
+ * neural network").  With bidirectional = 1 a second, independent DLR runs on
+ * the time-reversed input and its reversed output is added (DLR page,
+ * section 2, bidirectional paragraph):
+ *
+ *   y[b,h,k] += sum_{j=0}^{L-1-k} Re(K_b[h,j]) u[b,h,k+j] + D_b[h] u[b,h,k]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Layouts are row-major, last index fastest.  ndir = 1 + bidirectional.
+ * - Every array argument is a DEVICE pointer (memory of the current HIP
+ *   device), float32, 16-byte aligned.  Complex values are interleaved
+ *   (re, im) float32 pairs, i.e. torch.complex64 / view_as_real layout.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *   only enqueues kernels on `stream` and returns; it never synchronises.
+ * - Ownership: the caller allocates and owns every buffer, including the
+ *   workspace `ws` of at least the size reported by dssm_workspace_size().
+ *   The library allocates no device memory and keeps no pointer after return.
+ *   Outputs must not alias inputs.  The workspace may be reused by later calls
+ *   on the same stream; concurrent calls need distinct workspaces.
+ * - Errors: every call returns a dssm_status.  Arguments are validated on the
+ *   host before anything is launched, so an error return means nothing was
+ *   enqueued (except DSSM_ERR_HIP, reported by the launch itself).  No call
+ *   aborts or throws.  dssm_last_error() gives a per-thread message.
+ * - Thread safety: calls may be made from several threads; the only mutable
+ *   library state is the per-thread last-error message.
+ */
+#ifndef DSSM_H
+#define DSSM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSSM_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+/* Status codes. */
+typedef enum {
+  DSSM_OK = 0,
+  DSSM_ERR_INVALID_ARG = -1,  /* null pointer, bad dimension or flag, misaligned pointer */
+  DSSM_ERR_UNSUPPORTED = -2,  /* valid but outside what this library computes */
+  DSSM_ERR_WORKSPACE = -3,    /* ws_bytes smaller than dssm_workspace_size() */
+  DSSM_ERR_HIP = -4           /* a HIP launch reported an error */
+} dssm_status;
+
+/* Operations, for dssm_workspace_size(). */
+typedef enum {
+  DSSM_OP_GEN = 0,   /* dssm_gen_kernel */
+  DSSM_OP_FFT = 1,   /* dssm_forward_fft */
+  DSSM_OP_SCAN = 2   /* dssm_forward_scan */
+} dssm_op;
+
+/* Shape of a DLR bank: batch B, channels H, modes N, length L. */
+typedef struct {
+  int B, H, N, L;
+  int bidirectional; /* 0 or 1 */
+} dssm_shape;
+
+/* DLR parameters (device pointers, float32).
+ *   log_re [ndir, H, N]      (log Lambda)_re
+ *   log_im [ndir, H, N]      (log Lambda)_im
+ *   W      [ndir, H, N, 2]   complex output weights w
+ *   D      [ndir, H]         real feed-through
+ * Direction 0 is left-to-right, direction 1 (if bidirectional) right-to-left. */
+typedef struct {
+  const float* log_re;
+  const float* log_im;
+  const float* W;
+  const float* D;
+} dssm_dlr_params;
+
+/* Library version (DSSM_VERSION of the build). */
+int dssm_version(void);
+
+/* Static text for a status code. */
+const char* dssm_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* dssm_last_error(void);
+
+/* Bytes of workspace needed by `op` for shape `s` (host only; launches
+ * nothing).  Returns DSSM_ERR_INVALID_ARG / DSSM_ERR_UNSUPPORTED exactly
+ * when the corresponding compute call would. */
+int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes);
+
+/* Kernel generation: K[d,h,j] = sum_n W[d,h,n] lambda[d,h,n]^j for 0 <= j < L
+ * (DLR page, section 2: K = (<w, Lambda^k>)_{0<=k<L}).
+ *   complex_out = 0: K is [ndir, H, L] float32 holding Re K.
+ *   complex_out = 1: K is [ndir, H, L, 2] float32 holding K (re, im).
+ * Powers are formed from lambda^r (r < 64) and anchors lambda^(64q) that are
+ * computed in float64 and rounded once to float32.  B and p->D are ignored
+ * (D may be NULL).
+ * Requires 1 <= N <= 4096, 1 <= L <= 2^24. */
+int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_out,
+                    float* K, void* ws, size_t ws_bytes, void* stream);
+
+/* Layer forward by the convolution view: y [B, H, L] from u [B, H, L].
+ * Generates Re K, takes its spectrum on a zero-padded circle of length 2M
+ * (M = the smallest power of two >= max(L, 16)), and for each channel forms
+ * y = first L samples of IFFT(FFT(pad(u)) * spectrum) + D u -- the Toeplitz
+ * product computed as a circulant product of size 2M (DLR page, section 2;
+ * "The Annotated S4", Part 1, "Training SSMs: the convolutional
+ * representation").  For bidirectional = 1 the backward kernel enters as the
+ * conjugate spectrum (a correlation) and D_f + D_b multiplies u.
+ * Requires L <= 16384 (the FFT is staged in one compute unit's LDS); longer L
+ * returns DSSM_ERR_UNSUPPORTED (use dssm_forward_scan). */
+int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                     float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Layer forward by the recurrence view: x_k = lambda x_{k-1} + u_k (x_{-1} = 0,
+ * every mode driven by u), y_k = Re(sum_n W_n x_{k,n}) + D u_k; the backward
+ * direction runs over k = L-1 .. 0 and is added ("The Annotated S4", Part 1,
+ * "Discrete-time SSM: the recurrent representation"; the diagonal parallel
+ * scan of "Simplified State Space Layers for Sequence Modeling", section 2.2).
+ * Time is split into segments, one per lane; segment carries are combined with
+ * powers of lambda computed in float64.  Accepts any L >= 1. */
+int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                      float* y, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSSM_H */

@@ -1,0 +1,195 @@
+"""ctypes binding of libdssm.so (C ABI in include/dssm.h).
+
+Argument marshalling only: every step of the forward map runs in the library's
+HIP kernels.  Torch supplies device memory and the current stream.  If the
+library is missing or a call fails, an exception is raised -- there is no
+fallback path.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdssm.so")
+
+DSSM_OK = 0
+DSSM_ERR_INVALID_ARG = -1
+DSSM_ERR_UNSUPPORTED = -2
+DSSM_ERR_WORKSPACE = -3
+DSSM_ERR_HIP = -4
+
+OP_GEN, OP_FFT, OP_SCAN = 0, 1, 2
+
+# Every function the header declares (checked by the ABI tests).
+EXPORTS = [
+    "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
+    "dssm_gen_kernel", "dssm_forward_fft", "dssm_forward_scan",
+]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int),
+                ("L", ctypes.c_int), ("bidirectional", ctypes.c_int)]
+
+
+class DLRParams(ctypes.Structure):
+    _fields_ = [("log_re", ctypes.c_void_p), ("log_im", ctypes.c_void_p),
+                ("W", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+class DSSMError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("dssm status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libdssm.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libdssm.so is not built; run `python -m long_convolution_sequence_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.dssm_version.restype = ctypes.c_int
+    L.dssm_version.argtypes = []
+    L.dssm_status_string.restype = ctypes.c_char_p
+    L.dssm_status_string.argtypes = [ctypes.c_int]
+    L.dssm_last_error.restype = ctypes.c_char_p
+    L.dssm_last_error.argtypes = []
+    L.dssm_workspace_size.restype = ctypes.c_int
+    L.dssm_workspace_size.argtypes = [ctypes.c_int, ctypes.POINTER(Shape), ctypes.POINTER(sz)]
+    L.dssm_gen_kernel.restype = ctypes.c_int
+    L.dssm_gen_kernel.argtypes = [ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), ctypes.c_int,
+                                  vp, vp, sz, vp]
+    for name in ("dssm_forward_fft", "dssm_forward_scan"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def check(status):
+    if status != DSSM_OK:
+        raise DSSMError(status, lib().dssm_last_error().decode())
+
+
+def workspace_size(op, B, H, N, L, bidirectional=False):
+    shape = Shape(B, H, N, L, int(bool(bidirectional)))
+    out = ctypes.c_size_t(0)
+    check(lib().dssm_workspace_size(op, ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+# ----------------------------------------------------------------------------
+# torch-facing wrappers
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_f32(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype == torch.complex64:
+        t = torch.view_as_real(t)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32 (or complex64), got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(op, shape, workspace, device):
+    torch = _torch()
+    need = ctypes.c_size_t(0)
+    check(lib().dssm_workspace_size(op, ctypes.byref(shape), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _params(log_re, log_im, W, D, ndir, H, N):
+    lr = _dev_f32(log_re, "log_re")
+    li = _dev_f32(log_im, "log_im")
+    w = _dev_f32(W, "W")
+    if D is None:  # generator only
+        if lr.numel() != ndir * H * N or li.numel() != ndir * H * N or w.numel() != 2 * ndir * H * N:
+            raise ValueError("parameter sizes do not match [ndir, H, N]")
+        return DLRParams(lr.data_ptr(), li.data_ptr(), w.data_ptr(), None), (lr, li, w)
+    d = _dev_f32(D, "D")
+    if lr.numel() != ndir * H * N or li.numel() != ndir * H * N:
+        raise ValueError("log_re/log_im must have ndir*H*N elements")
+    if w.numel() != 2 * ndir * H * N:
+        raise ValueError("W must have ndir*H*N complex elements")
+    if d.numel() != ndir * H:
+        raise ValueError("D must have ndir*H elements")
+    keep = (lr, li, w, d)
+    return DLRParams(lr.data_ptr(), li.data_ptr(), w.data_ptr(), d.data_ptr()), keep
+
+
+def gen_kernel(log_re, log_im, W, L, complex_out=False, out=None, workspace=None, stream=None):
+    """K[d,h,j] = sum_n W lambda^j for j < L.  log_re/log_im [ndir,H,N] f32,
+    W [ndir,H,N] c64.  Returns Re K [ndir,H,L] f32 or K [ndir,H,L] c64."""
+    torch = _torch()
+    ndir, H, N = log_re.shape
+    shape = Shape(1, H, N, L, ndir - 1)
+    p, keep = _params(log_re, log_im, W, None, ndir, H, N)
+    if out is None:
+        if complex_out:
+            out = torch.empty(ndir, H, L, dtype=torch.complex64, device=log_re.device)
+        else:
+            out = torch.empty(ndir, H, L, dtype=torch.float32, device=log_re.device)
+    o = _dev_f32(out, "out")
+    ws, nbytes = _workspace(OP_GEN, shape, workspace, log_re.device)
+    check(lib().dssm_gen_kernel(ctypes.byref(p), ctypes.byref(shape), int(bool(complex_out)),
+                                o.data_ptr(), ws.data_ptr(), nbytes, _stream(stream)))
+    del keep
+    return out
+
+
+def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream):
+    torch = _torch()
+    uu = _dev_f32(u, "u")
+    if uu.dim() != 3:
+        raise ValueError("u must be [B, H, L]")
+    B, H, L = uu.shape
+    ndir = 2 if bidirectional else 1
+    N = log_re.shape[-1]
+    shape = Shape(B, H, N, L, int(bool(bidirectional)))
+    p, keep = _params(log_re, log_im, W, D, ndir, H, N)
+    if y is None:
+        y = torch.empty_like(uu)
+    yy = _dev_f32(y, "y")
+    ws, nbytes = _workspace(op, shape, workspace, uu.device)
+    check(fn(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape), yy.data_ptr(), ws.data_ptr(),
+             nbytes, _stream(stream)))
+    del keep
+    return y
+
+
+def forward_fft(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace=None, stream=None):
+    """Layer forward by the FFT convolution view.  u [B,H,L] f32 -> y [B,H,L]."""
+    return _forward(lib().dssm_forward_fft, OP_FFT, u, log_re, log_im, W, D, bidirectional, y,
+                    workspace, stream)
+
+
+def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace=None, stream=None):
+    """Layer forward by the recurrence (scan) view.  u [B,H,L] f32 -> y [B,H,L]."""
+    return _forward(lib().dssm_forward_scan, OP_SCAN, u, log_re, log_im, W, D, bidirectional, y,
+                    workspace, stream)

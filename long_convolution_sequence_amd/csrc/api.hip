@@ -1,0 +1,244 @@
+// Host entry points of libdssm.so (C ABI declared in include/dssm.h):
+// argument validation, workspace carving and kernel launches on the caller's
+// stream.  No device memory is allocated here.
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dssm.h"
+#include "dssm_internal.h"
+
+using namespace dssm;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DSSM_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DSSM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DSSM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxN = 4096;
+constexpr int kMaxLScan = 1 << 24;
+constexpr int kMaxFFTL = 1 << kMaxLog2M;
+constexpr int kMaxGrid = 65535;
+
+// Validate a shape for `op`; on success *empty tells whether there is no work.
+int check_shape(int op, const dssm_shape* s, bool* empty) {
+  if (!s) return fail(DSSM_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 0 || s->H < 0 || s->L < 0)
+    return fail(DSSM_ERR_INVALID_ARG, "negative dimension (B=%d H=%d L=%d)", s->B, s->H, s->L);
+  if (s->N < 1) return fail(DSSM_ERR_INVALID_ARG, "N must be >= 1 (got %d)", s->N);
+  if (s->bidirectional != 0 && s->bidirectional != 1)
+    return fail(DSSM_ERR_INVALID_ARG, "bidirectional must be 0 or 1 (got %d)", s->bidirectional);
+  if (op != DSSM_OP_GEN && op != DSSM_OP_FFT && op != DSSM_OP_SCAN)
+    return fail(DSSM_ERR_INVALID_ARG, "unknown op %d", op);
+  const int ndir = 1 + s->bidirectional;
+  if (s->N > kMaxN) return fail(DSSM_ERR_UNSUPPORTED, "N=%d exceeds %d", s->N, kMaxN);
+  if ((long)s->H * ndir > kMaxGrid)
+    return fail(DSSM_ERR_UNSUPPORTED, "H*ndir=%ld exceeds %d", (long)s->H * ndir, kMaxGrid);
+  if (s->L > kMaxLScan) return fail(DSSM_ERR_UNSUPPORTED, "L=%d exceeds %d", s->L, kMaxLScan);
+  if (op == DSSM_OP_FFT && s->L > kMaxFFTL)
+    return fail(DSSM_ERR_UNSUPPORTED, "FFT path needs L <= %d (got %d); use the scan path",
+                kMaxFFTL, s->L);
+  if ((long)s->B * s->H * s->L > (1L << 40))
+    return fail(DSSM_ERR_UNSUPPORTED, "B*H*L too large");
+  const bool no_rows = (op == DSSM_OP_GEN) ? false : (s->B == 0);
+  *empty = no_rows || s->H == 0 || s->L == 0;
+  return DSSM_OK;
+}
+
+// D is read by the forward calls only (dssm_gen_kernel ignores it).
+int check_params(const dssm_dlr_params* p, bool need_d) {
+  if (!p) return fail(DSSM_ERR_INVALID_ARG, "params is NULL");
+  if (!p->log_re || !p->log_im || !p->W || (need_d && !p->D))
+    return fail(DSSM_ERR_INVALID_ARG, "a parameter pointer is NULL");
+  if (!aligned16(p->log_re) || !aligned16(p->log_im) || !aligned16(p->W) ||
+      (need_d && !aligned16(p->D)))
+    return fail(DSSM_ERR_INVALID_ARG, "parameter pointers must be 16-byte aligned");
+  return DSSM_OK;
+}
+
+// Workspace layout, every region aligned to 256 bytes.
+struct Layout {
+  size_t pw = 0, anchor = 0, reK = 0, spec = 0, deff = 0, consts = 0, carry = 0, total = 0;
+};
+
+Layout layout(int op, const dssm_shape* s) {
+  Layout l;
+  const size_t ndh = (size_t)(1 + s->bidirectional) * s->H;
+  const size_t N = s->N, L = s->L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  if (op == DSSM_OP_GEN || op == DSSM_OP_FFT) {
+    const size_t Q = (L + kAnchor - 1) / kAnchor;
+    l.pw = take(ndh * N * kAnchor * sizeof(float2));
+    l.anchor = take(ndh * N * Q * sizeof(float2));
+  }
+  if (op == DSSM_OP_FFT) {
+    const size_t M = (size_t)1 << fft_log2m(s->L);
+    l.reK = take(ndh * L * sizeof(float));
+    l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
+    l.deff = take((size_t)s->H * sizeof(float));
+  }
+  if (op == DSSM_OP_SCAN) {
+    const ScanPlan plan = scan_plan(s->B, s->L);
+    l.consts = take(ndh * N * plan.nconst * sizeof(float));
+    l.carry = take((size_t)s->B * s->H * N * sizeof(float2));
+  }
+  l.total = off;
+  return l;
+}
+
+int check_ws(int op, const dssm_shape* s, void* ws, size_t ws_bytes, Layout* l) {
+  *l = layout(op, s);
+  if (ws_bytes < l->total)
+    return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, l->total);
+  if (l->total > 0 && !ws) return fail(DSSM_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(DSSM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return DSSM_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Enqueue the table and generator kernels: Re K (or complex K) into K.
+int run_gen(const dssm_dlr_params* p, const dssm_shape* s, int complex_out, float* K, void* ws,
+            const Layout& l, hipStream_t st) {
+  const int ndh = (1 + s->bidirectional) * s->H;
+  GenTables t;
+  t.pw = at<float2>(ws, l.pw);
+  t.anchor = at<float2>(ws, l.anchor);
+  t.Q = (s->L + kAnchor - 1) / kAnchor;
+  int rc = hip_check(launch_gen_tables(p->log_re, p->log_im, p->W, ndh, s->N, s->L, t, st),
+                     "gen_tables launch");
+  if (rc) return rc;
+  return hip_check(launch_gen_kernel(t, ndh, s->N, s->L, complex_out, K, st), "gen launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int dssm_version(void) { return DSSM_VERSION; }
+
+const char* dssm_status_string(int status) {
+  switch (status) {
+    case DSSM_OK: return "ok";
+    case DSSM_ERR_INVALID_ARG: return "invalid argument";
+    case DSSM_ERR_UNSUPPORTED: return "unsupported";
+    case DSSM_ERR_WORKSPACE: return "workspace too small";
+    case DSSM_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* dssm_last_error(void) { return g_last_error.c_str(); }
+
+int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes) {
+  if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
+  bool empty = false;
+  int rc = check_shape(op, s, &empty);
+  if (rc) return rc;
+  *bytes = empty ? 0 : layout(op, s).total;
+  return ok();
+}
+
+int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_out, float* K,
+                    void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_GEN, s, &empty);
+  if (rc) return rc;
+  if (complex_out != 0 && complex_out != 1)
+    return fail(DSSM_ERR_INVALID_ARG, "complex_out must be 0 or 1");
+  if (empty) return ok();
+  if ((rc = check_params(p, false))) return rc;
+  if (!K || !aligned16(K)) return fail(DSSM_ERR_INVALID_ARG, "K is NULL or not 16-byte aligned");
+  Layout l;
+  if ((rc = check_ws(DSSM_OP_GEN, s, ws, ws_bytes, &l))) return rc;
+  if ((rc = run_gen(p, s, complex_out, K, ws, l, static_cast<hipStream_t>(stream)))) return rc;
+  return ok();
+}
+
+int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
+                     void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_FFT, s, &empty);
+  if (rc) return rc;
+  if (empty) return ok();
+  if ((rc = check_params(p, true))) return rc;
+  if (!u || !y || !aligned16(u) || !aligned16(y))
+    return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
+  if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
+  Layout l;
+  if ((rc = check_ws(DSSM_OP_FFT, s, ws, ws_bytes, &l))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ndir = 1 + s->bidirectional;
+  float* reK = at<float>(ws, l.reK);
+  if ((rc = run_gen(p, s, 0, reK, ws, l, st))) return rc;
+  const int log2m = fft_log2m(s->L);
+  float2* spec = at<float2>(ws, l.spec);
+  float* deff = at<float>(ws, l.deff);
+  if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, deff, st),
+                      "spectrum launch")))
+    return rc;
+  if ((rc = hip_check(launch_conv(u, spec, deff, s->B, s->H, s->L, log2m, y, st), "conv launch")))
+    return rc;
+  return ok();
+}
+
+int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
+                      void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_SCAN, s, &empty);
+  if (rc) return rc;
+  if (empty) return ok();
+  if ((rc = check_params(p, true))) return rc;
+  if (!u || !y || !aligned16(u) || !aligned16(y))
+    return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
+  if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
+  Layout l;
+  if ((rc = check_ws(DSSM_OP_SCAN, s, ws, ws_bytes, &l))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ndir = 1 + s->bidirectional;
+  const ScanPlan plan = scan_plan(s->B, s->L);
+  float* consts = at<float>(ws, l.consts);
+  if ((rc = hip_check(launch_scan_consts(p->log_re, p->log_im, p->W, ndir * s->H, s->N, plan,
+                                         consts, st),
+                      "scan consts launch")))
+    return rc;
+  if ((rc = hip_check(launch_scan(u, consts, p->D, s->B, s->H, s->N, s->L, ndir, plan, y, st,
+                                  at<float2>(ws, l.carry)),
+                      "scan launch")))
+    return rc;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal declarations shared by the host entry points (api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dssm {
+
+// Anchor spacing of the kernel generator: K[64 q + r] is built from
+// lambda^r (r < 64) and the anchor W lambda^(64 q).
+constexpr int kAnchor = 64;
+// Largest FFT half-length: the circle has length 2M <= 32768, the complex
+// half-length transform holds M <= 16384 points in one workgroup's LDS.
+constexpr int kMaxLog2M = 14;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Kernel generation (eig_gen.hip)
+// ---------------------------------------------------------------------------
+struct GenTables {
+  float2* pw;      // [ndir*H, N, 64]  lambda^r, r < 64
+  float2* anchor;  // [ndir*H, N, Q]   W lambda^(64 q), q < Q = ceil(L/64)
+  int Q;
+};
+
+// Fill pw and anchor from the DLR parameters (float64 arithmetic).
+hipError_t launch_gen_tables(const float* log_re, const float* log_im, const float* W,
+                             int ndh, int N, int L, const GenTables& t, hipStream_t st);
+
+// K[dh, j] = sum_n anchor[dh,n,j/64] * pw[dh,n,j%64] for j < L.
+// complex_out = 0: Re K into float [ndh, L]; 1: (Re, Im) into float2 [ndh, L].
+hipError_t launch_gen_kernel(const GenTables& t, int ndh, int N, int L, int complex_out,
+                             float* K, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// FFT convolution (fft.hip)
+// ---------------------------------------------------------------------------
+// Spectrum tables: spec[h, half, M] float2, position-ordered (the order the
+// in-place decimation-in-frequency passes leave the bins in), scaled by
+// 1/(2M).  half 0 holds the even bins of the 2M-point transform of the
+// zero-padded real kernel, half 1 the odd bins.  For ndir = 2 the backward
+// kernel enters conjugated.  Also writes Deff[h] = sum_d D[d,h].
+hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
+                           float2* spec, float* Deff, hipStream_t st);
+
+// y[b,h,:L] = first L samples of the 2M-circular convolution of u[b,h,:] with
+// the kernel whose spectrum is spec[h], plus Deff[h] u.
+hipError_t launch_conv(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
+                       int log2m, float* y, hipStream_t st);
+
+int fft_log2m(int L);  // log2 of M = max(16, next power of two >= L)
+
+// ---------------------------------------------------------------------------
+// Recurrence scan (scan.hip)
+// ---------------------------------------------------------------------------
+struct ScanPlan {
+  int seg;        // time steps per lane
+  int lpc;        // lanes per channel (power of two, <= 256)
+  int cpw;        // channels per wave (64 / lpc when lpc < 64, else 1)
+  int waves;      // waves per workgroup
+  int tile;       // time steps covered per tile = seg * lpc
+  int ntile;      // tiles per channel
+  int nconst;     // floats per (d,h,n) in the constant table
+};
+ScanPlan scan_plan(int B, int L);
+
+// Per-(d,h,n) constants for the scan (float64 arithmetic, rounded once).
+hipError_t launch_scan_consts(const float* log_re, const float* log_im, const float* W,
+                             int ndh, int N, const ScanPlan& plan, float* consts, hipStream_t st);
+
+// carry: [B, H, N] float2 scratch, used when plan.ntile > 1.
+hipError_t launch_scan(const float* u, const float* consts, const float* D, int B, int H, int N,
+                       int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
+                       float2* carry);
+
+}  // namespace dssm

@@ -1,0 +1,573 @@
+// Causal long convolution of a DLR bank by FFT, staged in LDS.
+//
+// What is computed ("Simplifying and Understanding State Space Models with
+// Diagonal Linear RNNs", section 2: the convolution y = K * u is a Toeplitz
+// mat-vec, computed as a circulant mat-vec of size 2L on zero-padded
+// operands; "The Annotated S4", Part 1, "Training SSMs: the convolutional
+// representation": pad to twice the length, transform, multiply, invert,
+// keep the first L samples):
+//
+//   y[b,h,:L] = ( IDFT_2M( DFT_2M(pad u[b,h]) * DFT_2M(pad Re K[h]) ) )[:L]
+//               + D[h] u[b,h]
+//
+// with M = max(16, next power of two >= L), so 2M >= 2L and no wrap-around
+// reaches the first L outputs.
+//
+// How (MI355X design):
+// * Two batch rows of the same channel ride in one complex sequence
+//   z = u[b1] + i u[b2].  The kernel spectrum is Hermitian and the product is
+//   linear, so Re/Im of the inverse transform are the two real outputs; no
+//   even/odd untangling step is needed.
+// * The 2M-point transform of a sequence that is zero on its upper half splits
+//   exactly into two M-point transforms: the even bins are DFT_M(z) and the
+//   odd bins DFT_M(z * t) with t[n] = exp(-i pi n / M).  The inverse is the sum
+//   of the two M-point inverses, the odd one multiplied by conj(t).  So a
+//   workgroup only ever holds M complex points (<= 128 KiB + padding of LDS).
+// * Each M-point transform is a sequence of in-place decimation-in-frequency
+//   passes (radix 16, last pass radix 2/4/8/16) with 16 points per thread in
+//   registers and one LDS exchange between passes.  The bins are left in the
+//   passes' own (digit-reversed) order; the kernel spectrum is stored in the
+//   same order, so the pointwise product happens in registers right after the
+//   last forward pass and the inverse (decimation-in-time, the passes run
+//   backwards with conjugate twiddles) starts from the same registers and ends
+//   in natural order, ready for a coalesced store.
+// * Twiddles: one table value exp(-2 pi i m / S) per thread and pass, powers by
+//   a depth <= 5 product tree; the table (exact float32 roundings of float64
+//   values) is built into the library.
+#include <algorithm>
+
+#include "dssm_internal.h"
+#include "twiddle_table.inc"
+
+namespace dssm {
+namespace {
+
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+
+// a * exp(-+ 2 pi i k / 16): forward (INV = false) multiplies by exp(-i theta),
+// inverse by exp(+i theta), theta = 2 pi k / 16.  Exact for multiples of pi/2.
+template <int K, bool INV>
+__device__ __forceinline__ float2 rot16(float2 a) {
+  constexpr int k = ((K % 16) + 16) % 16;
+  constexpr float C1 = 0.92387953251128674f;  // cos(pi/8)
+  constexpr float S1 = 0.38268343236508977f;  // sin(pi/8)
+  constexpr float R = 0.70710678118654752f;   // sqrt(2)/2
+  // (c, s) = (cos theta, sin theta)
+  constexpr float cs[16][2] = {{1, 0},   {C1, S1},  {R, R},     {S1, C1},  {0, 1},   {-S1, C1},
+                               {-R, R},  {-C1, S1}, {-1, 0},    {-C1, -S1}, {-R, -R}, {-S1, -C1},
+                               {0, -1},  {S1, -C1}, {R, -R},    {C1, -S1}};
+  constexpr float c = cs[k][0];
+  constexpr float s = INV ? cs[k][1] : -cs[k][1];
+  if constexpr (k == 0) {
+    return a;
+  } else if constexpr (k == 8) {
+    return make_float2(-a.x, -a.y);
+  } else if constexpr (k == 4 || k == 12) {
+    // multiply by (0 + i s), s = +-1
+    if constexpr (s > 0) return make_float2(-a.y, a.x);
+    else return make_float2(a.y, -a.x);
+  } else {
+    return make_float2(fmaf(a.x, c, -a.y * s), fmaf(a.x, s, a.y * c));
+  }
+}
+
+// cos and sin of pi k / 32 for 0 <= k <= 8 (the rest follow by symmetry).
+__device__ constexpr float kCos32[9] = {1.0f, 0.99518472667219693f, 0.98078528040323043f,
+                                        0.95694033573220882f, 0.92387953251128674f,
+                                        0.88192126434835505f, 0.83146961230254524f,
+                                        0.77301045336273699f, 0.70710678118654752f};
+__device__ constexpr float kSin32[9] = {0.0f, 0.09801714032956060f, 0.19509032201612825f,
+                                        0.29028467725446233f, 0.38268343236508978f,
+                                        0.47139673682599764f, 0.55557023301960218f,
+                                        0.63439328416364549f, 0.70710678118654752f};
+constexpr float cos_pi32(int k) {  // cos(pi k / 32), 0 <= k < 32
+  return k <= 8 ? kCos32[k] : k <= 16 ? kSin32[16 - k] : -cos_pi32(32 - k);
+}
+constexpr float sin_pi32(int k) {  // sin(pi k / 32), 0 <= k < 32
+  return k <= 8 ? kSin32[k] : k <= 16 ? kCos32[16 - k] : sin_pi32(32 - k);
+}
+
+// a * exp(-+ i pi K / 32), K in [0, 32): the fixed part of the odd-bin
+// pre-twiddle.  Exact for K = 0 and K = 16.
+template <int K, bool INV>
+__device__ __forceinline__ float2 rotpi32(float2 a) {
+  static_assert(K >= 0 && K < 32, "rotpi32 index");
+  if constexpr (K == 0) {
+    return a;
+  } else if constexpr (K == 16) {
+    return INV ? make_float2(-a.y, a.x) : make_float2(a.y, -a.x);
+  } else {
+    constexpr float c = cos_pi32(K);
+    constexpr float s = INV ? sin_pi32(K) : -sin_pi32(K);
+    return make_float2(fmaf(a.x, c, -a.y * s), fmaf(a.x, s, a.y * c));
+  }
+}
+
+// In-place DFT of 2, 4, 8 or 16 points held in registers (natural order in
+// and out).  Forward kernel exp(-2 pi i n k / R); INV uses exp(+...).
+template <bool INV>
+__device__ __forceinline__ void dft2(float2& a, float2& b) {
+  const float2 t = a;
+  a = cadd(t, b);
+  b = csub(t, b);
+}
+
+template <bool INV>
+__device__ __forceinline__ void dft4(float2& a0, float2& a1, float2& a2, float2& a3) {
+  const float2 t0 = cadd(a0, a2), t1 = csub(a0, a2), t2 = cadd(a1, a3), t3 = csub(a1, a3);
+  a0 = cadd(t0, t2);
+  a2 = csub(t0, t2);
+  if (!INV) {  // t1 -+ i t3
+    a1 = make_float2(t1.x + t3.y, t1.y - t3.x);
+    a3 = make_float2(t1.x - t3.y, t1.y + t3.x);
+  } else {
+    a1 = make_float2(t1.x - t3.y, t1.y + t3.x);
+    a3 = make_float2(t1.x + t3.y, t1.y - t3.x);
+  }
+}
+
+// 8 points: n = 2 n1 + n2 (n1 < 4, n2 < 2), k = k1 + 4 k2.
+template <bool INV>
+__device__ __forceinline__ void dft8(float2* x) {
+  float2 y0[4] = {x[0], x[2], x[4], x[6]};
+  float2 y1[4] = {x[1], x[3], x[5], x[7]};
+  dft4<INV>(y0[0], y0[1], y0[2], y0[3]);
+  dft4<INV>(y1[0], y1[1], y1[2], y1[3]);
+  y1[1] = rot16<2, INV>(y1[1]);
+  y1[2] = rot16<4, INV>(y1[2]);
+  y1[3] = rot16<6, INV>(y1[3]);
+#pragma unroll
+  for (int k1 = 0; k1 < 4; ++k1) {
+    x[k1] = cadd(y0[k1], y1[k1]);
+    x[k1 + 4] = csub(y0[k1], y1[k1]);
+  }
+}
+
+// 16 points: n = 4 n1 + n2, k = k1 + 4 k2 (radix 4 x 4 with inner twiddles).
+template <bool INV>
+__device__ __forceinline__ void dft16(float2* x) {
+  float2 y[4][4];  // y[n2][k1]
+#pragma unroll
+  for (int n2 = 0; n2 < 4; ++n2) {
+    y[n2][0] = x[n2];
+    y[n2][1] = x[4 + n2];
+    y[n2][2] = x[8 + n2];
+    y[n2][3] = x[12 + n2];
+    dft4<INV>(y[n2][0], y[n2][1], y[n2][2], y[n2][3]);
+  }
+  y[1][1] = rot16<1, INV>(y[1][1]);
+  y[1][2] = rot16<2, INV>(y[1][2]);
+  y[1][3] = rot16<3, INV>(y[1][3]);
+  y[2][1] = rot16<2, INV>(y[2][1]);
+  y[2][2] = rot16<4, INV>(y[2][2]);
+  y[2][3] = rot16<6, INV>(y[2][3]);
+  y[3][1] = rot16<3, INV>(y[3][1]);
+  y[3][2] = rot16<6, INV>(y[3][2]);
+  y[3][3] = rot16<9, INV>(y[3][3]);
+#pragma unroll
+  for (int k1 = 0; k1 < 4; ++k1) {
+    dft4<INV>(y[0][k1], y[1][k1], y[2][k1], y[3][k1]);
+    x[k1] = y[0][k1];
+    x[k1 + 4] = y[1][k1];
+    x[k1 + 8] = y[2][k1];
+    x[k1 + 12] = y[3][k1];
+  }
+}
+
+template <int R, bool INV>
+__device__ __forceinline__ void dftR(float2* x) {
+  if constexpr (R == 16) {
+    dft16<INV>(x);
+  } else if constexpr (R == 8) {
+    dft8<INV>(x);
+  } else if constexpr (R == 4) {
+    dft4<INV>(x[0], x[1], x[2], x[3]);
+  } else {
+    static_assert(R == 2, "radix");
+    dft2<INV>(x[0], x[1]);
+  }
+}
+
+// v[q] *= w^q for q = 1..15 (w conjugated when CONJ).
+template <bool CONJ>
+__device__ __forceinline__ void twiddle16(float2* v, float2 w) {
+  // Opaque to the optimiser: the powers are recomputed at every use instead of
+  // being shared between the forward and inverse passes and kept live (they
+  // would cost 30 registers per pass for the whole kernel).
+  asm volatile("" : "+v"(w.x), "+v"(w.y));
+  if (CONJ) w = cconj(w);
+  float2 p[16];
+  p[1] = w;
+  p[2] = cmul(w, w);
+  p[3] = cmul(p[2], w);
+  p[4] = cmul(p[2], p[2]);
+  p[8] = cmul(p[4], p[4]);
+  p[12] = cmul(p[8], p[4]);
+#pragma unroll
+  for (int a = 4; a <= 12; a += 4)
+#pragma unroll
+    for (int b = 1; b < 4; ++b) p[a + b] = cmul(p[a], p[b]);
+#pragma unroll
+  for (int q = 1; q < 16; ++q) v[q] = cmul(v[q], p[q]);
+}
+
+template <int LOG2M>
+struct Cfg {
+  static_assert(LOG2M >= 4 && LOG2M <= kMaxLog2M, "transform size");
+  static constexpr int M = 1 << LOG2M;
+  // points per thread: 32 for the largest size keeps the workgroup at 512
+  // threads so each may hold 256 registers; 16 otherwise
+  static constexpr int PT = (LOG2M >= 14) ? 32 : 16;
+  static constexpr int NB = PT / 16;                      // radix-16 butterflies per thread
+  static constexpr int T = M / PT;                        // threads per transform
+  static constexpr int NP = (LOG2M + 3) / 4;              // passes
+  static constexpr int RLAST = 1 << (LOG2M - 4 * (NP - 1));  // radix of the last pass
+  static constexpr int G = T >= 64 ? 1 : 64 / T;          // transforms per workgroup
+  static constexpr int WG = T * G;
+  static constexpr int LDSN = M + M / 16;                 // padded complex slots
+  static_assert(M % PT == 0 && T >= 1, "shape");
+};
+
+__device__ __forceinline__ int pad(int e) { return e + (e >> 4); }
+
+// Register r = 16 i + j of thread lt holds, in a non-last pass, element j of
+// butterfly beta = lt + i T: radix 16 on sub-transforms of size S = M >> 4p
+// with stride s = S / 16 -> position g S + m + j s, g = beta / s, m = beta % s.
+// In the last pass register r holds position PT lt + r.  The pass reads and
+// writes the same positions (in place).  LDS slot = pad(position); because s
+// divides 16 or is a multiple of 16 and m < s, pad(base + j s) =
+// pad(base) + j s + (j s >> 4): a base per butterfly, compile-time offsets.
+template <int LOG2M, int P>
+struct PassGeom {
+  using C = Cfg<LOG2M>;
+  static constexpr bool kLast = (P == C::NP - 1);
+  static constexpr int S = kLast ? C::RLAST : (C::M >> (4 * P));
+  static constexpr int s = kLast ? 1 : S / 16;
+  __device__ static __forceinline__ int m_of(int lt, int i) { return (lt + i * C::T) % s; }
+  __device__ static __forceinline__ int base(int lt, int i) {
+    const int beta = lt + i * C::T;
+    return (beta / s) * S + (beta % s);
+  }
+  __device__ static constexpr int off(int j) { return j * s + ((j * s) >> 4); }
+};
+
+template <int LOG2M, int P>
+__device__ __forceinline__ void lds_write(float2* lds, int lt, const float2* v) {
+  using C = Cfg<LOG2M>;
+  using G = PassGeom<LOG2M, P>;
+  if constexpr (G::kLast) {
+    float2* b = lds + pad(C::PT * lt);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) b[r + (r >> 4)] = v[r];
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+      float2* b = lds + pad(G::base(lt, i));
+#pragma unroll
+      for (int j = 0; j < 16; ++j) b[G::off(j)] = v[16 * i + j];
+    }
+  }
+}
+
+template <int LOG2M, int P>
+__device__ __forceinline__ void lds_read(const float2* lds, int lt, float2* v) {
+  using C = Cfg<LOG2M>;
+  using G = PassGeom<LOG2M, P>;
+  if constexpr (G::kLast) {
+    const float2* b = lds + pad(C::PT * lt);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = b[r + (r >> 4)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+      const float2* b = lds + pad(G::base(lt, i));
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[16 * i + j] = b[G::off(j)];
+    }
+  }
+}
+
+// Forward pass p on registers (butterflies, then output twiddles).
+template <int LOG2M, int P>
+__device__ __forceinline__ void fwd_pass(float2* v, int lt) {
+  using C = Cfg<LOG2M>;
+  using G = PassGeom<LOG2M, P>;
+  if constexpr (G::kLast) {
+#pragma unroll
+    for (int i = 0; i < C::PT; i += C::RLAST) dftR<C::RLAST, false>(v + i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+      dft16<false>(v + 16 * i);
+      twiddle16<false>(v + 16 * i, g_twiddle[G::m_of(lt, i) * (DSSM_TWN / G::S)]);
+    }
+  }
+}
+
+// Inverse of pass p (conjugate input twiddles, then inverse butterflies).
+template <int LOG2M, int P>
+__device__ __forceinline__ void inv_pass(float2* v, int lt) {
+  using C = Cfg<LOG2M>;
+  using G = PassGeom<LOG2M, P>;
+  if constexpr (G::kLast) {
+#pragma unroll
+    for (int i = 0; i < C::PT; i += C::RLAST) dftR<C::RLAST, true>(v + i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+      twiddle16<true>(v + 16 * i, g_twiddle[G::m_of(lt, i) * (DSSM_TWN / G::S)]);
+      dft16<true>(v + 16 * i);
+    }
+  }
+}
+
+// Forward transform.  On entry register r = 16 i + j holds the point
+// n(lt, r) = lt + T (i + j NB) (natural order); on exit register r holds the
+// bin at position PT lt + r.  All threads of the workgroup must call it
+// together (it contains barriers).
+template <int LOG2M, int P = 0>
+__device__ __forceinline__ void forward(float2* v, float2* lds, int lt) {
+  using C = Cfg<LOG2M>;
+  fwd_pass<LOG2M, P>(v, lt);
+  if constexpr (P + 1 < C::NP) {
+    lds_write<LOG2M, P>(lds, lt, v);
+    __syncthreads();
+    lds_read<LOG2M, P + 1>(lds, lt, v);
+    forward<LOG2M, P + 1>(v, lds, lt);
+  }
+}
+
+// Inverse transform (unnormalised): bins at the last pass's positions on
+// entry, points at n(lt, r) on exit.
+template <int LOG2M, int P = Cfg<LOG2M>::NP - 1>
+__device__ __forceinline__ void inverse(float2* v, float2* lds, int lt) {
+  inv_pass<LOG2M, P>(v, lt);
+  if constexpr (P > 0) {
+    lds_write<LOG2M, P>(lds, lt, v);
+    __syncthreads();
+    lds_read<LOG2M, P - 1>(lds, lt, v);
+    inverse<LOG2M, P - 1>(v, lds, lt);
+  }
+}
+
+// Natural-order index of register r (= 16 i + j) of thread lt.
+template <int LOG2M>
+__device__ __forceinline__ int nat(int lt, int r) {
+  using C = Cfg<LOG2M>;
+  return lt + C::T * ((r >> 4) + (r & 15) * C::NB);
+}
+
+// v[r] *= exp(-+ i pi n(lt, r) / M) = t[lt] * exp(-+ i pi (i + j NB) / PT).
+template <int LOG2M, bool INV, int R = 0>
+__device__ __forceinline__ void odd_twiddle_fixed(float2* v) {
+  using C = Cfg<LOG2M>;
+  if constexpr (R < C::PT) {
+    constexpr int k = ((R >> 4) + (R & 15) * C::NB) * (32 / C::PT);
+    v[R] = rotpi32<k, INV>(v[R]);
+    odd_twiddle_fixed<LOG2M, INV, R + 1>(v);
+  }
+}
+
+// Spectrum of the (bidirectional) kernel: one transform per (h, half).
+//   spec[h, half, pos] = ( F_f + conj(F_b) ) / (2M),
+//   F_d = DFT_M( pad(Re K[d,h]) * t^half ),  t[n] = exp(-i pi n / M).
+// The backward DLR is a correlation with Re K_b, whose spectrum is the
+// conjugate (no wrap-around reaches the first L outputs on a 2M circle).
+template <int LOG2M>
+__global__ __launch_bounds__(Cfg<LOG2M>::WG) void spectrum_kernel(const float* __restrict__ reK,
+                                                                  const float* __restrict__ D,
+                                                                  int ndir, int H, int L,
+                                                                  float2* __restrict__ spec,
+                                                                  float* __restrict__ Deff) {
+  using C = Cfg<LOG2M>;
+  __shared__ float2 lds_all[C::G * C::LDSN];
+  const int lt = threadIdx.x % C::T;
+  const int gi = threadIdx.x / C::T;
+  float2* lds = lds_all + gi * C::LDSN;
+  const int prob = blockIdx.x * C::G + gi;
+  const bool active = prob < 2 * H;
+  const int h = active ? (prob >> 1) : 0;
+  const int half = prob & 1;
+
+  float2 acc[C::PT];
+  for (int d = 0; d < ndir; ++d) {
+    float2 v[C::PT];
+    const float* k = reK + ((size_t)d * H + h) * L;
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) {
+      const int n = nat<LOG2M>(lt, r);
+      v[r] = make_float2((active && n < L) ? k[n] : 0.f, 0.f);
+    }
+    if (half) {
+      const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * C::M))];
+      odd_twiddle_fixed<LOG2M, false>(v);
+#pragma unroll
+      for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
+    }
+    if (d > 0) __syncthreads();  // the previous direction's last reads are done
+    forward<LOG2M>(v, lds, lt);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) acc[r] = (d == 0) ? v[r] : cadd(acc[r], cconj(v[r]));
+  }
+  if (!active) return;
+  const float scale = 1.0f / (2.0f * (float)C::M);
+  float2* out = spec + ((size_t)h * 2 + half) * C::M + C::PT * lt;
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) out[r] = cscale(acc[r], scale);
+  if (half == 0 && lt == 0) {
+    float sum = 0.f;
+    for (int d = 0; d < ndir; ++d) sum += D[(size_t)d * H + h];
+    Deff[h] = sum;
+  }
+}
+
+// Convolution of a pair of batch rows (b1 = 2 pr, b2 = 2 pr + 1) of channel h.
+// u is deliberately not __restrict__: the odd half re-reads it after the
+// barriers of the even half instead of keeping the first read live.
+template <int LOG2M>
+__global__ __launch_bounds__(Cfg<LOG2M>::WG) void conv_kernel(const float* u,
+                                                              const float2* __restrict__ spec,
+                                                              const float* __restrict__ Deff,
+                                                              int B, int H, int L, int npairs,
+                                                              float* __restrict__ y) {
+  using C = Cfg<LOG2M>;
+  __shared__ float2 lds_all[C::G * C::LDSN];
+  const int lt = threadIdx.x % C::T;
+  const int gi = threadIdx.x / C::T;
+  float2* lds = lds_all + gi * C::LDSN;
+  const int prob = blockIdx.x * C::G + gi;
+  const bool active = prob < H * npairs;
+  const int h = active ? prob / npairs : 0;
+  const int pr = active ? prob % npairs : 0;
+  const int b1 = 2 * pr, b2 = 2 * pr + 1;
+  const bool has2 = active && b2 < B;
+  const float* u1 = u + ((size_t)b1 * H + h) * L;
+  const float* u2 = u + ((size_t)(has2 ? b2 : b1) * H + h) * L;
+  const float dsk = active ? Deff[h] : 0.f;
+
+  auto load_pair = [&](float2* v) {
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) {
+      const int n = nat<LOG2M>(lt, r);
+      float a = 0.f, b = 0.f;
+      if (active && n < L) {
+        a = u1[n];
+        if (has2) b = u2[n];
+      }
+      v[r] = make_float2(a, b);
+    }
+  };
+
+  float2 acc[C::PT];
+  float2 v[C::PT];
+  load_pair(v);
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) acc[r] = cscale(v[r], dsk);
+
+  // even bins
+  {
+    forward<LOG2M>(v, lds, lt);
+    const float2* sp = spec + ((size_t)h * 2 + 0) * C::M + C::PT * lt;
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], sp[r]);
+    inverse<LOG2M>(v, lds, lt);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) acc[r] = cadd(acc[r], v[r]);
+  }
+  // odd bins: pre-multiply by t[n] = exp(-i pi n / M), post-multiply by conj(t[n])
+  {
+    load_pair(v);
+    const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * C::M))];
+    odd_twiddle_fixed<LOG2M, false>(v);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
+    forward<LOG2M>(v, lds, lt);
+    const float2* sp = spec + ((size_t)h * 2 + 1) * C::M + C::PT * lt;
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], sp[r]);
+    inverse<LOG2M>(v, lds, lt);
+    const float2 tlc = cconj(g_twiddle[lt * (DSSM_TWN / (2 * C::M))]);
+    odd_twiddle_fixed<LOG2M, true>(v);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) acc[r] = cadd(acc[r], cmul(v[r], tlc));
+  }
+
+  if (!active) return;
+  float* y1 = y + ((size_t)b1 * H + h) * L;
+  float* y2 = y + ((size_t)b2 * H + h) * L;
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) {
+    const int n = nat<LOG2M>(lt, r);
+    if (n < L) {
+      y1[n] = acc[r].x;
+      if (has2) y2[n] = acc[r].y;
+    }
+  }
+}
+
+template <int LOG2M>
+hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, int L, float2* spec,
+                           float* Deff, hipStream_t st) {
+  using C = Cfg<LOG2M>;
+  const int nprob = 2 * H;
+  const int nblk = (nprob + C::G - 1) / C::G;
+  hipLaunchKernelGGL(spectrum_kernel<LOG2M>, dim3(nblk), dim3(C::WG), 0, st, reK, D, ndir, H, L,
+                     spec, Deff);
+  return hipGetLastError();
+}
+
+template <int LOG2M>
+hipError_t conv_launch(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
+                       float* y, hipStream_t st) {
+  using C = Cfg<LOG2M>;
+  const int npairs = (B + 1) / 2;
+  const long nprob = (long)H * npairs;
+  const long nblk = (nprob + C::G - 1) / C::G;
+  hipLaunchKernelGGL(conv_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), 0, st, u, spec, Deff,
+                     B, H, L, npairs, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int fft_log2m(int L) {
+  int l = 4;
+  while ((1 << l) < L) ++l;
+  return l;
+}
+
+#define DSSM_FFT_CASES(X) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14)
+
+hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
+                           float2* spec, float* Deff, hipStream_t st) {
+  switch (log2m) {
+#define X(n) \
+  case n:    \
+    return spectrum_launch<n>(reK, D, ndir, H, L, spec, Deff, st);
+    DSSM_FFT_CASES(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
+                       int log2m, float* y, hipStream_t st) {
+  switch (log2m) {
+#define X(n) \
+  case n:    \
+    return conv_launch<n>(u, spec, Deff, B, H, L, y, st);
+    DSSM_FFT_CASES(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dssm

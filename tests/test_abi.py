@@ -1,0 +1,142 @@
+"""C-ABI contract of libdssm.so, checked on the host (no kernel is launched):
+every symbol include/dssm.h declares is exported, and every invalid call is
+rejected by host-side validation with the documented status code."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_convolution_sequence_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dssm.h")
+
+FAKE = 1 << 20  # an aligned, never-dereferenced device address
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dssm_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(bd.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_matches_header():
+    m = re.search(r"#define DSSM_VERSION (\d+)", open(HEADER).read())
+    assert bd.lib().dssm_version() == int(m.group(1))
+
+
+def test_status_strings():
+    L = bd.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.dssm_status_string(code)
+    assert L.dssm_status_string(7) == b"unknown status"
+
+
+def _ws(op, B, H, N, L, bi=0):
+    s = bd.Shape(B, H, N, L, bi)
+    out = ctypes.c_size_t(123)
+    rc = bd.lib().dssm_workspace_size(op, ctypes.byref(s), ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("op", [bd.OP_GEN, bd.OP_FFT, bd.OP_SCAN])
+def test_workspace_size_invalid(op):
+    assert _ws(op, -1, 2, 4, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _ws(op, 1, -2, 4, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _ws(op, 1, 2, 0, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _ws(op, 1, 2, 4, -8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _ws(op, 1, 2, 4, 8, 2)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _ws(op, 1, 2, 5000, 8)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _ws(op, 1, 70000, 4, 8)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert bd.lib().dssm_workspace_size(op, None, ctypes.byref(ctypes.c_size_t())) == bd.DSSM_ERR_INVALID_ARG
+    s = bd.Shape(1, 2, 4, 8, 0)
+    assert bd.lib().dssm_workspace_size(op, ctypes.byref(s), None) == bd.DSSM_ERR_INVALID_ARG
+    assert bd.lib().dssm_last_error()
+
+
+def test_workspace_size_limits_and_empty():
+    assert _ws(9, 1, 1, 1, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _ws(bd.OP_FFT, 1, 1, 1, 16384) [0] == 0
+    assert _ws(bd.OP_FFT, 1, 1, 1, 16385)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _ws(bd.OP_SCAN, 1, 1, 1, 1 << 20)[0] == 0
+    assert _ws(bd.OP_SCAN, 1, 1, 1, (1 << 24) + 1)[0] == bd.DSSM_ERR_UNSUPPORTED
+    for op in (bd.OP_FFT, bd.OP_SCAN):
+        assert _ws(op, 0, 4, 4, 8) == (0, 0)
+        assert _ws(op, 2, 0, 4, 8) == (0, 0)
+        assert _ws(op, 2, 4, 4, 0) == (0, 0)
+    assert _ws(bd.OP_GEN, 0, 4, 4, 8)[1] > 0  # B is ignored by the generator
+    rc, n = _ws(bd.OP_FFT, 4, 128, 64, 16384)
+    assert rc == 0 and n % 256 == 0 and n > 0
+    rc2, n2 = _ws(bd.OP_FFT, 4, 128, 64, 16384, 1)
+    assert rc2 == 0 and n2 > n
+
+
+def _params(bad=None):
+    vals = dict(log_re=FAKE, log_im=FAKE + 4096, W=FAKE + 8192, D=FAKE + 12288)
+    if bad:
+        vals.update(bad)
+    return bd.DLRParams(vals["log_re"], vals["log_im"], vals["W"], vals["D"])
+
+
+def _call(fn, params, shape, u=FAKE * 2, y=FAKE * 3, ws=FAKE * 4, nbytes=1 << 40):
+    return fn(u, ctypes.byref(params) if params is not None else None,
+              ctypes.byref(shape) if shape is not None else None, y, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("name", ["dssm_forward_fft", "dssm_forward_scan"])
+def test_forward_rejects_bad_arguments(name):
+    fn = getattr(bd.lib(), name)
+    good = bd.Shape(2, 3, 4, 32, 0)
+    assert _call(fn, _params(), None) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, None, good) == bd.DSSM_ERR_INVALID_ARG
+    for k in ("log_re", "log_im", "W", "D"):
+        assert _call(fn, _params({k: None}), good) == bd.DSSM_ERR_INVALID_ARG
+        assert _call(fn, _params({k: FAKE + 4}), good) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), good, u=None) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), good, y=None) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), good, u=FAKE + 8) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), good, u=FAKE * 2, y=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), good, nbytes=16) == bd.DSSM_ERR_WORKSPACE
+    assert _call(fn, _params(), good, ws=None) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), good, ws=FAKE * 4 + 64) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), bd.Shape(2, 3, 4, 32, 3)) == bd.DSSM_ERR_INVALID_ARG
+    # empty problems are valid no-ops (nothing is launched, nothing is read)
+    assert _call(fn, None, bd.Shape(0, 3, 4, 32, 0)) == 0
+    assert _call(fn, None, bd.Shape(2, 3, 4, 0, 1)) == 0
+
+
+def test_fft_rejects_long_sequences():
+    fn = bd.lib().dssm_forward_fft
+    assert _call(fn, _params(), bd.Shape(1, 1, 4, 16385, 0)) == bd.DSSM_ERR_UNSUPPORTED
+    assert b"scan" in bd.lib().dssm_last_error()
+
+
+def test_gen_rejects_bad_arguments():
+    fn = bd.lib().dssm_gen_kernel
+    good = bd.Shape(1, 3, 4, 32, 0)
+    p = _params({"D": None})  # D is not needed by the generator
+    assert fn(ctypes.byref(p), ctypes.byref(good), 2, FAKE, FAKE * 4, 1 << 40, None) == bd.DSSM_ERR_INVALID_ARG
+    assert fn(ctypes.byref(p), ctypes.byref(good), 0, None, FAKE * 4, 1 << 40, None) == bd.DSSM_ERR_INVALID_ARG
+    assert fn(ctypes.byref(p), ctypes.byref(good), 0, FAKE, FAKE * 4, 8, None) == bd.DSSM_ERR_WORKSPACE
+    assert fn(ctypes.byref(_params({"W": None})), ctypes.byref(good), 0, FAKE, FAKE * 4, 1 << 40,
+              None) == bd.DSSM_ERR_INVALID_ARG
+    assert fn(ctypes.byref(p), ctypes.byref(bd.Shape(1, 0, 4, 32, 0)), 0, None, None, 0, None) == 0
+
+
+def test_error_message_is_per_call():
+    fn = bd.lib().dssm_forward_fft
+    _call(fn, _params(), bd.Shape(1, 1, 4, 16385, 0))
+    assert bd.lib().dssm_last_error()
+    assert _call(fn, None, bd.Shape(0, 1, 4, 8, 0)) == 0
+    assert bd.lib().dssm_last_error() == b""
