@@ -131,6 +131,24 @@ int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape*
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                       float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* Timing variants: identical results to dssm_forward_fft / dssm_forward_scan,
+ * and additionally record the caller's hipEvent_t handles events[i] on
+ * `stream` at the stage boundaries, so a caller can time each kernel on the
+ * stream it runs on.
+ *   fft  (n_events = 5): [0] before the first kernel, [1] after the lambda
+ *        power/anchor tables, [2] after the kernel generator, [3] after the
+ *        kernel spectrum, [4] after the convolution.
+ *   scan (n_events = 3): [0] before, [1] after the per-mode constants,
+ *        [2] after the scan.
+ * The events are owned by the caller; a NULL array or handle, or a wrong
+ * n_events, returns DSSM_ERR_INVALID_ARG before anything is enqueued. */
+int dssm_forward_fft_timed(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                           float* y, void* ws, size_t ws_bytes, void* stream,
+                           void* const* events, int n_events);
+int dssm_forward_scan_timed(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                            float* y, void* ws, size_t ws_bytes, void* stream,
+                            void* const* events, int n_events);
+
 #ifdef __cplusplus
 }
 #endif

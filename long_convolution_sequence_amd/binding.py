@@ -23,6 +23,7 @@ OP_GEN, OP_FFT, OP_SCAN = 0, 1, 2
 EXPORTS = [
     "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
     "dssm_gen_kernel", "dssm_forward_fft", "dssm_forward_scan",
+    "dssm_forward_fft_timed", "dssm_forward_scan_timed",
 ]
 
 
@@ -69,6 +70,11 @@ def lib():
         f = getattr(L, name)
         f.restype = ctypes.c_int
         f.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, sz, vp]
+    for name in ("dssm_forward_fft_timed", "dssm_forward_scan_timed"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, sz, vp,
+                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     _lib = L
     return L
 
@@ -163,7 +169,7 @@ def gen_kernel(log_re, log_im, W, L, complex_out=False, out=None, workspace=None
     return out
 
 
-def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream):
+def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream, events=None):
     torch = _torch()
     uu = _dev_f32(u, "u")
     if uu.dim() != 3:
@@ -177,8 +183,12 @@ def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, strea
         y = torch.empty_like(uu)
     yy = _dev_f32(y, "y")
     ws, nbytes = _workspace(op, shape, workspace, uu.device)
-    check(fn(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape), yy.data_ptr(), ws.data_ptr(),
-             nbytes, _stream(stream)))
+    args = [uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape), yy.data_ptr(), ws.data_ptr(),
+            nbytes, _stream(stream)]
+    if events is not None:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        args += [arr, len(events)]
+    check(fn(*args))
     del keep
     return y
 
@@ -193,3 +203,15 @@ def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace
     """Layer forward by the recurrence (scan) view.  u [B,H,L] f32 -> y [B,H,L]."""
     return _forward(lib().dssm_forward_scan, OP_SCAN, u, log_re, log_im, W, D, bidirectional, y,
                     workspace, stream)
+
+
+def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=None,
+                  workspace=None, stream=None):
+    """forward_fft / forward_scan that also records the given raw hipEvent_t
+    handles (ints) at the library's stage boundaries (5 for fft, 3 for scan)."""
+    if path == "fft":
+        fn, op = lib().dssm_forward_fft_timed, OP_FFT
+    else:
+        fn, op = lib().dssm_forward_scan_timed, OP_SCAN
+    return _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream,
+                    events=list(events))

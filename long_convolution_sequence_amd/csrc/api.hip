@@ -187,58 +187,98 @@ int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_o
   return ok();
 }
 
-int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
-                     void* ws, size_t ws_bytes, void* stream) {
+// Shared body of the forward calls.  events (optional) are hipEvent_t
+// recorded on the stream at the stage boundaries.
+static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                        float* y, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                        int n_events) {
   bool empty = false;
-  int rc = check_shape(DSSM_OP_FFT, s, &empty);
+  int rc = check_shape(op, s, &empty);
   if (rc) return rc;
+  const int want = (op == DSSM_OP_FFT) ? 5 : 3;
+  if (events && n_events != want)
+    return fail(DSSM_ERR_INVALID_ARG, "n_events must be %d (got %d)", want, n_events);
   if (empty) return ok();
   if ((rc = check_params(p, true))) return rc;
   if (!u || !y || !aligned16(u) || !aligned16(y))
     return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
   if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
+  if (events)
+    for (int i = 0; i < n_events; ++i)
+      if (!events[i]) return fail(DSSM_ERR_INVALID_ARG, "events[%d] is NULL", i);
   Layout l;
-  if ((rc = check_ws(DSSM_OP_FFT, s, ws, ws_bytes, &l))) return rc;
+  if ((rc = check_ws(op, s, ws, ws_bytes, &l))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> int {
+    if (!events) return DSSM_OK;
+    return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
+  };
   const int ndir = 1 + s->bidirectional;
-  float* reK = at<float>(ws, l.reK);
-  if ((rc = run_gen(p, s, 0, reK, ws, l, st))) return rc;
-  const int log2m = fft_log2m(s->L);
-  float2* spec = at<float2>(ws, l.spec);
-  float* deff = at<float>(ws, l.deff);
-  if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, deff, st),
-                      "spectrum launch")))
-    return rc;
-  if ((rc = hip_check(launch_conv(u, spec, deff, s->B, s->H, s->L, log2m, y, st), "conv launch")))
-    return rc;
+  if ((rc = mark(0))) return rc;
+  if (op == DSSM_OP_FFT) {
+    const int ndh = ndir * s->H;
+    GenTables t;
+    t.pw = at<float2>(ws, l.pw);
+    t.anchor = at<float2>(ws, l.anchor);
+    t.Q = (s->L + kAnchor - 1) / kAnchor;
+    float* reK = at<float>(ws, l.reK);
+    if ((rc = hip_check(launch_gen_tables(p->log_re, p->log_im, p->W, ndh, s->N, s->L, t, st),
+                        "gen_tables launch")))
+      return rc;
+    if ((rc = mark(1))) return rc;
+    if ((rc = hip_check(launch_gen_kernel(t, ndh, s->N, s->L, 0, reK, st), "gen launch")))
+      return rc;
+    if ((rc = mark(2))) return rc;
+    const int log2m = fft_log2m(s->L);
+    float2* spec = at<float2>(ws, l.spec);
+    float* deff = at<float>(ws, l.deff);
+    if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, deff, st),
+                        "spectrum launch")))
+      return rc;
+    if ((rc = mark(3))) return rc;
+    if ((rc = hip_check(launch_conv(u, spec, deff, s->B, s->H, s->L, log2m, y, st),
+                        "conv launch")))
+      return rc;
+    if ((rc = mark(4))) return rc;
+  } else {
+    const ScanPlan plan = scan_plan(s->B, s->L);
+    float* consts = at<float>(ws, l.consts);
+    if ((rc = hip_check(launch_scan_consts(p->log_re, p->log_im, p->W, ndir * s->H, s->N, plan,
+                                           consts, st),
+                        "scan consts launch")))
+      return rc;
+    if ((rc = mark(1))) return rc;
+    if ((rc = hip_check(launch_scan(u, consts, p->D, s->B, s->H, s->N, s->L, ndir, plan, y, st,
+                                    at<float2>(ws, l.carry)),
+                        "scan launch")))
+      return rc;
+    if ((rc = mark(2))) return rc;
+  }
   return ok();
+}
+
+int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
 }
 
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
                       void* ws, size_t ws_bytes, void* stream) {
-  bool empty = false;
-  int rc = check_shape(DSSM_OP_SCAN, s, &empty);
-  if (rc) return rc;
-  if (empty) return ok();
-  if ((rc = check_params(p, true))) return rc;
-  if (!u || !y || !aligned16(u) || !aligned16(y))
-    return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
-  if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
-  Layout l;
-  if ((rc = check_ws(DSSM_OP_SCAN, s, ws, ws_bytes, &l))) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int ndir = 1 + s->bidirectional;
-  const ScanPlan plan = scan_plan(s->B, s->L);
-  float* consts = at<float>(ws, l.consts);
-  if ((rc = hip_check(launch_scan_consts(p->log_re, p->log_im, p->W, ndir * s->H, s->N, plan,
-                                         consts, st),
-                      "scan consts launch")))
-    return rc;
-  if ((rc = hip_check(launch_scan(u, consts, p->D, s->B, s->H, s->N, s->L, ndir, plan, y, st,
-                                  at<float2>(ws, l.carry)),
-                      "scan launch")))
-    return rc;
-  return ok();
+  return forward_impl(DSSM_OP_SCAN, u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
+}
+
+int dssm_forward_fft_timed(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                           float* y, void* ws, size_t ws_bytes, void* stream,
+                           void* const* events, int n_events) {
+  if (!events) return fail(DSSM_ERR_INVALID_ARG, "events is NULL");
+  return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, ws_bytes, stream, events, n_events);
+}
+
+int dssm_forward_scan_timed(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                            float* y, void* ws, size_t ws_bytes, void* stream,
+                            void* const* events, int n_events) {
+  if (!events) return fail(DSSM_ERR_INVALID_ARG, "events is NULL");
+  return forward_impl(DSSM_OP_SCAN, u, p, s, y, ws, ws_bytes, stream, events, n_events);
 }
 
 }  // extern "C"
