@@ -91,6 +91,44 @@ def time_path(path, dev, us, ys, ws, steps, warmup, bi, hip):
     return (t1 - t0) * 1e3 / steps, stages, gpu
 
 
+def time_s5(steps, warmup, hip):
+    """Timed S5 layer forwards on the S5 workload (B=4, H=256, P=128, L=16384)."""
+    import numpy as np
+    import torch
+    from long_convolution_sequence_amd import binding as bd
+    from long_convolution_sequence_amd import inputs
+
+    c = inputs.config("s5_mimo")
+    x = inputs.inputs_for(c)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    y = torch.empty_like(t["u"])
+    ws = torch.empty(bd.s5_workspace_size(c["B"], c["H"], c["P"], c["L"]), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], y=y, workspace=ws)
+    evs = [hip.create(5) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], y=y, workspace=ws, events=evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st = [sum(hip.ms(e[i], e[i + 1]) for e in evs) / steps for i in range(4)]
+    for e in evs:
+        hip.destroy(e)
+    ms = (t1 - t0) * 1e3 / steps
+    B, H, P, L = c["B"], c["H"], c["P"], c["L"]
+    gemm_flop = 2.0 * (2 * P) * H * L * B  # one projection
+    return {
+        "workload": "s5_mimo", "B": B, "H": H, "P": P, "L": L,
+        "ms_per_step": ms, "elements_per_s": B * H * L / (ms * 1e-3),
+        "stage_ms": {"pack": st[0], "proj_in": st[1], "scan": st[2], "proj_out": st[3]},
+        "proj_in_fp32_tflops": gemm_flop / (st[1] * 1e-3) / 1e12,
+        "proj_out_fp32_tflops": gemm_flop / (st[3] * 1e-3) / 1e12,
+        "mfma_fp32_peak_tflops": 157.3,
+    }
+
+
 def cpu_baseline(x, bi, y_gpu):
     """The float64 oracle as it stands, single process, on the host: the
     sequential recurrence over the whole workload, plus the direct O(L^2) sum
@@ -210,6 +248,7 @@ def main():
                           "stage_ms": {"consts": stages_scan[0], "scan": stages_scan[1]},
                           "gpu_ms_events": gpu_scan},
             "rotated_sets": a.rotate,
+            "s5_path": time_s5(max(2, a.scan_steps), 2, hip),
         },
     }
     if not a.no_cpu_baseline:

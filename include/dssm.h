@@ -131,6 +131,51 @@ int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape*
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                       float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * S5-style multi-input multi-output diagonal SSM ("Simplified State Space
+ * Layers for Sequence Modeling", section 3): one diagonal state of size P
+ * shared by all H inputs,
+ *   v_k = Bbar u_k,  x_k = lambda * x_{k-1} + v_k  (x_{-1} = 0),
+ *   y_k = Re(C x_k) + D * u_k,
+ * with the discrete lambda and Bbar given directly (no discretisation is
+ * applied) and no factor 2 on the real part.  Layouts:
+ *   u, y   [B, H, L] float32
+ *   lambda [P, 2]    complex
+ *   Bbar   [P, H, 2] complex
+ *   C      [H, P, 2] complex
+ *   D      [H]       float32
+ * The projections run on the matrix cores in float32 (a dense contraction
+ * over H and over 2P); the recurrence is a segmented complex scan whose
+ * carries use powers of lambda computed in float64.  bidirectional = 1 is
+ * DSSM_ERR_UNSUPPORTED (the pages define no bidirectional S5).
+ * Requires 1 <= P <= 4096, L <= 2^24, B <= 65535.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int B, H, P, L;
+  int bidirectional; /* must be 0 */
+} dssm_s5_shape;
+
+typedef struct {
+  const float* lambda;
+  const float* Bbar;
+  const float* C;
+  const float* D;
+} dssm_s5_params;
+
+/* Bytes of workspace dssm_s5_forward needs (host only). */
+int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes);
+
+/* y [B, H, L] from u [B, H, L]; same conventions as the DLR calls. */
+int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Timing variant of dssm_s5_forward (n_events = 5): [0] before, [1] after
+ * packing Bbar and C, [2] after the input projection, [3] after the scan,
+ * [4] after the output projection. */
+int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s,
+                          float* y, void* ws, size_t ws_bytes, void* stream,
+                          void* const* events, int n_events);
+
 /* Timing variants: identical results to dssm_forward_fft / dssm_forward_scan,
  * and additionally record the caller's hipEvent_t handles events[i] on
  * `stream` at the stage boundaries, so a caller can time each kernel on the

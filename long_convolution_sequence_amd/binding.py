@@ -24,6 +24,7 @@ EXPORTS = [
     "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
     "dssm_gen_kernel", "dssm_forward_fft", "dssm_forward_scan",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
+    "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed",
 ]
 
 
@@ -35,6 +36,16 @@ class Shape(ctypes.Structure):
 class DLRParams(ctypes.Structure):
     _fields_ = [("log_re", ctypes.c_void_p), ("log_im", ctypes.c_void_p),
                 ("W", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+class S5Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("P", ctypes.c_int),
+                ("L", ctypes.c_int), ("bidirectional", ctypes.c_int)]
+
+
+class S5Params(ctypes.Structure):
+    _fields_ = [("lam", ctypes.c_void_p), ("Bbar", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("D", ctypes.c_void_p)]
 
 
 class DSSMError(RuntimeError):
@@ -75,6 +86,14 @@ def lib():
         f.restype = ctypes.c_int
         f.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, sz, vp,
                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.dssm_s5_workspace_size.restype = ctypes.c_int
+    L.dssm_s5_workspace_size.argtypes = [ctypes.POINTER(S5Shape), ctypes.POINTER(sz)]
+    L.dssm_s5_forward.restype = ctypes.c_int
+    L.dssm_s5_forward.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape), vp, vp,
+                                  sz, vp]
+    L.dssm_s5_forward_timed.restype = ctypes.c_int
+    L.dssm_s5_forward_timed.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape), vp,
+                                        vp, sz, vp, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     _lib = L
     return L
 
@@ -215,3 +234,45 @@ def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=
         fn, op = lib().dssm_forward_scan_timed, OP_SCAN
     return _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream,
                     events=list(events))
+
+
+def s5_workspace_size(B, H, P, L):
+    shape = S5Shape(B, H, P, L, 0)
+    out = ctypes.c_size_t(0)
+    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
+def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=None):
+    """S5 layer forward.  u [B,H,L] f32, lam [P] c64, Bbar [P,H] c64,
+    C [H,P] c64, D [H] f32 -> y [B,H,L] f32."""
+    torch = _torch()
+    uu = _dev_f32(u, "u")
+    if uu.dim() != 3:
+        raise ValueError("u must be [B, H, L]")
+    B, H, L = uu.shape
+    lm = _dev_f32(lam, "lam")
+    P = lm.numel() // 2
+    bb = _dev_f32(Bbar, "Bbar")
+    cc = _dev_f32(C, "C")
+    dd = _dev_f32(D, "D")
+    if bb.numel() != 2 * P * H or cc.numel() != 2 * H * P or dd.numel() != H:
+        raise ValueError("Bbar must be [P,H], C [H,P] complex and D [H]")
+    shape = S5Shape(B, H, P, L, 0)
+    prm = S5Params(lm.data_ptr(), bb.data_ptr(), cc.data_ptr(), dd.data_ptr())
+    if y is None:
+        y = torch.empty_like(uu)
+    yy = _dev_f32(y, "y")
+    need = ctypes.c_size_t(0)
+    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=uu.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    args = [uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape), yy.data_ptr(),
+            workspace.data_ptr(), nbytes, _stream(stream)]
+    if events is None:
+        check(lib().dssm_s5_forward(*args))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        check(lib().dssm_s5_forward_timed(*(args + [arr, len(events)])))
+    return y

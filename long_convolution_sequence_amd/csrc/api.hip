@@ -281,4 +281,100 @@ int dssm_forward_scan_timed(const float* u, const dssm_dlr_params* p, const dssm
   return forward_impl(DSSM_OP_SCAN, u, p, s, y, ws, ws_bytes, stream, events, n_events);
 }
 
+// ---------------------------------------------------------------------------
+// S5
+// ---------------------------------------------------------------------------
+static int s5_check_shape(const dssm_s5_shape* s, bool* empty) {
+  if (!s) return fail(DSSM_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 0 || s->H < 0 || s->L < 0)
+    return fail(DSSM_ERR_INVALID_ARG, "negative dimension (B=%d H=%d L=%d)", s->B, s->H, s->L);
+  if (s->P < 1) return fail(DSSM_ERR_INVALID_ARG, "P must be >= 1 (got %d)", s->P);
+  if (s->bidirectional != 0 && s->bidirectional != 1)
+    return fail(DSSM_ERR_INVALID_ARG, "bidirectional must be 0 or 1 (got %d)", s->bidirectional);
+  if (s->bidirectional)
+    return fail(DSSM_ERR_UNSUPPORTED, "the S5 layer has no bidirectional form here");
+  if (s->P > kMaxN) return fail(DSSM_ERR_UNSUPPORTED, "P=%d exceeds %d", s->P, kMaxN);
+  if (s->H > kMaxGrid * 64) return fail(DSSM_ERR_UNSUPPORTED, "H=%d too large", s->H);
+  if (s->B > kMaxGrid) return fail(DSSM_ERR_UNSUPPORTED, "B=%d exceeds %d", s->B, kMaxGrid);
+  if (s->L > kMaxLScan) return fail(DSSM_ERR_UNSUPPORTED, "L=%d exceeds %d", s->L, kMaxLScan);
+  if ((long)s->B * s->P > (1L << 31) - 1) return fail(DSSM_ERR_UNSUPPORTED, "B*P too large");
+  if ((long)s->B * (s->H > 2 * s->P ? s->H : 2 * s->P) * s->L > (1L << 40))
+    return fail(DSSM_ERR_UNSUPPORTED, "problem too large");
+  *empty = s->B == 0 || s->H == 0 || s->L == 0;
+  return DSSM_OK;
+}
+
+static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
+                   void* ws, size_t ws_bytes, void* stream, void* const* events, int n_events) {
+  bool empty = false;
+  int rc = s5_check_shape(s, &empty);
+  if (rc) return rc;
+  if (events && n_events != 5)
+    return fail(DSSM_ERR_INVALID_ARG, "n_events must be 5 (got %d)", n_events);
+  if (empty) return ok();
+  if (!p) return fail(DSSM_ERR_INVALID_ARG, "params is NULL");
+  if (!p->lambda || !p->Bbar || !p->C || !p->D)
+    return fail(DSSM_ERR_INVALID_ARG, "a parameter pointer is NULL");
+  if (!aligned16(p->lambda) || !aligned16(p->Bbar) || !aligned16(p->C) || !aligned16(p->D))
+    return fail(DSSM_ERR_INVALID_ARG, "parameter pointers must be 16-byte aligned");
+  if (!u || !y || !aligned16(u) || !aligned16(y))
+    return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
+  if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
+  if (events)
+    for (int i = 0; i < n_events; ++i)
+      if (!events[i]) return fail(DSSM_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L);
+  if (ws_bytes < l.total)
+    return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, l.total);
+  if (!ws) return fail(DSSM_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(DSSM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> int {
+    if (!events) return DSSM_OK;
+    return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
+  };
+  float* apk_in = at<float>(ws, l.apk_in);
+  float* apk_out = at<float>(ws, l.apk_out);
+  float* v = at<float>(ws, l.v);
+  float* x = at<float>(ws, l.x);
+  if ((rc = mark(0))) return rc;
+  if ((rc = hip_check(launch_s5_pack(p->Bbar, p->C, s->H, s->P, apk_in, apk_out, st), "s5 pack")))
+    return rc;
+  if ((rc = mark(1))) return rc;
+  if ((rc = hip_check(launch_s5_proj_in(apk_in, u, s->B, s->H, s->P, s->L, v, st), "s5 proj_in")))
+    return rc;
+  if ((rc = mark(2))) return rc;
+  if ((rc = hip_check(launch_s5_scan(p->lambda, v, s->B, s->P, s->L, x, st), "s5 scan")))
+    return rc;
+  if ((rc = mark(3))) return rc;
+  if ((rc = hip_check(launch_s5_proj_out(apk_out, x, p->D, u, s->B, s->H, s->P, s->L, y, st),
+                      "s5 proj_out")))
+    return rc;
+  if ((rc = mark(4))) return rc;
+  return ok();
+}
+
+int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes) {
+  if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
+  bool empty = false;
+  int rc = s5_check_shape(s, &empty);
+  if (rc) return rc;
+  *bytes = empty ? 0 : s5_layout(s->B, s->H, s->P, s->L).total;
+  return ok();
+}
+
+int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return s5_impl(u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
+}
+
+int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s,
+                          float* y, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                          int n_events) {
+  if (!events) return fail(DSSM_ERR_INVALID_ARG, "events is NULL");
+  return s5_impl(u, p, s, y, ws, ws_bytes, stream, events, n_events);
+}
+
 }  // extern "C"

@@ -140,3 +140,46 @@ def test_error_message_is_per_call():
     assert bd.lib().dssm_last_error()
     assert _call(fn, None, bd.Shape(0, 1, 4, 8, 0)) == 0
     assert bd.lib().dssm_last_error() == b""
+
+
+def _s5ws(B, H, P, L, bi=0):
+    s = bd.S5Shape(B, H, P, L, bi)
+    out = ctypes.c_size_t(0)
+    return bd.lib().dssm_s5_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
+
+
+def test_s5_workspace_and_validation():
+    assert _s5ws(4, 256, 128, 16384)[0] == 0
+    assert _s5ws(-1, 2, 2, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _s5ws(1, 2, 0, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _s5ws(1, 2, 2, 8, 1)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _s5ws(1, 2, 2, 8, 5)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert _s5ws(1, 2, 5000, 8)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _s5ws(0, 2, 2, 8) == (0, 0)
+    fn = bd.lib().dssm_s5_forward
+    good = bd.S5Shape(2, 3, 4, 32, 0)
+    prm = bd.S5Params(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
+    call = lambda p, s, u=FAKE * 2, y=FAKE * 3, ws=FAKE * 4, n=1 << 40: fn(
+        u, ctypes.byref(p) if p is not None else None, ctypes.byref(s), y, ws, n, None)
+    assert call(None, good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(bd.S5Params(None, FAKE, FAKE, FAKE), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(bd.S5Params(FAKE + 8, FAKE, FAKE, FAKE), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, u=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, y=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, n=64) == bd.DSSM_ERR_WORKSPACE
+    assert call(prm, good, ws=FAKE * 4 + 16) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, bd.S5Shape(2, 3, 4, 32, 1)) == bd.DSSM_ERR_UNSUPPORTED
+    assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
+
+
+@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 5), ("dssm_forward_scan_timed", 3)])
+def test_timed_variants_validate_events(name, n):
+    fn = getattr(bd.lib(), name)
+    good = bd.Shape(2, 3, 4, 32, 0)
+    p = _params()
+    evs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    args = [FAKE * 2, ctypes.byref(p), ctypes.byref(good), FAKE * 3, FAKE * 4, 1 << 40, None]
+    assert fn(*(args + [None, n])) == bd.DSSM_ERR_INVALID_ARG
+    assert fn(*(args + [evs, n + 1])) == bd.DSSM_ERR_INVALID_ARG
+    bad = (ctypes.c_void_p * n)(*([FAKE] * (n - 1) + [None]))
+    assert fn(*(args + [bad, n])) == bd.DSSM_ERR_INVALID_ARG
