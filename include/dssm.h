@@ -101,9 +101,10 @@ int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes);
  * (DLR page, section 2: K = (<w, Lambda^k>)_{0<=k<L}).
  *   complex_out = 0: K is [ndir, H, L] float32 holding Re K.
  *   complex_out = 1: K is [ndir, H, L, 2] float32 holding K (re, im).
- * Powers are formed from lambda^r (r < 64) and anchors lambda^(64q) that are
- * computed in float64 and rounded once to float32.  B and p->D are ignored
- * (D may be NULL).
+ * Powers are formed from lambda^r (r < 64) and anchors W lambda^(64q) that
+ * are computed in float64 and rounded once to float32; the sum over modes is
+ * a float32 matrix-core contraction.  B and p->D are ignored (D may be NULL);
+ * the workspace size is 0 (ws may be NULL).
  * Requires 1 <= N <= 4096, 1 <= L <= 2^24. */
 int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_out,
                     float* K, void* ws, size_t ws_bytes, void* stream);
@@ -180,9 +181,8 @@ int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5
  * and additionally record the caller's hipEvent_t handles events[i] on
  * `stream` at the stage boundaries, so a caller can time each kernel on the
  * stream it runs on.
- *   fft  (n_events = 5): [0] before the first kernel, [1] after the lambda
- *        power/anchor tables, [2] after the kernel generator, [3] after the
- *        kernel spectrum, [4] after the convolution.
+ *   fft  (n_events = 4): [0] before the first kernel, [1] after the kernel
+ *        generator, [2] after the kernel spectrum, [3] after the convolution.
  *   scan (n_events = 3): [0] before, [1] after the per-mode constants,
  *        [2] after the scan.
  * The events are owned by the caller; a NULL array or handle, or a wrong

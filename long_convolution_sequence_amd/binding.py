@@ -227,7 +227,7 @@ def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace
 def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=None,
                   workspace=None, stream=None):
     """forward_fft / forward_scan that also records the given raw hipEvent_t
-    handles (ints) at the library's stage boundaries (5 for fft, 3 for scan)."""
+    handles (ints) at the library's stage boundaries (4 for fft, 3 for scan)."""
     if path == "fft":
         fn, op = lib().dssm_forward_fft_timed, OP_FFT
     else:

@@ -80,7 +80,7 @@ int check_params(const dssm_dlr_params* p, bool need_d) {
 
 // Workspace layout, every region aligned to 256 bytes.
 struct Layout {
-  size_t pw = 0, anchor = 0, reK = 0, spec = 0, deff = 0, consts = 0, carry = 0, total = 0;
+  size_t reK = 0, spec = 0, deff = 0, consts = 0, carry = 0, total = 0;
 };
 
 Layout layout(int op, const dssm_shape* s) {
@@ -93,11 +93,6 @@ Layout layout(int op, const dssm_shape* s) {
     off = align_up(off + bytes, 256);
     return at;
   };
-  if (op == DSSM_OP_GEN || op == DSSM_OP_FFT) {
-    const size_t Q = (L + kAnchor - 1) / kAnchor;
-    l.pw = take(ndh * N * kAnchor * sizeof(float2));
-    l.anchor = take(ndh * N * Q * sizeof(float2));
-  }
   if (op == DSSM_OP_FFT) {
     const size_t M = (size_t)1 << fft_log2m(s->L);
     l.reK = take(ndh * L * sizeof(float));
@@ -127,20 +122,6 @@ int check_ws(int op, const dssm_shape* s, void* ws, size_t ws_bytes, Layout* l) 
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
-}
-
-// Enqueue the table and generator kernels: Re K (or complex K) into K.
-int run_gen(const dssm_dlr_params* p, const dssm_shape* s, int complex_out, float* K, void* ws,
-            const Layout& l, hipStream_t st) {
-  const int ndh = (1 + s->bidirectional) * s->H;
-  GenTables t;
-  t.pw = at<float2>(ws, l.pw);
-  t.anchor = at<float2>(ws, l.anchor);
-  t.Q = (s->L + kAnchor - 1) / kAnchor;
-  int rc = hip_check(launch_gen_tables(p->log_re, p->log_im, p->W, ndh, s->N, s->L, t, st),
-                     "gen_tables launch");
-  if (rc) return rc;
-  return hip_check(launch_gen_kernel(t, ndh, s->N, s->L, complex_out, K, st), "gen launch");
 }
 
 }  // namespace
@@ -183,7 +164,10 @@ int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_o
   if (!K || !aligned16(K)) return fail(DSSM_ERR_INVALID_ARG, "K is NULL or not 16-byte aligned");
   Layout l;
   if ((rc = check_ws(DSSM_OP_GEN, s, ws, ws_bytes, &l))) return rc;
-  if ((rc = run_gen(p, s, complex_out, K, ws, l, static_cast<hipStream_t>(stream)))) return rc;
+  if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, (1 + s->bidirectional) * s->H, s->N,
+                                 s->L, complex_out, K, static_cast<hipStream_t>(stream)),
+                      "gen launch")))
+    return rc;
   return ok();
 }
 
@@ -195,7 +179,7 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
   bool empty = false;
   int rc = check_shape(op, s, &empty);
   if (rc) return rc;
-  const int want = (op == DSSM_OP_FFT) ? 5 : 3;
+  const int want = (op == DSSM_OP_FFT) ? 4 : 3;
   if (events && n_events != want)
     return fail(DSSM_ERR_INVALID_ARG, "n_events must be %d (got %d)", want, n_events);
   if (empty) return ok();
@@ -217,29 +201,22 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
   if ((rc = mark(0))) return rc;
   if (op == DSSM_OP_FFT) {
     const int ndh = ndir * s->H;
-    GenTables t;
-    t.pw = at<float2>(ws, l.pw);
-    t.anchor = at<float2>(ws, l.anchor);
-    t.Q = (s->L + kAnchor - 1) / kAnchor;
     float* reK = at<float>(ws, l.reK);
-    if ((rc = hip_check(launch_gen_tables(p->log_re, p->log_im, p->W, ndh, s->N, s->L, t, st),
-                        "gen_tables launch")))
+    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndh, s->N, s->L, 0, reK, st),
+                        "gen launch")))
       return rc;
     if ((rc = mark(1))) return rc;
-    if ((rc = hip_check(launch_gen_kernel(t, ndh, s->N, s->L, 0, reK, st), "gen launch")))
-      return rc;
-    if ((rc = mark(2))) return rc;
     const int log2m = fft_log2m(s->L);
     float2* spec = at<float2>(ws, l.spec);
     float* deff = at<float>(ws, l.deff);
     if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, deff, st),
                         "spectrum launch")))
       return rc;
-    if ((rc = mark(3))) return rc;
+    if ((rc = mark(2))) return rc;
     if ((rc = hip_check(launch_conv(u, spec, deff, s->B, s->H, s->L, log2m, y, st),
                         "conv launch")))
       return rc;
-    if ((rc = mark(4))) return rc;
+    if ((rc = mark(3))) return rc;
   } else {
     const ScanPlan plan = scan_plan(s->B, s->L);
     float* consts = at<float>(ws, l.consts);

@@ -20,20 +20,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---------------------------------------------------------------------------
 // Kernel generation (eig_gen.hip)
 // ---------------------------------------------------------------------------
-struct GenTables {
-  float2* pw;      // [ndir*H, N, 64]  lambda^r, r < 64
-  float2* anchor;  // [ndir*H, N, Q]   W lambda^(64 q), q < Q = ceil(L/64)
-  int Q;
-};
-
-// Fill pw and anchor from the DLR parameters (float64 arithmetic).
-hipError_t launch_gen_tables(const float* log_re, const float* log_im, const float* W,
-                             int ndh, int N, int L, const GenTables& t, hipStream_t st);
-
-// K[dh, j] = sum_n anchor[dh,n,j/64] * pw[dh,n,j%64] for j < L.
+// K[dh, j] = sum_n W[dh,n] lambda[dh,n]^j for j < L, from the parameters
+// directly (float64 powers, float32 matrix-core contraction over the modes).
 // complex_out = 0: Re K into float [ndh, L]; 1: (Re, Im) into float2 [ndh, L].
-hipError_t launch_gen_kernel(const GenTables& t, int ndh, int N, int L, int complex_out,
-                             float* K, hipStream_t st);
+hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, int ndh, int N,
+                      int L, int complex_out, float* K, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // FFT convolution (fft.hip)

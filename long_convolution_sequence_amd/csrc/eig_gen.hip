@@ -3,139 +3,144 @@
 // ("Simplifying and Understanding State Space Models with Diagonal Linear
 // RNNs", section 2: the parameterisation of Lambda and K = (<w, Lambda^k>)_k).
 //
-// Precision: lambda^j is never formed by a long float32 chain.  With
-// j = 64 q + r, K[j] = sum_n (W lambda^(64 q)) * lambda^r, where both factors
-// are computed in float64 (exp and sincos of exactly-formed arguments) and
-// rounded once to float32.  The contraction over n is then an ordinary float32
-// dot product of length N per output.
+// One workgroup produces a 64 x 64 block of K for one channel: j = 64 q + r
+// with q in a tile of 64 anchors and r < 64, via
+//   K[64 q + r] = sum_n (W_n lambda_n^(64 q)) * lambda_n^r.
+// Precision: both factors are formed in float64 -- lambda from exp/sincos of
+// the exactly promoted parameters, lambda^(16 t) and (lambda^64)^e by binary
+// powering, then chains of at most 15 float64 products -- and rounded once to
+// float32; no float32 power chain exists.  The contraction over the modes is
+// a real product of a (64 x 2N) by a (2N x 64) matrix, done on the matrix
+// cores in float32 (v_mfma_f32_16x16x4f32):
+//   Re K = sum_n Re A Re P - Im A Im P,   Im K = sum_n Re A Im P + Im A Re P.
 #include "dssm_internal.h"
 
 namespace dssm {
 namespace {
 
-constexpr int kAnchorBlock = 16;  // anchors per thread, chained in float64
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-__device__ inline double2 cis_scaled(double a, double theta, double k) {
-  // exp(k*a) * (cos(k*theta), sin(k*theta)); k*theta is exact for the
-  // integer k and float32 theta used here (k < 2^24, theta has 24 bits).
-  double s, c;
-  sincos(k * theta, &s, &c);
-  double m = exp(k * a);
-  return make_double2(m * c, m * s);
-}
-
-__device__ inline double2 cmul(double2 x, double2 y) {
+__device__ __forceinline__ double2 zmul(double2 x, double2 y) {
   return make_double2(x.x * y.x - x.y * y.y, x.x * y.y + x.y * y.x);
 }
 
-// blockIdx.y == 0: pw[dhn, r] = lambda^r (r < 64), one thread per entry.
-// blockIdx.y == 1: anchor[dhn, q] = W lambda^(64 q), one thread per block of
-//                  16 consecutive q, chained by mu = lambda^64 in float64.
-__global__ __launch_bounds__(256) void gen_tables_kernel(const float* __restrict__ log_re,
-                                                         const float* __restrict__ log_im,
-                                                         const float2* __restrict__ W, int ndhn,
-                                                         int Q, float2* __restrict__ pw,
-                                                         float2* __restrict__ anchor) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.y == 0) {
-    const int dhn = idx >> 6, r = idx & 63;
-    if (dhn >= ndhn) return;
-    const double re = (double)log_re[dhn];
-    const double a = -re * re;
-    const double2 v = cis_scaled(a, (double)log_im[dhn], (double)r);
-    pw[(size_t)dhn * kAnchor + r] = make_float2((float)v.x, (float)v.y);
-  } else {
-    const int qblocks = (Q + kAnchorBlock - 1) / kAnchorBlock;
-    const int dhn = idx / qblocks, qb = idx % qblocks;
-    if (dhn >= ndhn) return;
-    const double re = (double)log_re[dhn];
-    const double a = -re * re;
-    const double theta = (double)log_im[dhn];
-    const float2 wf = W[dhn];
-    const double2 w = make_double2((double)wf.x, (double)wf.y);
-    const int q0 = qb * kAnchorBlock;
-    double2 cur = cmul(w, cis_scaled(a, theta, (double)kAnchor * q0));
-    const double2 mu = cis_scaled(a, theta, (double)kAnchor);
-    float2* out = anchor + (size_t)dhn * Q;
-    const int qend = min(Q, q0 + kAnchorBlock);
-    for (int q = q0; q < qend; ++q) {
-      out[q] = make_float2((float)cur.x, (float)cur.y);
-      cur = cmul(cur, mu);
-    }
-  }
-}
+// Row stride (floats) of the LDS operand tables: rows k' = 2n + part (part 0
+// = real, 1 = imaginary) of 64 entries; 80 keeps the four rows an MFMA step
+// reads in different LDS banks.
+constexpr int kRow = 80;
+constexpr int kModes = 64;  // modes staged per chunk
 
-// One workgroup per (dh, tile of 64 anchors): a 64 (q) x 64 (r) block of
-// K = Re/Im sum_n anchor[n, q] * pw[n, r], staged through LDS in chunks of 64
-// modes.  Each thread owns 4 q x 4 r outputs.
 template <bool kComplex>
-__global__ __launch_bounds__(256) void gen_kernel(const float2* __restrict__ pw,
-                                                  const float2* __restrict__ anchor, int N, int Q,
-                                                  int L, float* __restrict__ K) {
-  __shared__ float2 sP[64][64];
-  __shared__ float2 sA[64][64 + 2];
+__global__ __launch_bounds__(256) void gen_kernel(const float* __restrict__ log_re,
+                                                  const float* __restrict__ log_im,
+                                                  const float2* __restrict__ W, int N, int L,
+                                                  float* __restrict__ K) {
+  __shared__ float sA[2 * kModes * kRow];  // [2n + part][q]: W lambda^(64 q)
+  __shared__ float sP[2 * kModes * kRow];  // [2n + part][r]: lambda^r
   const int t = threadIdx.x;
-  const int tq = t >> 4, tr = t & 15;
+  const int lane = t & 63, w = t >> 6;
   const int dh = blockIdx.y;
+  const int Q = (L + kAnchor - 1) / kAnchor;
   const int q0 = blockIdx.x * 64;
-  const float2* pwh = pw + (size_t)dh * N * kAnchor;
-  const float2* anh = anchor + (size_t)dh * N * Q;
 
-  float acc_re[4][4], acc_im[4][4];
+  v4f acc_re[4], acc_im[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc_re[i][j] = 0.f;
-      acc_im[i][j] = 0.f;
-    }
+  for (int c = 0; c < 4; ++c) {
+    acc_re[c] = v4f{0.f, 0.f, 0.f, 0.f};
+    acc_im[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
 
-  for (int n0 = 0; n0 < N; n0 += 64) {
-    const int nn = min(64, N - n0);
-    for (int e = t; e < 64 * 64; e += 256) {
-      const int n = e >> 6, c = e & 63;
-      float2 pv = make_float2(0.f, 0.f), av = make_float2(0.f, 0.f);
-      if (n < nn) {
-        pv = pwh[(size_t)(n0 + n) * kAnchor + c];
-        if (q0 + c < Q) av = anh[(size_t)(n0 + n) * Q + q0 + c];
+  for (int n0 = 0; n0 < N; n0 += kModes) {
+    const int nn = min(kModes, N - n0);
+    // ---- tables: 4 threads per mode, 16 entries of each table per thread
+    {
+      const int nl = t >> 2, tq = t & 3;
+      double2 lam = make_double2(0.0, 0.0), wv = make_double2(0.0, 0.0);
+      if (nl < nn) {
+        const int dhn = dh * N + n0 + nl;
+        const double re = (double)log_re[dhn];
+        double s, c;
+        sincos((double)log_im[dhn], &s, &c);
+        const double m = exp(-re * re);
+        lam = make_double2(m * c, m * s);
+        const float2 wf = W[dhn];
+        wv = make_double2((double)wf.x, (double)wf.y);
       }
-      sP[n][c] = pv;
-      sA[n][c] = av;
+      // lambda^16, lambda^32, lambda^48, lambda^64
+      double2 l2 = zmul(lam, lam), l4 = zmul(l2, l2), l8 = zmul(l4, l4), l16 = zmul(l8, l8);
+      const double2 l32 = zmul(l16, l16);
+      const double2 mu = zmul(l32, l32);  // lambda^64
+      double2 x = tq == 0 ? make_double2(1.0, 0.0)
+                 : tq == 1 ? l16
+                 : tq == 2 ? l32
+                           : zmul(l32, l16);
+      float* prow = sP + (2 * nl) * kRow + 16 * tq;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {  // lambda^r, r = 16 tq + i
+        prow[i] = (float)x.x;
+        prow[kRow + i] = (float)x.y;
+        x = zmul(x, lam);
+      }
+      // W mu^e, e = q0 + 16 tq, by binary powering of mu, then a chain of 15
+      int e = q0 + 16 * tq;
+      double2 a = wv, base = mu;
+      while (e) {
+        if (e & 1) a = zmul(a, base);
+        base = zmul(base, base);
+        e >>= 1;
+      }
+      float* arow = sA + (2 * nl) * kRow + 16 * tq;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool in = (q0 + 16 * tq + i) < Q;
+        arow[i] = in ? (float)a.x : 0.f;
+        arow[kRow + i] = in ? (float)a.y : 0.f;
+        a = zmul(a, mu);
+      }
     }
     __syncthreads();
-    for (int n = 0; n < nn; ++n) {
-      float2 a[4], p[4];
+    // ---- contraction: wave w owns anchors q0 + 16 w .. +15, all 64 r
+    {
+      const int kq = lane >> 4;  // k' offset inside a step (0..3)
+      const int part = kq & 1;
+      const int qa = 16 * w + (lane & 15);
+      const int steps = (2 * nn + 3) / 4;
+      for (int ks = 0; ks < steps; ++ks) {
+        const int kk = 4 * ks + kq;  // row 2n + part
+        const bool inrow = kk < 2 * nn;
+        // A = [Re A, -Im A] along k'
+        float a = inrow ? sA[kk * kRow + qa] : 0.f;
+        if (part) a = -a;
+        const float* pr = sP + kk * kRow + (lane & 15);
+        const float* pr_sw = sP + (kk ^ 1) * kRow + (lane & 15);  // other part of the mode
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sA[n][tq * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[j] = sP[n][tr + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc_re[i][j] = fmaf(a[i].x, p[j].x, acc_re[i][j]);
-          acc_re[i][j] = fmaf(-a[i].y, p[j].y, acc_re[i][j]);
+        for (int c = 0; c < 4; ++c) {
+          const float b = inrow ? pr[16 * c] : 0.f;  // [Re P; Im P]
+          acc_re[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc_re[c], 0, 0, 0);
           if (kComplex) {
-            acc_im[i][j] = fmaf(a[i].x, p[j].y, acc_im[i][j]);
-            acc_im[i][j] = fmaf(a[i].y, p[j].x, acc_im[i][j]);
+            // Im K: [Re A, -Im A] . [Im P; -Re P]
+            float bi = inrow ? pr_sw[16 * c] : 0.f;
+            if (part) bi = -bi;
+            acc_im[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bi, acc_im[c], 0, 0, 0);
           }
         }
+      }
     }
     __syncthreads();
   }
 
+  // acc[c][v]: q = q0 + 16 w + 4 (lane / 16) + v, r = 16 c + lane % 16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = q0 + tq * 4 + i;
+  for (int v = 0; v < 4; ++v) {
+    const int q = q0 + 16 * w + 4 * (lane >> 4) + v;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long k = (long)q * kAnchor + tr + 16 * j;
-      if (q < Q && k < L) {
-        if (kComplex) {
-          reinterpret_cast<float2*>(K)[(size_t)dh * L + k] = make_float2(acc_re[i][j], acc_im[i][j]);
-        } else {
-          K[(size_t)dh * L + k] = acc_re[i][j];
-        }
+    for (int c = 0; c < 4; ++c) {
+      const long j = (long)q * kAnchor + 16 * c + (lane & 15);
+      if (q < Q && j < L) {
+        if (kComplex)
+          reinterpret_cast<float2*>(K)[(size_t)dh * L + j] = make_float2(acc_re[c][v], acc_im[c][v]);
+        else
+          K[(size_t)dh * L + j] = acc_re[c][v];
       }
     }
   }
@@ -143,25 +148,15 @@ __global__ __launch_bounds__(256) void gen_kernel(const float2* __restrict__ pw,
 
 }  // namespace
 
-hipError_t launch_gen_tables(const float* log_re, const float* log_im, const float* W, int ndh,
-                             int N, int L, const GenTables& t, hipStream_t st) {
-  const int ndhn = ndh * N;
-  const int qblocks = (t.Q + kAnchorBlock - 1) / kAnchorBlock;
-  const long thr0 = (long)ndhn * kAnchor;
-  const long thr1 = (long)ndhn * qblocks;
-  const long nblk = (std::max(thr0, thr1) + 255) / 256;
-  hipLaunchKernelGGL(gen_tables_kernel, dim3((unsigned)nblk, 2), dim3(256), 0, st, log_re, log_im,
-                     reinterpret_cast<const float2*>(W), ndhn, t.Q, t.pw, t.anchor);
-  return hipGetLastError();
-}
-
-hipError_t launch_gen_kernel(const GenTables& t, int ndh, int N, int L, int complex_out, float* K,
-                             hipStream_t st) {
-  const dim3 grid((unsigned)((t.Q + 63) / 64), (unsigned)ndh);
+hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, int ndh, int N,
+                      int L, int complex_out, float* K, hipStream_t st) {
+  const int Q = (L + kAnchor - 1) / kAnchor;
+  const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)ndh);
+  const float2* w2 = reinterpret_cast<const float2*>(W);
   if (complex_out)
-    hipLaunchKernelGGL(gen_kernel<true>, grid, dim3(256), 0, st, t.pw, t.anchor, N, t.Q, L, K);
+    hipLaunchKernelGGL(gen_kernel<true>, grid, dim3(256), 0, st, log_re, log_im, w2, N, L, K);
   else
-    hipLaunchKernelGGL(gen_kernel<false>, grid, dim3(256), 0, st, t.pw, t.anchor, N, t.Q, L, K);
+    hipLaunchKernelGGL(gen_kernel<false>, grid, dim3(256), 0, st, log_re, log_im, w2, N, L, K);
   return hipGetLastError();
 }
 

@@ -194,15 +194,8 @@ __device__ __forceinline__ void dftR(float2* x) {
   }
 }
 
-// v[q] *= w^q for q = 1..15 (w conjugated when CONJ).
-template <bool CONJ>
-__device__ __forceinline__ void twiddle16(float2* v, float2 w) {
-  // Opaque to the optimiser: the powers are recomputed at every use instead of
-  // being shared between the forward and inverse passes and kept live (they
-  // would cost 30 registers per pass for the whole kernel).
-  asm volatile("" : "+v"(w.x), "+v"(w.y));
-  if (CONJ) w = cconj(w);
-  float2 p[16];
+// Powers p[q] = w^q, q = 1..15, by a product tree of depth <= 5.
+__device__ __forceinline__ void powers16(float2 w, float2* p) {
   p[1] = w;
   p[2] = cmul(w, w);
   p[3] = cmul(p[2], w);
@@ -213,91 +206,129 @@ __device__ __forceinline__ void twiddle16(float2* v, float2 w) {
   for (int a = 4; a <= 12; a += 4)
 #pragma unroll
     for (int b = 1; b < 4; ++b) p[a + b] = cmul(p[a], p[b]);
-#pragma unroll
-  for (int q = 1; q < 16; ++q) v[q] = cmul(v[q], p[q]);
 }
 
-template <int LOG2M>
+__device__ __forceinline__ float2 cmulc(float2 a, float2 b) {  // a * conj(b)
+  return make_float2(fmaf(a.x, b.x, a.y * b.y), fmaf(a.y, b.x, -a.x * b.y));
+}
+
+// v[q] *= p[q] (or conj(p[q]) when CONJ), q = 1..15; with SHIFT also by the
+// constant exp(-+ i pi q / 16) (the twiddle offset of a thread's second
+// butterfly in the first pass).
+template <bool CONJ, bool SHIFT, int Q = 1>
+__device__ __forceinline__ void apply16(float2* v, const float2* p) {
+  if constexpr (Q < 16) {
+    float2 a = v[Q];
+    if constexpr (SHIFT && CONJ) a = rotpi32<2 * Q, true>(a);
+    a = CONJ ? cmulc(a, p[Q]) : cmul(a, p[Q]);
+    if constexpr (SHIFT && !CONJ) a = rotpi32<2 * Q, false>(a);
+    v[Q] = a;
+    apply16<CONJ, SHIFT, Q + 1>(v, p);
+  }
+}
+
+// Transform geometry.  M = 2^LOG2M points, PT points per thread (16 or 32),
+// NB = PT / 16 radix-16 butterflies per thread, T = M / PT threads per
+// transform.  Passes 0 .. NP-2 are radix 16 on sub-transforms of size
+// S = M >> 4p (stride s = S / 16); the last pass has radix RLAST = M >> 4(NP-1).
+template <int LOG2M, int PT_>
 struct Cfg {
   static_assert(LOG2M >= 4 && LOG2M <= kMaxLog2M, "transform size");
+  static_assert(PT_ == 16 || PT_ == 32, "points per thread");
   static constexpr int M = 1 << LOG2M;
-  // points per thread: 32 for the largest size keeps the workgroup at 512
-  // threads so each may hold 256 registers; 16 otherwise
-  static constexpr int PT = (LOG2M >= 14) ? 32 : 16;
-  static constexpr int NB = PT / 16;                      // radix-16 butterflies per thread
-  static constexpr int T = M / PT;                        // threads per transform
-  static constexpr int NP = (LOG2M + 3) / 4;              // passes
-  static constexpr int RLAST = 1 << (LOG2M - 4 * (NP - 1));  // radix of the last pass
-  static constexpr int G = T >= 64 ? 1 : 64 / T;          // transforms per workgroup
+  static constexpr int PT = PT_;
+  static constexpr int NB = PT / 16;
+  static constexpr int T = M / PT;
+  static constexpr int NP = (LOG2M + 3) / 4;
+  static constexpr int RLAST = 1 << (LOG2M - 4 * (NP - 1));
+  static constexpr int G = T >= 64 ? 1 : 64 / T;  // transforms per workgroup
   static constexpr int WG = T * G;
-  static constexpr int LDSN = M + M / 16;                 // padded complex slots
-  static_assert(M % PT == 0 && T >= 1, "shape");
+  // LDS slot of position e: e + (e >> PADSH).  One pad slot per 16 (or 32)
+  // points keeps every pass's access pattern at the minimum number of LDS
+  // bank cycles for its lane stride.
+  static constexpr int PADSH = (PT == 32) ? 5 : 4;
+  static constexpr int LDSN = M + (M >> PADSH);   // padded complex slots
+  static_assert(T >= 1 && (NB == 1 || NP >= 2), "shape");
+  __device__ static __forceinline__ int pad(int e) { return e + (e >> PADSH); }
 };
 
-__device__ __forceinline__ int pad(int e) { return e + (e >> 4); }
-
-// Register r = 16 i + j of thread lt holds, in a non-last pass, element j of
-// butterfly beta = lt + i T: radix 16 on sub-transforms of size S = M >> 4p
-// with stride s = S / 16 -> position g S + m + j s, g = beta / s, m = beta % s.
-// In the last pass register r holds position PT lt + r.  The pass reads and
-// writes the same positions (in place).  LDS slot = pad(position); because s
-// divides 16 or is a multiple of 16 and m < s, pad(base + j s) =
-// pad(base) + j s + (j s >> 4): a base per butterfly, compile-time offsets.
-template <int LOG2M, int P>
+// Which positions thread lt's registers r = 16 i + j occupy in pass p (a pass
+// reads and writes the same positions):
+//   pass 0:        butterfly beta = lt + i T, element j at beta + j M/16
+//   pass p >= 1:   butterfly (g, m) = (NB (lt / s) + i, lt % s), element j
+//                  at g S + m + j s  -- a thread's NB butterflies share m,
+//                  hence their twiddles
+//   last pass:     positions PT lt + r.
+// LDS slot = pad(position) = pad(base) + j s + (j s >> PADSH): s divides 2^PADSH
+// or is a multiple of it, base is a multiple of S = 16 s plus m < s, so no
+// carry crosses a pad boundary -- one base per butterfly, constant offsets.
+// After pass 0 every sub-transform lies inside the positions owned by one wave
+// (a wave owns the contiguous range [64 PT w, 64 PT (w + 1))), so only the
+// exchange between passes 0 and 1 needs a workgroup barrier.
+template <class C, int P>
 struct PassGeom {
-  using C = Cfg<LOG2M>;
   static constexpr bool kLast = (P == C::NP - 1);
   static constexpr int S = kLast ? C::RLAST : (C::M >> (4 * P));
   static constexpr int s = kLast ? 1 : S / 16;
-  __device__ static __forceinline__ int m_of(int lt, int i) { return (lt + i * C::T) % s; }
+  __device__ static __forceinline__ int m_of(int lt) { return P == 0 ? lt : lt % s; }
   __device__ static __forceinline__ int base(int lt, int i) {
-    const int beta = lt + i * C::T;
-    return (beta / s) * S + (beta % s);
+    if (P == 0) return lt + i * C::T;
+    return (C::NB * (lt / s) + i) * S + (lt % s);
   }
-  __device__ static constexpr int off(int j) { return j * s + ((j * s) >> 4); }
+  __device__ static constexpr int off(int j) { return j * s + ((j * s) >> C::PADSH); }
 };
 
-template <int LOG2M, int P>
+template <class C, int P>
 __device__ __forceinline__ void lds_write(float2* lds, int lt, const float2* v) {
-  using C = Cfg<LOG2M>;
-  using G = PassGeom<LOG2M, P>;
+  using G = PassGeom<C, P>;
   if constexpr (G::kLast) {
-    float2* b = lds + pad(C::PT * lt);
+    float2* b = lds + C::pad(C::PT * lt);
 #pragma unroll
-    for (int r = 0; r < C::PT; ++r) b[r + (r >> 4)] = v[r];
+    for (int r = 0; r < C::PT; ++r) b[r + (r >> C::PADSH)] = v[r];
   } else {
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
-      float2* b = lds + pad(G::base(lt, i));
+      float2* b = lds + C::pad(G::base(lt, i));
 #pragma unroll
       for (int j = 0; j < 16; ++j) b[G::off(j)] = v[16 * i + j];
     }
   }
 }
 
-template <int LOG2M, int P>
+template <class C, int P>
 __device__ __forceinline__ void lds_read(const float2* lds, int lt, float2* v) {
-  using C = Cfg<LOG2M>;
-  using G = PassGeom<LOG2M, P>;
+  using G = PassGeom<C, P>;
   if constexpr (G::kLast) {
-    const float2* b = lds + pad(C::PT * lt);
+    const float2* b = lds + C::pad(C::PT * lt);
 #pragma unroll
-    for (int r = 0; r < C::PT; ++r) v[r] = b[r + (r >> 4)];
+    for (int r = 0; r < C::PT; ++r) v[r] = b[r + (r >> C::PADSH)];
   } else {
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
-      const float2* b = lds + pad(G::base(lt, i));
+      const float2* b = lds + C::pad(G::base(lt, i));
 #pragma unroll
       for (int j = 0; j < 16; ++j) v[16 * i + j] = b[G::off(j)];
     }
   }
 }
 
-// Forward pass p on registers (butterflies, then output twiddles).
-template <int LOG2M, int P>
-__device__ __forceinline__ void fwd_pass(float2* v, int lt) {
-  using C = Cfg<LOG2M>;
-  using G = PassGeom<LOG2M, P>;
+// Twiddle powers of pass p for thread lt: w = exp(-2 pi i m / S).  The load
+// is made opaque so the powers are recomputed per pass instead of being
+// shared across the kernel and kept live.
+template <class C, int P>
+__device__ __forceinline__ void pass_powers(int lt, float2* p) {
+  using G = PassGeom<C, P>;
+  if constexpr (!G::kLast) {
+    float2 w = g_twiddle[G::m_of(lt) * (DSSM_TWN / G::S)];
+    asm volatile("" : "+v"(w.x), "+v"(w.y));
+    powers16(w, p);
+  }
+}
+
+// Forward pass p on one register array: butterflies, then output twiddles.
+template <class C, int P>
+__device__ __forceinline__ void fwd_compute(float2* v, const float2* p) {
+  using G = PassGeom<C, P>;
   if constexpr (G::kLast) {
 #pragma unroll
     for (int i = 0; i < C::PT; i += C::RLAST) dftR<C::RLAST, false>(v + i);
@@ -305,72 +336,114 @@ __device__ __forceinline__ void fwd_pass(float2* v, int lt) {
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
       dft16<false>(v + 16 * i);
-      twiddle16<false>(v + 16 * i, g_twiddle[G::m_of(lt, i) * (DSSM_TWN / G::S)]);
+      if (P == 0 && i == 1) apply16<false, true>(v + 16 * i, p);
+      else apply16<false, false>(v + 16 * i, p);
     }
   }
 }
 
-// Inverse of pass p (conjugate input twiddles, then inverse butterflies).
-template <int LOG2M, int P>
-__device__ __forceinline__ void inv_pass(float2* v, int lt) {
-  using C = Cfg<LOG2M>;
-  using G = PassGeom<LOG2M, P>;
+// Inverse of pass p: conjugate input twiddles, then inverse butterflies.
+template <class C, int P>
+__device__ __forceinline__ void inv_compute(float2* v, const float2* p) {
+  using G = PassGeom<C, P>;
   if constexpr (G::kLast) {
 #pragma unroll
     for (int i = 0; i < C::PT; i += C::RLAST) dftR<C::RLAST, true>(v + i);
   } else {
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
-      twiddle16<true>(v + 16 * i, g_twiddle[G::m_of(lt, i) * (DSSM_TWN / G::S)]);
+      if (P == 0 && i == 1) apply16<true, true>(v + 16 * i, p);
+      else apply16<true, false>(v + 16 * i, p);
       dft16<true>(v + 16 * i);
     }
   }
 }
 
-// Forward transform.  On entry register r = 16 i + j holds the point
-// n(lt, r) = lt + T (i + j NB) (natural order); on exit register r holds the
-// bin at position PT lt + r.  All threads of the workgroup must call it
-// together (it contains barriers).
-template <int LOG2M, int P = 0>
-__device__ __forceinline__ void forward(float2* v, float2* lds, int lt) {
-  using C = Cfg<LOG2M>;
-  fwd_pass<LOG2M, P>(v, lt);
+// Orders the LDS accesses of one wave (the exchanges after pass 0 stay inside
+// the wave's own positions, so no workgroup barrier is needed): the LDS
+// executes a wave's accesses in issue order; this keeps the compiler from
+// moving them across.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Forward passes P .. NP-1 (P >= 1) of one array, wave-local.  Entry: v holds
+// pass-P inputs; exit: the bins at positions PT lt + r.
+template <class C, int P>
+__device__ __forceinline__ void fwd_tail(float2* v, float2* lds, int lt) {
+  float2 p[16];
+  pass_powers<C, P>(lt, p);
+  fwd_compute<C, P>(v, p);
   if constexpr (P + 1 < C::NP) {
-    lds_write<LOG2M, P>(lds, lt, v);
-    __syncthreads();
-    lds_read<LOG2M, P + 1>(lds, lt, v);
-    forward<LOG2M, P + 1>(v, lds, lt);
+    lds_write<C, P>(lds, lt, v);
+    wave_sync();
+    lds_read<C, P + 1>(lds, lt, v);
+    fwd_tail<C, P + 1>(v, lds, lt);
   }
 }
 
-// Inverse transform (unnormalised): bins at the last pass's positions on
-// entry, points at n(lt, r) on exit.
-template <int LOG2M, int P = Cfg<LOG2M>::NP - 1>
-__device__ __forceinline__ void inverse(float2* v, float2* lds, int lt) {
-  inv_pass<LOG2M, P>(v, lt);
-  if constexpr (P > 0) {
-    lds_write<LOG2M, P>(lds, lt, v);
-    __syncthreads();
-    lds_read<LOG2M, P - 1>(lds, lt, v);
-    inverse<LOG2M, P - 1>(v, lds, lt);
+// Inverse passes P .. 1 of one array, wave-local.  Entry: v holds pass-P
+// outputs (P = NP-1: the bins); exit: the pass-1 inputs at pass-1 positions.
+template <class C, int P = C::NP - 1>
+__device__ __forceinline__ void inv_head(float2* v, float2* lds, int lt) {
+  if constexpr (P >= 1) {
+    float2 p[16];
+    pass_powers<C, P>(lt, p);
+    inv_compute<C, P>(v, p);
+    if constexpr (P > 1) {
+      lds_write<C, P>(lds, lt, v);
+      wave_sync();
+      lds_read<C, P - 1>(lds, lt, v);
+      inv_head<C, P - 1>(v, lds, lt);
+    }
   }
+}
+
+// Forward transform of one array.  Entry: register r holds the point
+// nat(lt, r); exit: the bin at position PT lt + r.  One workgroup barrier;
+// all threads of the workgroup call it together.
+template <class C>
+__device__ __forceinline__ void forward1(float2* v, float2* lds, int lt) {
+  float2 p[16];
+  pass_powers<C, 0>(lt, p);
+  fwd_compute<C, 0>(v, p);
+  if constexpr (C::NP > 1) {
+    lds_write<C, 0>(lds, lt, v);
+    __syncthreads();
+    lds_read<C, 1>(lds, lt, v);
+    fwd_tail<C, 1>(v, lds, lt);
+  }
+}
+
+// Pass-0 inverse of an array whose passes NP-1 .. 1 were inverted by
+// inv_head (one workgroup barrier); exit: the points nat(lt, r).
+template <class C>
+__device__ __forceinline__ void inverse_finish(float2* v, float2* lds, int lt) {
+  if constexpr (C::NP > 1) {
+    lds_write<C, 1>(lds, lt, v);
+    __syncthreads();
+    lds_read<C, 0>(lds, lt, v);
+  }
+  float2 p[16];
+  pass_powers<C, 0>(lt, p);
+  inv_compute<C, 0>(v, p);
 }
 
 // Natural-order index of register r (= 16 i + j) of thread lt.
-template <int LOG2M>
+template <class C>
 __device__ __forceinline__ int nat(int lt, int r) {
-  using C = Cfg<LOG2M>;
   return lt + C::T * ((r >> 4) + (r & 15) * C::NB);
 }
 
-// v[r] *= exp(-+ i pi n(lt, r) / M) = t[lt] * exp(-+ i pi (i + j NB) / PT).
-template <int LOG2M, bool INV, int R = 0>
+// v[r] *= exp(-+ i pi n(lt, r) / M) / t[lt] = exp(-+ i pi (i + j NB) / PT).
+template <class C, bool INV, int R = 0>
 __device__ __forceinline__ void odd_twiddle_fixed(float2* v) {
-  using C = Cfg<LOG2M>;
   if constexpr (R < C::PT) {
     constexpr int k = ((R >> 4) + (R & 15) * C::NB) * (32 / C::PT);
     v[R] = rotpi32<k, INV>(v[R]);
-    odd_twiddle_fixed<LOG2M, INV, R + 1>(v);
+    odd_twiddle_fixed<C, INV, R + 1>(v);
   }
 }
 
@@ -380,12 +453,10 @@ __device__ __forceinline__ void odd_twiddle_fixed(float2* v) {
 // The backward DLR is a correlation with Re K_b, whose spectrum is the
 // conjugate (no wrap-around reaches the first L outputs on a 2M circle).
 template <int LOG2M>
-__global__ __launch_bounds__(Cfg<LOG2M>::WG) void spectrum_kernel(const float* __restrict__ reK,
-                                                                  const float* __restrict__ D,
-                                                                  int ndir, int H, int L,
-                                                                  float2* __restrict__ spec,
-                                                                  float* __restrict__ Deff) {
-  using C = Cfg<LOG2M>;
+__global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void spectrum_kernel(
+    const float* __restrict__ reK, const float* __restrict__ D, int ndir, int H, int L,
+    float2* __restrict__ spec, float* __restrict__ Deff) {
+  using C = Cfg<LOG2M, 16>;
   __shared__ float2 lds_all[C::G * C::LDSN];
   const int lt = threadIdx.x % C::T;
   const int gi = threadIdx.x / C::T;
@@ -401,17 +472,17 @@ __global__ __launch_bounds__(Cfg<LOG2M>::WG) void spectrum_kernel(const float* _
     const float* k = reK + ((size_t)d * H + h) * L;
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) {
-      const int n = nat<LOG2M>(lt, r);
+      const int n = nat<C>(lt, r);
       v[r] = make_float2((active && n < L) ? k[n] : 0.f, 0.f);
     }
     if (half) {
       const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * C::M))];
-      odd_twiddle_fixed<LOG2M, false>(v);
+      odd_twiddle_fixed<C, false>(v);
 #pragma unroll
       for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
     }
     if (d > 0) __syncthreads();  // the previous direction's last reads are done
-    forward<LOG2M>(v, lds, lt);
+    forward1<C>(v, lds, lt);
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) acc[r] = (d == 0) ? v[r] : cadd(acc[r], cconj(v[r]));
   }
@@ -427,16 +498,20 @@ __global__ __launch_bounds__(Cfg<LOG2M>::WG) void spectrum_kernel(const float* _
   }
 }
 
-// Convolution of a pair of batch rows (b1 = 2 pr, b2 = 2 pr + 1) of channel h.
-// u is deliberately not __restrict__: the odd half re-reads it after the
-// barriers of the even half instead of keeping the first read live.
+// Points per thread of the convolution.  16 (1024 threads at M = 16384, four
+// waves per SIMD) measured faster on MI355X than 32 (512 threads, two waves per
+// SIMD): 56 us against 76 us for the long-sequence workload.
 template <int LOG2M>
-__global__ __launch_bounds__(Cfg<LOG2M>::WG) void conv_kernel(const float* u,
-                                                              const float2* __restrict__ spec,
-                                                              const float* __restrict__ Deff,
-                                                              int B, int H, int L, int npairs,
-                                                              float* __restrict__ y) {
-  using C = Cfg<LOG2M>;
+constexpr int conv_pt() { return 16; }
+
+// Convolution of a pair of batch rows (b1 = 2 pr, b2 = 2 pr + 1) of channel
+// h.  Both halves of the 2M spectrum are transformed together: ve = z (even
+// bins), vo = z t (odd bins), where z = u[b1] + i u[b2].
+template <int LOG2M>
+__global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kernel(
+    const float* __restrict__ u, const float2* __restrict__ spec, const float* __restrict__ Deff,
+    int B, int H, int L, int npairs, float* __restrict__ y) {
+  using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   __shared__ float2 lds_all[C::G * C::LDSN];
   const int lt = threadIdx.x % C::T;
   const int gi = threadIdx.x / C::T;
@@ -449,64 +524,73 @@ __global__ __launch_bounds__(Cfg<LOG2M>::WG) void conv_kernel(const float* u,
   const bool has2 = active && b2 < B;
   const float* u1 = u + ((size_t)b1 * H + h) * L;
   const float* u2 = u + ((size_t)(has2 ? b2 : b1) * H + h) * L;
-  const float dsk = active ? Deff[h] : 0.f;
 
-  auto load_pair = [&](float2* v) {
+  float2 ve[C::PT], vo[C::PT];
 #pragma unroll
-    for (int r = 0; r < C::PT; ++r) {
-      const int n = nat<LOG2M>(lt, r);
-      float a = 0.f, b = 0.f;
-      if (active && n < L) {
-        a = u1[n];
-        if (has2) b = u2[n];
-      }
-      v[r] = make_float2(a, b);
+  for (int r = 0; r < C::PT; ++r) {
+    const int n = nat<C>(lt, r);
+    float a = 0.f, b = 0.f;
+    if (active && n < L) {
+      a = u1[n];
+      if (has2) b = u2[n];
     }
-  };
-
-  float2 acc[C::PT];
-  float2 v[C::PT];
-  load_pair(v);
-#pragma unroll
-  for (int r = 0; r < C::PT; ++r) acc[r] = cscale(v[r], dsk);
-
-  // even bins
-  {
-    forward<LOG2M>(v, lds, lt);
-    const float2* sp = spec + ((size_t)h * 2 + 0) * C::M + C::PT * lt;
-#pragma unroll
-    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], sp[r]);
-    inverse<LOG2M>(v, lds, lt);
-#pragma unroll
-    for (int r = 0; r < C::PT; ++r) acc[r] = cadd(acc[r], v[r]);
+    ve[r] = make_float2(a, b);
+    vo[r] = ve[r];
   }
-  // odd bins: pre-multiply by t[n] = exp(-i pi n / M), post-multiply by conj(t[n])
-  {
-    load_pair(v);
+  {  // odd bins: pre-multiply by t[n] = t[lt] exp(-i pi (i + j NB) / PT)
     const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * C::M))];
-    odd_twiddle_fixed<LOG2M, false>(v);
+    odd_twiddle_fixed<C, false>(vo);
 #pragma unroll
-    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
-    forward<LOG2M>(v, lds, lt);
-    const float2* sp = spec + ((size_t)h * 2 + 1) * C::M + C::PT * lt;
-#pragma unroll
-    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], sp[r]);
-    inverse<LOG2M>(v, lds, lt);
-    const float2 tlc = cconj(g_twiddle[lt * (DSSM_TWN / (2 * C::M))]);
-    odd_twiddle_fixed<LOG2M, true>(v);
-#pragma unroll
-    for (int r = 0; r < C::PT; ++r) acc[r] = cadd(acc[r], cmul(v[r], tlc));
+    for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], tl);
   }
-
+  const float2* se = spec + ((size_t)h * 2 + 0) * C::M + C::PT * lt;
+  const float2* so = spec + ((size_t)h * 2 + 1) * C::M + C::PT * lt;
+  // pass 0 of both halves (shared twiddles)
+  {
+    float2 p[16];
+    pass_powers<C, 0>(lt, p);
+    fwd_compute<C, 0>(ve, p);
+    fwd_compute<C, 0>(vo, p);
+  }
+  // even half: exchange, wave-local passes, product, inverse back to pass 0
+  if constexpr (C::NP > 1) {
+    lds_write<C, 0>(lds, lt, ve);
+    __syncthreads();
+    lds_read<C, 1>(lds, lt, ve);
+    fwd_tail<C, 1>(ve, lds, lt);
+  }
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[r]);
+  inv_head<C>(ve, lds, lt);
+  inverse_finish<C>(ve, lds, lt);
+  // odd half: its pass-0 positions are disjoint from every other thread's,
+  // so it may be written while others still read the even half's
+  if constexpr (C::NP > 1) {
+    lds_write<C, 0>(lds, lt, vo);
+    __syncthreads();
+    lds_read<C, 1>(lds, lt, vo);
+    fwd_tail<C, 1>(vo, lds, lt);
+  }
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[r]);
+  inv_head<C>(vo, lds, lt);
+  inverse_finish<C>(vo, lds, lt);
+  {  // y = ye + conj(t) yo + D u
+    const float2 tlc = cconj(g_twiddle[lt * (DSSM_TWN / (2 * C::M))]);
+    odd_twiddle_fixed<C, true>(vo);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) ve[r] = cadd(ve[r], cmul(vo[r], tlc));
+  }
   if (!active) return;
+  const float dsk = Deff[h];
   float* y1 = y + ((size_t)b1 * H + h) * L;
   float* y2 = y + ((size_t)b2 * H + h) * L;
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) {
-    const int n = nat<LOG2M>(lt, r);
+    const int n = nat<C>(lt, r);
     if (n < L) {
-      y1[n] = acc[r].x;
-      if (has2) y2[n] = acc[r].y;
+      y1[n] = fmaf(dsk, u1[n], ve[r].x);
+      if (has2) y2[n] = fmaf(dsk, u2[n], ve[r].y);
     }
   }
 }
@@ -514,7 +598,7 @@ __global__ __launch_bounds__(Cfg<LOG2M>::WG) void conv_kernel(const float* u,
 template <int LOG2M>
 hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, int L, float2* spec,
                            float* Deff, hipStream_t st) {
-  using C = Cfg<LOG2M>;
+  using C = Cfg<LOG2M, 16>;
   const int nprob = 2 * H;
   const int nblk = (nprob + C::G - 1) / C::G;
   hipLaunchKernelGGL(spectrum_kernel<LOG2M>, dim3(nblk), dim3(C::WG), 0, st, reK, D, ndir, H, L,
@@ -525,7 +609,7 @@ hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, in
 template <int LOG2M>
 hipError_t conv_launch(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
                        float* y, hipStream_t st) {
-  using C = Cfg<LOG2M>;
+  using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   const int npairs = (B + 1) / 2;
   const long nprob = (long)H * npairs;
   const long nblk = (nprob + C::G - 1) / C::G;

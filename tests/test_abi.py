@@ -75,7 +75,7 @@ def test_workspace_size_limits_and_empty():
         assert _ws(op, 0, 4, 4, 8) == (0, 0)
         assert _ws(op, 2, 0, 4, 8) == (0, 0)
         assert _ws(op, 2, 4, 4, 0) == (0, 0)
-    assert _ws(bd.OP_GEN, 0, 4, 4, 8)[1] > 0  # B is ignored by the generator
+    assert _ws(bd.OP_GEN, 0, 4, 4, 8) == (0, 0)  # the generator needs no workspace
     rc, n = _ws(bd.OP_FFT, 4, 128, 64, 16384)
     assert rc == 0 and n % 256 == 0 and n > 0
     rc2, n2 = _ws(bd.OP_FFT, 4, 128, 64, 16384, 1)
@@ -128,7 +128,6 @@ def test_gen_rejects_bad_arguments():
     p = _params({"D": None})  # D is not needed by the generator
     assert fn(ctypes.byref(p), ctypes.byref(good), 2, FAKE, FAKE * 4, 1 << 40, None) == bd.DSSM_ERR_INVALID_ARG
     assert fn(ctypes.byref(p), ctypes.byref(good), 0, None, FAKE * 4, 1 << 40, None) == bd.DSSM_ERR_INVALID_ARG
-    assert fn(ctypes.byref(p), ctypes.byref(good), 0, FAKE, FAKE * 4, 8, None) == bd.DSSM_ERR_WORKSPACE
     assert fn(ctypes.byref(_params({"W": None})), ctypes.byref(good), 0, FAKE, FAKE * 4, 1 << 40,
               None) == bd.DSSM_ERR_INVALID_ARG
     assert fn(ctypes.byref(p), ctypes.byref(bd.Shape(1, 0, 4, 32, 0)), 0, None, None, 0, None) == 0
@@ -172,7 +171,7 @@ def test_s5_workspace_and_validation():
     assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
 
 
-@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 5), ("dssm_forward_scan_timed", 3)])
+@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 4), ("dssm_forward_scan_timed", 3)])
 def test_timed_variants_validate_events(name, n):
     fn = getattr(bd.lib(), name)
     good = bd.Shape(2, 3, 4, 32, 0)
