@@ -95,11 +95,11 @@ __global__ __launch_bounds__(256) void s5_gemm_kernel(const float* __restrict__ 
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int ks = 0; ks < KS; ++ks) {
-    const v4f a = ap[(size_t)ks * 64];
+  // operands of k step ks: one float4 of A fragments, one float4 of B
+  auto load_b = [&](int ks) {
     const int k = ks * 4 + (lane >> 4);
     v4f bv = v4f{0.f, 0.f, 0.f, 0.f};
-    if (k < K) {
+    if (ks < KS && k < K) {
       const float* row = Bb + (size_t)k * L;
       if (vec) {
         bv = *reinterpret_cast<const v4f*>(row + jl);
@@ -108,11 +108,22 @@ __global__ __launch_bounds__(256) void s5_gemm_kernel(const float* __restrict__ 
         for (int c = 0; c < 4; ++c) bv[c] = (jl + c < L) ? row[jl + c] : 0.f;
       }
     }
+    return bv;
+  };
+  // one step of prefetch: the loads of step ks+1 are in flight while the 16
+  // MFMAs of step ks run
+  v4f a = ap[0];
+  v4f bv = load_b(0);
+  for (int ks = 0; ks < KS; ++ks) {
+    const v4f a_n = (ks + 1 < KS) ? ap[(size_t)(ks + 1) * 64] : a;
+    const v4f b_n = load_b(ks + 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], bv[c], acc[r][c], 0, 0, 0);
+    a = a_n;
+    bv = b_n;
   }
 
   // acc[r][c][v] holds row rb*64 + r*16 + 4*(lane/16) + v, column jl + c.
@@ -158,10 +169,17 @@ __device__ __forceinline__ float2 cm(float2 a, float2 b) {
 }
 
 // x[b,p,:] = scan of v[b,p,:] with multiplier lambda[p]; planar re/im rows.
+// Each tile of 4096 steps is staged through LDS (coalesced float4 global
+// accesses; lane l then owns steps 16 l .. 16 l + 15, padded one slot per 16
+// so the per-lane reads are conflict-free).
+constexpr int kPadT = kTile + kTile / 16;
+__device__ __forceinline__ int tpad(int e) { return e + (e >> 4); }
+
 __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restrict__ lam,
                                                          const float* __restrict__ v, int P, int L,
                                                          float* __restrict__ x) {
-  __shared__ float2 mu[kLevels + 1];  // lambda^(kSeg 2^j) for j <= 8 (j = 8: a whole tile)
+  __shared__ float sre[kPadT], sim[kPadT];
+  __shared__ float2 mu[kLevels + 1];  // lambda^(kSeg 2^j) for j <= 8
   __shared__ float2 blk[4];           // per-wave inclusive totals
   __shared__ float2 carry;
   const int p = blockIdx.x % P;
@@ -174,26 +192,47 @@ __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restric
     const double k = (double)kSeg * (double)(1 << t);
     const double lmag = 0.5 * log(lr * lr + li * li);
     const double ang = atan2(li, lr);
-    double s, c;
-    sincos(k * ang, &s, &c);
+    double sn, cs;
+    sincos(k * ang, &sn, &cs);
     const double m = exp(k * lmag);
-    mu[t] = make_float2((float)(m * c), (float)(m * s));
+    mu[t] = make_float2((float)(m * cs), (float)(m * sn));
   }
   if (t == 0) carry = make_float2(0.f, 0.f);
-  __syncthreads();
 
   const float* vre = v + ((size_t)b * P + p) * 2 * L;
   const float* vim = vre + L;
   float* xre = x + ((size_t)b * P + p) * 2 * L;
   float* xim = xre + L;
+  const bool vec = (L & 3) == 0;
 
   for (int base = 0; base < L; base += kTile) {
-    const int p0 = base + t * kSeg;
+    const int n = min(kTile, L - base);
+    // stage the tile (zero beyond L)
+    if (vec) {
+#pragma unroll
+      for (int k = 0; k < kTile / (4 * kLanes); ++k) {
+        const int e = 4 * (t + kLanes * k);
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+        if (e < n) {
+          a = *reinterpret_cast<const float4*>(vre + base + e);
+          c = *reinterpret_cast<const float4*>(vim + base + e);
+        }
+        const int q = tpad(e);  // e is a multiple of 4: the 4 slots stay contiguous
+        sre[q] = a.x; sre[q + 1] = a.y; sre[q + 2] = a.z; sre[q + 3] = a.w;
+        sim[q] = c.x; sim[q + 1] = c.y; sim[q + 2] = c.z; sim[q + 3] = c.w;
+      }
+    } else {
+      for (int e = t; e < kTile; e += kLanes) {
+        sre[tpad(e)] = e < n ? vre[base + e] : 0.f;
+        sim[tpad(e)] = e < n ? vim[base + e] : 0.f;
+      }
+    }
+    __syncthreads();
     float2 vv[kSeg];
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
-      const int q = p0 + i;
-      vv[i] = (q < L) ? make_float2(vre[q], vim[q]) : make_float2(0.f, 0.f);
+      const int q = 17 * t + i;  // tpad(16 t + i)
+      vv[i] = make_float2(sre[q], sim[q]);
     }
     // local end state
     float2 s = make_float2(0.f, 0.f);
@@ -246,21 +285,36 @@ __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restric
       q.y = __shfl(s.y, max(lane - 1, 0));
       xin = (t == 0) ? cin : (lane == 0 ? cw : q);
     }
-    __syncthreads();  // everyone has read `carry` and `blk`
+    __syncthreads();  // everyone has read `carry`, `blk` and its inputs
     if (t == kLanes - 1) carry = s;
-    // outputs
+    // outputs, back into the staging buffers
     float2 st = xin;
 #pragma unroll
     for (int i = 0; i < kSeg; ++i) {
       const float2 m = cm(lm, st);
       st = make_float2(m.x + vv[i].x, m.y + vv[i].y);
-      const int q = p0 + i;
-      if (q < L) {
-        xre[q] = st.x;
-        xim[q] = st.y;
+      const int q = 17 * t + i;
+      sre[q] = st.x;
+      sim[q] = st.y;
+    }
+    __syncthreads();
+    if (vec) {
+#pragma unroll
+      for (int k = 0; k < kTile / (4 * kLanes); ++k) {
+        const int e = 4 * (t + kLanes * k);
+        if (e < n) {
+          const int q = tpad(e);
+          *reinterpret_cast<float4*>(xre + base + e) = make_float4(sre[q], sre[q + 1], sre[q + 2], sre[q + 3]);
+          *reinterpret_cast<float4*>(xim + base + e) = make_float4(sim[q], sim[q + 1], sim[q + 2], sim[q + 3]);
+        }
+      }
+    } else {
+      for (int e = t; e < n; e += kLanes) {
+        xre[base + e] = sre[tpad(e)];
+        xim[base + e] = sim[tpad(e)];
       }
     }
-    __syncthreads();  // carry visible before the next tile
+    __syncthreads();  // staging buffers and carry are reused by the next tile
   }
 }
 

@@ -68,108 +68,153 @@ __global__ __launch_bounds__(256) void scan_consts_kernel(const float* __restric
   }
 }
 
-// One direction of one mode over the current tile.
-//   uu/yy: this lane's SEG inputs / output accumulators (positions ascending).
-//   carry_ptr: per-(channel, mode) state entering the tile (read if
-//   use_carry) and leaving it (written by the channel's last lane if
-//   write_carry).
-// Lanes of a channel are numbered along the scan direction ("virtual" lanes);
-// they form blocks of up to 64 inside one wave.  Within a block the scan uses
-// shuffles; blocks of a channel spanning several waves are chained through LDS.
-template <int SEG, bool REV>
-__device__ __forceinline__ void scan_mode(const float* uu, float* yy, const float* __restrict__ cst,
-                                          int cl, int lpc, float2* xs, float2* carry_ptr,
-                                          bool use_carry, bool write_carry) {
-  const float2 lam = make_float2(cst[0], cst[1]);
-  const float2 w = make_float2(cst[2], cst[3]);
+__device__ __forceinline__ float2 rec_step(float2 lam, float2 x, float u) {
+  // lambda * x + u
+  return make_float2(fmaf(lam.x, x.x, fmaf(-lam.y, x.y, u)), fmaf(lam.x, x.y, lam.y * x.x));
+}
 
-  // 1. local end state from a zero start
-  float2 x = make_float2(0.f, 0.f);
+__device__ __forceinline__ float2 cfma(float2 m, float2 p, float2 acc) {  // acc + m p
+  return make_float2(fmaf(m.x, p.x, fmaf(-m.y, p.y, acc.x)), fmaf(m.x, p.y, fmaf(m.y, p.x, acc.y)));
+}
+
+// Two modes (a, b) of one direction over the current tile: two independent
+// recurrences per lane in flight.  uu/yy: this lane's SEG inputs / output
+// accumulators (positions ascending); carry_a/b: per-(channel, mode) state
+// entering the tile (read if use_carry) and leaving it (written by the
+// channel's last lane if write_carry).  Lanes of a channel are numbered along
+// the scan direction ("virtual" lanes) in blocks of up to 64 per wave: the
+// scan uses shuffles inside a block and LDS between the blocks of a channel.
+template <int SEG, bool REV>
+__device__ __forceinline__ void scan_pair(const float* uu, float* yy, const float* __restrict__ ca,
+                                          const float* __restrict__ cb, bool has_b, int cl,
+                                          int lpc, float4* xs, float2* carry_a, float2* carry_b,
+                                          bool use_carry, bool write_carry) {
+  const float2 la = make_float2(ca[0], ca[1]);
+  const float2 lb = make_float2(cb[0], cb[1]);
+  const float2 wa = make_float2(ca[2], ca[3]);
+  const float2 wb = has_b ? make_float2(cb[2], cb[3]) : make_float2(0.f, 0.f);
+
+  // 1. local end states from a zero start
+  float2 xa = make_float2(0.f, 0.f), xb = xa;
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
     const float uv = uu[REV ? SEG - 1 - i : i];
-    x = make_float2(fmaf(lam.x, x.x, fmaf(-lam.y, x.y, uv)), fmaf(lam.x, x.y, lam.y * x.x));
+    xa = rec_step(la, xa, uv);
+    xb = rec_step(lb, xb, uv);
   }
-  const int vl = REV ? lpc - 1 - cl : cl;  // virtual lane along the scan
-  const int wb = lpc < 64 ? lpc : 64;      // virtual lanes per block
-  const int vlw = vl & (wb - 1);           // virtual lane inside its block
+  const int vl = REV ? lpc - 1 - cl : cl;
+  const int wbk = lpc < 64 ? lpc : 64;
+  const int vlw = vl & (wbk - 1);
   const int lane = threadIdx.x & 63;
-  float2 cin = make_float2(0.f, 0.f);
+  float2 cin_a = make_float2(0.f, 0.f), cin_b = cin_a;
   if (use_carry) {
-    cin = *carry_ptr;
+    cin_a = *carry_a;
+    if (has_b) cin_b = *carry_b;
     if (vl == 0) {  // the tile's first segment starts from the carried state
-      const float2 t = cmulf(make_float2(cst[4], cst[5]), cin);
-      x.x += t.x;
-      x.y += t.y;
+      xa = cfma(make_float2(ca[4], ca[5]), cin_a, xa);
+      xb = cfma(make_float2(cb[4], cb[5]), cin_b, xb);
     }
   }
   // 2a. inclusive scan inside the block: X(v) = sum_{v' <= v} mu^(v - v') x(v')
-  for (int j = 0; (1 << j) < wb; ++j) {
+  for (int j = 0; (1 << j) < wbk; ++j) {
     const int o = 1 << j;
     const int src = min(max(REV ? lane + o : lane - o, 0), 63);
-    float2 p;
-    p.x = __shfl(x.x, src);
-    p.y = __shfl(x.y, src);
+    float2 pa, pb;
+    pa.x = __shfl(xa.x, src);
+    pa.y = __shfl(xa.y, src);
+    pb.x = __shfl(xb.x, src);
+    pb.y = __shfl(xb.y, src);
     if (vlw >= o) {
-      const float2 t = cmulf(make_float2(cst[4 + 2 * j], cst[5 + 2 * j]), p);
-      x.x += t.x;
-      x.y += t.y;
+      xa = cfma(make_float2(ca[4 + 2 * j], ca[5 + 2 * j]), pa, xa);
+      xb = cfma(make_float2(cb[4 + 2 * j], cb[5 + 2 * j]), pb, xb);
     }
   }
-  // 2b. blocks of one channel in different waves: carry into block vb is
-  //     C = sum_{k < vb} nu^(vb-1-k) X_k(last), nu = lambda^(64 SEG); each lane
-  //     adds mu^(vlw+1) C.
-  float2 cblk = make_float2(0.f, 0.f);
+  // 2b. blocks of one channel in different waves: the carry into block vb is
+  //     C = sum_{k < vb} nu^(vb-1-k) X_k(last), nu = lambda^(64 SEG); every
+  //     lane adds mu^(vlw+1) C.
+  float2 ka = make_float2(0.f, 0.f), kb = ka;
   if (lpc > 64) {
     const int vb = vl >> 6;
     const int ch = threadIdx.x / lpc;
     __syncthreads();
-    if (vlw == 63) xs[ch * 4 + vb] = x;
+    if (vlw == 63) xs[ch * 4 + vb] = make_float4(xa.x, xa.y, xb.x, xb.y);
     __syncthreads();
-    const float2 nu = make_float2(cst[4 + 12], cst[5 + 12]);
+    const float2 nua = make_float2(ca[16], ca[17]), nub = make_float2(cb[16], cb[17]);
     for (int k = 0; k < vb; ++k) {
-      const float2 t = cmulf(nu, cblk);
-      const float2 xk = xs[ch * 4 + k];
-      cblk = make_float2(t.x + xk.x, t.y + xk.y);
+      const float4 t = xs[ch * 4 + k];
+      ka = cfma(nua, ka, make_float2(t.x, t.y));
+      kb = cfma(nub, kb, make_float2(t.z, t.w));
     }
-    float2 pw = make_float2(1.f, 0.f);
+    float2 pwa = make_float2(1.f, 0.f), pwb = pwa;
     const int e = vlw + 1;
 #pragma unroll
-    for (int j = 0; j < 7; ++j)
-      if ((e >> j) & 1) pw = cmulf(pw, make_float2(cst[4 + 2 * j], cst[5 + 2 * j]));
-    const float2 t = cmulf(pw, cblk);
-    x.x += t.x;
-    x.y += t.y;
+    for (int j = 0; j < 7; ++j) {
+      if ((e >> j) & 1) {
+        pwa = cfma(pwa, make_float2(ca[4 + 2 * j], ca[5 + 2 * j]), make_float2(0.f, 0.f));
+        pwb = cfma(pwb, make_float2(cb[4 + 2 * j], cb[5 + 2 * j]), make_float2(0.f, 0.f));
+      }
+    }
+    xa = cfma(pwa, ka, xa);
+    xb = cfma(pwb, kb, xb);
   }
   // exclusive carry-in: the previous virtual lane's inclusive state
-  float2 xin;
+  float2 ina, inb;
   {
     const int src = min(max(REV ? lane + 1 : lane - 1, 0), 63);
-    float2 p;
-    p.x = __shfl(x.x, src);
-    p.y = __shfl(x.y, src);
-    xin = (vl == 0) ? cin : ((vlw == 0) ? cblk : p);
+    float2 pa, pb;
+    pa.x = __shfl(xa.x, src);
+    pa.y = __shfl(xa.y, src);
+    pb.x = __shfl(xb.x, src);
+    pb.y = __shfl(xb.y, src);
+    ina = (vl == 0) ? cin_a : ((vlw == 0) ? ka : pa);
+    inb = (vl == 0) ? cin_b : ((vlw == 0) ? kb : pb);
   }
-  if (write_carry && vl == lpc - 1) *carry_ptr = x;  // state leaving the tile
+  if (write_carry && vl == lpc - 1) {  // state leaving the tile
+    *carry_a = xa;
+    if (has_b) *carry_b = xb;
+  }
   // 3. outputs from the true carry-in
-  x = xin;
+  xa = ina;
+  xb = inb;
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
     const int s = REV ? SEG - 1 - i : i;
     const float uv = uu[s];
-    x = make_float2(fmaf(lam.x, x.x, fmaf(-lam.y, x.y, uv)), fmaf(lam.x, x.y, lam.y * x.x));
-    yy[s] = fmaf(w.x, x.x, fmaf(-w.y, x.y, yy[s]));
+    xa = rec_step(la, xa, uv);
+    xb = rec_step(lb, xb, uv);
+    float acc = yy[s];
+    acc = fmaf(wa.x, xa.x, acc);
+    acc = fmaf(-wa.y, xa.y, acc);
+    acc = fmaf(wb.x, xb.x, acc);
+    acc = fmaf(-wb.y, xb.y, acc);
+    yy[s] = acc;
+  }
+}
+
+// All modes of one direction over the current tile, two at a time.
+template <int SEG, bool REV>
+__device__ __forceinline__ void scan_modes(const float* uu, float* yy,
+                                           const float* __restrict__ cst0, int N, int cl, int lpc,
+                                           float4* xs, float2* cc, bool use_carry,
+                                           bool write_carry, bool sync_each) {
+  for (int n = 0; n < N; n += 2) {
+    const bool has_b = n + 1 < N;
+    if (sync_each) __syncthreads();  // orders the carry write and reads between tiles
+    scan_pair<SEG, REV>(uu, yy, cst0 + (size_t)n * kNConst,
+                        cst0 + (size_t)(has_b ? n + 1 : n) * kNConst, has_b, cl, lpc, xs,
+                        cc + n, cc + (has_b ? n + 1 : n), use_carry, write_carry);
   }
 }
 
 // Grid: (channel groups of one h) x H.  Workgroup = 256 lanes = cpg channels
-// (batch rows b0 .. b0+cpg-1 of channel h) x lpc lanes.
-template <int SEG>
+// (batch rows b0 .. b0+cpg-1 of channel h) x lpc lanes.  MULTI: the sequence
+// spans several tiles and carries cross them through `carry`.
+template <int SEG, bool MULTI>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const float* __restrict__ u, const float* __restrict__ consts, const float* __restrict__ D,
     float2* __restrict__ carry, int B, int H, int N, int L, int ndir, int lpc, int ntile,
     float* __restrict__ y) {
-  __shared__ float2 xs[8];  // block totals: 2 channels x 4 blocks at most
+  __shared__ float4 xs[8];  // block totals (two modes): 2 channels x 4 blocks at most
   const int cpg = kScanThreads / lpc;
   const int h = blockIdx.y;
   const int cl = threadIdx.x % lpc;
@@ -183,67 +228,52 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
   for (int d = 0; d < ndir; ++d) deff += D[(size_t)d * H + h];
 
   float uu[SEG], yy[SEG];
-  auto load_u = [&](int t) {
-    const int p0 = t * tile + cl * SEG;
+  if (!MULTI) {
+    const int p0 = cl * SEG;
 #pragma unroll
     for (int i = 0; i < SEG; ++i) {
       const int p = p0 + i;
       uu[i] = (active && p < L) ? uc[p] : 0.f;
+      yy[i] = deff * uu[i];
     }
-  };
-  auto store_y = [&](int t) {
-    const int p0 = t * tile + cl * SEG;
+    for (int d = 0; d < ndir; ++d) {
+      const float* cst0 = consts + ((size_t)d * H + h) * N * kNConst;
+      if (d == 0)
+        scan_modes<SEG, false>(uu, yy, cst0, N, cl, lpc, xs, cc, false, false, false);
+      else
+        scan_modes<SEG, true>(uu, yy, cst0, N, cl, lpc, xs, cc, false, false, false);
+    }
 #pragma unroll
     for (int i = 0; i < SEG; ++i) {
       const int p = p0 + i;
       if (active && p < L) yc[p] = yy[i];
     }
-  };
-
-  if (ntile == 1) {
-    load_u(0);
-#pragma unroll
-    for (int i = 0; i < SEG; ++i) yy[i] = deff * uu[i];
-    for (int d = 0; d < ndir; ++d) {
-      const float* cst0 = consts + ((size_t)d * H + h) * N * kNConst;
-      for (int n = 0; n < N; ++n) {
-        if (d == 0)
-          scan_mode<SEG, false>(uu, yy, cst0 + (size_t)n * kNConst, cl, lpc, xs, nullptr, false, false);
-        else
-          scan_mode<SEG, true>(uu, yy, cst0 + (size_t)n * kNConst, cl, lpc, xs, nullptr, false, false);
-      }
-    }
-    store_y(0);
     return;
   }
 
-  // Several tiles: the state of each mode is carried between tiles through
-  // `carry`; the backward direction walks the tiles in reverse and adds to y.
+  // Several tiles: the backward direction walks the tiles in reverse and adds
+  // to the y written by the forward direction.
   for (int d = 0; d < ndir; ++d) {
     const float* cst0 = consts + ((size_t)d * H + h) * N * kNConst;
     for (int k = 0; k < ntile; ++k) {
       const int t = d == 0 ? k : ntile - 1 - k;
-      load_u(t);
-      if (d == 0) {
+      const int p0 = t * tile + cl * SEG;
 #pragma unroll
-        for (int i = 0; i < SEG; ++i) yy[i] = deff * uu[i];
-      } else {
-        const int p0 = t * tile + cl * SEG;
+      for (int i = 0; i < SEG; ++i) {
+        const int p = p0 + i;
+        uu[i] = (active && p < L) ? uc[p] : 0.f;
+        if (d == 0) yy[i] = deff * uu[i];
+        else yy[i] = (active && p < L) ? yc[p] : 0.f;
+      }
+      if (d == 0)
+        scan_modes<SEG, false>(uu, yy, cst0, N, cl, lpc, xs, cc, k > 0, active, true);
+      else
+        scan_modes<SEG, true>(uu, yy, cst0, N, cl, lpc, xs, cc, k > 0, active, true);
 #pragma unroll
-        for (int i = 0; i < SEG; ++i) yy[i] = (active && p0 + i < L) ? yc[p0 + i] : 0.f;
+      for (int i = 0; i < SEG; ++i) {
+        const int p = p0 + i;
+        if (active && p < L) yc[p] = yy[i];
       }
-      for (int n = 0; n < N; ++n) {
-        // lanes of one channel read the carry written by its last lane in the
-        // previous tile; a barrier orders the write and the reads
-        __syncthreads();
-        if (d == 0)
-          scan_mode<SEG, false>(uu, yy, cst0 + (size_t)n * kNConst, cl, lpc, xs, cc + n, k > 0,
-                                active);
-        else
-          scan_mode<SEG, true>(uu, yy, cst0 + (size_t)n * kNConst, cl, lpc, xs, cc + n, k > 0,
-                               active);
-      }
-      store_y(t);
       __syncthreads();
     }
   }
@@ -254,8 +284,12 @@ void scan_launch(const float* u, const float* consts, const float* D, float2* ca
                  int N, int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st) {
   const int cpg = kScanThreads / plan.lpc;
   const dim3 grid((unsigned)((B + cpg - 1) / cpg), (unsigned)H);
-  hipLaunchKernelGGL(scan_kernel<SEG>, grid, dim3(kScanThreads), 0, st, u, consts, D, carry, B, H,
-                     N, L, ndir, plan.lpc, plan.ntile, y);
+  if (plan.ntile == 1)
+    hipLaunchKernelGGL((scan_kernel<SEG, false>), grid, dim3(kScanThreads), 0, st, u, consts, D,
+                       carry, B, H, N, L, ndir, plan.lpc, plan.ntile, y);
+  else
+    hipLaunchKernelGGL((scan_kernel<SEG, true>), grid, dim3(kScanThreads), 0, st, u, consts, D,
+                       carry, B, H, N, L, ndir, plan.lpc, plan.ntile, y);
 }
 
 }  // namespace
