@@ -29,9 +29,9 @@ hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, 
 // ---------------------------------------------------------------------------
 // FFT convolution (fft.hip)
 // ---------------------------------------------------------------------------
-// Spectrum tables: spec[h, half, M] float2, position-ordered (the order the
-// in-place decimation-in-frequency passes leave the bins in), scaled by
-// 1/(2M).  half 0 holds the even bins of the 2M-point transform of the
+// Spectrum tables: spec[h, half, M] float2 in transform order (the order the
+// in-place decimation-in-frequency passes leave the bins in; the bin at
+// position 16 t + r is stored at r M/16 + t), scaled by 1/(2M).  half 0 holds the even bins of the 2M-point transform of the
 // zero-padded real kernel, half 1 the odd bins.  For ndir = 2 the backward
 // kernel enters conjugated.  Also writes Deff[h] = sum_d D[d,h].
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,

@@ -105,24 +105,39 @@ __global__ __launch_bounds__(256) void gen_kernel(const float* __restrict__ log_
       const int part = kq & 1;
       const int qa = 16 * w + (lane & 15);
       const int steps = (2 * nn + 3) / 4;
-      for (int ks = 0; ks < steps; ++ks) {
+      // operands of one k step: a (A column) and b[c] / bi[c] (B rows)
+      auto load = [&](int ks, float& a, float* b, float* bi) {
         const int kk = 4 * ks + kq;  // row 2n + part
         const bool inrow = kk < 2 * nn;
-        // A = [Re A, -Im A] along k'
-        float a = inrow ? sA[kk * kRow + qa] : 0.f;
+        a = inrow ? sA[kk * kRow + qa] : 0.f;  // A = [Re A, -Im A] along k'
         if (part) a = -a;
         const float* pr = sP + kk * kRow + (lane & 15);
         const float* pr_sw = sP + (kk ^ 1) * kRow + (lane & 15);  // other part of the mode
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float b = inrow ? pr[16 * c] : 0.f;  // [Re P; Im P]
-          acc_re[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc_re[c], 0, 0, 0);
+          b[c] = inrow ? pr[16 * c] : 0.f;  // [Re P; Im P]
           if (kComplex) {
-            // Im K: [Re A, -Im A] . [Im P; -Re P]
-            float bi = inrow ? pr_sw[16 * c] : 0.f;
-            if (part) bi = -bi;
-            acc_im[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bi, acc_im[c], 0, 0, 0);
+            const float v = inrow ? pr_sw[16 * c] : 0.f;  // [Im P; -Re P]
+            bi[c] = part ? -v : v;
           }
+        }
+      };
+      float a, b[4], bi[4];
+      load(0, a, b, bi);
+      for (int ks = 0; ks < steps; ++ks) {
+        float an, bn[4], bin[4];
+        load(min(ks + 1, steps - 1), an, bn, bin);  // prefetch the next step
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc_re[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[c], acc_re[c], 0, 0, 0);
+          if (kComplex)
+            acc_im[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bi[c], acc_im[c], 0, 0, 0);
+        }
+        a = an;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          b[c] = bn[c];
+          bi[c] = bin[c];
         }
       }
     }

@@ -488,9 +488,10 @@ __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void spectrum_kernel(
   }
   if (!active) return;
   const float scale = 1.0f / (2.0f * (float)C::M);
-  float2* out = spec + ((size_t)h * 2 + half) * C::M + C::PT * lt;
+  // bin at position PT lt + r is stored at r T + lt (coalesced across lanes)
+  float2* out = spec + ((size_t)h * 2 + half) * C::M + lt;
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) out[r] = cscale(acc[r], scale);
+  for (int r = 0; r < C::PT; ++r) out[(size_t)r * C::T] = cscale(acc[r], scale);
   if (half == 0 && lt == 0) {
     float sum = 0.f;
     for (int d = 0; d < ndir; ++d) sum += D[(size_t)d * H + h];
@@ -543,8 +544,11 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], tl);
   }
-  const float2* se = spec + ((size_t)h * 2 + 0) * C::M + C::PT * lt;
-  const float2* so = spec + ((size_t)h * 2 + 1) * C::M + C::PT * lt;
+  // spectrum bin at position PT lt + r lives at r T + lt (as the spectrum kernel,
+  // which uses the same PT, stores it)
+  static_assert(C::PT == Cfg<LOG2M, 16>::PT, "spectrum layout is shared with spectrum_kernel");
+  const float2* se = spec + ((size_t)h * 2 + 0) * C::M + lt;
+  const float2* so = spec + ((size_t)h * 2 + 1) * C::M + lt;
   // pass 0 of both halves (shared twiddles)
   {
     float2 p[16];
@@ -560,7 +564,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
     fwd_tail<C, 1>(ve, lds, lt);
   }
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[r]);
+  for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[(size_t)r * C::T]);
   inv_head<C>(ve, lds, lt);
   inverse_finish<C>(ve, lds, lt);
   // odd half: its pass-0 positions are disjoint from every other thread's,
@@ -572,7 +576,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
     fwd_tail<C, 1>(vo, lds, lt);
   }
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[r]);
+  for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[(size_t)r * C::T]);
   inv_head<C>(vo, lds, lt);
   inverse_finish<C>(vo, lds, lt);
   {  // y = ye + conj(t) yo + D u
