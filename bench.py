@@ -129,6 +129,28 @@ def time_s5(steps, warmup, hip):
     }
 
 
+def time_copy(src, dst, reps, hip):
+    """A plain device copy of `src` into `dst` (torch's copy kernel): the
+    practically attainable HBM rate, and the calibration kernel of known size
+    for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    dst.copy_(src)
+    ev = hip.create(2)
+    torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.h.hipEventRecord(ctypes.c_void_p(ev[0]), stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    hip.h.hipEventRecord(ctypes.c_void_p(ev[1]), stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(ev[0], ev[1]) / reps
+    hip.destroy(ev)
+    nbytes = 2 * src.numel() * src.element_size()
+    return {"bytes_per_copy": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(x, bi, y_gpu):
     """The float64 oracle as it stands, single process, on the host: the
     sequential recurrence over the whole workload, plus the direct O(L^2) sum
@@ -197,6 +219,7 @@ def main():
                           device="cuda")
     hip = HipEvents()
 
+    copy = time_copy(us[1], ys[1], 10, hip)
     ms, stages, gpu_ms = time_path("fft", dev, us, ys, ws_fft, a.steps, a.warmup, bi, hip)
     y_fft = ys[(a.steps - 1) % a.rotate].cpu().numpy()
     ms_scan, stages_scan, gpu_scan = time_path("scan", dev, us, ys, ws_scan, a.scan_steps,
@@ -247,6 +270,7 @@ def main():
                           "stage_ms": {"consts": stages_scan[0], "scan": stages_scan[1]},
                           "gpu_ms_events": gpu_scan},
             "rotated_sets": a.rotate,
+            "device_copy": copy,
             "s5_path": time_s5(max(2, a.scan_steps), 2, hip),
         },
     }

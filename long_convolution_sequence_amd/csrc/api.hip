@@ -80,7 +80,7 @@ int check_params(const dssm_dlr_params* p, bool need_d) {
 
 // Workspace layout, every region aligned to 256 bytes.
 struct Layout {
-  size_t reK = 0, spec = 0, deff = 0, consts = 0, carry = 0, total = 0;
+  size_t reK = 0, spec = 0, consts = 0, carry = 0, total = 0;
 };
 
 Layout layout(int op, const dssm_shape* s) {
@@ -97,7 +97,6 @@ Layout layout(int op, const dssm_shape* s) {
     const size_t M = (size_t)1 << fft_log2m(s->L);
     l.reK = take(ndh * L * sizeof(float));
     l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
-    l.deff = take((size_t)s->H * sizeof(float));
   }
   if (op == DSSM_OP_SCAN) {
     const ScanPlan plan = scan_plan(s->B, s->L);
@@ -208,12 +207,11 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
     if ((rc = mark(1))) return rc;
     const int log2m = fft_log2m(s->L);
     float2* spec = at<float2>(ws, l.spec);
-    float* deff = at<float>(ws, l.deff);
-    if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, deff, st),
+    if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st),
                         "spectrum launch")))
       return rc;
     if ((rc = mark(2))) return rc;
-    if ((rc = hip_check(launch_conv(u, spec, deff, s->B, s->H, s->L, log2m, y, st),
+    if ((rc = hip_check(launch_conv(u, spec, s->B, s->H, s->L, log2m, y, st),
                         "conv launch")))
       return rc;
     if ((rc = mark(3))) return rc;

@@ -31,16 +31,17 @@ hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, 
 // ---------------------------------------------------------------------------
 // Spectrum tables: spec[h, half, M] float2 in transform order (the order the
 // in-place decimation-in-frequency passes leave the bins in; the bin at
-// position 16 t + r is stored at r M/16 + t), scaled by 1/(2M).  half 0 holds the even bins of the 2M-point transform of the
-// zero-padded real kernel, half 1 the odd bins.  For ndir = 2 the backward
-// kernel enters conjugated.  Also writes Deff[h] = sum_d D[d,h].
+// position 16 t + r is stored at r M/16 + t), scaled by 1/(2M).  half 0 holds
+// the even bins of the 2M-point transform of the zero-padded real kernel,
+// half 1 the odd bins.  For ndir = 2 the backward kernel enters conjugated.
+// sum_d D[d,h] is added to every bin (the feed-through as tap 0).
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
-                           float2* spec, float* Deff, hipStream_t st);
+                           float2* spec, hipStream_t st);
 
 // y[b,h,:L] = first L samples of the 2M-circular convolution of u[b,h,:] with
-// the kernel whose spectrum is spec[h], plus Deff[h] u.
-hipError_t launch_conv(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
-                       int log2m, float* y, hipStream_t st);
+// the kernel whose spectrum is spec[h] (D u included through tap 0).
+hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, int log2m, float* y,
+                       hipStream_t st);
 
 int fft_log2m(int L);  // log2 of M = max(16, next power of two >= L)
 

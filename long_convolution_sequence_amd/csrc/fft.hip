@@ -448,14 +448,16 @@ __device__ __forceinline__ void odd_twiddle_fixed(float2* v) {
 }
 
 // Spectrum of the (bidirectional) kernel: one transform per (h, half).
-//   spec[h, half, pos] = ( F_f + conj(F_b) ) / (2M),
+//   spec[h, half, pos] = ( F_f + conj(F_b) + D_f + D_b ) / (2M),
 //   F_d = DFT_M( pad(Re K[d,h]) * t^half ),  t[n] = exp(-i pi n / M).
+// The feed-through D u is the convolution with D at tap 0, whose transform is
+// the constant D: adding it to every bin makes the convolution produce y + D u.
 // The backward DLR is a correlation with Re K_b, whose spectrum is the
 // conjugate (no wrap-around reaches the first L outputs on a 2M circle).
 template <int LOG2M>
 __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void spectrum_kernel(
     const float* __restrict__ reK, const float* __restrict__ D, int ndir, int H, int L,
-    float2* __restrict__ spec, float* __restrict__ Deff) {
+    float2* __restrict__ spec) {
   using C = Cfg<LOG2M, 16>;
   __shared__ float2 lds_all[C::G * C::LDSN];
   const int lt = threadIdx.x % C::T;
@@ -487,16 +489,14 @@ __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void spectrum_kernel(
     for (int r = 0; r < C::PT; ++r) acc[r] = (d == 0) ? v[r] : cadd(acc[r], cconj(v[r]));
   }
   if (!active) return;
+  float deff = 0.f;
+  for (int d = 0; d < ndir; ++d) deff += D[(size_t)d * H + h];
   const float scale = 1.0f / (2.0f * (float)C::M);
   // bin at position PT lt + r is stored at r T + lt (coalesced across lanes)
   float2* out = spec + ((size_t)h * 2 + half) * C::M + lt;
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) out[(size_t)r * C::T] = cscale(acc[r], scale);
-  if (half == 0 && lt == 0) {
-    float sum = 0.f;
-    for (int d = 0; d < ndir; ++d) sum += D[(size_t)d * H + h];
-    Deff[h] = sum;
-  }
+  for (int r = 0; r < C::PT; ++r)
+    out[(size_t)r * C::T] = cscale(make_float2(acc[r].x + deff, acc[r].y), scale);
 }
 
 // Points per thread of the convolution.  16 (1024 threads at M = 16384, four
@@ -510,14 +510,19 @@ constexpr int conv_pt() { return 16; }
 // bins), vo = z t (odd bins), where z = u[b1] + i u[b2].
 template <int LOG2M>
 __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kernel(
-    const float* __restrict__ u, const float2* __restrict__ spec, const float* __restrict__ Deff,
-    int B, int H, int L, int npairs, float* __restrict__ y) {
+    const float* __restrict__ u, const float2* __restrict__ spec, int B, int H, int L, int npairs,
+    float* __restrict__ y) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   __shared__ float2 lds_all[C::G * C::LDSN];
   const int lt = threadIdx.x % C::T;
   const int gi = threadIdx.x / C::T;
   float2* lds = lds_all + gi * C::LDSN;
-  const int prob = blockIdx.x * C::G + gi;
+  // Workgroup i runs on XCD i % 8; when the grid divides by 8, consecutive
+  // problems -- the pairs of one channel, which read the same spectrum -- are
+  // placed on the same XCD so the second read is served by its L2.
+  const int nblk = gridDim.x;
+  const int blk = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int prob = blk * C::G + gi;
   const bool active = prob < H * npairs;
   const int h = active ? prob / npairs : 0;
   const int pr = active ? prob % npairs : 0;
@@ -579,46 +584,45 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[(size_t)r * C::T]);
   inv_head<C>(vo, lds, lt);
   inverse_finish<C>(vo, lds, lt);
-  {  // y = ye + conj(t) yo + D u
+  {  // y = ye + conj(t) yo (D u is already in the spectrum)
     const float2 tlc = cconj(g_twiddle[lt * (DSSM_TWN / (2 * C::M))]);
     odd_twiddle_fixed<C, true>(vo);
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) ve[r] = cadd(ve[r], cmul(vo[r], tlc));
   }
   if (!active) return;
-  const float dsk = Deff[h];
   float* y1 = y + ((size_t)b1 * H + h) * L;
   float* y2 = y + ((size_t)b2 * H + h) * L;
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) {
     const int n = nat<C>(lt, r);
     if (n < L) {
-      y1[n] = fmaf(dsk, u1[n], ve[r].x);
-      if (has2) y2[n] = fmaf(dsk, u2[n], ve[r].y);
+      y1[n] = ve[r].x;
+      if (has2) y2[n] = ve[r].y;
     }
   }
 }
 
 template <int LOG2M>
 hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, int L, float2* spec,
-                           float* Deff, hipStream_t st) {
+                           hipStream_t st) {
   using C = Cfg<LOG2M, 16>;
   const int nprob = 2 * H;
   const int nblk = (nprob + C::G - 1) / C::G;
   hipLaunchKernelGGL(spectrum_kernel<LOG2M>, dim3(nblk), dim3(C::WG), 0, st, reK, D, ndir, H, L,
-                     spec, Deff);
+                     spec);
   return hipGetLastError();
 }
 
 template <int LOG2M>
-hipError_t conv_launch(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
-                       float* y, hipStream_t st) {
+hipError_t conv_launch(const float* u, const float2* spec, int B, int H, int L, float* y,
+                       hipStream_t st) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   const int npairs = (B + 1) / 2;
   const long nprob = (long)H * npairs;
   const long nblk = (nprob + C::G - 1) / C::G;
-  hipLaunchKernelGGL(conv_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), 0, st, u, spec, Deff,
-                     B, H, L, npairs, y);
+  hipLaunchKernelGGL(conv_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), 0, st, u, spec, B, H,
+                     L, npairs, y);
   return hipGetLastError();
 }
 
@@ -633,11 +637,11 @@ int fft_log2m(int L) {
 #define DSSM_FFT_CASES(X) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14)
 
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
-                           float2* spec, float* Deff, hipStream_t st) {
+                           float2* spec, hipStream_t st) {
   switch (log2m) {
 #define X(n) \
   case n:    \
-    return spectrum_launch<n>(reK, D, ndir, H, L, spec, Deff, st);
+    return spectrum_launch<n>(reK, D, ndir, H, L, spec, st);
     DSSM_FFT_CASES(X)
 #undef X
     default:
@@ -645,12 +649,12 @@ hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, in
   }
 }
 
-hipError_t launch_conv(const float* u, const float2* spec, const float* Deff, int B, int H, int L,
-                       int log2m, float* y, hipStream_t st) {
+hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, int log2m, float* y,
+                       hipStream_t st) {
   switch (log2m) {
 #define X(n) \
   case n:    \
-    return conv_launch<n>(u, spec, Deff, B, H, L, y, st);
+    return conv_launch<n>(u, spec, B, H, L, y, st);
     DSSM_FFT_CASES(X)
 #undef X
     default:
