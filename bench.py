@@ -11,13 +11,12 @@ the step's inputs from the previous step.
 
 Prints ONE JSON line: value = elements (B*H*L) per second over the timed
 steps (wall clock between two device synchronisations), the per-kernel
-durations from HIP events recorded by the library on the launch stream, the
+durations from the start/stop HIP events the GPU stamps around each kernel, the
 roofline of the dominant kernel (the convolution) on algorithmic bytes
 (u read + y write = 8 bytes per element), and the float64 oracle timed on
 the host as the CPU baseline.
 """
 import argparse
-import ctypes
 import json
 import os
 import sys
@@ -32,63 +31,86 @@ METRIC = "SSM layer fwd elements/s (B·H·L) and achieved HBM GB/s vs peak, L=16
 WORKLOAD = "long_sequence"
 
 
-class HipEvents:
-    """Raw hipEvent_t handles through libamdhip64 (timing plumbing only)."""
-
-    def __init__(self):
-        self.h = ctypes.CDLL("libamdhip64.so")
-        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                               ctypes.c_void_p]
-        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
-
-    def create(self, n):
-        out = []
-        for _ in range(n):
-            e = ctypes.c_void_p()
-            rc = self.h.hipEventCreate(ctypes.byref(e))
-            if rc != 0:
-                raise RuntimeError("hipEventCreate failed: %d" % rc)
-            out.append(e.value)
-        return out
-
-    def ms(self, a, b):
-        t = ctypes.c_float()
-        rc = self.h.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
-        if rc != 0:
-            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
-        return t.value
-
-    def destroy(self, evs):
-        for e in evs:
-            self.h.hipEventDestroy(ctypes.c_void_p(e))
+# Counter record of the convolution kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# calibrated on a device copy of known size), valid only for the kernel
+# sources it was taken on.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "conv_kernel_long_sequence_counters.md")
+KERNEL_SOURCES = ["long_convolution_sequence_amd/csrc/fft.hip",
+                  "long_convolution_sequence_amd/csrc/dssm_internal.h",
+                  "long_convolution_sequence_amd/csrc/gen_twiddles.py",
+                  "long_convolution_sequence_amd/build.py"]
 
 
-def time_path(path, dev, us, ys, ws, steps, warmup, bi, hip):
-    """Run `warmup` untimed and `steps` timed steps; return wall ms/step and
-    mean per-stage ms from the library's events."""
+def kernel_sources_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the convolution from the committed counter
+    record, or None when there is none or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            for ln in f:
+                if ln.startswith("traffic-record: "):
+                    rec = json.loads(ln[len("traffic-record: "):])
+                    if rec.get("sources_sha256") == kernel_sources_digest():
+                        return rec["fetch_bytes"] + rec["write_bytes"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def time_path(path, dev, us, ys, ws, steps, warmup, bi, hip, breakdown_steps=20):
+    """Run `warmup` untimed steps, then `steps` timed steps in which only the
+    dominant kernel (the convolution, or the scan) is bracketed by the
+    start/stop events the GPU stamps around it -- an event-stamped launch costs
+    the host tens of microseconds, so stamping every kernel would starve the
+    GPU -- then `breakdown_steps` more with every kernel stamped.
+
+    Returns wall ms/step of the timed steps, the dominant kernel's mean ms in
+    them, and the mean per-kernel ms of the breakdown steps."""
     import torch
     from long_convolution_sequence_amd import binding as bd
 
-    nev = 4 if path == "fft" else 3
+    nk = 3 if path == "fft" else 2
     R = len(us)
     f = bd.forward_fft if path == "fft" else bd.forward_scan
+
+    def call(k, evs=None):
+        if evs is None:
+            f(us[k % R], dev["log_re"], dev["log_im"], dev["W"], dev["D"], bidirectional=bi,
+              y=ys[k % R], workspace=ws)
+        else:
+            bd.forward_timed(path, us[k % R], dev["log_re"], dev["log_im"], dev["W"], dev["D"],
+                             evs, bidirectional=bi, y=ys[k % R], workspace=ws)
+
     for k in range(warmup):
-        f(us[k % R], dev["log_re"], dev["log_im"], dev["W"], dev["D"], bidirectional=bi,
-          y=ys[k % R], workspace=ws)
-    evs = [hip.create(nev) for _ in range(steps)]
+        call(k)
+    main = [hip.create(2) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        bd.forward_timed(path, us[k % R], dev["log_re"], dev["log_im"], dev["W"], dev["D"], evs[k],
-                         bidirectional=bi, y=ys[k % R], workspace=ws)
+        call(k, [None] * (2 * nk - 2) + main[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    stages = [sum(hip.ms(e[i], e[i + 1]) for e in evs) / steps for i in range(nev - 1)]
-    gpu = sum(hip.ms(e[0], e[-1]) for e in evs) / steps
-    for e in evs:
+    dom = sum(hip.ms(e[0], e[1]) for e in main) / steps
+    for e in main:
         hip.destroy(e)
-    return (t1 - t0) * 1e3 / steps, stages, gpu
+    full = [hip.create(2 * nk) for _ in range(breakdown_steps)]
+    for k in range(breakdown_steps):
+        call(k, full[k])
+    torch.cuda.synchronize()
+    stages = [sum(hip.ms(e[2 * i], e[2 * i + 1]) for e in full) / breakdown_steps
+              for i in range(nk)]
+    for e in full:
+        hip.destroy(e)
+    return (t1 - t0) * 1e3 / steps, dom, stages
 
 
 def time_s5(steps, warmup, hip):
@@ -106,14 +128,14 @@ def time_s5(steps, warmup, hip):
                      device="cuda")
     for _ in range(warmup):
         bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], y=y, workspace=ws)
-    evs = [hip.create(5) for _ in range(steps)]
+    evs = [hip.create(8) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
         bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], y=y, workspace=ws, events=evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    st = [sum(hip.ms(e[i], e[i + 1]) for e in evs) / steps for i in range(4)]
+    st = [sum(hip.ms(e[2 * i], e[2 * i + 1]) for e in evs) / steps for i in range(4)]
     for e in evs:
         hip.destroy(e)
     ms = (t1 - t0) * 1e3 / steps
@@ -138,12 +160,11 @@ def time_copy(src, dst, reps, hip):
     dst.copy_(src)
     ev = hip.create(2)
     torch.cuda.synchronize()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    hip.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    hip.h.hipEventRecord(ctypes.c_void_p(ev[0]), stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.record(ev[0], stream)
     for _ in range(reps):
         dst.copy_(src)
-    hip.h.hipEventRecord(ctypes.c_void_p(ev[1]), stream)
+    hip.record(ev[1], stream)
     torch.cuda.synchronize()
     ms = hip.ms(ev[0], ev[1]) / reps
     hip.destroy(ev)
@@ -217,17 +238,16 @@ def main():
                          device="cuda")
     ws_scan = torch.empty(bd.workspace_size(bd.OP_SCAN, B, H, N, L, bi), dtype=torch.uint8,
                           device="cuda")
-    hip = HipEvents()
+    hip = bd.HipEvents()
 
     copy = time_copy(us[1], ys[1], 10, hip)
-    ms, stages, gpu_ms = time_path("fft", dev, us, ys, ws_fft, a.steps, a.warmup, bi, hip)
+    ms, conv_ms, stages = time_path("fft", dev, us, ys, ws_fft, a.steps, a.warmup, bi, hip)
     y_fft = ys[(a.steps - 1) % a.rotate].cpu().numpy()
-    ms_scan, stages_scan, gpu_scan = time_path("scan", dev, us, ys, ws_scan, a.scan_steps,
-                                               min(a.warmup, 2), bi, hip)
+    ms_scan, scan_ms, stages_scan = time_path("scan", dev, us, ys, ws_scan, a.scan_steps,
+                                              min(a.warmup, 2), bi, hip, a.scan_steps)
 
     elems = B * H * L
     alg_bytes = 8 * elems  # u read + y write, float32
-    conv_ms = stages[2]
     achieved = alg_bytes / (conv_ms * 1e-3) / 1e9
     # convolution flops on the 2M = 32768 circle: 4 complex transforms of
     # M = 16384 points per pair of rows, counted as 5 M log2 M each, plus the
@@ -257,18 +277,19 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": conv_ms,
         },
         "extra": {
-            "gpu_ms_per_step_events": gpu_ms,
-            "stage_ms": {"kernel_gen": stages[0], "spectrum": stages[1], "conv": stages[2]},
+            "stage_ms_breakdown": {"kernel_gen": stages[0], "spectrum": stages[1],
+                                   "conv": stages[2]},
             "full_call_hbm_gbs": alg_bytes / (ms * 1e-3) / 1e9,
             "conv_fp32_tflops_est": conv_flop / (conv_ms * 1e-3) / 1e12,
             "scan_path": {"ms_per_step": ms_scan, "elements_per_s": elems / (ms_scan * 1e-3),
-                          "stage_ms": {"consts": stages_scan[0], "scan": stages_scan[1]},
-                          "gpu_ms_events": gpu_scan},
+                          "scan_kernel_ms": scan_ms,
+                          "stage_ms_breakdown": {"consts": stages_scan[0],
+                                                 "scan": stages_scan[1]}},
             "rotated_sets": a.rotate,
             "device_copy": copy,
             "s5_path": time_s5(max(2, a.scan_steps), 2, hip),

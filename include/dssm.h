@@ -170,23 +170,24 @@ int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes);
 int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* Timing variant of dssm_s5_forward (n_events = 5): [0] before, [1] after
- * packing Bbar and C, [2] after the input projection, [3] after the scan,
- * [4] after the output projection. */
+/* Timing variant of dssm_s5_forward (n_events = 8): start/stop pairs of the
+ * four kernels, in order: packing of Bbar and C, input projection, scan,
+ * output projection (same event conventions as the DLR timing variants). */
 int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s,
                           float* y, void* ws, size_t ws_bytes, void* stream,
                           void* const* events, int n_events);
 
-/* Timing variants: identical results to dssm_forward_fft / dssm_forward_scan,
- * and additionally record the caller's hipEvent_t handles events[i] on
- * `stream` at the stage boundaries, so a caller can time each kernel on the
- * stream it runs on.
- *   fft  (n_events = 4): [0] before the first kernel, [1] after the kernel
- *        generator, [2] after the kernel spectrum, [3] after the convolution.
- *   scan (n_events = 3): [0] before, [1] after the per-mode constants,
- *        [2] after the scan.
- * The events are owned by the caller; a NULL array or handle, or a wrong
- * n_events, returns DSSM_ERR_INVALID_ARG before anything is enqueued. */
+/* Timing variants: identical results to dssm_forward_fft / dssm_forward_scan;
+ * kernel k is launched with hipExtLaunchKernel so that the GPU itself stamps
+ * events[2k] when it starts and events[2k+1] when it ends
+ * (hipEventElapsedTime of a pair is that kernel's duration, without the
+ * dispatch gap before it).  A pair of NULL handles leaves that kernel untimed
+ * (plain launch: an event-stamped launch costs more host time).
+ *   fft  (n_events = 6): kernel generator, kernel spectrum, convolution.
+ *   scan (n_events = 4): per-mode constants, scan.
+ * The events are owned by the caller and must have timing enabled; a NULL
+ * array, a pair with one NULL handle, or a wrong n_events returns
+ * DSSM_ERR_INVALID_ARG before anything is enqueued. */
 int dssm_forward_fft_timed(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                            float* y, void* ws, size_t ws_bytes, void* stream,
                            void* const* events, int n_events);

@@ -226,8 +226,9 @@ def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace
 
 def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=None,
                   workspace=None, stream=None):
-    """forward_fft / forward_scan that also records the given raw hipEvent_t
-    handles (ints) at the library's stage boundaries (4 for fft, 3 for scan)."""
+    """forward_fft / forward_scan whose kernels the GPU brackets with the given
+    raw hipEvent_t handles (ints): a start/stop pair per kernel, 6 for fft
+    (generator, spectrum, convolution), 4 for scan (constants, scan)."""
     if path == "fft":
         fn, op = lib().dssm_forward_fft_timed, OP_FFT
     else:
@@ -245,7 +246,9 @@ def s5_workspace_size(B, H, P, L):
 
 def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=None):
     """S5 layer forward.  u [B,H,L] f32, lam [P] c64, Bbar [P,H] c64,
-    C [H,P] c64, D [H] f32 -> y [B,H,L] f32."""
+    C [H,P] c64, D [H] f32 -> y [B,H,L] f32.  events: optional 8 raw
+    hipEvent_t handles, a start/stop pair per kernel (pack, proj_in, scan,
+    proj_out)."""
     torch = _torch()
     uu = _dev_f32(u, "u")
     if uu.dim() != 3:
@@ -276,3 +279,42 @@ def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=N
         arr = (ctypes.c_void_p * len(events))(*events)
         check(lib().dssm_s5_forward_timed(*(args + [arr, len(events)])))
     return y
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through libamdhip64, for the timing variants
+    (plumbing only: create, elapsed time, destroy)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.h.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return t.value
+
+    def record(self, e, stream):
+        rc = self.h.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(ctypes.c_void_p(e))

@@ -170,15 +170,35 @@ int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_o
   return ok();
 }
 
-// Shared body of the forward calls.  events (optional) are hipEvent_t
-// recorded on the stream at the stage boundaries.
+// A kernel's start/stop pair is both handles or neither (kernel untimed).
+static int check_events(void* const* events, int n_events) {
+  if (!events) return DSSM_OK;
+  for (int k = 0; 2 * k < n_events; ++k)
+    if (!events[2 * k] != !events[2 * k + 1])
+      return fail(DSSM_ERR_INVALID_ARG, "events[%d] and events[%d] must both be set or both NULL",
+                  2 * k, 2 * k + 1);
+  return DSSM_OK;
+}
+
+// Start/stop event pair of kernel k of a timed call (none when untimed).
+static KEvents kev(void* const* events, int k) {
+  KEvents e;
+  if (events) {
+    e.start = static_cast<hipEvent_t>(events[2 * k]);
+    e.stop = static_cast<hipEvent_t>(events[2 * k + 1]);
+  }
+  return e;
+}
+
+// Shared body of the forward calls.  events (optional) are hipEvent_t pairs
+// that the GPU stamps at the start and the end of each kernel.
 static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                         float* y, void* ws, size_t ws_bytes, void* stream, void* const* events,
                         int n_events) {
   bool empty = false;
   int rc = check_shape(op, s, &empty);
   if (rc) return rc;
-  const int want = (op == DSSM_OP_FFT) ? 4 : 3;
+  const int want = (op == DSSM_OP_FFT) ? 6 : 4;
   if (events && n_events != want)
     return fail(DSSM_ERR_INVALID_ARG, "n_events must be %d (got %d)", want, n_events);
   if (empty) return ok();
@@ -186,48 +206,38 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
   if (!u || !y || !aligned16(u) || !aligned16(y))
     return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
   if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
-  if (events)
-    for (int i = 0; i < n_events; ++i)
-      if (!events[i]) return fail(DSSM_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  if ((rc = check_events(events, n_events))) return rc;
   Layout l;
   if ((rc = check_ws(op, s, ws, ws_bytes, &l))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> int {
-    if (!events) return DSSM_OK;
-    return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
-  };
   const int ndir = 1 + s->bidirectional;
-  if ((rc = mark(0))) return rc;
   if (op == DSSM_OP_FFT) {
     const int ndh = ndir * s->H;
     float* reK = at<float>(ws, l.reK);
-    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndh, s->N, s->L, 0, reK, st),
+    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndh, s->N, s->L, 0, reK, st,
+                                   kev(events, 0)),
                         "gen launch")))
       return rc;
-    if ((rc = mark(1))) return rc;
     const int log2m = fft_log2m(s->L);
     float2* spec = at<float2>(ws, l.spec);
-    if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st),
-                        "spectrum launch")))
+    if ((rc = hip_check(
+             launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st, kev(events, 1)),
+             "spectrum launch")))
       return rc;
-    if ((rc = mark(2))) return rc;
-    if ((rc = hip_check(launch_conv(u, spec, s->B, s->H, s->L, log2m, y, st),
+    if ((rc = hip_check(launch_conv(u, spec, s->B, s->H, s->L, log2m, y, st, kev(events, 2)),
                         "conv launch")))
       return rc;
-    if ((rc = mark(3))) return rc;
   } else {
     const ScanPlan plan = scan_plan(s->B, s->L);
     float* consts = at<float>(ws, l.consts);
     if ((rc = hip_check(launch_scan_consts(p->log_re, p->log_im, p->W, ndir * s->H, s->N, plan,
-                                           consts, st),
+                                           consts, st, kev(events, 0)),
                         "scan consts launch")))
       return rc;
-    if ((rc = mark(1))) return rc;
     if ((rc = hip_check(launch_scan(u, consts, p->D, s->B, s->H, s->N, s->L, ndir, plan, y, st,
-                                    at<float2>(ws, l.carry)),
+                                    at<float2>(ws, l.carry), kev(events, 1)),
                         "scan launch")))
       return rc;
-    if ((rc = mark(2))) return rc;
   }
   return ok();
 }
@@ -284,8 +294,8 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   bool empty = false;
   int rc = s5_check_shape(s, &empty);
   if (rc) return rc;
-  if (events && n_events != 5)
-    return fail(DSSM_ERR_INVALID_ARG, "n_events must be 5 (got %d)", n_events);
+  if (events && n_events != 8)
+    return fail(DSSM_ERR_INVALID_ARG, "n_events must be 8 (got %d)", n_events);
   if (empty) return ok();
   if (!p) return fail(DSSM_ERR_INVALID_ARG, "params is NULL");
   if (!p->lambda || !p->Bbar || !p->C || !p->D)
@@ -295,9 +305,7 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   if (!u || !y || !aligned16(u) || !aligned16(y))
     return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
   if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
-  if (events)
-    for (int i = 0; i < n_events; ++i)
-      if (!events[i]) return fail(DSSM_ERR_INVALID_ARG, "events[%d] is NULL", i);
+  if ((rc = check_events(events, n_events))) return rc;
   const S5Layout l = s5_layout(s->B, s->H, s->P, s->L);
   if (ws_bytes < l.total)
     return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -306,28 +314,25 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(DSSM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  auto mark = [&](int i) -> int {
-    if (!events) return DSSM_OK;
-    return hip_check(hipEventRecord(static_cast<hipEvent_t>(events[i]), st), "event record");
-  };
   float* apk_in = at<float>(ws, l.apk_in);
   float* apk_out = at<float>(ws, l.apk_out);
   float* v = at<float>(ws, l.v);
   float* x = at<float>(ws, l.x);
-  if ((rc = mark(0))) return rc;
-  if ((rc = hip_check(launch_s5_pack(p->Bbar, p->C, s->H, s->P, apk_in, apk_out, st), "s5 pack")))
+  if ((rc = hip_check(
+           launch_s5_pack(p->Bbar, p->C, s->H, s->P, apk_in, apk_out, st, kev(events, 0)),
+           "s5 pack")))
     return rc;
-  if ((rc = mark(1))) return rc;
-  if ((rc = hip_check(launch_s5_proj_in(apk_in, u, s->B, s->H, s->P, s->L, v, st), "s5 proj_in")))
+  if ((rc = hip_check(
+           launch_s5_proj_in(apk_in, u, s->B, s->H, s->P, s->L, v, st, kev(events, 1)),
+           "s5 proj_in")))
     return rc;
-  if ((rc = mark(2))) return rc;
-  if ((rc = hip_check(launch_s5_scan(p->lambda, v, s->B, s->P, s->L, x, st), "s5 scan")))
+  if ((rc = hip_check(launch_s5_scan(p->lambda, v, s->B, s->P, s->L, x, st, kev(events, 2)),
+                      "s5 scan")))
     return rc;
-  if ((rc = mark(3))) return rc;
-  if ((rc = hip_check(launch_s5_proj_out(apk_out, x, p->D, u, s->B, s->H, s->P, s->L, y, st),
+  if ((rc = hip_check(launch_s5_proj_out(apk_out, x, p->D, u, s->B, s->H, s->P, s->L, y, st,
+                                         kev(events, 3)),
                       "s5 proj_out")))
     return rc;
-  if ((rc = mark(4))) return rc;
   return ok();
 }
 

@@ -2,11 +2,32 @@
 // kernel translation units.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dssm {
+
+// Optional pair of caller-owned events that the GPU stamps at the start and
+// the end of one kernel (hipExtLaunchKernel): timing of that kernel alone,
+// without the dispatch gap before it.
+struct KEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// Launch `k` on `st`, stamping `ev` around it when given (a plain launch
+// otherwise).
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*k)(KArgs...), dim3 grid, dim3 block, hipStream_t st, KEvents ev,
+                     Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(k, grid, block, 0, st, ev.start, ev.stop, 0,
+                          static_cast<KArgs>(args)...);
+  else
+    hipLaunchKernelGGL(k, grid, block, 0, st, static_cast<KArgs>(args)...);
+}
 
 // Anchor spacing of the kernel generator: K[64 q + r] is built from
 // lambda^r (r < 64) and the anchor W lambda^(64 q).
@@ -24,7 +45,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // directly (float64 powers, float32 matrix-core contraction over the modes).
 // complex_out = 0: Re K into float [ndh, L]; 1: (Re, Im) into float2 [ndh, L].
 hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, int ndh, int N,
-                      int L, int complex_out, float* K, hipStream_t st);
+                      int L, int complex_out, float* K, hipStream_t st, KEvents ev = {});
 
 // ---------------------------------------------------------------------------
 // FFT convolution (fft.hip)
@@ -36,12 +57,12 @@ hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, 
 // half 1 the odd bins.  For ndir = 2 the backward kernel enters conjugated.
 // sum_d D[d,h] is added to every bin (the feed-through as tap 0).
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
-                           float2* spec, hipStream_t st);
+                           float2* spec, hipStream_t st, KEvents ev = {});
 
 // y[b,h,:L] = first L samples of the 2M-circular convolution of u[b,h,:] with
 // the kernel whose spectrum is spec[h] (D u included through tap 0).
 hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, int log2m, float* y,
-                       hipStream_t st);
+                       hipStream_t st, KEvents ev = {});
 
 int fft_log2m(int L);  // log2 of M = max(16, next power of two >= L)
 
@@ -61,12 +82,13 @@ ScanPlan scan_plan(int B, int L);
 
 // Per-(d,h,n) constants for the scan (float64 arithmetic, rounded once).
 hipError_t launch_scan_consts(const float* log_re, const float* log_im, const float* W,
-                             int ndh, int N, const ScanPlan& plan, float* consts, hipStream_t st);
+                             int ndh, int N, const ScanPlan& plan, float* consts, hipStream_t st,
+                             KEvents ev = {});
 
 // carry: [B, H, N] float2 scratch, used when plan.ntile > 1.
 hipError_t launch_scan(const float* u, const float* consts, const float* D, int B, int H, int N,
                        int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
-                       float2* carry);
+                       float2* carry, KEvents ev = {});
 
 // ---------------------------------------------------------------------------
 // S5 multi-input multi-output diagonal SSM (s5.hip)
@@ -78,16 +100,16 @@ S5Layout s5_layout(int B, int H, int P, int L);
 
 // Bbar [P,H] c64, C [H,P] c64 -> MFMA A-fragment tables.
 hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, float* apk_in,
-                          float* apk_out, hipStream_t st);
+                          float* apk_out, hipStream_t st, KEvents ev = {});
 // v [B][P][2][L] = Bbar u
 hipError_t launch_s5_proj_in(const float* apk_in, const float* u, int B, int H, int P, int L,
-                             float* v, hipStream_t st);
+                             float* v, hipStream_t st, KEvents ev = {});
 // x [B][P][2][L]: x_k = lambda x_{k-1} + v_k
 hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int L, float* x,
-                          hipStream_t st);
+                          hipStream_t st, KEvents ev = {});
 // y [B][H][L] = Re(C x) + D u
 hipError_t launch_s5_proj_out(const float* apk_out, const float* x, const float* D,
                               const float* u, int B, int H, int P, int L, float* y,
-                              hipStream_t st);
+                              hipStream_t st, KEvents ev = {});
 
 }  // namespace dssm

@@ -164,14 +164,14 @@ __global__ __launch_bounds__(256) void gen_kernel(const float* __restrict__ log_
 }  // namespace
 
 hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, int ndh, int N,
-                      int L, int complex_out, float* K, hipStream_t st) {
+                      int L, int complex_out, float* K, hipStream_t st, KEvents ev) {
   const int Q = (L + kAnchor - 1) / kAnchor;
   const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)ndh);
   const float2* w2 = reinterpret_cast<const float2*>(W);
   if (complex_out)
-    hipLaunchKernelGGL(gen_kernel<true>, grid, dim3(256), 0, st, log_re, log_im, w2, N, L, K);
+    launch_k(gen_kernel<true>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
   else
-    hipLaunchKernelGGL(gen_kernel<false>, grid, dim3(256), 0, st, log_re, log_im, w2, N, L, K);
+    launch_k(gen_kernel<false>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
   return hipGetLastError();
 }
 

@@ -312,14 +312,29 @@ __device__ __forceinline__ void lds_read(const float2* lds, int lt, float2* v) {
   }
 }
 
-// Twiddle powers of pass p for thread lt: w = exp(-2 pi i m / S).  The load
-// is made opaque so the powers are recomputed per pass instead of being
-// shared across the kernel and kept live.
+// The value of x, hidden from the optimiser (it cannot reuse values derived
+// from x before this point).
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Twiddle root of pass p for thread lt, w = exp(-2 pi i m / S) (unused by the
+// last pass).  The index is opaque, so each pass loads its root afresh, one
+// pass ahead of its use, instead of the compiler keeping every pass's root
+// live across the kernel.
 template <class C, int P>
-__device__ __forceinline__ void pass_powers(int lt, float2* p) {
+__device__ __forceinline__ float2 pass_w(int lt) {
   using G = PassGeom<C, P>;
-  if constexpr (!G::kLast) {
-    float2 w = g_twiddle[G::m_of(lt) * (DSSM_TWN / G::S)];
+  if constexpr (G::kLast) return make_float2(1.f, 0.f);
+  else return g_twiddle[G::m_of(opaque(lt)) * (DSSM_TWN / G::S)];
+}
+
+// Powers of the root of pass p; opaque, so they are recomputed per pass and
+// not shared (and kept live) between passes that use the same root.
+template <class C, int P>
+__device__ __forceinline__ void pass_powers(float2 w, float2* p) {
+  if constexpr (!PassGeom<C, P>::kLast) {
     asm volatile("" : "+v"(w.x), "+v"(w.y));
     powers16(w, p);
   }
@@ -370,33 +385,38 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Forward passes P .. NP-1 (P >= 1) of one array, wave-local.  Entry: v holds
-// pass-P inputs; exit: the bins at positions PT lt + r.
+// pass-P inputs, w the pass-P root; exit: the bins at positions PT lt + r.
 template <class C, int P>
-__device__ __forceinline__ void fwd_tail(float2* v, float2* lds, int lt) {
+__device__ __forceinline__ void fwd_tail(float2* v, float2* lds, int lt, float2 w) {
+  float2 wn = make_float2(1.f, 0.f);
+  if constexpr (P + 1 < C::NP) wn = pass_w<C, P + 1>(lt);
   float2 p[16];
-  pass_powers<C, P>(lt, p);
+  pass_powers<C, P>(w, p);
   fwd_compute<C, P>(v, p);
   if constexpr (P + 1 < C::NP) {
     lds_write<C, P>(lds, lt, v);
     wave_sync();
     lds_read<C, P + 1>(lds, lt, v);
-    fwd_tail<C, P + 1>(v, lds, lt);
+    fwd_tail<C, P + 1>(v, lds, lt, wn);
   }
 }
 
 // Inverse passes P .. 1 of one array, wave-local.  Entry: v holds pass-P
-// outputs (P = NP-1: the bins); exit: the pass-1 inputs at pass-1 positions.
+// outputs (P = NP-1: the bins), w the pass-P root; exit: the pass-1 inputs at
+// pass-1 positions.
 template <class C, int P = C::NP - 1>
-__device__ __forceinline__ void inv_head(float2* v, float2* lds, int lt) {
+__device__ __forceinline__ void inv_head(float2* v, float2* lds, int lt, float2 w) {
   if constexpr (P >= 1) {
+    float2 wn = make_float2(1.f, 0.f);
+    if constexpr (P > 1) wn = pass_w<C, P - 1>(lt);
     float2 p[16];
-    pass_powers<C, P>(lt, p);
+    pass_powers<C, P>(w, p);
     inv_compute<C, P>(v, p);
     if constexpr (P > 1) {
       lds_write<C, P>(lds, lt, v);
       wave_sync();
       lds_read<C, P - 1>(lds, lt, v);
-      inv_head<C, P - 1>(v, lds, lt);
+      inv_head<C, P - 1>(v, lds, lt, wn);
     }
   }
 }
@@ -407,27 +427,37 @@ __device__ __forceinline__ void inv_head(float2* v, float2* lds, int lt) {
 template <class C>
 __device__ __forceinline__ void forward1(float2* v, float2* lds, int lt) {
   float2 p[16];
-  pass_powers<C, 0>(lt, p);
+  pass_powers<C, 0>(pass_w<C, 0>(lt), p);
+  float2 w1 = make_float2(1.f, 0.f);
+  if constexpr (C::NP > 1) w1 = pass_w<C, 1>(lt);
   fwd_compute<C, 0>(v, p);
   if constexpr (C::NP > 1) {
     lds_write<C, 0>(lds, lt, v);
     __syncthreads();
     lds_read<C, 1>(lds, lt, v);
-    fwd_tail<C, 1>(v, lds, lt);
+    fwd_tail<C, 1>(v, lds, lt, w1);
   }
+}
+
+// Inverse passes NP-1 .. 1 of one array (inv_head with its root loaded).
+template <class C>
+__device__ __forceinline__ void inverse_head(float2* v, float2* lds, int lt) {
+  inv_head<C>(v, lds, lt, pass_w<C, C::NP - 1>(lt));
 }
 
 // Pass-0 inverse of an array whose passes NP-1 .. 1 were inverted by
 // inv_head (one workgroup barrier); exit: the points nat(lt, r).
 template <class C>
 __device__ __forceinline__ void inverse_finish(float2* v, float2* lds, int lt) {
+  lt = opaque(lt);  // LDS addresses recomputed rather than kept from pass 0
+  const float2 w0 = pass_w<C, 0>(lt);
   if constexpr (C::NP > 1) {
     lds_write<C, 1>(lds, lt, v);
     __syncthreads();
     lds_read<C, 0>(lds, lt, v);
   }
   float2 p[16];
-  pass_powers<C, 0>(lt, p);
+  pass_powers<C, 0>(w0, p);
   inv_compute<C, 0>(v, p);
 }
 
@@ -557,35 +587,41 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   // pass 0 of both halves (shared twiddles)
   {
     float2 p[16];
-    pass_powers<C, 0>(lt, p);
+    pass_powers<C, 0>(pass_w<C, 0>(lt), p);
     fwd_compute<C, 0>(ve, p);
     fwd_compute<C, 0>(vo, p);
   }
   // even half: exchange, wave-local passes, product, inverse back to pass 0
   if constexpr (C::NP > 1) {
+    const float2 w1 = pass_w<C, 1>(lt);
     lds_write<C, 0>(lds, lt, ve);
     __syncthreads();
     lds_read<C, 1>(lds, lt, ve);
-    fwd_tail<C, 1>(ve, lds, lt);
+    fwd_tail<C, 1>(ve, lds, lt, w1);
   }
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[(size_t)r * C::T]);
-  inv_head<C>(ve, lds, lt);
+  inverse_head<C>(ve, lds, lt);
   inverse_finish<C>(ve, lds, lt);
   // odd half: its pass-0 positions are disjoint from every other thread's,
   // so it may be written while others still read the even half's
   if constexpr (C::NP > 1) {
+    const float2 w1 = pass_w<C, 1>(lt);
     lds_write<C, 0>(lds, lt, vo);
     __syncthreads();
     lds_read<C, 1>(lds, lt, vo);
-    fwd_tail<C, 1>(vo, lds, lt);
+    fwd_tail<C, 1>(vo, lds, lt, w1);
   }
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[(size_t)r * C::T]);
-  inv_head<C>(vo, lds, lt);
+  inverse_head<C>(vo, lds, lt);
   inverse_finish<C>(vo, lds, lt);
+  // The thread index is re-derived here (opaque to the compiler) so the store
+  // addresses and t[lt] are recomputed instead of being kept live -- and
+  // spilled -- across both transforms.
+  const int lte = opaque(lt);
   {  // y = ye + conj(t) yo (D u is already in the spectrum)
-    const float2 tlc = cconj(g_twiddle[lt * (DSSM_TWN / (2 * C::M))]);
+    const float2 tlc = cconj(g_twiddle[lte * (DSSM_TWN / (2 * C::M))]);
     odd_twiddle_fixed<C, true>(vo);
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) ve[r] = cadd(ve[r], cmul(vo[r], tlc));
@@ -595,7 +631,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   float* y2 = y + ((size_t)b2 * H + h) * L;
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) {
-    const int n = nat<C>(lt, r);
+    const int n = nat<C>(lte, r);
     if (n < L) {
       y1[n] = ve[r].x;
       if (has2) y2[n] = ve[r].y;
@@ -605,24 +641,23 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
 
 template <int LOG2M>
 hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, int L, float2* spec,
-                           hipStream_t st) {
+                           hipStream_t st, KEvents ev) {
   using C = Cfg<LOG2M, 16>;
   const int nprob = 2 * H;
   const int nblk = (nprob + C::G - 1) / C::G;
-  hipLaunchKernelGGL(spectrum_kernel<LOG2M>, dim3(nblk), dim3(C::WG), 0, st, reK, D, ndir, H, L,
-                     spec);
+  launch_k(spectrum_kernel<LOG2M>, dim3(nblk), dim3(C::WG), st, ev, reK, D, ndir, H, L, spec);
   return hipGetLastError();
 }
 
 template <int LOG2M>
 hipError_t conv_launch(const float* u, const float2* spec, int B, int H, int L, float* y,
-                       hipStream_t st) {
+                       hipStream_t st, KEvents ev) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   const int npairs = (B + 1) / 2;
   const long nprob = (long)H * npairs;
   const long nblk = (nprob + C::G - 1) / C::G;
-  hipLaunchKernelGGL(conv_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), 0, st, u, spec, B, H,
-                     L, npairs, y);
+  launch_k(conv_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), st, ev, u, spec, B, H, L, npairs,
+           y);
   return hipGetLastError();
 }
 
@@ -637,11 +672,11 @@ int fft_log2m(int L) {
 #define DSSM_FFT_CASES(X) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14)
 
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
-                           float2* spec, hipStream_t st) {
+                           float2* spec, hipStream_t st, KEvents ev) {
   switch (log2m) {
 #define X(n) \
   case n:    \
-    return spectrum_launch<n>(reK, D, ndir, H, L, spec, st);
+    return spectrum_launch<n>(reK, D, ndir, H, L, spec, st, ev);
     DSSM_FFT_CASES(X)
 #undef X
     default:
@@ -650,11 +685,11 @@ hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, in
 }
 
 hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, int log2m, float* y,
-                       hipStream_t st) {
+                       hipStream_t st, KEvents ev) {
   switch (log2m) {
 #define X(n) \
   case n:    \
-    return conv_launch<n>(u, spec, B, H, L, y, st);
+    return conv_launch<n>(u, spec, B, H, L, y, st, ev);
     DSSM_FFT_CASES(X)
 #undef X
     default:

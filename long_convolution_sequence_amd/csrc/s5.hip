@@ -339,36 +339,34 @@ S5Layout s5_layout(int B, int H, int P, int L) {
 }
 
 hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, float* apk_in,
-                          float* apk_out, hipStream_t st) {
-  hipLaunchKernelGGL(s5_pack_kernel, dim3(256, 2), dim3(256), 0, st,
-                     reinterpret_cast<const float2*>(Bbar), reinterpret_cast<const float2*>(C), H,
-                     P, apk_in, apk_out);
+                          float* apk_out, hipStream_t st, KEvents ev) {
+  launch_k(s5_pack_kernel, dim3(256, 2), dim3(256), st, ev, reinterpret_cast<const float2*>(Bbar),
+           reinterpret_cast<const float2*>(C), H, P, apk_in, apk_out);
   return hipGetLastError();
 }
 
 hipError_t launch_s5_proj_in(const float* apk_in, const float* u, int B, int H, int P, int L,
-                             float* v, hipStream_t st) {
+                             float* v, hipStream_t st, KEvents ev) {
   const int M = 2 * P;
   const dim3 grid((unsigned)((L + 63) / 64), (unsigned)(((M + 63) / 64 + 3) / 4), (unsigned)B);
-  hipLaunchKernelGGL(s5_gemm_kernel<false>, grid, dim3(256), 0, st, apk_in, u, M, H, L, nullptr,
-                     nullptr, v);
+  launch_k(s5_gemm_kernel<false>, grid, dim3(256), st, ev, apk_in, u, M, H, L,
+           static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), v);
   return hipGetLastError();
 }
 
 hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int L, float* x,
-                          hipStream_t st) {
-  hipLaunchKernelGGL(s5_scan_kernel, dim3((unsigned)(B * P)), dim3(kLanes), 0, st,
-                     reinterpret_cast<const float2*>(lambda), v, P, L, x);
+                          hipStream_t st, KEvents ev) {
+  launch_k(s5_scan_kernel, dim3((unsigned)(B * P)), dim3(kLanes), st, ev,
+           reinterpret_cast<const float2*>(lambda), v, P, L, x);
   return hipGetLastError();
 }
 
 hipError_t launch_s5_proj_out(const float* apk_out, const float* x, const float* D,
                               const float* u, int B, int H, int P, int L, float* y,
-                              hipStream_t st) {
+                              hipStream_t st, KEvents ev) {
   const int M = H;
   const dim3 grid((unsigned)((L + 63) / 64), (unsigned)(((M + 63) / 64 + 3) / 4), (unsigned)B);
-  hipLaunchKernelGGL(s5_gemm_kernel<true>, grid, dim3(256), 0, st, apk_out, x, M, 2 * P, L, D, u,
-                     y);
+  launch_k(s5_gemm_kernel<true>, grid, dim3(256), st, ev, apk_out, x, M, 2 * P, L, D, u, y);
   return hipGetLastError();
 }
 

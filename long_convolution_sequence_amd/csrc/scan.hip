@@ -281,15 +281,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 
 template <int SEG>
 void scan_launch(const float* u, const float* consts, const float* D, float2* carry, int B, int H,
-                 int N, int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st) {
+                 int N, int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
+                 KEvents ev) {
   const int cpg = kScanThreads / plan.lpc;
   const dim3 grid((unsigned)((B + cpg - 1) / cpg), (unsigned)H);
   if (plan.ntile == 1)
-    hipLaunchKernelGGL((scan_kernel<SEG, false>), grid, dim3(kScanThreads), 0, st, u, consts, D,
-                       carry, B, H, N, L, ndir, plan.lpc, plan.ntile, y);
+    launch_k(scan_kernel<SEG, false>, grid, dim3(kScanThreads), st, ev, u, consts, D, carry, B, H, N,
+             L, ndir, plan.lpc, plan.ntile, y);
   else
-    hipLaunchKernelGGL((scan_kernel<SEG, true>), grid, dim3(kScanThreads), 0, st, u, consts, D,
-                       carry, B, H, N, L, ndir, plan.lpc, plan.ntile, y);
+    launch_k(scan_kernel<SEG, true>, grid, dim3(kScanThreads), st, ev, u, consts, D, carry, B, H, N,
+             L, ndir, plan.lpc, plan.ntile, y);
 }
 
 }  // namespace
@@ -313,22 +314,23 @@ ScanPlan scan_plan(int B, int L) {
 }
 
 hipError_t launch_scan_consts(const float* log_re, const float* log_im, const float* W, int ndh,
-                              int N, const ScanPlan& plan, float* consts, hipStream_t st) {
+                              int N, const ScanPlan& plan, float* consts, hipStream_t st,
+                              KEvents ev) {
   const int ndhn = ndh * N;
-  hipLaunchKernelGGL(scan_consts_kernel, dim3((unsigned)((ndhn + 255) / 256)), dim3(256), 0, st,
-                     log_re, log_im, reinterpret_cast<const float2*>(W), ndhn, plan.seg, consts);
+  launch_k(scan_consts_kernel, dim3((unsigned)((ndhn + 255) / 256)), dim3(256), st, ev, log_re,
+           log_im, reinterpret_cast<const float2*>(W), ndhn, plan.seg, consts);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const float* u, const float* consts, const float* D, int B, int H, int N,
                        int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
-                       float2* carry) {
+                       float2* carry, KEvents ev) {
   switch (plan.seg) {
-    case 4: scan_launch<4>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st); break;
-    case 8: scan_launch<8>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st); break;
-    case 16: scan_launch<16>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st); break;
-    case 32: scan_launch<32>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st); break;
-    case 64: scan_launch<64>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st); break;
+    case 4: scan_launch<4>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
+    case 8: scan_launch<8>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
+    case 16: scan_launch<16>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
+    case 32: scan_launch<32>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
+    case 64: scan_launch<64>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -171,7 +171,7 @@ def test_s5_workspace_and_validation():
     assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
 
 
-@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 4), ("dssm_forward_scan_timed", 3)])
+@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 6), ("dssm_forward_scan_timed", 4)])
 def test_timed_variants_validate_events(name, n):
     fn = getattr(bd.lib(), name)
     good = bd.Shape(2, 3, 4, 32, 0)
@@ -182,3 +182,20 @@ def test_timed_variants_validate_events(name, n):
     assert fn(*(args + [evs, n + 1])) == bd.DSSM_ERR_INVALID_ARG
     bad = (ctypes.c_void_p * n)(*([FAKE] * (n - 1) + [None]))
     assert fn(*(args + [bad, n])) == bd.DSSM_ERR_INVALID_ARG
+    # a NULL pair (kernel untimed) passes validation: the call then fails on
+    # the workspace, which is checked after the events
+    half = (ctypes.c_void_p * n)(*([None, None] + [FAKE] * (n - 2)))
+    small = [FAKE * 2, ctypes.byref(p), ctypes.byref(good), FAKE * 3, FAKE * 4, 8, None]
+    assert fn(*(small + [half, n])) == bd.DSSM_ERR_WORKSPACE
+
+
+def test_s5_timed_validates_events():
+    fn = bd.lib().dssm_s5_forward_timed
+    good = bd.S5Shape(2, 3, 4, 32, 0)
+    prm = bd.S5Params(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
+    evs = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    args = [FAKE * 2, ctypes.byref(prm), ctypes.byref(good), FAKE * 3, FAKE * 4, 1 << 40, None]
+    assert fn(*(args + [None, 8])) == bd.DSSM_ERR_INVALID_ARG
+    assert fn(*(args + [evs, 5])) == bd.DSSM_ERR_INVALID_ARG
+    bad = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))
+    assert fn(*(args + [bad, 8])) == bd.DSSM_ERR_INVALID_ARG

@@ -220,6 +220,29 @@ def test_fft_and_scan_agree_and_are_deterministic():
     assert rel < 2 * REL_L2 and mx < 2 * MAX_VS_RMS
 
 
+@pytest.mark.parametrize("path,nk", [("fft", 3), ("scan", 2)])
+def test_timed_variants_match_and_stamp_each_kernel(path, nk):
+    """The timed calls give the untimed calls' bits; each kernel's start/stop
+    pair is a positive duration and the pairs are ordered in time."""
+    torch = _torch()
+    c = dict(inputs.config("tiny"), B=3, H=8, N=16, L=2000, bidirectional=1)
+    x = inputs.inputs_for(c)
+    t = dev(x)
+    f = bd.forward_fft if path == "fft" else bd.forward_scan
+    y0 = f(t["u"], t["log_re"], t["log_im"], t["W"], t["D"], bidirectional=True)
+    hip = bd.HipEvents()
+    evs = hip.create(2 * nk)
+    y1 = bd.forward_timed(path, t["u"], t["log_re"], t["log_im"], t["W"], t["D"], evs,
+                          bidirectional=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    for k in range(nk):
+        assert hip.ms(evs[2 * k], evs[2 * k + 1]) > 0.0
+        if k:
+            assert hip.ms(evs[2 * k - 1], evs[2 * k]) >= 0.0
+    hip.destroy(evs)
+
+
 def test_empty_inputs_are_noops():
     torch = _torch()
     say("case: empty inputs")

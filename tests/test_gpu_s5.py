@@ -68,6 +68,22 @@ def test_s5_reduces_to_dlr_bank_on_device():
     assert_close(y, ref, "s5/reduction")
 
 
+def test_s5_timed_matches_untimed():
+    torch = _torch()
+    x = inputs.s5_inputs(2, 24, 9, 3000, seed=17)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    say("case: s5 timed variant B=2 H=24 P=9 L=3000")
+    y0 = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"])
+    hip = bd.HipEvents()
+    evs = hip.create(8)
+    y1 = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    for k in range(4):
+        assert hip.ms(evs[2 * k], evs[2 * k + 1]) > 0.0
+    hip.destroy(evs)
+
+
 def test_s5_empty_is_noop():
     torch = _torch()
     x = inputs.s5_inputs(1, 3, 2, 8, seed=1)
