@@ -78,7 +78,7 @@ def time_path(path, dev, us, ys, ws, steps, warmup, bi, hip, breakdown_steps=20)
     import torch
     from long_convolution_sequence_amd import binding as bd
 
-    nk = 3 if path == "fft" else 2
+    nk = 2
     R = len(us)
     f = bd.forward_fft if path == "fft" else bd.forward_scan
 
@@ -282,8 +282,7 @@ def main():
             "avg_launch_ms": conv_ms,
         },
         "extra": {
-            "stage_ms_breakdown": {"kernel_gen": stages[0], "spectrum": stages[1],
-                                   "conv": stages[2]},
+            "stage_ms_breakdown": {"kernel_spectrum": stages[0], "conv": stages[1]},
             "full_call_hbm_gbs": alg_bytes / (ms * 1e-3) / 1e9,
             "conv_fp32_tflops_est": conv_flop / (conv_ms * 1e-3) / 1e12,
             "scan_path": {"ms_per_step": ms_scan, "elements_per_s": elems / (ms_scan * 1e-3),

@@ -178,13 +178,15 @@ int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5
                           void* const* events, int n_events);
 
 /* Timing variants: identical results to dssm_forward_fft / dssm_forward_scan;
- * kernel k is launched with hipExtLaunchKernel so that the GPU itself stamps
- * events[2k] when it starts and events[2k+1] when it ends
- * (hipEventElapsedTime of a pair is that kernel's duration, without the
- * dispatch gap before it).  A pair of NULL handles leaves that kernel untimed
- * (plain launch: an event-stamped launch costs more host time).
- *   fft  (n_events = 6): kernel generator, kernel spectrum, convolution.
- *   scan (n_events = 4): per-mode constants, scan.
+ * the kernels of stage k are launched with hipExtLaunchKernel so that the GPU
+ * itself stamps events[2k] when the stage's first kernel starts and
+ * events[2k+1] when its last kernel ends (hipEventElapsedTime of a pair is
+ * the stage's duration, without the dispatch gap before it).  A pair of NULL
+ * handles leaves that stage untimed (plain launches: an event-stamped launch
+ * costs more host time).  n_events = 4 for both:
+ *   fft:  [0,1] parameters -> kernel spectrum (generator and spectrum
+ *         kernels), [2,3] convolution.
+ *   scan: [0,1] per-mode constants, [2,3] scan.
  * The events are owned by the caller and must have timing enabled; a NULL
  * array, a pair with one NULL handle, or a wrong n_events returns
  * DSSM_ERR_INVALID_ARG before anything is enqueued. */

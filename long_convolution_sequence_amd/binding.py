@@ -226,9 +226,10 @@ def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace
 
 def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=None,
                   workspace=None, stream=None):
-    """forward_fft / forward_scan whose kernels the GPU brackets with the given
-    raw hipEvent_t handles (ints): a start/stop pair per kernel, 6 for fft
-    (generator, spectrum, convolution), 4 for scan (constants, scan)."""
+    """forward_fft / forward_scan whose stages the GPU brackets with the given
+    raw hipEvent_t handles (ints, None for an untimed stage): a start/stop pair
+    per stage, 4 in all -- fft: kernel spectrum (from the parameters),
+    convolution; scan: constants, scan."""
     if path == "fft":
         fn, op = lib().dssm_forward_fft_timed, OP_FFT
     else:

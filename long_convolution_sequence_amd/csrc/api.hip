@@ -94,7 +94,8 @@ Layout layout(int op, const dssm_shape* s) {
     return at;
   };
   if (op == DSSM_OP_FFT) {
-    const size_t M = (size_t)1 << fft_log2m(s->L);
+    const int log2m = fft_log2m(s->L);
+    const size_t M = (size_t)1 << log2m;
     l.reK = take(ndh * L * sizeof(float));
     l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
   }
@@ -198,7 +199,7 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
   bool empty = false;
   int rc = check_shape(op, s, &empty);
   if (rc) return rc;
-  const int want = (op == DSSM_OP_FFT) ? 6 : 4;
+  const int want = 4;
   if (events && n_events != want)
     return fail(DSSM_ERR_INVALID_ARG, "n_events must be %d (got %d)", want, n_events);
   if (empty) return ok();
@@ -212,19 +213,19 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int ndir = 1 + s->bidirectional;
   if (op == DSSM_OP_FFT) {
-    const int ndh = ndir * s->H;
-    float* reK = at<float>(ws, l.reK);
-    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndh, s->N, s->L, 0, reK, st,
-                                   kev(events, 0)),
-                        "gen launch")))
-      return rc;
     const int log2m = fft_log2m(s->L);
     float2* spec = at<float2>(ws, l.spec);
-    if ((rc = hip_check(
-             launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st, kev(events, 1)),
-             "spectrum launch")))
+    const KEvents e0 = kev(events, 0);  // parameters -> spectrum: generator + spectrum
+    float* reK = at<float>(ws, l.reK);
+    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndir * s->H, s->N, s->L, 0, reK,
+                                   st, KEvents{e0.start, nullptr}),
+                        "gen launch")))
       return rc;
-    if ((rc = hip_check(launch_conv(u, spec, s->B, s->H, s->L, log2m, y, st, kev(events, 2)),
+    if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st,
+                                        KEvents{nullptr, e0.stop}),
+                        "spectrum launch")))
+      return rc;
+    if ((rc = hip_check(launch_conv(u, spec, s->B, s->H, s->L, log2m, y, st, kev(events, 1)),
                         "conv launch")))
       return rc;
   } else {

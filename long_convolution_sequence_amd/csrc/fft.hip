@@ -319,24 +319,63 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// Twiddle root of pass p for thread lt, w = exp(-2 pi i m / S) (unused by the
-// last pass).  The index is opaque, so each pass loads its root afresh, one
-// pass ahead of its use, instead of the compiler keeping every pass's root
+// Twiddle root of pass 0 for thread lt, w = exp(-2 pi i lt / M).  The index is
+// opaque, so each use loads the root afresh instead of the compiler keeping it
 // live across the kernel.
-template <class C, int P>
-__device__ __forceinline__ float2 pass_w(int lt) {
-  using G = PassGeom<C, P>;
+template <class C>
+__device__ __forceinline__ float2 pass0_w(int lt) {
+  using G = PassGeom<C, 0>;
   if constexpr (G::kLast) return make_float2(1.f, 0.f);
   else return g_twiddle[G::m_of(opaque(lt)) * (DSSM_TWN / G::S)];
 }
 
-// Powers of the root of pass p; opaque, so they are recomputed per pass and
-// not shared (and kept live) between passes that use the same root.
-template <class C, int P>
-__device__ __forceinline__ void pass_powers(float2 w, float2* p) {
-  if constexpr (!PassGeom<C, P>::kLast) {
+// Powers of the pass-0 root (product tree); opaque, so they are recomputed
+// per use and not kept live between uses.
+template <class C>
+__device__ __forceinline__ void pass0_powers(float2 w, float2* p) {
+  if constexpr (!PassGeom<C, 0>::kLast) {
     asm volatile("" : "+v"(w.x), "+v"(w.y));
     powers16(w, p);
+  }
+}
+
+// Twiddles of the wave-local radix-16 passes 1 .. NP-2, one LDS table per
+// workgroup: entry off(P) + (q - 1) s + m = exp(-2 pi i m q / S) for q = 1..15,
+// m < s (s = S / 16 <= 64), the exactly rounded table values.  A pass reads
+// its 15 powers instead of forming them by a product tree.
+template <class C>
+struct TwTab {
+  static constexpr int s_of(int P) { return C::M >> (4 * P + 4); }
+  static constexpr int off(int P) {
+    int o = 0;
+    for (int q = 1; q < P; ++q) o += 15 * s_of(q);
+    return o;
+  }
+  static constexpr int N = C::NP >= 3 ? off(C::NP - 1) : 0;  // entries
+  static constexpr int kAlloc = N > 0 ? N : 1;
+};
+
+template <class C>
+__device__ __forceinline__ void twtab_init(float2* tab) {
+  using TT = TwTab<C>;
+  for (int idx = threadIdx.x; idx < TT::N; idx += blockDim.x) {
+    int P = 1;
+    while (idx >= TT::off(P + 1)) ++P;
+    const int sp = TT::s_of(P), rel = idx - TT::off(P);
+    const int q = rel / sp + 1, m = rel % sp;
+    tab[idx] = g_twiddle[m * q * (DSSM_TWN / (16 * sp))];  // m q < 16 sp = S
+  }
+}
+
+// Powers of pass P >= 1 for thread lt, from the table.
+template <class C, int P>
+__device__ __forceinline__ void table_powers(const float2* tab, int lt, float2* p) {
+  using G = PassGeom<C, P>;
+  if constexpr (!G::kLast) {
+    // opaque index: reloaded per use, not kept live between the halves
+    const float2* t = tab + TwTab<C>::off(P) + G::m_of(opaque(lt)) - G::s;
+#pragma unroll
+    for (int q = 1; q < 16; ++q) p[q] = t[q * G::s];
   }
 }
 
@@ -385,64 +424,52 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // Forward passes P .. NP-1 (P >= 1) of one array, wave-local.  Entry: v holds
-// pass-P inputs, w the pass-P root; exit: the bins at positions PT lt + r.
+// pass-P inputs; exit: the bins at positions PT lt + r.
 template <class C, int P>
-__device__ __forceinline__ void fwd_tail(float2* v, float2* lds, int lt, float2 w) {
-  float2 wn = make_float2(1.f, 0.f);
-  if constexpr (P + 1 < C::NP) wn = pass_w<C, P + 1>(lt);
+__device__ __forceinline__ void fwd_tail(float2* v, float2* lds, int lt, const float2* tab) {
   float2 p[16];
-  pass_powers<C, P>(w, p);
+  table_powers<C, P>(tab, lt, p);
   fwd_compute<C, P>(v, p);
   if constexpr (P + 1 < C::NP) {
     lds_write<C, P>(lds, lt, v);
     wave_sync();
     lds_read<C, P + 1>(lds, lt, v);
-    fwd_tail<C, P + 1>(v, lds, lt, wn);
+    fwd_tail<C, P + 1>(v, lds, lt, tab);
   }
 }
 
 // Inverse passes P .. 1 of one array, wave-local.  Entry: v holds pass-P
-// outputs (P = NP-1: the bins), w the pass-P root; exit: the pass-1 inputs at
-// pass-1 positions.
+// outputs (P = NP-1: the bins); exit: the pass-1 inputs at pass-1 positions.
 template <class C, int P = C::NP - 1>
-__device__ __forceinline__ void inv_head(float2* v, float2* lds, int lt, float2 w) {
+__device__ __forceinline__ void inv_head(float2* v, float2* lds, int lt, const float2* tab) {
   if constexpr (P >= 1) {
-    float2 wn = make_float2(1.f, 0.f);
-    if constexpr (P > 1) wn = pass_w<C, P - 1>(lt);
     float2 p[16];
-    pass_powers<C, P>(w, p);
+    table_powers<C, P>(tab, lt, p);
     inv_compute<C, P>(v, p);
     if constexpr (P > 1) {
       lds_write<C, P>(lds, lt, v);
       wave_sync();
       lds_read<C, P - 1>(lds, lt, v);
-      inv_head<C, P - 1>(v, lds, lt, wn);
+      inv_head<C, P - 1>(v, lds, lt, tab);
     }
   }
 }
 
 // Forward transform of one array.  Entry: register r holds the point
-// nat(lt, r); exit: the bin at position PT lt + r.  One workgroup barrier;
-// all threads of the workgroup call it together.
+// nat(lt, r); exit: the bin at position PT lt + r.  One workgroup barrier
+// (which also publishes the twiddle table); all threads of the workgroup call
+// it together.
 template <class C>
-__device__ __forceinline__ void forward1(float2* v, float2* lds, int lt) {
+__device__ __forceinline__ void forward1(float2* v, float2* lds, int lt, const float2* tab) {
   float2 p[16];
-  pass_powers<C, 0>(pass_w<C, 0>(lt), p);
-  float2 w1 = make_float2(1.f, 0.f);
-  if constexpr (C::NP > 1) w1 = pass_w<C, 1>(lt);
+  pass0_powers<C>(pass0_w<C>(lt), p);
   fwd_compute<C, 0>(v, p);
   if constexpr (C::NP > 1) {
     lds_write<C, 0>(lds, lt, v);
     __syncthreads();
     lds_read<C, 1>(lds, lt, v);
-    fwd_tail<C, 1>(v, lds, lt, w1);
+    fwd_tail<C, 1>(v, lds, lt, tab);
   }
-}
-
-// Inverse passes NP-1 .. 1 of one array (inv_head with its root loaded).
-template <class C>
-__device__ __forceinline__ void inverse_head(float2* v, float2* lds, int lt) {
-  inv_head<C>(v, lds, lt, pass_w<C, C::NP - 1>(lt));
 }
 
 // Pass-0 inverse of an array whose passes NP-1 .. 1 were inverted by
@@ -450,14 +477,14 @@ __device__ __forceinline__ void inverse_head(float2* v, float2* lds, int lt) {
 template <class C>
 __device__ __forceinline__ void inverse_finish(float2* v, float2* lds, int lt) {
   lt = opaque(lt);  // LDS addresses recomputed rather than kept from pass 0
-  const float2 w0 = pass_w<C, 0>(lt);
+  const float2 w0 = pass0_w<C>(lt);
   if constexpr (C::NP > 1) {
     lds_write<C, 1>(lds, lt, v);
     __syncthreads();
     lds_read<C, 0>(lds, lt, v);
   }
   float2 p[16];
-  pass_powers<C, 0>(w0, p);
+  pass0_powers<C>(w0, p);
   inv_compute<C, 0>(v, p);
 }
 
@@ -477,19 +504,64 @@ __device__ __forceinline__ void odd_twiddle_fixed(float2* v) {
   }
 }
 
-// Spectrum of the (bidirectional) kernel: one transform per (h, half).
-//   spec[h, half, pos] = ( F_f + conj(F_b) + D_f + D_b ) / (2M),
-//   F_d = DFT_M( pad(Re K[d,h]) * t^half ),  t[n] = exp(-i pi n / M).
+// Frequency index of transform position P, and its inverse, for the passes of
+// Cfg C (in-place DIF: position digits, most significant first, are the
+// frequency digits, least significant first; radix 16 except the last pass,
+// radix RLAST).
+template <class C>
+__device__ __forceinline__ int freq_of_pos(int P) {
+  int k = (P % C::RLAST) << (4 * (C::NP - 1));
+  int q = P / C::RLAST;
+#pragma unroll
+  for (int i = C::NP - 2; i >= 0; --i) {
+    k |= (q & 15) << (4 * i);
+    q >>= 4;
+  }
+  return k;
+}
+
+template <class C>
+__device__ __forceinline__ int pos_of_freq(int k) {
+  int P = 0;
+#pragma unroll
+  for (int i = 0; i < C::NP - 1; ++i) P = P * 16 + ((k >> (4 * i)) & 15);
+  return P * C::RLAST + (k >> (4 * (C::NP - 1)));
+}
+
+// Spectrum of the kernel, in the convolution's layout:
+//   spec[h, half, e] = ( X[2 k + half] + D_f + D_b ) / (2M),   e = r T + t,
+//   k = frequency of the convolution's transform position 16 t + r,
+//   X = DFT_2M( pad(Re K_f) ) + conj( DFT_2M( pad(Re K_b) ) ).
 // The feed-through D u is the convolution with D at tap 0, whose transform is
 // the constant D: adding it to every bin makes the convolution produce y + D u.
 // The backward DLR is a correlation with Re K_b, whose spectrum is the
 // conjugate (no wrap-around reaches the first L outputs on a 2M circle).
-template <int LOG2M>
-__global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void spectrum_kernel(
+//
+// Both real sequences of a channel ride in ONE complex transform, and the two
+// real spectra are separated afterwards from the bins k and -k (the Hermitian
+// symmetry of a real sequence's spectrum):
+// * PACK (one direction): z[n] = K[2n] + i K[2n+1], n < S = M/2 (the even and
+//   odd samples).  With Z = DFT_M(z): E = (Z[k] + conj Z[-k]) / 2 and
+//   O = (Z[k] - conj Z[-k]) / 2i are the spectra of the even and odd samples,
+//   and X[m] = E[m] + exp(-i pi m / M) O[m].  Even m need only Z at even
+//   indices, DFT_S(z); odd m only Z at odd indices, DFT_S(z exp(-2 pi i n/M)):
+//   workgroup `half` computes one S-point transform.
+// * otherwise (two directions, or M = 16): z[n] = K_f[n] + i K_b[n], n < M,
+//   and workgroup `half` computes the even or odd bins of its 2M-point
+//   transform Z (an M-point transform of z, or of z t, t[n] = exp(-i pi n/M)),
+//   then X[m] = (Z[m] + conj Z[-m]) / 2 + i (conj Z[m] - Z[-m]) / 2.
+// After the transform the bins go to LDS in position order; each thread then
+// reads the pairs its outputs need.
+template <int LOG2M, bool PACK>
+__global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spectrum_kernel(
     const float* __restrict__ reK, const float* __restrict__ D, int ndir, int H, int L,
     float2* __restrict__ spec) {
-  using C = Cfg<LOG2M, 16>;
+  using C = Cfg<PACK ? LOG2M - 1 : LOG2M, 16>;  // the transform computed here
+  using CM = Cfg<LOG2M, 16>;                     // the convolution's transform
+  constexpr int M = CM::M, S = C::M;
   __shared__ float2 lds_all[C::G * C::LDSN];
+  __shared__ float2 tab[TwTab<C>::kAlloc];
+  twtab_init<C>(tab);
   const int lt = threadIdx.x % C::T;
   const int gi = threadIdx.x / C::T;
   float2* lds = lds_all + gi * C::LDSN;
@@ -498,35 +570,94 @@ __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void spectrum_kernel(
   const int h = active ? (prob >> 1) : 0;
   const int half = prob & 1;
 
-  float2 acc[C::PT];
-  for (int d = 0; d < ndir; ++d) {
-    float2 v[C::PT];
-    const float* k = reK + ((size_t)d * H + h) * L;
+  // The factors 1/2 of the separation and 1/2M of the inverse transform are
+  // applied to the input (the transform is linear).
+  const float c = 0.25f / (float)M;
+  float2 v[C::PT];
+  {
+    const float* kf = reK + (size_t)h * L;
+    const float* kb = reK + ((size_t)(ndir - 1) * H + h) * L;
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) {
       const int n = nat<C>(lt, r);
-      v[r] = make_float2((active && n < L) ? k[n] : 0.f, 0.f);
+      float a = 0.f, b = 0.f;
+      if (PACK) {
+        if (active && 2 * n < L) a = kf[2 * n];
+        if (active && 2 * n + 1 < L) b = kf[2 * n + 1];
+      } else if (active && n < L) {
+        a = kf[n];
+        if (ndir == 2) b = kb[n];
+      }
+      v[r] = make_float2(a, b);
     }
-    if (half) {
-      const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * C::M))];
-      odd_twiddle_fixed<C, false>(v);
-#pragma unroll
-      for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
-    }
-    if (d > 0) __syncthreads();  // the previous direction's last reads are done
-    forward1<C>(v, lds, lt);
-#pragma unroll
-    for (int r = 0; r < C::PT; ++r) acc[r] = (d == 0) ? v[r] : cadd(acc[r], cconj(v[r]));
   }
+  if (half) {  // z t_S, t_S[n] = exp(-i pi n / S)
+    const float2 tl = cscale(g_twiddle[lt * (DSSM_TWN / (2 * S))], c);
+    odd_twiddle_fixed<C, false>(v);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
+  } else {
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = cscale(v[r], c);
+  }
+  forward1<C>(v, lds, lt, tab);
+  // bins to LDS at their positions (this thread's own, wave-local positions)
+  wave_sync();
+  lds_write<C, C::NP - 1>(lds, lt, v);
+  __syncthreads();
   if (!active) return;
+
   float deff = 0.f;
   for (int d = 0; d < ndir; ++d) deff += D[(size_t)d * H + h];
-  const float scale = 1.0f / (2.0f * (float)C::M);
-  // bin at position PT lt + r is stored at r T + lt (coalesced across lanes)
-  float2* out = spec + ((size_t)h * 2 + half) * C::M + lt;
+  deff *= 1.0f / (2.0f * (float)M);
+  float2* out = spec + ((size_t)h * 2 + half) * M;
+  // Outputs of this thread: t = lt + T_S i (all the convolution's t), every r.
+  // freq_of_pos is a permutation of bit fields, so the frequency of 16 t + r is
+  // kt | kr, with kr a compile-time constant.
+  static_assert(CM::T % C::T == 0, "output split");
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r)
-    out[(size_t)r * C::T] = cscale(make_float2(acc[r].x + deff, acc[r].y), scale);
+  for (int i = 0; i < CM::T / C::T; ++i) {
+    const int t = lt + C::T * i;
+    const int kt = freq_of_pos<CM>(16 * t);
+    if constexpr (PACK) {
+      // Bins k and k + S share the pair Z[k mod S], Z[mirror]; k + S is the
+      // position bit RLAST/2 of the convolution's transform (top bit of its
+      // last digit), and its twiddle is -w.
+      constexpr int RB = CM::RLAST / 2;
+      const int kt1 = kt & (S - 1);
+      const int pt = pos_of_freq<C>(kt1);
+      // exp(-i pi (2 kt + half) / M): per-t table value
+      const float2 wt = g_twiddle[(2 * kt + half) * (DSSM_TWN / (2 * M))];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (r & RB) continue;
+        const int kr = freq_of_pos<CM>(r);
+        const int k1 = kt1 | (kr & (S - 1));
+        const int pa = pt + pos_of_freq<C>(kr & (S - 1));  // disjoint bit fields
+        const int pb = half ? ((S - 1) ^ pa) : pos_of_freq<C>((S - k1) & (S - 1));
+        const float2 A = lds[C::pad(pa)];
+        const float2 B = lds[C::pad(pb)];
+        // E = A + conj B, O = -i (A - conj B), X[k] = E + w O, X[k + S] = E - w O
+        const float2 e = make_float2(A.x + B.x, A.y - B.y);
+        const float2 o = make_float2(A.y + B.y, B.x - A.x);
+        const float2 w = cmul(wt, g_twiddle[kr * (DSSM_TWN / M)]);
+        const float2 wo = cmul(w, o);
+        out[(size_t)r * CM::T + t] = make_float2(e.x + wo.x + deff, e.y + wo.y);
+        out[(size_t)(r | RB) * CM::T + t] = make_float2(e.x - wo.x + deff, e.y - wo.y);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k = kt | freq_of_pos<CM>(r);  // output bin X[2k + half]
+        const int k2 = half ? (M - 1 - k) : ((M - k) & (M - 1));
+        const float2 A = lds[C::pad(pos_of_freq<C>(k))];
+        const float2 B = lds[C::pad(pos_of_freq<C>(k2))];
+        // (A + conj B) + i (conj A - B)
+        out[(size_t)r * CM::T + t] =
+            make_float2(A.x + B.x + A.y + B.y + deff, A.y - B.y + A.x - B.x);
+      }
+    }
+  }
 }
 
 // Points per thread of the convolution.  16 (1024 threads at M = 16384, four
@@ -544,6 +675,8 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
     float* __restrict__ y) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   __shared__ float2 lds_all[C::G * C::LDSN];
+  __shared__ float2 tab[TwTab<C>::kAlloc];
+  twtab_init<C>(tab);  // published by the first barrier, before its first use
   const int lt = threadIdx.x % C::T;
   const int gi = threadIdx.x / C::T;
   float2* lds = lds_all + gi * C::LDSN;
@@ -587,34 +720,32 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   // pass 0 of both halves (shared twiddles)
   {
     float2 p[16];
-    pass_powers<C, 0>(pass_w<C, 0>(lt), p);
+    pass0_powers<C>(pass0_w<C>(lt), p);
     fwd_compute<C, 0>(ve, p);
     fwd_compute<C, 0>(vo, p);
   }
   // even half: exchange, wave-local passes, product, inverse back to pass 0
   if constexpr (C::NP > 1) {
-    const float2 w1 = pass_w<C, 1>(lt);
     lds_write<C, 0>(lds, lt, ve);
     __syncthreads();
     lds_read<C, 1>(lds, lt, ve);
-    fwd_tail<C, 1>(ve, lds, lt, w1);
+    fwd_tail<C, 1>(ve, lds, lt, tab);
   }
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[(size_t)r * C::T]);
-  inverse_head<C>(ve, lds, lt);
+  inv_head<C>(ve, lds, lt, tab);
   inverse_finish<C>(ve, lds, lt);
   // odd half: its pass-0 positions are disjoint from every other thread's,
   // so it may be written while others still read the even half's
   if constexpr (C::NP > 1) {
-    const float2 w1 = pass_w<C, 1>(lt);
     lds_write<C, 0>(lds, lt, vo);
     __syncthreads();
     lds_read<C, 1>(lds, lt, vo);
-    fwd_tail<C, 1>(vo, lds, lt, w1);
+    fwd_tail<C, 1>(vo, lds, lt, tab);
   }
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[(size_t)r * C::T]);
-  inverse_head<C>(vo, lds, lt);
+  inv_head<C>(vo, lds, lt, tab);
   inverse_finish<C>(vo, lds, lt);
   // The thread index is re-derived here (opaque to the compiler) so the store
   // addresses and t[lt] are recomputed instead of being kept live -- and
@@ -639,14 +770,26 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   }
 }
 
+template <int LOG2M, bool PACK>
+hipError_t spectrum_launch2(const float* reK, const float* D, int ndir, int H, int L,
+                            float2* spec, hipStream_t st, KEvents ev) {
+  using C = Cfg<PACK ? LOG2M - 1 : LOG2M, 16>;
+  const int nprob = 2 * H;
+  const int nblk = (nprob + C::G - 1) / C::G;
+  launch_k(spectrum_kernel<LOG2M, PACK>, dim3(nblk), dim3(C::WG), st, ev, reK, D, ndir, H, L,
+           spec);
+  return hipGetLastError();
+}
+
+// One direction packs even and odd samples (transforms of M/2 points) when M
+// allows it; two directions pack forward and backward kernels.
 template <int LOG2M>
 hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, int L, float2* spec,
                            hipStream_t st, KEvents ev) {
-  using C = Cfg<LOG2M, 16>;
-  const int nprob = 2 * H;
-  const int nblk = (nprob + C::G - 1) / C::G;
-  launch_k(spectrum_kernel<LOG2M>, dim3(nblk), dim3(C::WG), st, ev, reK, D, ndir, H, L, spec);
-  return hipGetLastError();
+  if constexpr (LOG2M >= 5) {
+    if (ndir == 1) return spectrum_launch2<LOG2M, true>(reK, D, ndir, H, L, spec, st, ev);
+  }
+  return spectrum_launch2<LOG2M, false>(reK, D, ndir, H, L, spec, st, ev);
 }
 
 template <int LOG2M>

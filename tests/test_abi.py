@@ -171,7 +171,7 @@ def test_s5_workspace_and_validation():
     assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
 
 
-@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 6), ("dssm_forward_scan_timed", 4)])
+@pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 4), ("dssm_forward_scan_timed", 4)])
 def test_timed_variants_validate_events(name, n):
     fn = getattr(bd.lib(), name)
     good = bd.Shape(2, 3, 4, 32, 0)
