@@ -6,8 +6,8 @@ A step is one full forward of the layer by the convolution view (kernel
 generation, kernel spectrum, FFT convolution with the D skip)
 on the long-sequence workload B=4, H=128, N=64, L=16384 (log_re scaled by
 0.1), seeded synthetic inputs already resident in device memory.  Several
-input/output sets are rotated so that the 256 MB Infinity Cache does not hold
-the step's inputs from the previous step.
+input/output sets (576 MiB in all) are rotated so that the 256 MB Infinity Cache
+does not hold the step's inputs from an earlier step.
 
 Prints ONE JSON line: value = elements (B*H*L) per second over the timed
 steps (wall clock between two device synchronisations), the per-kernel
@@ -211,7 +211,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--rotate", type=int, default=6, help="input/output sets rotated per step")
+    ap.add_argument("--rotate", type=int, default=9,
+                    help="input/output sets rotated per step (9 x 64 MiB > the 256 MB MALL x 2)")
     ap.add_argument("--scan-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     a = ap.parse_args()

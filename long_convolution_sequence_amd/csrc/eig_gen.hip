@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void gen_kernel(const float* __restrict__ log_
     gen::build_tables<4, 16, 16, kRow, kRow, kComplex>(log_re, log_im, W, dh * N + n0, nn, t >> 2,
                                                        t & 3, q0, Q, sA, sP, sQ);
     __syncthreads();
-    gen::contract<kRow, kRow, kComplex>(sA, sP, sQ, 16 * w, (2 * nn + 3) / 4, lane, acc_re,
+    gen::contract<kRow, kRow, kComplex>(sA, sP, sQ, 16 * w, 0, (2 * nn + 3) / 4, lane, acc_re,
                                         acc_im);
     __syncthreads();
   }

@@ -39,6 +39,8 @@
 #include "dssm_internal.h"
 #include "twiddle_table.inc"
 
+#define DSSM_FFT_CASES(X) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14)
+
 namespace dssm {
 namespace {
 
@@ -504,6 +506,14 @@ __device__ __forceinline__ void odd_twiddle_fixed(float2* v) {
   }
 }
 
+// Workgroup i runs on XCD i % 8; when the grid divides by 8, consecutive
+// problems -- which read the same data: the two halves of a channel's
+// spectrum, or the row pairs of a channel -- are placed on the same XCD so
+// the second read is served by its L2.
+__device__ __forceinline__ int xcd_grouped(int i, int n) {
+  return (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
+}
+
 // Frequency index of transform position P, and its inverse, for the passes of
 // Cfg C (in-place DIF: position digits, most significant first, are the
 // frequency digits, least significant first; radix 16 except the last pass,
@@ -526,6 +536,44 @@ __device__ __forceinline__ int pos_of_freq(int k) {
 #pragma unroll
   for (int i = 0; i < C::NP - 1; ++i) P = P * 16 + ((k >> (4 * i)) & 15);
   return P * C::RLAST + (k >> (4 * (C::NP - 1)));
+}
+
+// Separated outputs of a PACK spectrum half for the convolution's column t
+// (its 16 rows): lds holds the bins of the M/2-point transform of the packed
+// z (or z exp(-2 pi i n / M) for half 1) at their transform positions.
+// freq_of_pos is a permutation of bit fields, so the frequency of 16 t + r is
+// kt | kr, with kr a compile-time constant.  Bins k and k + S share the pair
+// Z[k mod S], Z[mirror]; k + S is the position bit RLAST/2 of the
+// convolution's transform (top bit of its last digit), and its twiddle is -w.
+template <int LOG2M>
+__device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t, float deff,
+                                             float2* out) {
+  using C = Cfg<LOG2M - 1, 16>;
+  using CM = Cfg<LOG2M, 16>;
+  constexpr int M = CM::M, S = C::M;
+  constexpr int RB = CM::RLAST / 2;
+  const int kt = freq_of_pos<CM>(16 * t);
+  const int kt1 = kt & (S - 1);
+  const int pt = pos_of_freq<C>(kt1);
+  // exp(-i pi (2 kt + half) / M): per-t table value
+  const float2 wt = g_twiddle[(2 * kt + half) * (DSSM_TWN / (2 * M))];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    if (r & RB) continue;
+    const int kr = freq_of_pos<CM>(r);
+    const int k1 = kt1 | (kr & (S - 1));
+    const int pa = pt + pos_of_freq<C>(kr & (S - 1));  // disjoint bit fields
+    const int pb = half ? ((S - 1) ^ pa) : pos_of_freq<C>((S - k1) & (S - 1));
+    const float2 A = lds[C::pad(pa)];
+    const float2 B = lds[C::pad(pb)];
+    // E = A + conj B, O = -i (A - conj B), X[k] = E + w O, X[k + S] = E - w O
+    const float2 e = make_float2(A.x + B.x, A.y - B.y);
+    const float2 o = make_float2(A.y + B.y, B.x - A.x);
+    const float2 w = cmul(wt, g_twiddle[kr * (DSSM_TWN / M)]);
+    const float2 wo = cmul(w, o);
+    out[(size_t)r * CM::T + t] = make_float2(e.x + wo.x + deff, e.y + wo.y);
+    out[(size_t)(r | RB) * CM::T + t] = make_float2(e.x - wo.x + deff, e.y - wo.y);
+  }
 }
 
 // Spectrum of the kernel, in the convolution's layout:
@@ -565,7 +613,8 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
   const int lt = threadIdx.x % C::T;
   const int gi = threadIdx.x / C::T;
   float2* lds = lds_all + gi * C::LDSN;
-  const int prob = blockIdx.x * C::G + gi;
+  // the two halves of a channel, which read the same K row, share an XCD
+  const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
   const bool active = prob < 2 * H;
   const int h = active ? (prob >> 1) : 0;
   const int half = prob & 1;
@@ -620,31 +669,7 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
     const int t = lt + C::T * i;
     const int kt = freq_of_pos<CM>(16 * t);
     if constexpr (PACK) {
-      // Bins k and k + S share the pair Z[k mod S], Z[mirror]; k + S is the
-      // position bit RLAST/2 of the convolution's transform (top bit of its
-      // last digit), and its twiddle is -w.
-      constexpr int RB = CM::RLAST / 2;
-      const int kt1 = kt & (S - 1);
-      const int pt = pos_of_freq<C>(kt1);
-      // exp(-i pi (2 kt + half) / M): per-t table value
-      const float2 wt = g_twiddle[(2 * kt + half) * (DSSM_TWN / (2 * M))];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (r & RB) continue;
-        const int kr = freq_of_pos<CM>(r);
-        const int k1 = kt1 | (kr & (S - 1));
-        const int pa = pt + pos_of_freq<C>(kr & (S - 1));  // disjoint bit fields
-        const int pb = half ? ((S - 1) ^ pa) : pos_of_freq<C>((S - k1) & (S - 1));
-        const float2 A = lds[C::pad(pa)];
-        const float2 B = lds[C::pad(pb)];
-        // E = A + conj B, O = -i (A - conj B), X[k] = E + w O, X[k + S] = E - w O
-        const float2 e = make_float2(A.x + B.x, A.y - B.y);
-        const float2 o = make_float2(A.y + B.y, B.x - A.x);
-        const float2 w = cmul(wt, g_twiddle[kr * (DSSM_TWN / M)]);
-        const float2 wo = cmul(w, o);
-        out[(size_t)r * CM::T + t] = make_float2(e.x + wo.x + deff, e.y + wo.y);
-        out[(size_t)(r | RB) * CM::T + t] = make_float2(e.x - wo.x + deff, e.y - wo.y);
-      }
+      pack_outputs<LOG2M>(lds, half, t, deff, out);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -667,28 +692,16 @@ template <int LOG2M>
 constexpr int conv_pt() { return 16; }
 
 // Convolution of a pair of batch rows (b1 = 2 pr, b2 = 2 pr + 1) of channel
-// h.  Both halves of the 2M spectrum are transformed together: ve = z (even
-// bins), vo = z t (odd bins), where z = u[b1] + i u[b2].
-template <int LOG2M>
-__global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kernel(
-    const float* __restrict__ u, const float2* __restrict__ spec, int B, int H, int L, int npairs,
-    float* __restrict__ y) {
+// h by one workgroup (C::G problems per workgroup when a transform is
+// smaller than a wave).  Both halves of the 2M spectrum are transformed:
+// ve = z (even bins), vo = z t (odd bins), where z = u[b1] + i u[b2].
+// `ready()` is called by every thread before the spectrum is first read.
+template <int LOG2M, class Ready>
+__device__ __forceinline__ void conv_body(const float* __restrict__ u,
+                                          const float2* __restrict__ spec, int B, int H, int L,
+                                          int h, int pr, bool active, int lt, float2* lds,
+                                          const float2* tab, float* __restrict__ y, Ready ready) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
-  __shared__ float2 lds_all[C::G * C::LDSN];
-  __shared__ float2 tab[TwTab<C>::kAlloc];
-  twtab_init<C>(tab);  // published by the first barrier, before its first use
-  const int lt = threadIdx.x % C::T;
-  const int gi = threadIdx.x / C::T;
-  float2* lds = lds_all + gi * C::LDSN;
-  // Workgroup i runs on XCD i % 8; when the grid divides by 8, consecutive
-  // problems -- the pairs of one channel, which read the same spectrum -- are
-  // placed on the same XCD so the second read is served by its L2.
-  const int nblk = gridDim.x;
-  const int blk = (nblk % 8 == 0) ? (blockIdx.x % 8) * (nblk / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int prob = blk * C::G + gi;
-  const bool active = prob < H * npairs;
-  const int h = active ? prob / npairs : 0;
-  const int pr = active ? prob % npairs : 0;
   const int b1 = 2 * pr, b2 = 2 * pr + 1;
   const bool has2 = active && b2 < B;
   const float* u1 = u + ((size_t)b1 * H + h) * L;
@@ -712,8 +725,8 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], tl);
   }
-  // spectrum bin at position PT lt + r lives at r T + lt (as the spectrum kernel,
-  // which uses the same PT, stores it)
+  // spectrum bin at position PT lt + r lives at r T + lt (as the spectrum
+  // kernels, which use the same PT, store it)
   static_assert(C::PT == Cfg<LOG2M, 16>::PT, "spectrum layout is shared with spectrum_kernel");
   const float2* se = spec + ((size_t)h * 2 + 0) * C::M + lt;
   const float2* so = spec + ((size_t)h * 2 + 1) * C::M + lt;
@@ -731,6 +744,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
     lds_read<C, 1>(lds, lt, ve);
     fwd_tail<C, 1>(ve, lds, lt, tab);
   }
+  ready();
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[(size_t)r * C::T]);
   inv_head<C>(ve, lds, lt, tab);
@@ -768,6 +782,22 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
       if (has2) y2[n] = ve[r].y;
     }
   }
+}
+
+template <int LOG2M>
+__global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kernel(
+    const float* __restrict__ u, const float2* __restrict__ spec, int B, int H, int L, int npairs,
+    float* __restrict__ y) {
+  using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
+  __shared__ float2 lds_all[C::G * C::LDSN];
+  __shared__ float2 tab[TwTab<C>::kAlloc];
+  twtab_init<C>(tab);  // published by the first barrier, before its first use
+  const int lt = threadIdx.x % C::T;
+  const int gi = threadIdx.x / C::T;
+  const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
+  const bool active = prob < H * npairs;
+  conv_body<LOG2M>(u, spec, B, H, L, active ? prob / npairs : 0, active ? prob % npairs : 0,
+                   active, lt, lds_all + gi * C::LDSN, tab, y, [] {});
 }
 
 template <int LOG2M, bool PACK>
@@ -812,7 +842,6 @@ int fft_log2m(int L) {
   return l;
 }
 
-#define DSSM_FFT_CASES(X) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14)
 
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
                            float2* spec, hipStream_t st, KEvents ev) {

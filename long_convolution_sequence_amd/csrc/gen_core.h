@@ -95,30 +95,31 @@ __device__ __forceinline__ void build_tables(const float* __restrict__ log_re,
 }
 
 // Contraction of one chunk for one wave: anchors [qw, qw + 16) (columns of
-// sA) by all 64 r, over rows 0 .. 4 steps - 1.  acc[c][v] accumulates
-// K[64 (qw + 4 (lane / 16) + v) + 16 c + lane % 16].
-template <int RA, int RP, bool Q_OUT>
+// sA) by the NC blocks of 16 taps r0 .. r0 + 16 NC - 1, over rows
+// 0 .. 4 steps - 1.  acc[c][v] accumulates
+// K[64 (qw + 4 (lane / 16) + v) + r0 + 16 c + lane % 16].
+template <int RA, int RP, bool Q_OUT, int NC = 4>
 __device__ __forceinline__ void contract(const float* sA, const float* sP, const float* sQ, int qw,
-                                         int steps, int lane, v4f* acc_re, v4f* acc_im) {
+                                         int r0, int steps, int lane, v4f* acc_re, v4f* acc_im) {
   const float* pa = sA + (lane >> 4) * RA + qw + (lane & 15);
-  const float* pp = sP + (lane >> 4) * RP + (lane & 15);
-  const float* pq = sQ + (Q_OUT ? (lane >> 4) * RP + (lane & 15) : 0);
+  const float* pp = sP + (lane >> 4) * RP + r0 + (lane & 15);
+  const float* pq = sQ + (Q_OUT ? (lane >> 4) * RP + r0 + (lane & 15) : 0);
   // Two operand sets alternate: the loads of one step are in flight while
   // the previous step multiplies (no register copies between steps).
-  float a0, a1, b0[4], b1[4], q0v[4], q1v[4];
+  float a0, a1, b0[NC], b1[NC], q0v[NC], q1v[NC];
   auto load = [&](int ks, float& a, float* b, float* q) {
     const int ka = 4 * min(ks, steps - 1) * RA;
     const int kp = 4 * min(ks, steps - 1) * RP;
     a = pa[ka];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       b[c] = pp[kp + 16 * c];
       q[c] = Q_OUT ? pq[kp + 16 * c] : 0.f;
     }
   };
   auto mul = [&](float a, const float* b, const float* q) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < NC; ++c) {
       acc_re[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[c], acc_re[c], 0, 0, 0);
       if (Q_OUT) acc_im[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, q[c], acc_im[c], 0, 0, 0);
     }

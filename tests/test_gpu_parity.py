@@ -162,6 +162,9 @@ EDGE = [
     # one direction at every transform size of the packed spectrum (M = 32 .. 8192)
     (2, 3, 8, 17, 0), (1, 2, 8, 33, 0), (2, 2, 8, 64, 0), (1, 3, 8, 129, 0), (2, 2, 8, 300, 0),
     (1, 2, 8, 2047, 0), (2, 2, 8, 2049, 0), (1, 2, 8, 5000, 0), (2, 1, 8, 8192, 0),
+    # three or more row pairs per channel, several mode chunks (N = 100), ragged L
+    (4, 3, 8, 1500, 0), (5, 2, 16, 3000, 0), (6, 2, 100, 2048, 0), (3, 3, 64, 9000, 0),
+    (4, 2, 64, 16384, 0),
 ]
 
 
