@@ -13,7 +13,8 @@ pages define, in float64, from the float32 input values promoted exactly:
   State Space Models with Diagonal Linear RNNs", section 2: the parameterisation
   of Lambda, the kernel K_j = sum_n w_n lambda_n^j, the real cast, the causal
   convolution and the bidirectional sum; computed twice, as an O(L^2) direct sum
-  and as a sequential recurrence.
+  and as a sequential recurrence; and the recurrence continued from a given
+  state (streaming / one-token decode), returning the state it ends in.
 * ``s5``   -- the multi-input multi-output diagonal SSM of "Simplified State
   Space Layers for Sequence Modeling", section 3, computed as a sequential
   recurrence and as a direct causal sum over a prefix.
@@ -28,5 +29,6 @@ from .dlr import (  # noqa: F401
     dlr_kernel,
     dlr_direct,
     dlr_recurrence,
+    dlr_recurrence_state,
 )
 from .s5 import s5_recurrence, s5_direct_prefix  # noqa: F401

@@ -138,3 +138,30 @@ def dlr_recurrence(u, log_re, log_im, W, D, bidirectional=False):
             x = lam[d][None] * x + u[:, :, k, None]
             y[:, :, k] += (x * w[d][None]).sum(axis=-1).real
     return y
+
+
+def dlr_recurrence_state(u, log_re, log_im, W, D, x0=None):
+    """One-direction DLR forward from a given initial state, float64.
+
+    The recurrence of dlr_recurrence with x_{-1} = x0 instead of zero:
+      x_k = lambda * x_{k-1} + u_k,  y_k = Re(sum_n W_n x_{k,n}) + D u_k,
+    returning (y [B,H,L], x_{L-1} [B,H,N] complex) -- the state a later call
+    continues from.  This is the recurrent (RNN) view run in chunks ("The
+    Annotated S4", Part 1, "Discrete-time SSM: the recurrent representation":
+    the state carries everything the past contributes), and with x0 = 0 it
+    is dlr_recurrence.  With L = 0 the state passes through unchanged.
+    x0 is [B, H, N] complex (None = zero).
+    """
+    u = _real64(u)
+    Bsz, H, L = u.shape
+    lam = dlr_lambda(log_re, log_im)
+    if lam.shape[0] != 1:
+        raise ValueError("the stateful form has one direction")
+    w = _cplx128(W)[0]
+    N = lam.shape[-1]
+    x = np.zeros((Bsz, H, N), dtype=np.complex128) if x0 is None else _cplx128(x0).copy()
+    y = u * _real64(D)[0][None, :, None]
+    for k in range(L):
+        x = lam[0][None] * x + u[:, :, k, None]
+        y[:, :, k] += (x * w[None]).sum(axis=-1).real
+    return y, x
