@@ -685,6 +685,32 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
   }
 }
 
+// Raw buffer resource over `bytes` bytes at `base`.  The hardware range
+// check of raw buffers returns zero for loads at or beyond `bytes` and drops
+// such stores, so a row's tail and an inactive problem (bytes = 0) need no
+// branches; one SGPR descriptor plus one lane offset addresses all of a
+// thread's strided accesses.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float buf_load_f32(BufRes r, int voff, int soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ float2 buf_load_f32x2(BufRes r, int voff, int soff) {
+  const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+}
+
+__device__ __forceinline__ void buf_store_f32(BufRes r, int voff, int soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
 // Points per thread of the convolution.  16 (1024 threads at M = 16384, four
 // waves per SIMD) measured faster on MI355X than 32 (512 threads, two waves per
 // SIMD): 56 us against 76 us for the long-sequence workload.
@@ -704,32 +730,40 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   const int b1 = 2 * pr, b2 = 2 * pr + 1;
   const bool has2 = active && b2 < B;
-  const float* u1 = u + ((size_t)b1 * H + h) * L;
-  const float* u2 = u + ((size_t)(has2 ? b2 : b1) * H + h) * L;
+  // rows as buffers: element n of register r sits at byte 4 n, n = lt + T(...)
+  const BufRes ur1 = buf_res(u + ((size_t)b1 * H + h) * L, active ? 4u * L : 0u);
+  const BufRes ur2 = buf_res(u + ((size_t)(has2 ? b2 : b1) * H + h) * L, has2 ? 4u * L : 0u);
 
-  float2 ve[C::PT], vo[C::PT];
+  // The whole element offset goes in the range-checked lane offset (the
+  // scalar offset is added after the check).
+  auto load_pair = [&](float2* v) {
+    const int lo = opaque(lt);
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) {
-    const int n = nat<C>(lt, r);
-    float a = 0.f, b = 0.f;
-    if (active && n < L) {
-      a = u1[n];
-      if (has2) b = u2[n];
+    for (int r = 0; r < C::PT; ++r) {
+      const int o = 4 * nat<C>(lo, r);
+      v[r] = make_float2(buf_load_f32(ur1, o, 0), buf_load_f32(ur2, o, 0));
     }
-    ve[r] = make_float2(a, b);
-    vo[r] = ve[r];
-  }
+  };
+  // spectrum bin at position PT lt + r lives at r T + lt (as the spectrum
+  // kernels, which use the same PT, store it); always in range
+  static_assert(C::PT == Cfg<LOG2M, 16>::PT, "spectrum layout is shared with spectrum_kernel");
+  const BufRes sr = buf_res(spec + (size_t)h * 2 * C::M, 2u * C::M * 8u);
+  auto load_spec = [&](int half, float2* v) {
+    const int o = 8 * opaque(lt);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) v[r] = buf_load_f32x2(sr, o, 8 * (half * C::M + r * C::T));
+  };
+
+  float2 ve[C::PT], vo[C::PT], sv[C::PT];
+  load_pair(ve);
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) vo[r] = ve[r];
   {  // odd bins: pre-multiply by t[n] = t[lt] exp(-i pi (i + j NB) / PT)
     const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * C::M))];
     odd_twiddle_fixed<C, false>(vo);
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], tl);
   }
-  // spectrum bin at position PT lt + r lives at r T + lt (as the spectrum
-  // kernels, which use the same PT, store it)
-  static_assert(C::PT == Cfg<LOG2M, 16>::PT, "spectrum layout is shared with spectrum_kernel");
-  const float2* se = spec + ((size_t)h * 2 + 0) * C::M + lt;
-  const float2* so = spec + ((size_t)h * 2 + 1) * C::M + lt;
   // pass 0 of both halves (shared twiddles)
   {
     float2 p[16];
@@ -745,8 +779,9 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
     fwd_tail<C, 1>(ve, lds, lt, tab);
   }
   ready();
+  load_spec(0, sv);
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], se[(size_t)r * C::T]);
+  for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], sv[r]);
   inv_head<C>(ve, lds, lt, tab);
   inverse_finish<C>(ve, lds, lt);
   // odd half: its pass-0 positions are disjoint from every other thread's,
@@ -757,8 +792,9 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
     lds_read<C, 1>(lds, lt, vo);
     fwd_tail<C, 1>(vo, lds, lt, tab);
   }
+  load_spec(1, sv);
 #pragma unroll
-  for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], so[(size_t)r * C::T]);
+  for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], sv[r]);
   inv_head<C>(vo, lds, lt, tab);
   inverse_finish<C>(vo, lds, lt);
   // The thread index is re-derived here (opaque to the compiler) so the store
@@ -771,16 +807,13 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) ve[r] = cadd(ve[r], cmul(vo[r], tlc));
   }
-  if (!active) return;
-  float* y1 = y + ((size_t)b1 * H + h) * L;
-  float* y2 = y + ((size_t)b2 * H + h) * L;
+  const BufRes yr1 = buf_res(y + ((size_t)b1 * H + h) * L, active ? 4u * L : 0u);
+  const BufRes yr2 = buf_res(y + ((size_t)(has2 ? b2 : b1) * H + h) * L, has2 ? 4u * L : 0u);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) {
-    const int n = nat<C>(lte, r);
-    if (n < L) {
-      y1[n] = ve[r].x;
-      if (has2) y2[n] = ve[r].y;
-    }
+    const int o = 4 * nat<C>(lte, r);
+    buf_store_f32(yr1, o, 0, ve[r].x);
+    buf_store_f32(yr2, o, 0, ve[r].y);
   }
 }
 
