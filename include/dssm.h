@@ -132,6 +132,36 @@ int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape*
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                       float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* Streaming (stateful) forward by the recurrence view, one direction: the
+ * recurrence of dssm_forward_scan continued from a given state instead of
+ * zero ("The Annotated S4", Part 1, "Discrete-time SSM: the recurrent
+ * representation": the state carries everything the past contributes, so a
+ * sequence processed in consecutive chunks gives the outputs of the whole):
+ *   x_{-1} = x (on entry),  x_k = lambda x_{k-1} + u_k,
+ *   y_k = Re(sum_n W_n x_{k,n}) + D u_k,  x = x_{L-1} (on exit).
+ *   x [B, H, N] complex (float32 pairs), read and then overwritten in place;
+ *   it must not alias u or y.  u, y [B, H, L] as for dssm_forward_scan.
+ * Requires bidirectional = 0 (a right-to-left direction needs the future:
+ * DSSM_ERR_UNSUPPORTED).  L = 0 leaves x unchanged.  Workspace: the size
+ * dssm_workspace_size(DSSM_OP_SCAN, s) reports.  Chunks of a long sequence
+ * agree with the unsplit call within float32 rounding (the segment carries
+ * are combined in a different order). */
+int dssm_forward_scan_state(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                            float* x, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step for every (b, h), the recurrent view advanced by one token
+ * (the constant work per generated token that the DLR page's PG-19
+ * language-modelling paragraph contrasts with attention; "The Annotated S4",
+ * Part 3, "Sampling and caching": the recurrent state is the cache):
+ *   x <- lambda x + u_t,  y_t = Re(sum_n W_n x_n) + D u_t.
+ *   u_t, y_t [B, H] float32; x [B, H, N] complex, updated in place (no alias).
+ * s->L must be 1 and s->bidirectional 0.  lambda is formed in float64 and
+ * rounded once to float32 per call; a run of k steps is the float32 chain of
+ * k products, so its error grows with k like any float32 recurrence.  No
+ * workspace. */
+int dssm_step(const float* u_t, const dssm_dlr_params* p, const dssm_shape* s, float* x,
+              float* y_t, void* stream);
+
 /* ------------------------------------------------------------------------
  * S5-style multi-input multi-output diagonal SSM ("Simplified State Space
  * Layers for Sequence Modeling", section 3): one diagonal state of size P

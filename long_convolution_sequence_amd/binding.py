@@ -24,6 +24,7 @@ EXPORTS = [
     "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
     "dssm_gen_kernel", "dssm_forward_fft", "dssm_forward_scan",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
+    "dssm_forward_scan_state", "dssm_step",
     "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed",
 ]
 
@@ -86,6 +87,11 @@ def lib():
         f.restype = ctypes.c_int
         f.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, sz, vp,
                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.dssm_forward_scan_state.restype = ctypes.c_int
+    L.dssm_forward_scan_state.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
+                                          vp, vp, vp, sz, vp]
+    L.dssm_step.restype = ctypes.c_int
+    L.dssm_step.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, vp]
     L.dssm_s5_workspace_size.restype = ctypes.c_int
     L.dssm_s5_workspace_size.argtypes = [ctypes.POINTER(S5Shape), ctypes.POINTER(sz)]
     L.dssm_s5_forward.restype = ctypes.c_int
@@ -222,6 +228,55 @@ def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace
     """Layer forward by the recurrence (scan) view.  u [B,H,L] f32 -> y [B,H,L]."""
     return _forward(lib().dssm_forward_scan, OP_SCAN, u, log_re, log_im, W, D, bidirectional, y,
                     workspace, stream)
+
+
+def forward_scan_state(u, log_re, log_im, W, D, x, y=None, workspace=None, stream=None):
+    """Streaming forward, one direction: continues the recurrence from the
+    state x [B,H,N] c64 (updated in place to the state after the last step).
+    u [B,H,L] f32 -> y [B,H,L]."""
+    torch = _torch()
+    uu = _dev_f32(u, "u")
+    if uu.dim() != 3:
+        raise ValueError("u must be [B, H, L]")
+    B, H, L = uu.shape
+    N = log_re.shape[-1]
+    shape = Shape(B, H, N, L, 0)
+    p, keep = _params(log_re, log_im, W, D, 1, H, N)
+    xx = _dev_f32(x, "x")
+    if xx.numel() != 2 * B * H * N:
+        raise ValueError("x must be [B, H, N] complex")
+    if y is None:
+        y = torch.empty_like(uu)
+    yy = _dev_f32(y, "y")
+    ws, nbytes = _workspace(OP_SCAN, shape, workspace, uu.device)
+    check(lib().dssm_forward_scan_state(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape),
+                                        xx.data_ptr(), yy.data_ptr(), ws.data_ptr(), nbytes,
+                                        _stream(stream)))
+    del keep
+    return y
+
+
+def step(u_t, log_re, log_im, W, D, x, y=None, stream=None):
+    """One decode step: u_t [B,H] f32 -> y_t [B,H]; x [B,H,N] c64 updated in
+    place."""
+    torch = _torch()
+    uu = _dev_f32(u_t, "u_t")
+    if uu.dim() != 2:
+        raise ValueError("u_t must be [B, H]")
+    B, H = uu.shape
+    N = log_re.shape[-1]
+    shape = Shape(B, H, N, 1, 0)
+    p, keep = _params(log_re, log_im, W, D, 1, H, N)
+    xx = _dev_f32(x, "x")
+    if xx.numel() != 2 * B * H * N:
+        raise ValueError("x must be [B, H, N] complex")
+    if y is None:
+        y = torch.empty_like(uu)
+    yy = _dev_f32(y, "y")
+    check(lib().dssm_step(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape), xx.data_ptr(),
+                          yy.data_ptr(), _stream(stream)))
+    del keep
+    return y
 
 
 def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=None,

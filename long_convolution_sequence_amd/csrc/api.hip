@@ -253,6 +253,57 @@ int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape
   return forward_impl(DSSM_OP_SCAN, u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
 }
 
+int dssm_forward_scan_state(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                            float* x, float* y, void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_SCAN, s, &empty);
+  if (rc) return rc;
+  if (s->bidirectional)
+    return fail(DSSM_ERR_UNSUPPORTED, "the stateful forward runs one direction (bidirectional=0)");
+  if (empty) return ok();  // L = 0: the state passes through unchanged
+  if ((rc = check_params(p, true))) return rc;
+  if (!u || !y || !aligned16(u) || !aligned16(y))
+    return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
+  if (!x || !aligned16(x)) return fail(DSSM_ERR_INVALID_ARG, "x is NULL or not 16-byte aligned");
+  if (u == y || x == u || x == y) return fail(DSSM_ERR_INVALID_ARG, "u, x and y must not alias");
+  Layout l;
+  if ((rc = check_ws(DSSM_OP_SCAN, s, ws, ws_bytes, &l))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ScanPlan plan = scan_plan(s->B, s->L);
+  float* consts = at<float>(ws, l.consts);
+  if ((rc = hip_check(launch_scan_consts(p->log_re, p->log_im, p->W, s->H, s->N, plan, consts, st),
+                      "scan consts launch")))
+    return rc;
+  if ((rc = hip_check(launch_scan(u, consts, p->D, s->B, s->H, s->N, s->L, 1, plan, y, st,
+                                  reinterpret_cast<float2*>(x), KEvents{}, true),
+                      "scan launch")))
+    return rc;
+  return ok();
+}
+
+int dssm_step(const float* u_t, const dssm_dlr_params* p, const dssm_shape* s, float* x,
+              float* y_t, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_SCAN, s, &empty);
+  if (rc) return rc;
+  if (s->L != 1) return fail(DSSM_ERR_INVALID_ARG, "dssm_step takes one time step (L must be 1, got %d)", s->L);
+  if (s->bidirectional)
+    return fail(DSSM_ERR_UNSUPPORTED, "a decode step runs one direction (bidirectional=0)");
+  if (empty) return ok();
+  if ((rc = check_params(p, true))) return rc;
+  if (!u_t || !y_t || !x || !aligned16(u_t) || !aligned16(y_t) || !aligned16(x))
+    return fail(DSSM_ERR_INVALID_ARG, "u_t, x or y_t is NULL or not 16-byte aligned");
+  if (u_t == y_t || x == u_t || x == y_t)
+    return fail(DSSM_ERR_INVALID_ARG, "u_t, x and y_t must not alias");
+  if ((long)s->B * s->H > (long)kMaxGrid * 4)
+    return fail(DSSM_ERR_UNSUPPORTED, "B*H=%ld exceeds %ld", (long)s->B * s->H, (long)kMaxGrid * 4);
+  if ((rc = hip_check(launch_step(u_t, p->log_re, p->log_im, p->W, p->D, s->B, s->H, s->N, x, y_t,
+                                  static_cast<hipStream_t>(stream)),
+                      "step launch")))
+    return rc;
+  return ok();
+}
+
 int dssm_forward_fft_timed(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                            float* y, void* ws, size_t ws_bytes, void* stream,
                            void* const* events, int n_events) {

@@ -85,10 +85,16 @@ hipError_t launch_scan_consts(const float* log_re, const float* log_im, const fl
                              int ndh, int N, const ScanPlan& plan, float* consts, hipStream_t st,
                              KEvents ev = {});
 
-// carry: [B, H, N] float2 scratch, used when plan.ntile > 1.
+// carry: [B, H, N] float2 scratch, used when plan.ntile > 1.  state (one
+// direction): carry holds x_{-1} on entry and receives x_{L-1}.
 hipError_t launch_scan(const float* u, const float* consts, const float* D, int B, int H, int N,
                        int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
-                       float2* carry, KEvents ev = {});
+                       float2* carry, KEvents ev = {}, bool state = false);
+
+// One token for every (b, h): x [B,H,N] c64 updated in place, y_t [B,H] from
+// u_t [B,H].
+hipError_t launch_step(const float* u, const float* log_re, const float* log_im, const float* W,
+                       const float* D, int B, int H, int N, float* x, float* y, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // S5 multi-input multi-output diagonal SSM (s5.hip)

@@ -84,11 +84,16 @@ __device__ __forceinline__ float2 cfma(float2 m, float2 p, float2 acc) {  // acc
 // channel's last lane if write_carry).  Lanes of a channel are numbered along
 // the scan direction ("virtual" lanes) in blocks of up to 64 per wave: the
 // scan uses shuffles inside a block and LDS between the blocks of a channel.
+//
+// cap_s >= 0 marks the lane holding the sequence's last position, at index
+// cap_s of its segment: it writes the state after that step to the carry (the
+// final state of a stateful call; a short last tile runs on past L with zero
+// input, so its end state is not it).
 template <int SEG, bool REV>
 __device__ __forceinline__ void scan_pair(const float* uu, float* yy, const float* __restrict__ ca,
                                           const float* __restrict__ cb, bool has_b, int cl,
                                           int lpc, float4* xs, float2* carry_a, float2* carry_b,
-                                          bool use_carry, bool write_carry) {
+                                          bool use_carry, bool write_carry, int cap_s = -1) {
   const float2 la = make_float2(ca[0], ca[1]);
   const float2 lb = make_float2(cb[0], cb[1]);
   const float2 wa = make_float2(ca[2], ca[3]);
@@ -176,9 +181,7 @@ __device__ __forceinline__ void scan_pair(const float* uu, float* yy, const floa
   // 3. outputs from the true carry-in
   xa = ina;
   xb = inb;
-#pragma unroll
-  for (int i = 0; i < SEG; ++i) {
-    const int s = REV ? SEG - 1 - i : i;
+  auto out_step = [&](int s) {
     const float uv = uu[s];
     xa = rec_step(la, xa, uv);
     xb = rec_step(lb, xb, uv);
@@ -188,6 +191,25 @@ __device__ __forceinline__ void scan_pair(const float* uu, float* yy, const floa
     acc = fmaf(wb.x, xb.x, acc);
     acc = fmaf(-wb.y, xb.y, acc);
     yy[s] = acc;
+  };
+  if (__any(cap_s >= 0)) {  // wave-uniform: only the wave holding the last position pays
+    float2 fa = xa, fb = xb;
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      const int s = REV ? SEG - 1 - i : i;
+      out_step(s);
+      if (s == cap_s) {
+        fa = xa;
+        fb = xb;
+      }
+    }
+    if (cap_s >= 0) {
+      *carry_a = fa;
+      if (has_b) *carry_b = fb;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) out_step(REV ? SEG - 1 - i : i);
   }
 }
 
@@ -196,24 +218,26 @@ template <int SEG, bool REV>
 __device__ __forceinline__ void scan_modes(const float* uu, float* yy,
                                            const float* __restrict__ cst0, int N, int cl, int lpc,
                                            float4* xs, float2* cc, bool use_carry,
-                                           bool write_carry, bool sync_each) {
+                                           bool write_carry, bool sync_each, int cap_s = -1) {
   for (int n = 0; n < N; n += 2) {
     const bool has_b = n + 1 < N;
     if (sync_each) __syncthreads();  // orders the carry write and reads between tiles
     scan_pair<SEG, REV>(uu, yy, cst0 + (size_t)n * kNConst,
                         cst0 + (size_t)(has_b ? n + 1 : n) * kNConst, has_b, cl, lpc, xs,
-                        cc + n, cc + (has_b ? n + 1 : n), use_carry, write_carry);
+                        cc + n, cc + (has_b ? n + 1 : n), use_carry, write_carry, cap_s);
   }
 }
 
 // Grid: (channel groups of one h) x H.  Workgroup = 256 lanes = cpg channels
 // (batch rows b0 .. b0+cpg-1 of channel h) x lpc lanes.  MULTI: the sequence
-// spans several tiles and carries cross them through `carry`.
+// spans several tiles and carries cross them through `carry`.  state (MULTI,
+// one direction): `carry` holds the state x_{-1} on entry (read by the first
+// tile) and receives x_{L-1} on exit, captured at the last position.
 template <int SEG, bool MULTI>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const float* __restrict__ u, const float* __restrict__ consts, const float* __restrict__ D,
     float2* __restrict__ carry, int B, int H, int N, int L, int ndir, int lpc, int ntile,
-    float* __restrict__ y) {
+    float* __restrict__ y, int state) {
   __shared__ float4 xs[8];  // block totals (two modes): 2 channels x 4 blocks at most
   const int cpg = kScanThreads / lpc;
   const int h = blockIdx.y;
@@ -265,8 +289,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
         if (d == 0) yy[i] = deff * uu[i];
         else yy[i] = (active && p < L) ? yc[p] : 0.f;
       }
+      const bool last = k == ntile - 1;
+      const int cap_s = (state && last && active && p0 <= L - 1 && L - 1 < p0 + SEG) ? L - 1 - p0
+                                                                                   : -1;
       if (d == 0)
-        scan_modes<SEG, false>(uu, yy, cst0, N, cl, lpc, xs, cc, k > 0, active, true);
+        scan_modes<SEG, false>(uu, yy, cst0, N, cl, lpc, xs, cc, k > 0 || state,
+                               active && !(state && last), true, cap_s);
       else
         scan_modes<SEG, true>(uu, yy, cst0, N, cl, lpc, xs, cc, k > 0, active, true);
 #pragma unroll
@@ -282,15 +310,52 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 template <int SEG>
 void scan_launch(const float* u, const float* consts, const float* D, float2* carry, int B, int H,
                  int N, int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
-                 KEvents ev) {
+                 KEvents ev, bool state) {
   const int cpg = kScanThreads / plan.lpc;
   const dim3 grid((unsigned)((B + cpg - 1) / cpg), (unsigned)H);
-  if (plan.ntile == 1)
+  if (plan.ntile == 1 && !state)
     launch_k(scan_kernel<SEG, false>, grid, dim3(kScanThreads), st, ev, u, consts, D, carry, B, H, N,
-             L, ndir, plan.lpc, plan.ntile, y);
+             L, ndir, plan.lpc, plan.ntile, y, 0);
   else
     launch_k(scan_kernel<SEG, true>, grid, dim3(kScanThreads), st, ev, u, consts, D, carry, B, H, N,
-             L, ndir, plan.lpc, plan.ntile, y);
+             L, ndir, plan.lpc, plan.ntile, y, state ? 1 : 0);
+}
+
+// One time step for every (b, h), one wave each (modes across the lanes):
+//   x <- lambda x + u_t,  y_t = Re(sum_n W_n x_n) + D u_t,
+// the recurrent view advanced by one token ("The Annotated S4", Part 1,
+// "Discrete-time SSM: the recurrent representation").  lambda is formed in
+// float64 from the exactly promoted parameters and rounded once, as the scan's
+// per-step multiplier is.
+__global__ __launch_bounds__(256) void step_kernel(const float* __restrict__ u,
+                                                   const float* __restrict__ log_re,
+                                                   const float* __restrict__ log_im,
+                                                   const float2* __restrict__ W,
+                                                   const float* __restrict__ D, int B, int H,
+                                                   int N, float2* __restrict__ x,
+                                                   float* __restrict__ y) {
+  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;  // b H + h
+  const int lane = threadIdx.x & 63;
+  if (row >= (long)B * H) return;  // whole waves
+  const int h = (int)(row % H);
+  const float uv = u[row];
+  float2* xr = x + (size_t)row * N;
+  float acc = 0.f;
+  for (int n = lane; n < N; n += 64) {
+    const size_t i = (size_t)h * N + n;
+    const double re = (double)log_re[i];
+    double sn, cs;
+    sincos((double)log_im[i], &sn, &cs);
+    const double m = exp(-re * re);
+    const float2 lam = make_float2((float)(m * cs), (float)(m * sn));
+    const float2 xv = rec_step(lam, xr[n], uv);
+    xr[n] = xv;
+    const float2 w = W[i];
+    acc = fmaf(w.x, xv.x, fmaf(-w.y, xv.y, acc));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) y[row] = fmaf(D[h], uv, acc);
 }
 
 }  // namespace
@@ -324,15 +389,25 @@ hipError_t launch_scan_consts(const float* log_re, const float* log_im, const fl
 
 hipError_t launch_scan(const float* u, const float* consts, const float* D, int B, int H, int N,
                        int L, int ndir, const ScanPlan& plan, float* y, hipStream_t st,
-                       float2* carry, KEvents ev) {
+                       float2* carry, KEvents ev, bool state) {
   switch (plan.seg) {
-    case 4: scan_launch<4>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
-    case 8: scan_launch<8>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
-    case 16: scan_launch<16>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
-    case 32: scan_launch<32>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
-    case 64: scan_launch<64>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev); break;
+    case 4: scan_launch<4>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev, state); break;
+    case 8: scan_launch<8>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev, state); break;
+    case 16: scan_launch<16>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev, state); break;
+    case 32: scan_launch<32>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev, state); break;
+    case 64: scan_launch<64>(u, consts, D, carry, B, H, N, L, ndir, plan, y, st, ev, state); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_step(const float* u, const float* log_re, const float* log_im, const float* W,
+                       const float* D, int B, int H, int N, float* x, float* y, hipStream_t st) {
+  const long waves = (long)B * H;
+  const long blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL(step_kernel, dim3((unsigned)blocks), dim3(256), 0, st, u, log_re, log_im,
+                     reinterpret_cast<const float2*>(W), D, B, H, N, reinterpret_cast<float2*>(x),
+                     y);
   return hipGetLastError();
 }
 

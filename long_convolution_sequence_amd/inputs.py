@@ -121,3 +121,14 @@ def inputs_for(cfg):
                           cfg.get("bidirectional", False), cfg.get("seed", 0),
                           cfg.get("re_scale", 1.0))
     return s5_inputs(cfg["B"], cfg["H"], cfg["P"], cfg["L"], cfg.get("seed", 4))
+
+
+def dlr_state(B, H, N, seed=0, scale=3.0):
+    """Seeded initial state for the stateful (streaming) forward: x [B,H,N]
+    complex64, real then imaginary parts ~ N(0, scale^2 / 2) (|x|^2 has mean
+    scale^2, the order of the states a N(0,1) input drives)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    sd = scale / np.sqrt(2.0)
+    re = rng.normal(0.0, sd, size=(B, H, N))
+    im = rng.normal(0.0, sd, size=(B, H, N))
+    return (re + 1j * im).astype(np.complex64)

@@ -199,3 +199,48 @@ def test_s5_timed_validates_events():
     assert fn(*(args + [evs, 5])) == bd.DSSM_ERR_INVALID_ARG
     bad = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))
     assert fn(*(args + [bad, 8])) == bd.DSSM_ERR_INVALID_ARG
+
+
+def test_stateful_forward_rejects_bad_arguments():
+    fn = bd.lib().dssm_forward_scan_state
+    good = bd.Shape(2, 3, 4, 32, 0)
+    p = _params()
+
+    def call(prm, s, u=FAKE * 2, x=FAKE * 5, y=FAKE * 3, ws=FAKE * 4, n=1 << 40):
+        return fn(u, ctypes.byref(prm) if prm is not None else None,
+                  ctypes.byref(s) if s is not None else None, x, y, ws, n, None)
+
+    assert call(p, None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(None, good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, good, x=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, good, x=FAKE * 5 + 8) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, good, x=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG  # aliases u
+    assert call(p, good, x=FAKE * 3) == bd.DSSM_ERR_INVALID_ARG  # aliases y
+    assert call(p, good, n=16) == bd.DSSM_ERR_WORKSPACE
+    assert call(p, bd.Shape(2, 3, 4, 32, 1)) == bd.DSSM_ERR_UNSUPPORTED  # needs the future
+    assert b"direction" in bd.lib().dssm_last_error()
+    assert call(p, bd.Shape(2, 3, 4, 32, 2)) == bd.DSSM_ERR_INVALID_ARG
+    # L = 0: the state passes through unchanged, nothing is launched
+    assert call(None, bd.Shape(2, 3, 4, 0, 0), x=None) == 0
+
+
+def test_step_rejects_bad_arguments():
+    fn = bd.lib().dssm_step
+    good = bd.Shape(2, 3, 4, 1, 0)
+    p = _params()
+
+    def call(prm, s, u=FAKE * 2, x=FAKE * 5, y=FAKE * 3):
+        return fn(u, ctypes.byref(prm) if prm is not None else None,
+                  ctypes.byref(s) if s is not None else None, x, y, None)
+
+    assert call(p, None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, bd.Shape(2, 3, 4, 2, 0)) == bd.DSSM_ERR_INVALID_ARG  # one step only
+    assert b"L must be 1" in bd.lib().dssm_last_error()
+    assert call(p, bd.Shape(2, 3, 4, 1, 1)) == bd.DSSM_ERR_UNSUPPORTED
+    assert call(p, good, x=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, good, u=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, good, y=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG
+    assert call(p, good, x=FAKE * 3) == bd.DSSM_ERR_INVALID_ARG
+    assert call(_params({"D": None}), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(_params({"W": FAKE + 4}), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(None, bd.Shape(0, 3, 4, 1, 0)) == 0

@@ -1,0 +1,185 @@
+"""GPU parity of the streaming (stateful) forward and the one-token decode
+step against the float64 oracle, through the C ABI.
+
+What is checked: the recurrence continued from a given state ("The Annotated
+S4", Part 1, "Discrete-time SSM: the recurrent representation"; Part 3,
+"Sampling and caching") -- dssm_forward_scan_state against
+oracle.dlr_recurrence_state (outputs and the returned state), a sequence fed
+in chunks with the state carried between calls, the zero state against the
+plain scan, and a run of dssm_step decode steps.  Same bar as the other GPU
+parity tests: relative L2 <= 1e-5 and max |error| <= 1e-4 RMS(reference),
+for y and for the final state.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from long_convolution_sequence_amd import binding as bd
+from long_convolution_sequence_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-5
+MAX_VS_RMS = 1e-4
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def assert_close(got, ref, what):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    d = (got.astype(np.complex128) - ref.astype(np.complex128)).ravel()
+    r = ref.astype(np.complex128).ravel()
+    rel = np.linalg.norm(d) / max(np.linalg.norm(r), 1e-300)
+    rms = np.sqrt(np.mean(np.abs(r) ** 2))
+    mx = np.max(np.abs(d)) / max(rms, 1e-300) if d.size else 0.0
+    say("  %s: rel_l2=%.3e max/rms=%.3e" % (what, rel, mx))
+    assert rel <= REL_L2, "%s rel L2 %.3e" % (what, rel)
+    assert mx <= MAX_VS_RMS, "%s max/rms %.3e" % (what, mx)
+
+
+def dev(a):
+    torch = _torch()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def params(x):
+    return dev(x["log_re"]), dev(x["log_im"]), dev(x["W"]), dev(x["D"])
+
+
+def run_state(x, x0, u=None):
+    torch = _torch()
+    u = x["u"] if u is None else u
+    st = dev(x0.copy())
+    y = bd.forward_scan_state(dev(u), *params(x), st)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), st.cpu().numpy()
+
+
+SHAPES = [
+    # (B, H, N, L): single tile, ragged tails, several tiles
+    (2, 3, 5, 37), (1, 2, 8, 1), (3, 2, 8, 2), (2, 2, 16, 255), (3, 2, 8, 257),
+    (2, 3, 64, 1000), (1, 2, 7, 4097), (1, 2, 64, 16384), (2, 2, 7, 40000),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=["B%dH%dN%dL%d" % s for s in SHAPES])
+def test_state_forward_matches_oracle(shape):
+    B, H, N, L = shape
+    say("case: stateful forward B=%d H=%d N=%d L=%d" % shape)
+    x = inputs.dlr_inputs(B, H, N, L, seed=500 + L + N, re_scale=0.3)
+    x0 = inputs.dlr_state(B, H, N, seed=600 + L)
+    y, xl = run_state(x, x0)
+    yr, xr = oracle.dlr_recurrence_state(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], x0)
+    assert_close(y, yr, "y")
+    assert_close(xl, xr, "final state")
+
+
+def test_state_long_sequence_workload():
+    """The long-sequence workload (B=4 H=128 N=64 L=16384) from a random state."""
+    c = inputs.config("long_sequence")
+    say("case: stateful forward, long_sequence workload")
+    x = inputs.inputs_for(c)
+    x0 = inputs.dlr_state(c["B"], c["H"], c["N"], seed=31)
+    y, xl = run_state(x, x0)
+    yr, xr = oracle.dlr_recurrence_state(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], x0)
+    assert_close(y, yr, "y")
+    assert_close(xl, xr, "final state")
+
+
+def test_chunked_stream_equals_whole():
+    """A sequence fed in chunks, the state carried between calls, equals the
+    oracle on the whole sequence (the state holds everything the past
+    contributes)."""
+    torch = _torch()
+    B, H, N, L = 2, 3, 16, 20000
+    say("case: chunked stream B=%d H=%d N=%d L=%d" % (B, H, N, L))
+    x = inputs.dlr_inputs(B, H, N, L, seed=41, re_scale=0.2)
+    x0 = inputs.dlr_state(B, H, N, seed=42)
+    st = dev(x0.copy())
+    p = params(x)
+    ys = []
+    for a, b in ((0, 1), (1, 100), (100, 3333), (3333, 3333), (3333, 17000), (17000, L)):
+        ys.append(bd.forward_scan_state(dev(x["u"][:, :, a:b]), *p, st))
+    torch.cuda.synchronize()
+    y = np.concatenate([t.cpu().numpy() for t in ys], axis=-1)
+    yr, xr = oracle.dlr_recurrence_state(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], x0)
+    assert_close(y, yr, "y (chunked)")
+    assert_close(st.cpu().numpy(), xr, "final state (chunked)")
+
+
+def test_zero_state_equals_plain_scan():
+    torch = _torch()
+    B, H, N, L = 3, 4, 16, 3000
+    say("case: zero state vs plain scan")
+    x = inputs.dlr_inputs(B, H, N, L, seed=43)
+    y0, _ = run_state(x, np.zeros((B, H, N), np.complex64))
+    p = params(x)
+    y1 = bd.forward_scan(dev(x["u"]), *p).cpu().numpy()
+    torch.cuda.synchronize()
+    ref = oracle.dlr_recurrence(x["u"], x["log_re"], x["log_im"], x["W"], x["D"])
+    assert_close(y0, ref, "zero state vs oracle")
+    assert_close(y0, y1, "zero state vs plain scan")
+
+
+def test_empty_sequence_keeps_state():
+    torch = _torch()
+    B, H, N = 2, 3, 8
+    say("case: L = 0 keeps the state")
+    x = inputs.dlr_inputs(B, H, N, 4, seed=44)
+    x0 = inputs.dlr_state(B, H, N, seed=45)
+    st = dev(x0.copy())
+    bd.forward_scan_state(dev(x["u"][:, :, :0].copy()), *params(x), st)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.cpu().numpy(), x0)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 16), (3, 5, 100), (1, 2, 1)])
+def test_decode_steps_match_oracle(shape):
+    """T one-token steps reproduce the oracle's recurrence over those T inputs."""
+    torch = _torch()
+    B, H, N = shape
+    T = 40
+    say("case: decode B=%d H=%d N=%d T=%d" % (B, H, N, T))
+    x = inputs.dlr_inputs(B, H, N, T, seed=46 + N)
+    x0 = inputs.dlr_state(B, H, N, seed=47)
+    st = dev(x0.copy())
+    p = params(x)
+    u = dev(x["u"])
+    ys = [bd.step(u[:, :, t].contiguous(), *p, st) for t in range(T)]
+    torch.cuda.synchronize()
+    y = np.stack([t.cpu().numpy() for t in ys], axis=-1)
+    yr, xr = oracle.dlr_recurrence_state(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], x0)
+    assert_close(y, yr, "decode y")
+    assert_close(st.cpu().numpy(), xr, "decode state")
+
+
+def test_decode_after_prefill():
+    """Prefill a prompt with the stateful forward, then decode token by token:
+    together they equal the oracle on the whole sequence."""
+    torch = _torch()
+    B, H, N, P, T = 2, 4, 32, 5000, 20
+    say("case: prefill %d then decode %d" % (P, T))
+    x = inputs.dlr_inputs(B, H, N, P + T, seed=48, re_scale=0.3)
+    st = dev(np.zeros((B, H, N), np.complex64))
+    p = params(x)
+    y1 = bd.forward_scan_state(dev(x["u"][:, :, :P]), *p, st)
+    u = dev(x["u"])
+    ys = [bd.step(u[:, :, P + t].contiguous(), *p, st) for t in range(T)]
+    torch.cuda.synchronize()
+    y = np.concatenate([y1.cpu().numpy()] + [t.cpu().numpy()[..., None] for t in ys], axis=-1)
+    yr, xr = oracle.dlr_recurrence_state(x["u"], x["log_re"], x["log_im"], x["W"], x["D"])
+    assert_close(y, yr, "prefill+decode y")
+    assert_close(st.cpu().numpy(), xr, "prefill+decode state")
