@@ -216,7 +216,9 @@ int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5
  * costs more host time).  n_events = 4 for both:
  *   fft:  [0,1] parameters -> kernel spectrum (generator and spectrum
  *         kernels), [2,3] convolution.
- *   scan: [0,1] per-mode constants, [2,3] scan.
+ *   scan: [0,1] per-mode constants of the segmented scan (with the chunked
+ *         matrix-core form, used for N <= 64, there is no such kernel and the
+ *         pair is recorded back to back: a duration of ~0), [2,3] scan.
  * The events are owned by the caller and must have timing enabled; a NULL
  * array, a pair with one NULL handle, or a wrong n_events returns
  * DSSM_ERR_INVALID_ARG before anything is enqueued. */

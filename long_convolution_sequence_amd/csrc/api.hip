@@ -78,6 +78,13 @@ int check_params(const dssm_dlr_params* p, bool need_d) {
   return DSSM_OK;
 }
 
+// The recurrence view runs in the chunked state-space form on the matrix
+// cores for up to 64 modes (one workgroup per (b, h)); otherwise in the
+// segmented scan.
+bool use_chunk(const dssm_shape* s) {
+  return chunk_supported(s->N) && (long)s->B * s->H <= (1L << 24);
+}
+
 // Workspace layout, every region aligned to 256 bytes.
 struct Layout {
   size_t reK = 0, spec = 0, consts = 0, carry = 0, total = 0;
@@ -227,6 +234,16 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
       return rc;
     if ((rc = hip_check(launch_conv(u, spec, s->B, s->H, s->L, log2m, y, st, kev(events, 1)),
                         "conv launch")))
+      return rc;
+  } else if (use_chunk(s)) {
+    // chunked state-space form on the matrix cores (operands formed in the
+    // kernel): stage 0 has no kernel, its pair is recorded back to back
+    const KEvents e0 = kev(events, 0);
+    if (e0.start && (rc = hip_check(hipEventRecord(e0.start, st), "event record"))) return rc;
+    if (e0.stop && (rc = hip_check(hipEventRecord(e0.stop, st), "event record"))) return rc;
+    if ((rc = hip_check(launch_chunk(u, p->log_re, p->log_im, p->W, p->D, s->B, s->H, s->N, s->L,
+                                     ndir, y, st, kev(events, 1)),
+                        "chunk launch")))
       return rc;
   } else {
     const ScanPlan plan = scan_plan(s->B, s->L);

@@ -1,0 +1,515 @@
+// Chunked state-space form of the DLR bank on the matrix cores.
+//
+// What is computed: the same map as the recurrence ("The Annotated S4",
+// Part 1, "Discrete-time SSM: the recurrent representation", with the DLR of
+// "Simplifying and Understanding State Space Models with Diagonal Linear
+// RNNs", section 2):
+//   x_k = lambda x_{k-1} + u_k (x_{-1} = 0),  y_k = Re(sum_n W_n x_{k,n}) + D u_k,
+// organised by chunks of T = 64 steps.  With S_c the state entering chunk c
+// and t = cT + i:
+//   s_c     = sum_{j<T} lambda^(T-1-j) u_{cT+j}                (chunk's own state)
+//   S_{c+1} = lambda^T S_c + s_c                                (chunk recurrence)
+//   y_t     = sum_{j<=i} K_{i-j} u_{cT+j} + D u_t + Re sum_n W_n lambda_n^(i+1) S_{c,n}
+// with K_j = Re sum_n W_n lambda_n^j the DLR kernel (section 2: the convolution
+// and recurrence views of the same map; within a chunk the convolution is a
+// T x T Toeplitz product, across chunks the recurrence carries the state).
+// The bidirectional form adds the same computation on the time-reversed input
+// with the second parameter set, reversed back (section 2, bidirectional
+// paragraph).
+//
+// How (MI355X design):
+// * s = A1 U and y = A3 [U; S] are dense contractions per channel
+//   (A1: 2N x T = 128 x 64, A3: T x (T + 2N) = 64 x 192, U: T x chunks) done on
+//   the matrix cores with v_mfma_f32_16x16x32_f16.  Every float32 operand is
+//   split as hi = fp16(v), lo = fp16(v - hi) and a product is
+//   hi.hi + hi.lo + lo.hi accumulated in float32 (each fp16 x fp16 product is
+//   exact in float32): ~22 significant bits per operand.
+// * One workgroup (4 waves) runs one (channel, batch row).  Its prologue forms
+//   the operands from the exactly promoted parameters (lambda, its powers and
+//   the taps in float64, rounded once) and splits them into the MFMA fragments
+//   each wave keeps in registers, while the first block's input is in flight.  Then blocks of 64 chunks: u to LDS (split), GEMM1 ->
+//   chunk states, the chunk recurrence (a wave per quarter of the block, a lane
+//   per mode; quarters combined with lambda^(16T)), GEMM3 -> y.  The next
+//   block's input is requested before the current block is computed.
+#include "dssm_internal.h"
+
+namespace dssm {
+namespace {
+
+constexpr int kT = 64;            // steps per chunk
+constexpr int kCB = 64;           // chunks per block
+constexpr int kModes = 64;        // modes handled (N <= 64; padded with zero modes)
+constexpr int kR = 2 * kModes;    // state rows (re, im interleaved)
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double2 zmul(double2 a, double2 b) {
+  return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
+// float32 value v split into fp16 (hi, lo) with hi + lo = v to ~22 bits.
+__device__ __forceinline__ void split16(float v, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)v;
+  lo = (_Float16)(v - (float)hi);
+}
+
+// Workgroup i runs on XCD i % 8; when the grid divides by 8, consecutive
+// logical workgroups (the batch rows of one channel) share an XCD.
+__device__ __forceinline__ int xcd_grouped(int i, int n) {
+  return (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
+}
+
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// The value of x, hidden from the optimiser: values derived from it are formed
+// where they are used, not hoisted out of the direction loop and kept live.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ float2 cfma(float2 m, float2 p, float2 acc) {  // acc + m p
+  return make_float2(fmaf(m.x, p.x, fmaf(-m.y, p.y, acc.x)), fmaf(m.x, p.y, fmaf(m.y, p.x, acc.y)));
+}
+
+// LDS row strides chosen so the 16-byte fragment reads of 16 consecutive
+// columns fall in different banks.  The chunk states S1[c] (float32) and the
+// carried states S[c] (fp16 hi at byte 0, lo at byte 272 of the same 528-byte
+// row) share row c: one wave reads all its rows' S1 values into registers
+// before it writes their S, and no other wave touches those rows in between.
+constexpr int kUS = kT + 8;          // U[c][j] fp16
+constexpr int kS1S = kR + 4;         // S1[c][r] fp32 (528-byte rows)
+constexpr int kSRow = kS1S * 4;      // bytes per chunk row
+constexpr int kSLo = 272;            // byte offset of the lo half within a row
+
+// LDS: the operand tables of the prologue and the block arrays of the main
+// loop are alive at different times and share one buffer.  Row strides and
+// plane offsets are padded so each table's accesses below are free of bank
+// conflicts.
+constexpr int kQS = kModes + 2;            // Q row stride (float2)
+constexpr int kKS = kT + 1;                // KR row stride (double)
+constexpr int kPS = kT + 4;                // power-plane row stride (float)
+constexpr int kPlane = kModes * kPS + 32;  // Im plane starts 32 banks after Re
+struct TablesLds {
+  float2 Q[kT][kQS];  // Q[i][n] = (Re, -Im) of W_n lambda_n^(i+1)
+  union {
+    double KR[kModes][kKS];  // Re(W_n lambda_n^p), p < T (the taps' terms)
+    float PP[2 * kPlane];    // planes Re, Im of lambda_n^p: [plane * kPlane + n * kPS + p]
+  };
+  double2 lam[kModes], wv[kModes];
+  float ktp[2 * kT];  // ktp[T + m] = K_m (+ D_f + D_b at m = 0 of d = 0); 0 for m < 0
+  float4 mult[kModes];  // lambda^T, lambda^(16T)
+};
+struct BlockLds {
+  _Float16 Uh[kCB * kUS], Ul[kCB * kUS];
+  float S1[kCB * kS1S];
+  float2 E[4][kModes];
+};
+constexpr int kLdsBytes = sizeof(TablesLds) > sizeof(BlockLds) ? sizeof(TablesLds) : sizeof(BlockLds);
+
+// 8 consecutive floats of LDS starting at a 16-byte aligned address.
+__device__ __forceinline__ void lds_read8(const float* p, f4& a, f4& b) {
+  a = *reinterpret_cast<const f4*>(p);
+  b = *reinterpret_cast<const f4*>(p + 4);
+}
+
+__device__ __forceinline__ void split8(const float* v, half8& hi, half8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    _Float16 a, b;
+    split16(v[e], a, b);
+    hi[e] = a;
+    lo[e] = b;
+  }
+}
+
+// Operand fragments of wave w for direction d of channel h:
+//   a1[(rt * 2 + ks) * 2 + hl]: A1 rows r = 32 w + 16 rt + lane % 16, columns
+//     j = 32 ks + 8 (lane / 16) + e: A1[2n][j] = Re lambda_n^(T-1-j),
+//     A1[2n+1][j] = Im lambda_n^(T-1-j)
+//   a3[ks * 2 + hl]: A3 row i = 16 w + lane % 16, columns k = 32 ks + 8 (lane / 16) + e:
+//     k < T: Toeplitz K_{i-k} (k <= i), with D_f + D_b on the diagonal (d = 0);
+//     k = T + 2n: Re(W_n lambda_n^(i+1)), k = T + 2n + 1: -Im(W_n lambda_n^(i+1))
+// and the chunk multipliers lambda^T, lambda^(16T) of mode `lane`.  lambda, its
+// powers (chains of 16 products from lambda^(16 q), q < 4), W lambda^p and the
+// taps K_m = Re sum_n W_n lambda_n^m are float64, each rounded once to float32.
+// Modes n >= N are zero.  Ends with a barrier (the LDS is reused after it).
+__device__ __forceinline__ void build_operands(
+    const float* __restrict__ log_re, const float* __restrict__ log_im,
+    const float2* __restrict__ W, const float* __restrict__ D, int ndir, int H, int N, int d,
+    int h, TablesLds& tl, half8* a1, half8* a3, float2& lamT, float2& lam16T) {
+  const int t = opaque(threadIdx.x), lane = t & 63, w = t >> 6;
+  if (w == 0) {  // lambda_n, W_n (float64, from the exactly promoted parameters)
+    const int n = lane;
+    double2 lam = make_double2(0.0, 0.0), wv = lam;
+    if (n < N) {
+      const size_t i = ((size_t)d * H + h) * N + n;
+      const double re = (double)log_re[i];
+      double sn, cs;
+      sincos((double)log_im[i], &sn, &cs);
+      const double m = exp(-re * re);
+      lam = make_double2(m * cs, m * sn);
+      wv = make_double2((double)W[i].x, (double)W[i].y);
+    }
+    tl.lam[n] = lam;
+    tl.wv[n] = wv;
+  }
+  __syncthreads();
+  float2 pw[16];  // lambda^p of this thread's 16 powers, kept for the planes
+  {  // mode n = lane, powers p = 16 w .. 16 w + 15
+    const int n = lane;
+    const double2 lam = tl.lam[n], wv = tl.wv[n];
+    double2 x = make_double2(n < N ? 1.0 : 0.0, 0.0), b = lam;  // lambda^(16 w)
+    for (int e = 16 * w; e; e >>= 1) {
+      if (e & 1) x = zmul(x, b);
+      b = zmul(b, b);
+    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int p = 16 * w + s;
+      pw[s] = make_float2((float)x.x, (float)x.y);
+      tl.KR[n][p] = wv.x * x.x - wv.y * x.y;
+      x = zmul(x, lam);
+      const double2 q = zmul(wv, x);
+      tl.Q[p][n] = make_float2((float)q.x, (float)-q.y);
+    }
+    if (w == 3) {  // x = lambda^T
+      double2 b16 = zmul(x, x);
+      b16 = zmul(b16, b16);
+      b16 = zmul(b16, b16);
+      b16 = zmul(b16, b16);
+      tl.mult[n] = make_float4((float)x.x, (float)x.y, (float)b16.x, (float)b16.y);
+    }
+  }
+  __syncthreads();
+  {  // taps: wave w sums taps 16 w .. +15, a quarter of the modes per 16 lanes
+    const int m = 16 * w + (lane & 15), q = lane >> 4;
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += tl.KR[16 * q + k][m];
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (m == 0 && d == 0)
+      for (int dd = 0; dd < ndir; ++dd) s += (double)D[(size_t)dd * H + h];
+    if (q == 0) tl.ktp[kT + m] = (float)s;
+    if (q == 1) tl.ktp[m] = 0.f;
+  }
+  __syncthreads();  // KR read: its space takes the power planes
+  {
+    float* pr = tl.PP + lane * kPS + 16 * w;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      *reinterpret_cast<f4*>(pr + 4 * s4) =
+          f4{pw[4 * s4].x, pw[4 * s4 + 1].x, pw[4 * s4 + 2].x, pw[4 * s4 + 3].x};
+      *reinterpret_cast<f4*>(pr + kPlane + 4 * s4) =
+          f4{pw[4 * s4].y, pw[4 * s4 + 1].y, pw[4 * s4 + 2].y, pw[4 * s4 + 3].y};
+    }
+  }
+  __syncthreads();
+  const int g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int r = 32 * w + 16 * rt + (lane & 15);
+    const float* row = tl.PP + (r & 1) * kPlane + (r >> 1) * kPS;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      // columns j = 32 ks + 8 g + e hold powers T - 1 - j = p0 + 7 - e
+      f4 lo4, hi4;
+      lds_read8(row + (kT - 8 - 32 * ks - 8 * g), lo4, hi4);
+      const float v[8] = {hi4[3], hi4[2], hi4[1], hi4[0], lo4[3], lo4[2], lo4[1], lo4[0]};
+      split8(v, a1[(rt * 2 + ks) * 2], a1[(rt * 2 + ks) * 2 + 1]);
+      __builtin_amdgcn_sched_barrier(0);  // one fragment's temporaries live at a time
+    }
+  }
+  const int i = 16 * w + (lane & 15);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {  // Toeplitz: K_{i-k} at ktp[T + i - k]
+    const float* kt = tl.ktp + kT + i - 32 * ks - 8 * g;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = kt[-e];
+    split8(v, a3[ks * 2], a3[ks * 2 + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ks = 2; ks < 6; ++ks) {  // modes 16 (ks - 2) + 4 g .. + 3 at power i + 1
+    f4 lo4, hi4;
+    lds_read8(reinterpret_cast<const float*>(&tl.Q[i][16 * (ks - 2) + 4 * g]), lo4, hi4);
+    const float v[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    split8(v, a3[ks * 2], a3[ks * 2 + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float4 m = tl.mult[lane];
+  lamT = make_float2(m.x, m.y);
+  lam16T = make_float2(m.z, m.w);
+  __syncthreads();
+}
+
+// One (channel h, batch row b) per workgroup.  The second direction (if any)
+// runs in reversed time t' = Lp - 1 - t (Lp = chunks x T) and adds to y.
+template <bool VEC>
+__global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__ u,
+                                                    const float* __restrict__ log_re,
+                                                    const float* __restrict__ log_im,
+                                                    const float2* __restrict__ W,
+                                                    const float* __restrict__ D, int B, int H,
+                                                    int N, int L, int ndir,
+                                                    float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
+  TablesLds& tl = *reinterpret_cast<TablesLds*>(lds_raw);
+  BlockLds& bl = *reinterpret_cast<BlockLds*>(lds_raw);
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int wg = xcd_grouped(blockIdx.x, gridDim.x);
+  const int h = wg / B, b = wg % B;
+  const int nchunk = (L + kT - 1) / kT;
+  const int nblk = (nchunk + kCB - 1) / kCB;
+  const int Lp = nchunk * kT;  // padded length (reversed-time origin)
+  const float* ur = u + ((size_t)b * H + h) * L;
+  float* yr = y + ((size_t)b * H + h) * L;
+  const BufRes ubuf = buf_res(ur, 4u * (unsigned)L);
+  const BufRes ybuf = buf_res(yr, 4u * (unsigned)L);
+
+  for (int d = 0; d < ndir; ++d) {
+    const bool rev = d == 1;
+    // element e of block blk in processing time -> sequence position (out of
+    // range, hence zero on load and dropped on store, beyond the sequence)
+    auto pos = [&](int blk, int e) {
+      const int q = blk * kCB * kT + e;
+      return rev ? Lp - 1 - q : q;
+    };
+    // input of block blk: thread t takes elements 4 t + 1024 q + c4 (c4 < 4, q < 4)
+    auto load_block = [&](int blk, float* v) {
+      if (VEC && !rev) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 x =
+              __builtin_amdgcn_raw_buffer_load_b128(ubuf, 4 * pos(blk, 4 * t + 1024 * q), 0, 0);
+          v[4 * q + 0] = __uint_as_float(x.x);
+          v[4 * q + 1] = __uint_as_float(x.y);
+          v[4 * q + 2] = __uint_as_float(x.z);
+          v[4 * q + 3] = __uint_as_float(x.w);
+        }
+      } else if (VEC) {  // reversed: the four elements sit at descending positions
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+              ubuf, 4 * pos(blk, 4 * t + 1024 * q + 3), 0, 0);
+          v[4 * q + 0] = __uint_as_float(x.w);
+          v[4 * q + 1] = __uint_as_float(x.z);
+          v[4 * q + 2] = __uint_as_float(x.y);
+          v[4 * q + 3] = __uint_as_float(x.x);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int e = 4 * t + 1024 * (q >> 2) + (q & 3);
+          v[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ubuf, 4 * pos(blk, e), 0, 0));
+        }
+      }
+    };
+    float un[16];
+    load_block(0, un);  // in flight while the operands are formed
+    half8 a1[8], a3[12];
+    float2 lamT, lam16T;
+    build_operands(log_re, log_im, W, D, ndir, H, N, d, h, tl, a1, a3, lamT, lam16T);
+    float2 carry = make_float2(0.f, 0.f);  // state entering the block, mode = lane
+    unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
+
+    for (int blk = 0; blk < nblk; ++blk) {
+      __syncthreads();  // the previous block's readers of U and S are done
+      // 1. input to LDS, split: element e = 4 t + 1024 q + c4 -> chunk e / 64, step e % 64
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * t + 1024 * q;
+        const int c = e >> 6, j = e & 63;
+        half4 vh, vl;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          _Float16 a, b;
+          split16(un[4 * q + c4], a, b);
+          vh[c4] = a;
+          vl[c4] = b;
+        }
+        *reinterpret_cast<half4*>(bl.Uh + c * kUS + j) = vh;
+        *reinterpret_cast<half4*>(bl.Ul + c * kUS + j) = vl;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_block(blk + 1, un);  // in flight during this block (zeros beyond the sequence)
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      // 2. chunk states: S1[c][r] = sum_j A1[r][j] U[j][c]; this wave: rows 32 w .. +31,
+      //    in two halves of 32 columns (fewer accumulators live)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        f4 acc[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const int c = 32 * ch + 16 * ct + (lane & 15);
+            const int k = 32 * ks + 8 * (lane >> 4);
+            const half8 bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
+            const half8 blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              const half8 ah = a1[(rt * 2 + ks) * 2], al = a1[(rt * 2 + ks) * 2 + 1];
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[rt][ct], 0, 0, 0);
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc[rt][ct], 0, 0, 0);
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[rt][ct], 0, 0, 0);
+            }
+          }
+        }
+        // acc[rt][ct][v]: row r = 32 w + 16 rt + 4 (lane / 16) + v, column c = 32 ch + 16 ct + lane % 16
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const int c = 32 * ch + 16 * ct + (lane & 15);
+            const int r = 32 * w + 16 * rt + 4 * (lane >> 4);
+            *reinterpret_cast<f4*>(bl.S1 + c * kS1S + r) = acc[rt][ct];
+          }
+      }
+      __syncthreads();
+      // 3. chunk recurrence: wave w takes chunks 16 w .. 16 w + 15, lane = mode.  The
+      //    wave reads its rows' S1 values before it writes S over them.
+      {
+        const int n = lane;
+        float2 sv[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          sv[c] = *reinterpret_cast<const float2*>(bl.S1 + (16 * w + c) * kS1S + 2 * n);
+        float2 e = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) e = cfma(lamT, e, sv[c]);
+        bl.E[w][n] = e;
+        __syncthreads();
+        float2 cin = carry;  // state entering quarter w
+        for (int q = 0; q < w; ++q) cin = cfma(lam16T, cin, bl.E[q][n]);
+        float2 cnext = carry;  // state leaving the block (every wave keeps it)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cnext = cfma(lam16T, cnext, bl.E[q][n]);
+        carry = cnext;
+        float2 st = cin;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          half2v hi, lo;
+          _Float16 a, b;
+          split16(st.x, a, b);
+          hi[0] = a;
+          lo[0] = b;
+          split16(st.y, a, b);
+          hi[1] = a;
+          lo[1] = b;
+          unsigned char* row = srow + (16 * w + c) * kSRow;
+          *reinterpret_cast<half2v*>(row + 4 * n) = hi;
+          *reinterpret_cast<half2v*>(row + kSLo + 4 * n) = lo;
+          st = cfma(lamT, st, sv[c]);
+        }
+      }
+      __syncthreads();
+      // 4. outputs: Y[i][c] = sum_k A3[i][k] [U; S][k][c]; this wave: rows 16 w .. +15,
+      //    in two halves of 32 columns
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        f4 acc[2];
+        acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 6; ++ks) {
+          __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
+          const half8 ah = a3[ks * 2], al = a3[ks * 2 + 1];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const int c = 32 * ch + 16 * ct + (lane & 15);
+            half8 bh, blo;
+            if (ks < 2) {
+              const int k = 32 * ks + 8 * (lane >> 4);
+              bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
+              blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
+            } else {
+              const int k = 32 * (ks - 2) + 8 * (lane >> 4);
+              const unsigned char* row = srow + c * kSRow;
+              bh = *reinterpret_cast<const half8*>(row + 2 * k);
+              blo = *reinterpret_cast<const half8*>(row + kSLo + 2 * k);
+            }
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc[ct], 0, 0, 0);
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[ct], 0, 0, 0);
+          }
+        }
+        // acc[ct][v]: step i = 16 w + 4 (lane / 16) + v of chunk c = 32 ch + 16 ct + lane % 16
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int c = 32 * ch + 16 * ct + (lane & 15);
+          const int e0 = (blk * kCB + c) * kT + 16 * w + 4 * (lane >> 4);  // processing time
+          if (!rev) {
+            if (VEC) {
+              u32x4 o;
+              o.x = __float_as_uint(acc[ct][0]);
+              o.y = __float_as_uint(acc[ct][1]);
+              o.z = __float_as_uint(acc[ct][2]);
+              o.w = __float_as_uint(acc[ct][3]);
+              __builtin_amdgcn_raw_buffer_store_b128(o, ybuf, 4 * e0, 0, 0);
+            } else {
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ct][v4]), ybuf,
+                                                      4 * (e0 + v4), 0, 0);
+            }
+          } else {
+            // reversed time: element v4 sits at position Lp - 1 - (e0 + v4); added to
+            // the forward direction's output (read past the L1, which may hold lines
+            // from before this workgroup's own stores)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+              const int p = Lp - 1 - (e0 + v4);
+              const float o =
+                  __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ybuf, 4 * p, 0, 1));
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o + acc[ct][v4]), ybuf,
+                                                    4 * p, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    if (d + 1 < ndir) {
+      __threadfence();  // the forward direction's stores are visible to the reversed sweep
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace
+
+bool chunk_supported(int N) { return N >= 1 && N <= kModes; }
+
+hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im, const float* W,
+                        const float* D, int B, int H, int N, int L, int ndir, float* y,
+                        hipStream_t st, KEvents ev) {
+  const long nwg = (long)B * H;
+  const float2* w2 = reinterpret_cast<const float2*>(W);
+  // 16-byte accesses need a length that a 16-byte access never straddles (rows
+  // then also start 16-byte aligned)
+  if ((L % 4) == 0)
+    launch_k(chunk_kernel<true>, dim3((unsigned)nwg), dim3(256), st, ev, u, log_re, log_im, w2, D,
+             B, H, N, L, ndir, y);
+  else
+    launch_k(chunk_kernel<false>, dim3((unsigned)nwg), dim3(256), st, ev, u, log_re, log_im, w2, D,
+             B, H, N, L, ndir, y);
+  return hipGetLastError();
+}
+
+}  // namespace dssm

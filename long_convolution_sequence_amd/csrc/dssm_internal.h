@@ -97,6 +97,16 @@ hipError_t launch_step(const float* u, const float* log_re, const float* log_im,
                        const float* D, int B, int H, int N, float* x, float* y, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Chunked state-space form on the matrix cores (chunk.hip)
+// ---------------------------------------------------------------------------
+bool chunk_supported(int N);  // N <= 64 modes
+// y [B,H,L] from u [B,H,L] (operands formed in the kernel, no workspace); the
+// second direction (if any) in reversed time.
+hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im, const float* W,
+                        const float* D, int B, int H, int N, int L, int ndir, float* y,
+                        hipStream_t st, KEvents ev = {});
+
+// ---------------------------------------------------------------------------
 // S5 multi-input multi-output diagonal SSM (s5.hip)
 // ---------------------------------------------------------------------------
 struct S5Layout {
