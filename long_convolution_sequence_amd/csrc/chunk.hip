@@ -80,6 +80,35 @@ __device__ __forceinline__ float2 cfma(float2 m, float2 p, float2 acc) {  // acc
   return make_float2(fmaf(m.x, p.x, fmaf(-m.y, p.y, acc.x)), fmaf(m.x, p.y, fmaf(m.y, p.x, acc.y)));
 }
 
+// Largest x >= 0 over the 16 lanes of a DPP row (non-negative floats order as
+// their bit patterns).  Every lane of the wave must be active.
+__device__ __forceinline__ float row_max16(float x) {
+  int v = __float_as_int(x);
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));  // row_mirror
+  return __int_as_float(v);
+}
+
+// Largest x >= 0 over the wave (uniform result).
+__device__ __forceinline__ float wave_max(float x) {
+  const int v = __float_as_int(row_max16(x));
+  const int a = max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
+  const int b = max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
+  return __int_as_float(max(a, b));
+}
+
+// Power-of-two exponent s that brings a group of values with largest
+// magnitude m into [2^14, 2^15) (s = 15 for m = 0): the fp16 hi parts stay
+// below the fp16 maximum and the lo parts clear of its subnormal range.
+// Scaling by 2^s (ldexp) is exact.
+__device__ __forceinline__ int scale_exp(float m) { return 15 - __builtin_amdgcn_frexp_expf(m); }
+
+__device__ __forceinline__ float amax4(const float* v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
 // LDS row strides chosen so the 16-byte fragment reads of 16 consecutive
 // columns fall in different banks.  The chunk states S1[c] (float32) and the
 // carried states S[c] (fp16 hi at byte 0, lo at byte 272 of the same 528-byte
@@ -107,11 +136,14 @@ struct TablesLds {
   double2 lam[kModes], wv[kModes];
   float ktp[2 * kT];  // ktp[T + m] = K_m (+ D_f + D_b at m = 0 of d = 0); 0 for m < 0
   float4 mult[kModes];  // lambda^T, lambda^(16T)
+  float red[8];         // per-wave largest |Q| (0..3) and |K_m| (4..7)
 };
 struct BlockLds {
   _Float16 Uh[kCB * kUS], Ul[kCB * kUS];
   float S1[kCB * kS1S];
   float2 E[4][kModes];
+  int eU[kCB];  // scale exponent of each chunk's input (U rows)
+  int eS[4];    // scale exponent of the carried states of each quarter
 };
 constexpr int kLdsBytes = sizeof(TablesLds) > sizeof(BlockLds) ? sizeof(TablesLds) : sizeof(BlockLds);
 
@@ -121,11 +153,11 @@ __device__ __forceinline__ void lds_read8(const float* p, f4& a, f4& b) {
   b = *reinterpret_cast<const f4*>(p + 4);
 }
 
-__device__ __forceinline__ void split8(const float* v, half8& hi, half8& lo) {
+__device__ __forceinline__ void split8(const float* v, half8& hi, half8& lo, int sc = 0) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     _Float16 a, b;
-    split16(v[e], a, b);
+    split16(__builtin_amdgcn_ldexpf(v[e], sc), a, b);
     hi[e] = a;
     lo[e] = b;
   }
@@ -138,6 +170,8 @@ __device__ __forceinline__ void split8(const float* v, half8& hi, half8& lo) {
 //   a3[ks * 2 + hl]: A3 row i = 16 w + lane % 16, columns k = 32 ks + 8 (lane / 16) + e:
 //     k < T: Toeplitz K_{i-k} (k <= i), with D_f + D_b on the diagonal (d = 0);
 //     k = T + 2n: Re(W_n lambda_n^(i+1)), k = T + 2n + 1: -Im(W_n lambda_n^(i+1))
+//     with the Toeplitz columns scaled by 2^eT and the others by 2^eW (each
+//     part's largest magnitude brought to [2^14, 2^15))
 // and the chunk multipliers lambda^T, lambda^(16T) of mode `lane`.  lambda, its
 // powers (chains of 16 products from lambda^(16 q), q < 4), W lambda^p and the
 // taps K_m = Re sum_n W_n lambda_n^m are float64, each rounded once to float32.
@@ -145,7 +179,7 @@ __device__ __forceinline__ void split8(const float* v, half8& hi, half8& lo) {
 __device__ __forceinline__ void build_operands(
     const float* __restrict__ log_re, const float* __restrict__ log_im,
     const float2* __restrict__ W, const float* __restrict__ D, int ndir, int H, int N, int d,
-    int h, TablesLds& tl, half8* a1, half8* a3, float2& lamT, float2& lam16T) {
+    int h, TablesLds& tl, half8* a1, half8* a3, float2& lamT, float2& lam16T, int& eT, int& eW) {
   const int t = opaque(threadIdx.x), lane = t & 63, w = t >> 6;
   if (w == 0) {  // lambda_n, W_n (float64, from the exactly promoted parameters)
     const int n = lane;
@@ -164,6 +198,7 @@ __device__ __forceinline__ void build_operands(
   }
   __syncthreads();
   float2 pw[16];  // lambda^p of this thread's 16 powers, kept for the planes
+  float qm = 0.f;  // largest |Q| entry written by this thread
   {  // mode n = lane, powers p = 16 w .. 16 w + 15
     const int n = lane;
     const double2 lam = tl.lam[n], wv = tl.wv[n];
@@ -179,7 +214,9 @@ __device__ __forceinline__ void build_operands(
       tl.KR[n][p] = wv.x * x.x - wv.y * x.y;
       x = zmul(x, lam);
       const double2 q = zmul(wv, x);
-      tl.Q[p][n] = make_float2((float)q.x, (float)-q.y);
+      const float2 qf = make_float2((float)q.x, (float)-q.y);
+      tl.Q[p][n] = qf;
+      qm = fmaxf(qm, fmaxf(fabsf(qf.x), fabsf(qf.y)));
     }
     if (w == 3) {  // x = lambda^T
       double2 b16 = zmul(x, x);
@@ -189,6 +226,8 @@ __device__ __forceinline__ void build_operands(
       tl.mult[n] = make_float4((float)x.x, (float)x.y, (float)b16.x, (float)b16.y);
     }
   }
+  qm = wave_max(qm);
+  if (lane == 0) tl.red[w] = qm;
   __syncthreads();
   {  // taps: wave w sums taps 16 w .. +15, a quarter of the modes per 16 lanes
     const int m = 16 * w + (lane & 15), q = lane >> 4;
@@ -199,10 +238,15 @@ __device__ __forceinline__ void build_operands(
     s += __shfl_xor(s, 32);
     if (m == 0 && d == 0)
       for (int dd = 0; dd < ndir; ++dd) s += (double)D[(size_t)dd * H + h];
-    if (q == 0) tl.ktp[kT + m] = (float)s;
+    const float kv = (float)s;
+    if (q == 0) tl.ktp[kT + m] = kv;
     if (q == 1) tl.ktp[m] = 0.f;
+    const float km = row_max16(q == 0 ? fabsf(kv) : 0.f);  // lanes 0..15 hold the taps
+    if (lane == 0) tl.red[4 + w] = km;
   }
   __syncthreads();  // KR read: its space takes the power planes
+  eW = scale_exp(fmaxf(fmaxf(tl.red[0], tl.red[1]), fmaxf(tl.red[2], tl.red[3])));
+  eT = scale_exp(fmaxf(fmaxf(tl.red[4], tl.red[5]), fmaxf(tl.red[6], tl.red[7])));
   {
     float* pr = tl.PP + lane * kPS + 16 * w;
 #pragma unroll
@@ -236,7 +280,7 @@ __device__ __forceinline__ void build_operands(
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = kt[-e];
-    split8(v, a3[ks * 2], a3[ks * 2 + 1]);
+    split8(v, a3[ks * 2], a3[ks * 2 + 1], eT);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -244,7 +288,7 @@ __device__ __forceinline__ void build_operands(
     f4 lo4, hi4;
     lds_read8(reinterpret_cast<const float*>(&tl.Q[i][16 * (ks - 2) + 4 * g]), lo4, hi4);
     const float v[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    split8(v, a3[ks * 2], a3[ks * 2 + 1]);
+    split8(v, a3[ks * 2], a3[ks * 2 + 1], eW);
     __builtin_amdgcn_sched_barrier(0);
   }
   const float4 m = tl.mult[lane];
@@ -320,22 +364,26 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
     load_block(0, un);  // in flight while the operands are formed
     half8 a1[8], a3[12];
     float2 lamT, lam16T;
-    build_operands(log_re, log_im, W, D, ndir, H, N, d, h, tl, a1, a3, lamT, lam16T);
+    int eT, eW;
+    build_operands(log_re, log_im, W, D, ndir, H, N, d, h, tl, a1, a3, lamT, lam16T, eT, eW);
     float2 carry = make_float2(0.f, 0.f);  // state entering the block, mode = lane
     unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
 
     for (int blk = 0; blk < nblk; ++blk) {
       __syncthreads();  // the previous block's readers of U and S are done
-      // 1. input to LDS, split: element e = 4 t + 1024 q + c4 -> chunk e / 64, step e % 64
+      // 1. input to LDS, split: element e = 4 t + 1024 q + c4 -> chunk e / 64, step e % 64;
+      //    the 16 lanes of a DPP row hold one chunk, scaled by 2^eU[chunk]
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int e = 4 * t + 1024 * q;
         const int c = e >> 6, j = e & 63;
+        const int sc = scale_exp(row_max16(amax4(un + 4 * q)));
+        if ((lane & 15) == 0) bl.eU[c] = sc;
         half4 vh, vl;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           _Float16 a, b;
-          split16(un[4 * q + c4], a, b);
+          split16(__builtin_amdgcn_ldexpf(un[4 * q + c4], sc), a, b);
           vh[c4] = a;
           vl[c4] = b;
         }
@@ -390,8 +438,11 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
         const int n = lane;
         float2 sv[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          sv[c] = *reinterpret_cast<const float2*>(bl.S1 + (16 * w + c) * kS1S + 2 * n);
+        for (int c = 0; c < 16; ++c) {  // chunk states, unscaled (S1 carries 2^eU)
+          const float2 v = *reinterpret_cast<const float2*>(bl.S1 + (16 * w + c) * kS1S + 2 * n);
+          const int ec = -bl.eU[16 * w + c];
+          sv[c] = make_float2(__builtin_amdgcn_ldexpf(v.x, ec), __builtin_amdgcn_ldexpf(v.y, ec));
+        }
         float2 e = make_float2(0.f, 0.f);
 #pragma unroll
         for (int c = 0; c < 16; ++c) e = cfma(lamT, e, sv[c]);
@@ -404,29 +455,39 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
         for (int q = 0; q < 4; ++q) cnext = cfma(lam16T, cnext, bl.E[q][n]);
         carry = cnext;
         float2 st = cin;
+        float m = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {  // sv[c] becomes the state entering chunk 16 w + c
+          const float2 nx = cfma(lamT, st, sv[c]);
+          sv[c] = st;
+          m = fmaxf(m, fmaxf(fabsf(st.x), fabsf(st.y)));
+          st = nx;
+        }
+        const int es = scale_exp(wave_max(m));  // one exponent for the quarter's states
+        if (lane == 0) bl.eS[w] = es;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
           half2v hi, lo;
           _Float16 a, b;
-          split16(st.x, a, b);
+          split16(__builtin_amdgcn_ldexpf(sv[c].x, es), a, b);
           hi[0] = a;
           lo[0] = b;
-          split16(st.y, a, b);
+          split16(__builtin_amdgcn_ldexpf(sv[c].y, es), a, b);
           hi[1] = a;
           lo[1] = b;
           unsigned char* row = srow + (16 * w + c) * kSRow;
           *reinterpret_cast<half2v*>(row + 4 * n) = hi;
           *reinterpret_cast<half2v*>(row + kSLo + 4 * n) = lo;
-          st = cfma(lamT, st, sv[c]);
         }
       }
       __syncthreads();
       // 4. outputs: Y[i][c] = sum_k A3[i][k] [U; S][k][c]; this wave: rows 16 w .. +15,
-      //    in two halves of 32 columns
+      //    in two halves of 32 columns.  The U part (k < T) and the S part are
+      //    accumulated apart: each carries its own scale.
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
-        f4 acc[2];
-        acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+        f4 accU[2], accS[2];
+        accU[0] = accU[1] = accS[0] = accS[1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 6; ++ks) {
           __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
@@ -445,28 +506,35 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
               bh = *reinterpret_cast<const half8*>(row + 2 * k);
               blo = *reinterpret_cast<const half8*>(row + kSLo + 2 * k);
             }
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[ct], 0, 0, 0);
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc[ct], 0, 0, 0);
-            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[ct], 0, 0, 0);
+            f4& acc = ks < 2 ? accU[ct] : accS[ct];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
           }
         }
-        // acc[ct][v]: step i = 16 w + 4 (lane / 16) + v of chunk c = 32 ch + 16 ct + lane % 16
+        // acc*[ct][v]: step i = 16 w + 4 (lane / 16) + v of chunk c = 32 ch + 16 ct + lane % 16
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           const int c = 32 * ch + 16 * ct + (lane & 15);
           const int e0 = (blk * kCB + c) * kT + 16 * w + 4 * (lane >> 4);  // processing time
+          const int xu = -(eT + bl.eU[c]), xs = -(eW + bl.eS[c >> 4]);
+          f4 acc;
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            acc[v4] = __builtin_amdgcn_ldexpf(accU[ct][v4], xu) +
+                      __builtin_amdgcn_ldexpf(accS[ct][v4], xs);
           if (!rev) {
             if (VEC) {
               u32x4 o;
-              o.x = __float_as_uint(acc[ct][0]);
-              o.y = __float_as_uint(acc[ct][1]);
-              o.z = __float_as_uint(acc[ct][2]);
-              o.w = __float_as_uint(acc[ct][3]);
+              o.x = __float_as_uint(acc[0]);
+              o.y = __float_as_uint(acc[1]);
+              o.z = __float_as_uint(acc[2]);
+              o.w = __float_as_uint(acc[3]);
               __builtin_amdgcn_raw_buffer_store_b128(o, ybuf, 4 * e0, 0, 0);
             } else {
 #pragma unroll
               for (int v4 = 0; v4 < 4; ++v4)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ct][v4]), ybuf,
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v4]), ybuf,
                                                       4 * (e0 + v4), 0, 0);
             }
           } else {
@@ -478,7 +546,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
               const int p = Lp - 1 - (e0 + v4);
               const float o =
                   __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ybuf, 4 * p, 0, 1));
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o + acc[ct][v4]), ybuf,
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o + acc[v4]), ybuf,
                                                     4 * p, 0, 0);
             }
           }

@@ -215,6 +215,45 @@ def test_shift_pin_no_decay(path):
     assert_close(y, ref, "shift/%s" % path)
 
 
+# Magnitudes far from 1.  The map is linear in u and jointly in (W, D), and a
+# power-of-two factor scales float32 values exactly, so the oracle of the
+# scaled problem is the scaled oracle.
+MAGS = [("u", -100), ("u", -20), ("u", 13), ("u", 100), ("WD", -20), ("WD", 17)]
+
+
+@pytest.mark.parametrize("what,k", MAGS, ids=["%s2^%d" % m for m in MAGS])
+@pytest.mark.parametrize("path", ["fft", "scan"])
+def test_magnitudes(path, what, k):
+    B, H, N, L = 2, 3, 64, 3000
+    say("case: magnitudes path=%s %s x 2^%d" % (path, what, k))
+    x = inputs.dlr_inputs(B, H, N, L, bidirectional=True, seed=515)
+    ref = oracle_rec(("mag",), x, True) * np.ldexp(1.0, k)
+    xs = dict(x)
+    if what == "u":
+        xs["u"] = np.ldexp(x["u"], k).astype(np.float32)
+    else:
+        xs["W"] = (x["W"] * np.float32(np.ldexp(1.0, k))).astype(np.complex64)
+        xs["D"] = np.ldexp(x["D"], k).astype(np.float32)
+    y = run(path, xs, True)
+    assert np.all(np.isfinite(y))
+    assert_close(y, ref, "magnitudes/%s" % path)
+
+
+@pytest.mark.parametrize("path", ["fft", "scan"])
+def test_large_states(path):
+    """A near-undamped mode under a constant input of 1000: its state grows to
+    about 8e6, far past the float16 range that the matrix-core operands have
+    before they are scaled."""
+    B, H, N, L = 1, 2, 64, 8192
+    say("case: large states path=%s" % path)
+    x = inputs.dlr_inputs(B, H, N, L, seed=616, re_scale=0.01)
+    x["u"] = np.full((B, H, L), 1000.0, np.float32)
+    ref = oracle_rec(("large",), x, False)
+    y = run(path, x, False)
+    assert np.all(np.isfinite(y))
+    assert_close(y, ref, "large states/%s" % path)
+
+
 def test_fft_and_scan_agree_and_are_deterministic():
     c = inputs.config(2)
     x = inputs.inputs_for(c)
