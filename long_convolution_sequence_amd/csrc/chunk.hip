@@ -20,42 +20,29 @@
 // How (MI355X design):
 // * s = A1 U and y = A3 [U; S] are dense contractions per channel
 //   (A1: 2N x T = 128 x 64, A3: T x (T + 2N) = 64 x 192, U: T x chunks) done on
-//   the matrix cores with v_mfma_f32_16x16x32_f16.  Every float32 operand is
-//   split as hi = fp16(v), lo = fp16(v - hi) and a product is
-//   hi.hi + hi.lo + lo.hi accumulated in float32 (each fp16 x fp16 product is
-//   exact in float32): ~22 significant bits per operand.
+//   the matrix cores with v_mfma_f32_16x16x32_f16 on split float32 operands
+//   (fp16 hi + lo, three products, float32 accumulation; each operand group
+//   scaled by an exact power of two first).
 // * One workgroup (4 waves) runs one (channel, batch row).  Its prologue forms
 //   the operands from the exactly promoted parameters (lambda, its powers and
 //   the taps in float64, rounded once) and splits them into the MFMA fragments
-//   each wave keeps in registers, while the first block's input is in flight.  Then blocks of 64 chunks: u to LDS (split), GEMM1 ->
-//   chunk states, the chunk recurrence (a wave per quarter of the block, a lane
-//   per mode; quarters combined with lambda^(16T)), GEMM3 -> y.  The next
-//   block's input is requested before the current block is computed.
+//   each wave keeps in registers, while the first block's input is in flight.
+//   Then blocks of 64 chunks: u to LDS (split), GEMM1 -> chunk states, the
+//   chunk recurrence (a wave per quarter of the block, a lane per mode;
+//   quarters combined with lambda^(16T)), GEMM3 -> y.  The next block's input
+//   is requested before the current block is computed.
 #include "dssm_internal.h"
+#include "mfma_split.h"
 
 namespace dssm {
 namespace {
+
+using namespace mx;
 
 constexpr int kT = 64;            // steps per chunk
 constexpr int kCB = 64;           // chunks per block
 constexpr int kModes = 64;        // modes handled (N <= 64; padded with zero modes)
 constexpr int kR = 2 * kModes;    // state rows (re, im interleaved)
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ double2 zmul(double2 a, double2 b) {
-  return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
-}
-
-// float32 value v split into fp16 (hi, lo) with hi + lo = v to ~22 bits.
-__device__ __forceinline__ void split16(float v, _Float16& hi, _Float16& lo) {
-  hi = (_Float16)v;
-  lo = (_Float16)(v - (float)hi);
-}
 
 // Workgroup i runs on XCD i % 8; when the grid divides by 8, consecutive
 // logical workgroups (the batch rows of one channel) share an XCD.
@@ -63,50 +50,8 @@ __device__ __forceinline__ int xcd_grouped(int i, int n) {
   return (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
 }
 
-typedef __amdgpu_buffer_rsrc_t BufRes;
-__device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// The value of x, hidden from the optimiser: values derived from it are formed
-// where they are used, not hoisted out of the direction loop and kept live.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 __device__ __forceinline__ float2 cfma(float2 m, float2 p, float2 acc) {  // acc + m p
   return make_float2(fmaf(m.x, p.x, fmaf(-m.y, p.y, acc.x)), fmaf(m.x, p.y, fmaf(m.y, p.x, acc.y)));
-}
-
-// Largest x >= 0 over the 16 lanes of a DPP row (non-negative floats order as
-// their bit patterns).  Every lane of the wave must be active.
-__device__ __forceinline__ float row_max16(float x) {
-  int v = __float_as_int(x);
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = max(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));  // row_mirror
-  return __int_as_float(v);
-}
-
-// Largest x >= 0 over the wave (uniform result).
-__device__ __forceinline__ float wave_max(float x) {
-  const int v = __float_as_int(row_max16(x));
-  const int a = max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
-  const int b = max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
-  return __int_as_float(max(a, b));
-}
-
-// Power-of-two exponent s that brings a group of values with largest
-// magnitude m into [2^14, 2^15) (s = 15 for m = 0): the fp16 hi parts stay
-// below the fp16 maximum and the lo parts clear of its subnormal range.
-// Scaling by 2^s (ldexp) is exact.
-__device__ __forceinline__ int scale_exp(float m) { return 15 - __builtin_amdgcn_frexp_expf(m); }
-
-__device__ __forceinline__ float amax4(const float* v) {
-  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 }
 
 // LDS row strides chosen so the 16-byte fragment reads of 16 consecutive
@@ -146,22 +91,6 @@ struct BlockLds {
   int eS[4];    // scale exponent of the carried states of each quarter
 };
 constexpr int kLdsBytes = sizeof(TablesLds) > sizeof(BlockLds) ? sizeof(TablesLds) : sizeof(BlockLds);
-
-// 8 consecutive floats of LDS starting at a 16-byte aligned address.
-__device__ __forceinline__ void lds_read8(const float* p, f4& a, f4& b) {
-  a = *reinterpret_cast<const f4*>(p);
-  b = *reinterpret_cast<const f4*>(p + 4);
-}
-
-__device__ __forceinline__ void split8(const float* v, half8& hi, half8& lo, int sc = 0) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    _Float16 a, b;
-    split16(__builtin_amdgcn_ldexpf(v[e], sc), a, b);
-    hi[e] = a;
-    lo[e] = b;
-  }
-}
 
 // Operand fragments of wave w for direction d of channel h:
 //   a1[(rt * 2 + ks) * 2 + hl]: A1 rows r = 32 w + 16 rt + lane % 16, columns

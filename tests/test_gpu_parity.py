@@ -121,6 +121,32 @@ def test_generator(idx):
         assert np.array_equal(Kr[d, hs], K[d, hs].real)
 
 
+GEN_EDGE = [  # (H, N, L, W scale exponent): ragged lengths, several mode chunks, magnitudes
+    (3, 8, 1, 0), (2, 16, 63, 0), (3, 100, 1001, 0), (2, 64, 4097, 0), (2, 130, 130, 0),
+    (2, 64, 3000, -60), (2, 64, 3000, 60),
+]
+
+
+@pytest.mark.parametrize("shape", GEN_EDGE, ids=["H%dN%dL%dW2^%d" % g for g in GEN_EDGE])
+def test_generator_edges(shape):
+    torch = _torch()
+    H, N, L, k = shape
+    say("case: generator edge H=%d N=%d L=%d W x 2^%d" % shape)
+    x = inputs.dlr_inputs(1, H, N, L, bidirectional=True, seed=900 + L)
+    x["W"] = (x["W"] * np.float32(np.ldexp(1.0, k))).astype(np.complex64)
+    t = dev(x)
+    K = bd.gen_kernel(t["log_re"], t["log_im"], t["W"], L, complex_out=True)
+    Kr = bd.gen_kernel(t["log_re"], t["log_im"], t["W"], L, complex_out=False)
+    torch.cuda.synchronize()
+    K = K.cpu().numpy()
+    Kr = Kr.cpu().numpy()
+    for d in range(2):
+        ref = oracle.dlr_kernel(x["log_re"][d], x["log_im"][d], x["W"][d], L)
+        assert_close(K[d].real, ref.real, "K re d=%d" % d)
+        assert_close(K[d].imag, ref.imag, "K im d=%d" % d)
+        assert np.array_equal(Kr[d], K[d].real)
+
+
 def test_generator_dft_identity():
     """log_re = 0, log_im = 2 pi n / N, L = N: K = N ifft(W) (DLR page, section 2).
 
