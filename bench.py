@@ -175,7 +175,8 @@ def time_copy(src, dst, reps, hip):
 def cpu_baseline(x, bi, y_gpu):
     """The float64 oracle as it stands, single process, on the host: the
     sequential recurrence over the whole workload, plus the direct O(L^2) sum
-    on a sample of rows.  Also reports the GPU output's error against it."""
+    on a sample of rows.  Also reports each GPU path's error against it
+    (y_gpu: path name -> output)."""
     import numpy as np
 
     import oracle
@@ -189,11 +190,14 @@ def cpu_baseline(x, bi, y_gpu):
     refd = oracle.dlr_direct(x["u"][:, :hs], x["log_re"][:, :hs], x["log_im"][:, :hs],
                              x["W"][:, :hs], x["D"][:, :hs], bi)
     t_dir = time.perf_counter() - t
-    d = y_gpu.astype(np.float64) - ref
-    rel = float(np.linalg.norm(d) / np.linalg.norm(ref))
-    mx = float(np.max(np.abs(d)) / np.sqrt(np.mean(ref ** 2)))
-    dd = y_gpu[:, :hs].astype(np.float64) - refd
-    rel_d = float(np.linalg.norm(dd) / np.linalg.norm(refd))
+    rms = np.sqrt(np.mean(ref ** 2))
+    errs = {}
+    for name, y in y_gpu.items():
+        d = y.astype(np.float64) - ref
+        dd = y[:, :hs].astype(np.float64) - refd
+        errs[name] = {"rel_l2": float(np.linalg.norm(d) / np.linalg.norm(ref)),
+                      "max_over_rms": float(np.max(np.abs(d)) / rms),
+                      "direct_sample_rel_l2": float(np.linalg.norm(dd) / np.linalg.norm(refd))}
     return {
         "value": B * H * L / t_rec,
         "unit": "elements/s",
@@ -202,8 +206,33 @@ def cpu_baseline(x, bi, y_gpu):
         "sample": "oracle.dlr_recurrence (float64 sequential recurrence) over the whole "
                   "workload (%d elements, %.1f s); oracle.dlr_direct (O(L^2) sum) on %d of %d "
                   "channels: %.3g elements/s" % (B * H * L, t_rec, hs, H, B * hs * L / t_dir),
-        "gpu_vs_oracle": {"rel_l2": rel, "max_over_rms": mx, "direct_sample_rel_l2": rel_d},
+        "gpu_vs_oracle": errs,
     }
+
+
+def scan_path_summary(B, H, N, L, bi, ms, kernel_ms, stages):
+    """The recurrence view's layer forward.  With N <= 64 modes it is one
+    kernel, the chunked matrix-core form (chunks of T = 64 steps, blocks of 64
+    chunks): per (direction, channel, batch row) and block, 4 waves x (48 + 72)
+    v_mfma_f32_16x16x32_f16 of 16384 flops each (the split operands triple the
+    contraction).  Otherwise the segmented scan (constants kernel + scan)."""
+    elems = B * H * L
+    ndir = 2 if bi else 1
+    out = {"ms_per_step": ms, "elements_per_s": elems / (ms * 1e-3), "kernel_ms": kernel_ms}
+    alg_bytes = 8 * elems
+    out["hbm_gbs"] = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    out["hbm_frac"] = out["hbm_gbs"] / HBM_PEAK_GBS
+    if N <= 64:
+        nblk = -(-(-(-L // 64)) // 64)
+        mfma_flop = ndir * H * B * nblk * 4 * (48 + 72) * 16384
+        out["kernel"] = "chunk_kernel (chunked matrix-core form)"
+        out["mfma_f16_tflops_executed"] = mfma_flop / (kernel_ms * 1e-3) / 1e12
+        out["mfma_f16_frac"] = out["mfma_f16_tflops_executed"] / 2500.0
+        out["alg_fp32_tflops"] = 12 * N * ndir * elems / (kernel_ms * 1e-3) / 1e12
+    else:
+        out["kernel"] = "scan_kernel (segmented scan)"
+        out["stage_ms_breakdown"] = {"consts": stages[0], "scan": stages[1]}
+    return out
 
 
 def main():
@@ -246,6 +275,7 @@ def main():
     y_fft = ys[(a.steps - 1) % a.rotate].cpu().numpy()
     ms_scan, scan_ms, stages_scan = time_path("scan", dev, us, ys, ws_scan, a.scan_steps,
                                               min(a.warmup, 2), bi, hip, a.scan_steps)
+    y_scan = ys[(a.scan_steps - 1) % a.rotate].cpu().numpy()
 
     elems = B * H * L
     alg_bytes = 8 * elems  # u read + y write, float32
@@ -286,17 +316,14 @@ def main():
             "stage_ms_breakdown": {"kernel_spectrum": stages[0], "conv": stages[1]},
             "full_call_hbm_gbs": alg_bytes / (ms * 1e-3) / 1e9,
             "conv_fp32_tflops_est": conv_flop / (conv_ms * 1e-3) / 1e12,
-            "scan_path": {"ms_per_step": ms_scan, "elements_per_s": elems / (ms_scan * 1e-3),
-                          "scan_kernel_ms": scan_ms,
-                          "stage_ms_breakdown": {"consts": stages_scan[0],
-                                                 "scan": stages_scan[1]}},
+            "scan_path": scan_path_summary(B, H, N, L, bi, ms_scan, scan_ms, stages_scan),
             "rotated_sets": a.rotate,
             "device_copy": copy,
             "s5_path": time_s5(max(2, a.scan_steps), 2, hip),
         },
     }
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(x, bi, y_fft)
+        line["cpu_baseline"] = cpu_baseline(x, bi, {"fft": y_fft, "scan": y_scan})
     print(json.dumps(line), flush=True)
 
 

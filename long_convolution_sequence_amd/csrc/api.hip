@@ -383,23 +383,25 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
     return fail(DSSM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* apk_in = at<float>(ws, l.apk_in);
-  float* apk_out = at<float>(ws, l.apk_out);
+  void* apk_in = at<unsigned char>(ws, l.apk_in);
+  void* apk_out = at<unsigned char>(ws, l.apk_out);
+  int* rexp_in = at<int>(ws, l.rexp_in);
+  int* rexp_out = at<int>(ws, l.rexp_out);
   float* v = at<float>(ws, l.v);
   float* x = at<float>(ws, l.x);
-  if ((rc = hip_check(
-           launch_s5_pack(p->Bbar, p->C, s->H, s->P, apk_in, apk_out, st, kev(events, 0)),
-           "s5 pack")))
+  if ((rc = hip_check(launch_s5_pack(p->Bbar, p->C, s->H, s->P, apk_in, rexp_in, apk_out,
+                                     rexp_out, st, kev(events, 0)),
+                      "s5 pack")))
     return rc;
   if ((rc = hip_check(
-           launch_s5_proj_in(apk_in, u, s->B, s->H, s->P, s->L, v, st, kev(events, 1)),
+           launch_s5_proj_in(apk_in, rexp_in, u, s->B, s->H, s->P, s->L, v, st, kev(events, 1)),
            "s5 proj_in")))
     return rc;
   if ((rc = hip_check(launch_s5_scan(p->lambda, v, s->B, s->P, s->L, x, st, kev(events, 2)),
                       "s5 scan")))
     return rc;
-  if ((rc = hip_check(launch_s5_proj_out(apk_out, x, p->D, u, s->B, s->H, s->P, s->L, y, st,
-                                         kev(events, 3)),
+  if ((rc = hip_check(launch_s5_proj_out(apk_out, rexp_out, x, p->D, u, s->B, s->H, s->P, s->L,
+                                         y, st, kev(events, 3)),
                       "s5 proj_out")))
     return rc;
   return ok();

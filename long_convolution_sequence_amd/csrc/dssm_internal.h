@@ -110,22 +110,24 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
 // S5 multi-input multi-output diagonal SSM (s5.hip)
 // ---------------------------------------------------------------------------
 struct S5Layout {
-  size_t apk_in = 0, apk_out = 0, v = 0, x = 0, total = 0;
+  size_t apk_in = 0, rexp_in = 0, apk_out = 0, rexp_out = 0, v = 0, x = 0, total = 0;
 };
 S5Layout s5_layout(int B, int H, int P, int L);
 
-// Bbar [P,H] c64, C [H,P] c64 -> MFMA A-fragment tables.
-hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, float* apk_in,
-                          float* apk_out, hipStream_t st, KEvents ev = {});
+// Bbar [P,H] c64, C [H,P] c64 -> split MFMA fragment tables (16-byte aligned)
+// and per-row scale exponents.
+hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, void* apk_in,
+                          int* rexp_in, void* apk_out, int* rexp_out, hipStream_t st,
+                          KEvents ev = {});
 // v [B][P][2][L] = Bbar u
-hipError_t launch_s5_proj_in(const float* apk_in, const float* u, int B, int H, int P, int L,
-                             float* v, hipStream_t st, KEvents ev = {});
+hipError_t launch_s5_proj_in(const void* apk_in, const int* rexp_in, const float* u, int B, int H,
+                             int P, int L, float* v, hipStream_t st, KEvents ev = {});
 // x [B][P][2][L]: x_k = lambda x_{k-1} + v_k
 hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int L, float* x,
                           hipStream_t st, KEvents ev = {});
 // y [B][H][L] = Re(C x) + D u
-hipError_t launch_s5_proj_out(const float* apk_out, const float* x, const float* D,
-                              const float* u, int B, int H, int P, int L, float* y,
+hipError_t launch_s5_proj_out(const void* apk_out, const int* rexp_out, const float* x,
+                              const float* D, const float* u, int B, int H, int P, int L, float* y,
                               hipStream_t st, KEvents ev = {});
 
 }  // namespace dssm

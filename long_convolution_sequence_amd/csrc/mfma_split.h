@@ -53,6 +53,17 @@ __device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
                                            0x00020000);
 }
 
+// Raw buffer over `bytes` bytes at a base the caller knows to be the same in
+// every lane: the fields are taken from the first lane, so the descriptor
+// lives in scalar registers (no per-lane loop around the access).
+__device__ __forceinline__ BufRes buf_res_uniform(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const void* p = reinterpret_cast<const void*>(((unsigned long long)hi << 32) | lo);
+  return buf_res(p, __builtin_amdgcn_readfirstlane(bytes));
+}
+
 // The value of x, hidden from the optimiser: values derived from it are formed
 // where they are used, not hoisted out of an enclosing loop and kept live.
 __device__ __forceinline__ int opaque(int x) {

@@ -8,154 +8,475 @@
 //   y_k = Re(C x_k) + D * u_k.
 //
 // How (MI355X design): the two projections are dense contractions over H and
-// over 2P real rows, done on the matrix cores in float32
-// (v_mfma_f32_16x16x4f32); the recurrence is a segmented complex scan per
-// (b, p) channel between them.  Intermediates v and x live in the workspace as
-// [B][P][2][L] float32 (real row, imaginary row), which is exactly the
-// [2P x L] right-hand operand of the output projection.
-//   * pack kernel: Bbar and C rearranged into MFMA A-fragment order
-//     (rows 2p / 2p+1 = Re / Im of Bbar[p,:]; columns 2p / 2p+1 = Re C[:,p] /
-//     -Im C[:,p]), zero padded.
-//   * gemm kernel: one workgroup = 4 waves x 64 rows x 64 time steps, the
-//     whole reduction in registers; each lane loads one float4 of A and one
-//     of B per 4-deep k step and issues 16 MFMAs.  The output projection adds
-//     D u in its epilogue.
+// over 2P real rows, done on the matrix cores (v_mfma_f32_16x16x32_f16) on
+// split float32 operands: fp16 hi + lo, three products, float32 accumulation,
+// each operand row or column first scaled by an exact power of two.  The
+// recurrence is a segmented complex scan per (b, p) channel between them.
+// Intermediates v and x live in the workspace as [B][P][2][L] float32 (real
+// row, imaginary row), which is exactly the [2P x L] right-hand operand of the
+// output projection.
+//   * pack kernel: Bbar and C as split MFMA fragments of A^T (rows 2p / 2p+1 =
+//     Re / Im of Bbar[p,:]; columns 2p / 2p+1 = Re C[:,p] / -Im C[:,p]), zero
+//     padded, with one scale exponent per row.
+//   * gemm kernel: one workgroup = 4 waves x 64 rows by 64 time steps; the
+//     right-hand tile is staged through LDS transposed and split (per-column
+//     scale), the products are formed transposed so each lane stores four
+//     consecutive time steps.  The output projection adds D u in its epilogue.
 //   * scan kernel: one channel per workgroup, 16 steps per lane, carries by a
 //     Hillis-Steele scan with multipliers lambda^(16 2^j) from float64, tiles
 //     of 4096 steps chained by the carried state.
 #include <algorithm>
 
 #include "dssm_internal.h"
+#include "mfma_split.h"
 
 namespace dssm {
 namespace {
 
+using namespace mx;
+
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// A-fragment layout for M x K (row block rb of 64 rows, k step ks of 4):
-//   apk[((rb * KS + ks) * 64 + lane) * 4 + r] = A[rb*64 + r*16 + lane%16][ks*4 + lane/16]
-// kind 0: A = [Re Bbar; Im Bbar] interleaved by p   (M = 2P, K = H)
-// kind 1: A = [Re C, -Im C] interleaved by p        (M = H,  K = 2P)
+// Tile sizes of the contractions out[b][i][j] = sum_k A[i][k] Bm[b][k][j]:
+// a workgroup (4 waves) owns 256 rows i (64 per wave) and 64 columns j (time
+// steps) and runs over k in chunks of 256.  Each workgroup reads the whole
+// split A^T table (from L2), so wider column tiles read it less often; 64 keeps
+// the LDS tile at 68 KB (two workgroups per CU) and makes each wave's tile load
+// instruction read one row (a wave-uniform row address).
+constexpr int kRowsWG = 256;
+constexpr int kColsWG = 64;
+constexpr int kKC = 256;
+constexpr int kNJ = kColsWG / 16;        // column tiles of 16
+constexpr int kQL = kKC / 32;            // 8-deep k groups per thread
+constexpr int kBTS = kKC + 8;  // LDS row stride (fp16) of the transposed B tile
+
+// Element A[i][k] of a contraction (zero outside M x K):
+// kind 0: A = [Re Bbar; Im Bbar] interleaved by p (M = 2P rows, K = H)
+// kind 1: A = [Re C, -Im C] interleaved by p      (M = H rows,  K = 2P)
+__device__ __forceinline__ float a_elem(int kind, const float2* __restrict__ Bbar,
+                                        const float2* __restrict__ C, int H, int P, int i, int k) {
+  if (kind == 0) {
+    if (i >= 2 * P || k >= H) return 0.f;
+    const float2 v = Bbar[(size_t)(i >> 1) * H + k];
+    return (i & 1) ? v.y : v.x;
+  }
+  if (i >= H || k >= 2 * P) return 0.f;
+  const float2 v = C[(size_t)i * P + (k >> 1)];
+  return (k & 1) ? -v.y : v.x;
+}
+
+// A^T as the B operand of v_mfma_f32_16x16x32_f16, split: for row tile it
+// (rows 16 it .. + 15) and k step ks (32 k), lane l holds
+// A[16 it + l % 16][32 ks + 8 (l / 16) + e] * 2^rexp[i], e < 8, as fp16 hi and
+// lo: apk[((it * KS + ks) * 2 + hl) * 64 + l].  rexp[i] brings row i's largest
+// magnitude into [2^14, 2^15).  One workgroup per (row tile, kind); a row
+// tile past a kind's rows returns at once (the whole workgroup).
 __global__ __launch_bounds__(256) void s5_pack_kernel(const float2* __restrict__ Bbar,
                                                       const float2* __restrict__ C, int H, int P,
-                                                      float* __restrict__ apk_in,
-                                                      float* __restrict__ apk_out) {
+                                                      half8* __restrict__ apk_in,
+                                                      int* __restrict__ rexp_in,
+                                                      half8* __restrict__ apk_out,
+                                                      int* __restrict__ rexp_out) {
+  __shared__ float red[16][17];
+  __shared__ int rexp_s[16];
   const int kind = blockIdx.y;
   const int M = kind == 0 ? 2 * P : H;
   const int K = kind == 0 ? H : 2 * P;
-  const int MB = (M + 63) / 64, KS = (K + 3) / 4;
-  const long total = (long)MB * KS * 64 * 4;
-  float* out = kind == 0 ? apk_in : apk_out;
-  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (long)gridDim.x * blockDim.x) {
-    const int r = (int)(e & 3);
-    const int lane = (int)((e >> 2) & 63);
-    const long t = e >> 8;
-    const int ks = (int)(t % KS);
-    const int rb = (int)(t / KS);
-    const int i = rb * 64 + r * 16 + (lane & 15);
-    const int k = ks * 4 + (lane >> 4);
-    float v = 0.f;
-    if (i < M && k < K) {
-      if (kind == 0) {
-        const float2 b = Bbar[(size_t)(i >> 1) * H + k];
-        v = (i & 1) ? b.y : b.x;
-      } else {
-        const float2 c = C[(size_t)i * P + (k >> 1)];
-        v = (k & 1) ? -c.y : c.x;
-      }
+  const int it = blockIdx.x;
+  if (16 * it >= M) return;
+  const int KS = (K + 31) / 32;
+  const int t = threadIdx.x, r = t & 15, part = t >> 4;
+  // row maxima: thread (r, part) scans k = part, part + 16, ... (16 independent
+  // loads in flight per step: one step covers K = 256)
+  float m = 0.f;
+  for (int k0 = part; k0 < K; k0 += 16 * 16) {
+    float e16[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      e16[e] = fabsf(a_elem(kind, Bbar, C, H, P, 16 * it + r, k0 + 16 * e));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, e16[e]);
+  }
+  red[r][part] = m;
+  __syncthreads();
+  if (t < 16) {
+    float mm = 0.f;
+    for (int q = 0; q < 16; ++q) mm = fmaxf(mm, red[t][q]);
+    rexp_s[t] = scale_exp(mm);
+    (kind == 0 ? rexp_in : rexp_out)[16 * it + t] = rexp_s[t];
+  }
+  __syncthreads();
+  half8* out = (kind == 0 ? apk_in : apk_out) + (size_t)it * KS * 2 * 64;
+  // fragments: two (k step, lane) entries per thread and step, all 16 loads
+  // issued before the first is used
+  for (int idx0 = t; idx0 < KS * 64; idx0 += 512) {
+    float v[2][8];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int idx = idx0 + 256 * h2;
+      const int ks = idx >> 6, l = idx & 63;
+      const int i = 16 * it + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[h2][e] = idx < KS * 64 ? a_elem(kind, Bbar, C, H, P, i, k0 + e) : 0.f;
     }
-    out[e] = v;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int idx = idx0 + 256 * h2;
+      if (idx >= KS * 64) break;
+      const int ks = idx >> 6, l = idx & 63;
+      half8 hi, lo;
+      split8(v[h2], hi, lo, rexp_s[l & 15]);
+      out[(size_t)(ks * 2) * 64 + l] = hi;
+      out[(size_t)(ks * 2 + 1) * 64 + l] = lo;
+    }
   }
 }
 
-// out[b][i][j] = sum_k A[i][k] Bm[b][k][j]  (+ D[i] u[b][i][j] when kAddDu)
-// A given as fragments (see above); Bm [B][K][L] row-major; out [B][M][L].
-template <bool kAddDu>
-__global__ __launch_bounds__(256) void s5_gemm_kernel(const float* __restrict__ apk,
-                                                      const float* __restrict__ Bm, int M, int K,
-                                                      int L, const float* __restrict__ D,
-                                                      const float* __restrict__ u,
-                                                      float* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int MB = (M + 63) / 64, KS = (K + 3) / 4;
-  const int rb = blockIdx.y * 4 + w;
-  if (rb >= MB) return;  // no barriers in this kernel
+// out[b][i][j] = sum_k A[i][k] Bm[b][k][j]  (+ D[i] u[b][i][j] when kAddDu);
+// Bm [B][K][L] row-major, out [B][M][L].  Computed transposed, outT = Bm^T A^T,
+// so each lane's four results are consecutive time steps (16-byte stores).
+// Per k chunk the workgroup stages Bm[chunk][j0 .. j0 + kColsWG) in LDS as
+// BT[j][k] (fp16 hi and lo), each column j scaled by 2^cexp[j] from its
+// largest magnitude in the chunk; the A^T fragments come prepacked (scaled per
+// row).  With several k chunks (kMulti) each chunk's products are unscaled into
+// a running total.
+template <bool kAddDu, bool kMulti>
+__global__ __launch_bounds__(256, 2) void s5_gemm_kernel(const half8* __restrict__ apk,
+                                                         const int* __restrict__ rexp,
+                                                         const float* __restrict__ Bm, int M,
+                                                         int K, int L, const float* __restrict__ D,
+                                                         const float* __restrict__ u,
+                                                         float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) _Float16 Bh[kColsWG][kBTS];
+  __shared__ __attribute__((aligned(16))) _Float16 Bl[kColsWG][kBTS];
+  __shared__ float cmax[4][kColsWG];
+  __shared__ __attribute__((aligned(16))) int cexp[kColsWG];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4;
   const int b = blockIdx.z;
-  const int j0 = blockIdx.x * 64;
-  const int jl = j0 + 4 * (lane & 15);  // this lane's 4 columns
-  const bool vec = ((L & 3) == 0) && (jl + 3 < L);
+  const int j0 = blockIdx.x * kColsWG;
+  const int i0 = blockIdx.y * kRowsWG + 64 * w;  // this wave's first row
+  const bool rows_here = i0 < M;                  // waves past M load but do not multiply
+  const int KS = (K + 31) / 32;
   const float* Bb = Bm + (size_t)b * K * L;
-  const v4f* ap = reinterpret_cast<const v4f*>(apk) + (size_t)rb * KS * 64 + lane;
 
-  v4f acc[4][4];
+  v4f acc[kNJ][4], tot[kNJ][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int jt = 0; jt < kNJ; ++jt)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < 4; ++it) tot[jt][it] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // operands of k step ks: one float4 of A fragments, one float4 of B
-  auto load_b = [&](int ks) {
-    const int k = ks * 4 + (lane >> 4);
-    v4f bv = v4f{0.f, 0.f, 0.f, 0.f};
-    if (ks < KS && k < K) {
-      const float* row = Bb + (size_t)k * L;
-      if (vec) {
-        bv = *reinterpret_cast<const v4f*>(row + jl);
-      } else {
+  for (int kc = 0; kc < K; kc += kKC) {
+    if (kc) __syncthreads();  // the previous chunk's tile is read
+    // 1. tile: thread (column j = lane, wave w) loads k = kc + 8 (w + 4 q) + e,
+    //    q < 8, e < 8: each load instruction reads 64 consecutive columns of one
+    //    row, through a raw buffer over that row (a wave-uniform descriptor):
+    //    columns past L read zero, and a row past K has an empty range.  No
+    //    load sits under a branch (each would be waited on).
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const unsigned jb = 4u * (unsigned)(j0 + lane);
+    float v[kQL][8];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) bv[c] = (jl + c < L) ? row[jl + c] : 0.f;
+    for (int q = 0; q < kQL; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = kc + 8 * (wu + 4 * q) + e;
+        const BufRes row =
+            buf_res_uniform(Bb + (size_t)min(k, K - 1) * L, k < K ? 4u * (unsigned)L : 0u);
+        v[q][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row, jb, 0, 0));
+      }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the tile in flight before the first wait
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < kQL; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[q][e]));
+    cmax[w][lane] = m;
+    __syncthreads();
+    const int sc = scale_exp(fmaxf(fmaxf(cmax[0][lane], cmax[1][lane]),
+                                   fmaxf(cmax[2][lane], cmax[3][lane])));
+    if (w == 0) cexp[lane] = sc;
+#pragma unroll
+    for (int q = 0; q < kQL; ++q) {
+      half8 hi, lo;
+      split8(v[q], hi, lo, sc);
+      *reinterpret_cast<half8*>(&Bh[lane][8 * (w + 4 * q)]) = hi;
+      *reinterpret_cast<half8*>(&Bl[lane][8 * (w + 4 * q)]) = lo;
+    }
+    __syncthreads();
+
+    // 2. outT[j][i] for the kColsWG columns (tiles jt) by this wave's 64 rows (4 tiles it)
+#pragma unroll
+    for (int jt = 0; jt < kNJ; ++jt)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) acc[jt][it] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (rows_here) {
+      const int ks0 = kc / 32, ks1 = min(KS, (kc + kKC) / 32);
+      const half8* ap = apk + (size_t)(i0 / 16) * KS * 2 * 64 + lane;
+      // A^T fragments of k step ks into buffer slot (the next step's loads are
+      // in flight while the current step multiplies)
+      half8 ah[2][4], al[2][4];
+      auto load_a = [&](int ks, int slot) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const half8* f = ap + ((size_t)it * KS + ks) * 2 * 64;
+          ah[slot][it] = f[0];
+          al[slot][it] = f[64];
+        }
+      };
+      auto multiply = [&](int ks, int slot) {
+        const int kk = 32 * (ks - ks0) + 8 * g;
+#pragma unroll
+        for (int jt = 0; jt < kNJ; ++jt) {
+          const half8 bh = *reinterpret_cast<const half8*>(&Bh[16 * jt + (lane & 15)][kk]);
+          const half8 bl = *reinterpret_cast<const half8*>(&Bl[16 * jt + (lane & 15)][kk]);
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh, ah[slot][it], acc[jt][it], 0, 0, 0);
+            acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh, al[slot][it], acc[jt][it], 0, 0, 0);
+            acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bl, ah[slot][it], acc[jt][it], 0, 0, 0);
+          }
+        }
+      };
+      // Loads are unconditional (a step index past the chunk is clamped, the
+      // fragments then simply unused): a load under a branch would make the
+      // wait at the join cover the prefetch too.
+      load_a(ks0, 0);
+      for (int ks = ks0; ks < ks1; ks += 2) {
+        load_a(min(ks + 1, ks1 - 1), 1);
+        multiply(ks, 0);
+        load_a(min(ks + 2, ks1 - 1), 0);
+        if (ks + 1 < ks1) multiply(ks + 1, 1);
       }
     }
-    return bv;
-  };
-  // one step of prefetch: the loads of step ks+1 are in flight while the 16
-  // MFMAs of step ks run
-  v4f a = ap[0];
-  v4f bv = load_b(0);
-  for (int ks = 0; ks < KS; ++ks) {
-    const v4f a_n = (ks + 1 < KS) ? ap[(size_t)(ks + 1) * 64] : a;
-    const v4f b_n = load_b(ks + 1);
+    // acc[jt][it][v]: column j0 + 16 jt + 4 g + v, row i0 + 16 it + lane % 16
+    if (kMulti) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int jt = 0; jt < kNJ; ++jt) {
+        const int4 ce = *reinterpret_cast<const int4*>(&cexp[16 * jt + 4 * g]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], bv[c], acc[r][c], 0, 0, 0);
-    a = a_n;
-    bv = b_n;
-  }
-
-  // acc[r][c][v] holds row rb*64 + r*16 + 4*(lane/16) + v, column jl + c.
-  float* ob = out + (size_t)b * M * L;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = rb * 64 + r * 16 + 4 * (lane >> 4) + v;
-      if (i >= M) continue;
-      v4f o = v4f{acc[r][0][v], acc[r][1][v], acc[r][2][v], acc[r][3][v]};
-      if (kAddDu) {
-        const float d = D[i];
-        const float* ur = u + ((size_t)b * M + i) * L;
-        if (vec) {
-          const v4f uu = *reinterpret_cast<const v4f*>(ur + jl);
-          o += d * uu;
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (jl + c < L) o[c] += d * ur[jl + c];
+        for (int it = 0; it < 4; ++it) {
+          tot[jt][it][0] += __builtin_amdgcn_ldexpf(acc[jt][it][0], -ce.x);
+          tot[jt][it][1] += __builtin_amdgcn_ldexpf(acc[jt][it][1], -ce.y);
+          tot[jt][it][2] += __builtin_amdgcn_ldexpf(acc[jt][it][2], -ce.z);
+          tot[jt][it][3] += __builtin_amdgcn_ldexpf(acc[jt][it][3], -ce.w);
         }
       }
-      float* orow = ob + (size_t)i * L;
-      if (vec) {
-        *reinterpret_cast<v4f*>(orow + jl) = o;
+    }
+  }
+  if (!rows_here) return;  // no barriers follow
+
+  // 3. epilogue: unscale (row exponent, and the column exponents of a single
+  //    chunk), add D u, store four consecutive time steps per lane.  The u
+  //    loads are all issued before the first store (a load issued after a
+  //    store would wait for it).
+  const bool vec = (L & 3) == 0;
+  float* ob = out + (size_t)b * M * L;
+  v4f du[kNJ][4];
+  if (kAddDu) {
+    const float* ub = u + (size_t)b * M * L;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = i0 + 16 * it + (lane & 15);
+      const float d = i < M ? D[i] : 0.f;
+#pragma unroll
+      for (int jt = 0; jt < kNJ; ++jt) {
+        const int jj = j0 + 16 * jt + 4 * g;
+        if (vec) {
+          const bool ok = i < M && jj + 3 < L;
+          const v4f x = *reinterpret_cast<const v4f*>(ok ? ub + (size_t)i * L + jj : ub);
+          du[jt][it] = ok ? d * x : v4f{0.f, 0.f, 0.f, 0.f};
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool ok = i < M && jj + c < L;
+            const float x = *(ok ? ub + (size_t)i * L + jj + c : ub);
+            du[jt][it][c] = ok ? d * x : 0.f;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = i0 + 16 * it + (lane & 15);
+    if (i >= M) continue;
+    const int re = rexp[i];
+    float* orow = ob + (size_t)i * L;
+#pragma unroll
+    for (int jt = 0; jt < kNJ; ++jt) {
+      const int jj = j0 + 16 * jt + 4 * g;
+      v4f o;
+      if (kMulti) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = __builtin_amdgcn_ldexpf(tot[jt][it][c], -re);
+      } else {
+        const int4 ce = *reinterpret_cast<const int4*>(&cexp[16 * jt + 4 * g]);
+        o[0] = __builtin_amdgcn_ldexpf(acc[jt][it][0], -(re + ce.x));
+        o[1] = __builtin_amdgcn_ldexpf(acc[jt][it][1], -(re + ce.y));
+        o[2] = __builtin_amdgcn_ldexpf(acc[jt][it][2], -(re + ce.z));
+        o[3] = __builtin_amdgcn_ldexpf(acc[jt][it][3], -(re + ce.w));
+      }
+      if (kAddDu) o += du[jt][it];
+      if (vec && jj + 3 < L) {
+        *reinterpret_cast<v4f*>(orow + jj) = o;
       } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (jl + c < L) orow[jl + c] = o[c];
+          if (jj + c < L) orow[jj + c] = o[c];
       }
     }
+  }
+}
+
+// Persistent form for K <= 256 (one k chunk).  A workgroup of 8 waves owns
+// 256 rows (32 per wave: its split A^T fragments stay in registers for the
+// whole kernel, read from L2 once) and walks the column tiles t = blockIdx.x,
+// blockIdx.x + gridDim.x, ... over all batch rows.  The right-hand tile of the
+// next column tile is loaded into registers while the current one is
+// multiplied from the other half of a double-buffered LDS tile; the products
+// read only LDS and registers, so the in-order completion of memory
+// operations never makes them wait for the prefetch.
+constexpr int kPW = 8;  // waves per workgroup of the persistent form
+
+template <bool kAddDu>
+__global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
+    const half8* __restrict__ apk, const int* __restrict__ rexp, const float* __restrict__ Bm,
+    int M, int K, int L, int B, const float* __restrict__ D, const float* __restrict__ u,
+    float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) _Float16 Bh[2][kColsWG][kBTS];
+  __shared__ __attribute__((aligned(16))) _Float16 Bl[2][kColsWG][kBTS];
+  __shared__ float cmax[kPW][kColsWG];
+  __shared__ __attribute__((aligned(16))) int cexp[2][kColsWG];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int i0 = blockIdx.y * kRowsWG + 32 * w;  // this wave's first row
+  const bool rows_here = i0 < M;
+  const int KS = (K + 31) / 32;  // <= 8
+  const int njb = (L + kColsWG - 1) / kColsWG;
+  const int ntiles = B * njb;
+
+  // this wave's A^T fragments: row tiles i0 / 16 + it (it < 2), k steps < KS
+  half8 ah[2][8], al[2][8];
+  int rx[2] = {0, 0};
+  if (rows_here) {
+    const half8* ap = apk + (size_t)(i0 / 16) * KS * 2 * 64 + lane;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const half8* f = ap + ((size_t)it * KS + min(ks, KS - 1)) * 2 * 64;
+        ah[it][ks] = f[0];
+        al[it][ks] = f[64];
+      }
+      const int i = i0 + 16 * it + (lane & 15);
+      rx[it] = rexp[min(i, M - 1)];
+    }
+  }
+
+  // right-hand tile tt = (b, jb): thread (column lane, wave w) loads rows
+  // k = 8 (w + 8 q) + e through a raw buffer over each row (wave-uniform):
+  // columns past L read zero, a row past K has an empty range
+  float v[4][8];
+  auto load_tile = [&](int tt) {
+    const int b = tt / njb, jb = tt - b * njb;
+    const float* Bb = Bm + (size_t)b * K * L;
+    const unsigned jbyte = 4u * (unsigned)(jb * kColsWG + lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 8 * (wu + kPW * q) + e;
+        const BufRes row =
+            buf_res_uniform(Bb + (size_t)min(k, K - 1) * L, k < K ? 4u * (unsigned)L : 0u);
+        v[q][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row, jbyte, 0, 0));
+      }
+  };
+  // split the loaded tile into LDS half sl, each column scaled by 2^cexp
+  auto stage = [&](int sl) {
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[q][e]));
+    cmax[w][lane] = m;
+    __syncthreads();
+    float cm = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kPW; ++w2) cm = fmaxf(cm, cmax[w2][lane]);
+    const int sc = scale_exp(cm);
+    if (w == 0) cexp[sl][lane] = sc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half8 hi, lo;
+      split8(v[q], hi, lo, sc);
+      *reinterpret_cast<half8*>(&Bh[sl][lane][8 * (w + kPW * q)]) = hi;
+      *reinterpret_cast<half8*>(&Bl[sl][lane][8 * (w + kPW * q)]) = lo;
+    }
+    __syncthreads();
+  };
+
+  int tt = blockIdx.x;
+  if (tt < ntiles) {
+    load_tile(tt);
+    stage(0);
+  }
+  const bool vec = (L & 3) == 0;
+  for (int sl = 0; tt < ntiles; tt += gridDim.x, sl ^= 1) {
+    const int tn = tt + gridDim.x;
+    const bool has_next = tn < ntiles;  // the same in the whole workgroup
+    load_tile(has_next ? tn : tt);      // unconditional: no load under a branch
+
+    v4f acc[4][2];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) acc[jt][0] = acc[jt][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (rows_here) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks >= KS) break;
+        const int kk = 32 * ks + 8 * g;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const half8 bh = *reinterpret_cast<const half8*>(&Bh[sl][16 * jt + (lane & 15)][kk]);
+          const half8 bl = *reinterpret_cast<const half8*>(&Bl[sl][16 * jt + (lane & 15)][kk]);
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh, ah[it][ks], acc[jt][it], 0, 0, 0);
+            acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh, al[it][ks], acc[jt][it], 0, 0, 0);
+            acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bl, ah[it][ks], acc[jt][it], 0, 0, 0);
+          }
+        }
+      }
+      // acc[jt][it][c]: column 64 jb + 16 jt + 4 g + c, row i0 + 16 it + lane % 16
+      const int b = tt / njb, jb = tt - b * njb;
+      float* ob = out + (size_t)b * M * L;
+      const float* ub = kAddDu ? u + (size_t)b * M * L : nullptr;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int i = i0 + 16 * it + (lane & 15);
+        if (i >= M) continue;
+        const float d = kAddDu ? D[i] : 0.f;
+        float* orow = ob + (size_t)i * L;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int jj = jb * kColsWG + 16 * jt + 4 * g;
+          const int4 ce = *reinterpret_cast<const int4*>(&cexp[sl][16 * jt + 4 * g]);
+          v4f o;
+          o[0] = __builtin_amdgcn_ldexpf(acc[jt][it][0], -(rx[it] + ce.x));
+          o[1] = __builtin_amdgcn_ldexpf(acc[jt][it][1], -(rx[it] + ce.y));
+          o[2] = __builtin_amdgcn_ldexpf(acc[jt][it][2], -(rx[it] + ce.z));
+          o[3] = __builtin_amdgcn_ldexpf(acc[jt][it][3], -(rx[it] + ce.w));
+          if (vec && jj + 3 < L) {
+            if (kAddDu) o += d * *reinterpret_cast<const v4f*>(ub + (size_t)i * L + jj);
+            *reinterpret_cast<v4f*>(orow + jj) = o;
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (jj + c < L) orow[jj + c] = kAddDu ? o[c] + d * ub[(size_t)i * L + jj + c] : o[c];
+          }
+        }
+      }
+    }
+    if (has_next) stage(sl ^ 1);
   }
 }
 
@@ -328,29 +649,67 @@ S5Layout s5_layout(int B, int H, int P, int L) {
     off = align_up(off + bytes, 256);
     return at;
   };
-  const size_t in_frag = (size_t)((2 * P + 63) / 64) * 64 * ((H + 3) / 4) * 4;
-  const size_t out_frag = (size_t)((H + 63) / 64) * 64 * ((2 * P + 3) / 4) * 4;
-  l.apk_in = take(in_frag * sizeof(float));
-  l.apk_out = take(out_frag * sizeof(float));
+  // split fragments: 16-row tiles x 32-deep k steps x (hi, lo) x 64 lanes x 16 B;
+  // whole 64-row groups, as a wave of the contraction reads four tiles (tiles
+  // past the rows are read, never written, and their products never stored)
+  auto frag_bytes = [](int M, int K) {
+    return (size_t)((M + 63) / 64) * 4 * ((K + 31) / 32) * 2 * 64 * sizeof(half8);
+  };
+  l.apk_in = take(frag_bytes(2 * P, H));
+  l.rexp_in = take((size_t)((2 * P + 15) / 16) * 16 * sizeof(int));
+  l.apk_out = take(frag_bytes(H, 2 * P));
+  l.rexp_out = take((size_t)((H + 15) / 16) * 16 * sizeof(int));
   l.v = take((size_t)B * P * 2 * L * sizeof(float));
   l.x = take((size_t)B * P * 2 * L * sizeof(float));
   l.total = off;
   return l;
 }
 
-hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, float* apk_in,
-                          float* apk_out, hipStream_t st, KEvents ev) {
-  launch_k(s5_pack_kernel, dim3(256, 2), dim3(256), st, ev, reinterpret_cast<const float2*>(Bbar),
-           reinterpret_cast<const float2*>(C), H, P, apk_in, apk_out);
+hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, void* apk_in,
+                          int* rexp_in, void* apk_out, int* rexp_out, hipStream_t st, KEvents ev) {
+  const int tiles = (std::max(2 * P, H) + 15) / 16;
+  launch_k(s5_pack_kernel, dim3((unsigned)tiles, 2), dim3(256), st, ev,
+           reinterpret_cast<const float2*>(Bbar), reinterpret_cast<const float2*>(C), H, P,
+           static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out);
   return hipGetLastError();
 }
 
-hipError_t launch_s5_proj_in(const float* apk_in, const float* u, int B, int H, int P, int L,
-                             float* v, hipStream_t st, KEvents ev) {
-  const int M = 2 * P;
-  const dim3 grid((unsigned)((L + 63) / 64), (unsigned)(((M + 63) / 64 + 3) / 4), (unsigned)B);
-  launch_k(s5_gemm_kernel<false>, grid, dim3(256), st, ev, apk_in, u, M, H, L,
-           static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), v);
+namespace {
+int cu_count() {
+  static int n = 0;
+  if (!n) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <bool kAddDu>
+void launch_gemm(const void* apk, const int* rexp, const float* Bm, int M, int K, int L, int B,
+                 const float* D, const float* u, float* out, hipStream_t st, KEvents ev) {
+  const half8* a = static_cast<const half8*>(apk);
+  const int nrb = (M + kRowsWG - 1) / kRowsWG;
+  if (K <= kKC) {
+    // one persistent workgroup per CU (per row block), walking the column tiles
+    const long ntiles = (long)B * ((L + kColsWG - 1) / kColsWG);
+    const long per = std::max(1, cu_count() / nrb);
+    const dim3 grid((unsigned)std::min(ntiles, per), (unsigned)nrb);
+    launch_k(s5_gemm_pipe_kernel<kAddDu>, grid, dim3(64 * kPW), st, ev, a, rexp, Bm, M, K, L, B,
+             D, u, out);
+    return;
+  }
+  const dim3 grid((unsigned)((L + kColsWG - 1) / kColsWG), (unsigned)nrb, (unsigned)B);
+  launch_k(s5_gemm_kernel<kAddDu, true>, grid, dim3(256), st, ev, a, rexp, Bm, M, K, L, D, u, out);
+}
+}  // namespace
+
+hipError_t launch_s5_proj_in(const void* apk_in, const int* rexp_in, const float* u, int B, int H,
+                             int P, int L, float* v, hipStream_t st, KEvents ev) {
+  launch_gemm<false>(apk_in, rexp_in, u, 2 * P, H, L, B, nullptr, nullptr, v, st, ev);
   return hipGetLastError();
 }
 
@@ -361,12 +720,10 @@ hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int
   return hipGetLastError();
 }
 
-hipError_t launch_s5_proj_out(const float* apk_out, const float* x, const float* D,
-                              const float* u, int B, int H, int P, int L, float* y,
+hipError_t launch_s5_proj_out(const void* apk_out, const int* rexp_out, const float* x,
+                              const float* D, const float* u, int B, int H, int P, int L, float* y,
                               hipStream_t st, KEvents ev) {
-  const int M = H;
-  const dim3 grid((unsigned)((L + 63) / 64), (unsigned)(((M + 63) / 64 + 3) / 4), (unsigned)B);
-  launch_k(s5_gemm_kernel<true>, grid, dim3(256), st, ev, apk_out, x, M, 2 * P, L, D, u, y);
+  launch_gemm<true>(apk_out, rexp_out, x, H, 2 * P, L, B, D, u, y, st, ev);
   return hipGetLastError();
 }
 

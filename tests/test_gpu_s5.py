@@ -36,6 +36,9 @@ S5_EDGE = [
     # (B, H, P, L)
     (1, 1, 1, 1), (1, 1, 1, 7), (3, 2, 1, 33), (2, 3, 5, 100), (1, 6, 3, 4096),
     (2, 70, 5, 130), (3, 5, 40, 257), (1, 4, 2, 5000), (2, 64, 32, 1024), (1, 300, 33, 96),
+    # contractions over several 256-deep k chunks and several 256-row blocks,
+    # ragged row counts inside a wave's 64 rows, ragged time tail
+    (1, 600, 140, 3001), (2, 72, 300, 515),
 ]
 
 
@@ -66,6 +69,30 @@ def test_s5_reduces_to_dlr_bank_on_device():
     y = run_s5(dict(u=u, lam=lam, Bbar=np.eye(H, dtype=np.complex64), C=np.diag(w).astype(np.complex64), D=D))
     ref = oracle.s5_recurrence(u, lam, np.eye(H), np.diag(w), D)
     assert_close(y, ref, "s5/reduction")
+
+
+# Magnitudes far from 1.  y is linear in u jointly with nothing else scaled
+# apart from D u and C x together, and Bbar -> 2^k Bbar with C -> 2^-k C leaves y
+# unchanged; power-of-two factors scale float32 values exactly.
+S5_MAGS = [("u", -70), ("u", 60), ("BC", 40), ("BC", -40)]
+
+
+@pytest.mark.parametrize("what,k", S5_MAGS, ids=["%s2^%d" % m for m in S5_MAGS])
+def test_s5_magnitudes(what, k):
+    B, H, P, L = 2, 40, 24, 2000
+    say("case: s5 magnitudes %s x 2^%d" % (what, k))
+    x = inputs.s5_inputs(B, H, P, L, seed=717)
+    ref = oracle.s5_recurrence(x["u"], x["lam"], x["Bbar"], x["C"], x["D"])
+    xs = dict(x)
+    if what == "u":
+        xs["u"] = np.ldexp(x["u"], k).astype(np.float32)
+        ref = ref * np.ldexp(1.0, k)
+    else:
+        xs["Bbar"] = (x["Bbar"] * np.float32(np.ldexp(1.0, k))).astype(np.complex64)
+        xs["C"] = (x["C"] * np.float32(np.ldexp(1.0, -k))).astype(np.complex64)
+    y = run_s5(xs)
+    assert np.all(np.isfinite(y))
+    assert_close(y, ref, "s5/magnitudes")
 
 
 def test_s5_timed_matches_untimed():
