@@ -11,8 +11,9 @@ pages define, in float64, from the float32 input values promoted exactly:
 
 * ``dlr``  -- the diagonal linear RNN (DLR) of "Simplifying and Understanding
   State Space Models with Diagonal Linear RNNs", section 2: the parameterisation
-  of Lambda, the kernel K_j = sum_n w_n lambda_n^j, the real cast, the causal
-  convolution and the bidirectional sum; computed twice, as an O(L^2) direct sum
+  of Lambda, the kernel K_j = sum_n w_n lambda_n^j, the real cast (and the
+  DLR-prod cast Re K Im K of section 2.1), the causal convolution and the
+  bidirectional sum; computed twice, as an O(L^2) direct sum
   and as a sequential recurrence; and the recurrence continued from a given
   state (streaming / one-token decode), returning the state it ends in.
 * ``s5``   -- the multi-input multi-output diagonal SSM of "Simplified State
@@ -27,6 +28,7 @@ Toeplitz/circulant matrices and invariants).  No function is "parity unpinned".
 from .dlr import (  # noqa: F401
     dlr_lambda,
     dlr_kernel,
+    dlr_kernel_cast,
     dlr_direct,
     dlr_recurrence,
     dlr_recurrence_state,

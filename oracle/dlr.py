@@ -85,12 +85,30 @@ def dlr_kernel(log_re, log_im, W, L):
     return out.reshape(lead + (L,))
 
 
-def dlr_direct(u, log_re, log_im, W, D, bidirectional=False):
+def dlr_kernel_cast(log_re, log_im, W, L, cast="re"):
+    """The real kernel the convolution applies, from K = dlr_kernel(...):
+
+    * cast "re":   Re K_j  (DLR page, section 2: the real cast of the kernel);
+    * cast "prod": Re K_j * Im K_j  (DLR page, section 2.1: the DLR-prod cast,
+      used in the Shift experiments of section 3).
+
+    Shapes as dlr_kernel; the result is real [..., L].
+    """
+    K = dlr_kernel(log_re, log_im, W, L)
+    if cast == "re":
+        return K.real
+    if cast == "prod":
+        return K.real * K.imag
+    raise ValueError("cast must be 're' or 'prod'")
+
+
+def dlr_direct(u, log_re, log_im, W, D, bidirectional=False, cast="re"):
     """DLR layer output by the direct O(L^2) causal sum, float64.
 
-    y[b,h,k] = sum_{j=0}^{k} Re K_f[h,j] u[b,h,k-j]
-             (+ sum_{j=0}^{L-1-k} Re K_b[h,j] u[b,h,k+j]   if bidirectional)
-             + (D_f[h] (+ D_b[h])) u[b,h,k].
+    y[b,h,k] = sum_{j=0}^{k} Kc_f[h,j] u[b,h,k-j]
+             (+ sum_{j=0}^{L-1-k} Kc_b[h,j] u[b,h,k+j]   if bidirectional)
+             + (D_f[h] (+ D_b[h])) u[b,h,k],
+    with Kc the cast kernel of dlr_kernel_cast (Re K by default).
 
     The sums are done by numpy.convolve (a direct, non-FFT method) on each
     channel and truncated to the first L outputs; the backward term convolves
@@ -106,7 +124,7 @@ def dlr_direct(u, log_re, log_im, W, D, bidirectional=False):
     y = u * D.sum(axis=0)[None, :, None]
     for d in range(ndir):
         for h in range(H):
-            k = dlr_kernel(re[d, h], _real64(log_im)[d, h], _cplx128(W)[d, h], L).real
+            k = dlr_kernel_cast(re[d, h], _real64(log_im)[d, h], _cplx128(W)[d, h], L, cast)
             for b in range(Bsz):
                 if d == 0:
                     y[b, h] += np.convolve(u[b, h], k)[:L]

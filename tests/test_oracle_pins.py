@@ -417,3 +417,140 @@ def test_inputs_are_seeded_and_float32():
         assert np.array_equal(a[k], b[k])
     c2 = inputs.dlr_inputs(1, 2, 4, 8, bidirectional=True, seed=2)
     assert c2["log_re"].shape == (2, 2, 4) and c2["D"].shape == (2, 2)
+
+
+# ----------------------------------------------------------------------------
+# DLR-prod cast (DLR page, section 2.1): the convolution applies Re K_j Im K_j
+# ----------------------------------------------------------------------------
+
+def _expanded_prod_params(log_re, log_im, W):
+    """The DLR whose real-cast kernel is Re K Im K, from the page's claim that
+    the DLR-prod kernel is the kernel of a DLR of at most 4N^2 modes: with
+    Re K Im K = Im(K^2) / 2 = Re(K^2 / 2i) and K_j^2 = sum_{n,m} W_n W_m
+    (lambda_n lambda_m)^j, the modes are lambda_n lambda_m
+    (log_re' = sqrt(re_n^2 + re_m^2), log_im' = im_n + im_m) with weights
+    W_n W_m / 2i -- N^2 modes."""
+    re = np.asarray(log_re, dtype=np.float64)
+    im = np.asarray(log_im, dtype=np.float64)
+    w = np.asarray(W).astype(np.complex128)
+    re2 = np.sqrt(re[..., :, None] ** 2 + re[..., None, :] ** 2)
+    im2 = im[..., :, None] + im[..., None, :]
+    w2 = w[..., :, None] * w[..., None, :] / 2j
+    lead = re.shape[:-1]
+    n2 = re.shape[-1] ** 2
+    return re2.reshape(lead + (n2,)), im2.reshape(lead + (n2,)), w2.reshape(lead + (n2,))
+
+
+def ppin_expanded_dlr(impl):
+    lr, li, W, _ = _params(3, 6, seed=31, re_scale=0.5)
+    L = 200
+    got = impl.kernel_cast(lr, li, W, L, "prod")
+    e_re, e_im, e_w = _expanded_prod_params(lr, li, W)
+    ref = oracle.dlr_kernel(e_re, e_im, e_w, L).real
+    return _rel(got, ref) < 1e-10
+
+
+def ppin_single_mode_closed_form(impl):
+    """N = 1, no decay: K_j = w e^{i j theta}, so Re K_j Im K_j =
+    |w|^2 sin(2 (j theta + arg w)) / 2."""
+    theta, w = 0.37, 1.3 * np.exp(0.4j)
+    L = 500
+    got = impl.kernel_cast(np.zeros((1,)), np.array([theta]), np.array([w]), L, "prod")
+    j = np.arange(L)
+    ref = abs(w) ** 2 * np.sin(2 * (j * theta + np.angle(w))) / 2
+    return np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def ppin_direct_is_toeplitz(impl):
+    """y = T u + D u with T the explicit (lower, plus upper for the backward
+    direction) Toeplitz matrix of the prod-cast kernels, built element by
+    element on a tiny length."""
+    ok = True
+    for bi in (False, True):
+        x = inputs.dlr_inputs(2, 3, 5, 23, bidirectional=bi, seed=41)
+        L = 23
+        y = impl.direct(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], bi, "prod")
+        for h in range(3):
+            Kf = impl.kernel_cast(x["log_re"][0, h], x["log_im"][0, h], x["W"][0, h], L, "prod")
+            T = np.zeros((L, L))
+            for k in range(L):
+                for j in range(k + 1):
+                    T[k, j] += Kf[k - j]
+            dsum = np.float64(x["D"][0, h])
+            if bi:
+                Kb = impl.kernel_cast(x["log_re"][1, h], x["log_im"][1, h], x["W"][1, h], L, "prod")
+                for k in range(L):
+                    for j in range(k, L):
+                        T[k, j] += Kb[j - k]
+                dsum = dsum + np.float64(x["D"][1, h])
+            for b in range(2):
+                ub = x["u"][b, h].astype(np.float64)
+                ref = T @ ub + dsum * ub
+                ok &= _rel(y[b, h], ref) < RTOL
+    return bool(ok)
+
+
+def ppin_real_modes_vanish(impl):
+    """Real lambda and real W make K real, so the prod-cast kernel is zero and
+    only D u remains."""
+    x = inputs.dlr_inputs(1, 2, 4, 40, seed=43)
+    W = x["W"].real.astype(np.complex64)
+    li = np.zeros_like(x["log_im"])
+    y = impl.direct(x["u"], x["log_re"], li, W, x["D"], False, "prod")
+    ref = x["u"].astype(np.float64) * x["D"][0].astype(np.float64)[None, :, None]
+    return np.allclose(y, ref, rtol=0, atol=1e-12)
+
+
+PROD_PINS = [ppin_expanded_dlr, ppin_single_mode_closed_form, ppin_direct_is_toeplitz,
+             ppin_real_modes_vanish]
+PROD_REAL = types.SimpleNamespace(kernel_cast=oracle.dlr_kernel_cast, direct=oracle.dlr_direct)
+
+
+@pytest.mark.parametrize("pin", PROD_PINS, ids=[p.__name__ for p in PROD_PINS])
+def test_prod_pin(pin):
+    assert pin(PROD_REAL)
+
+
+def _prod_mutant(kind):
+    def kernel_cast(log_re, log_im, W, L, cast="re"):
+        K = oracle.dlr_kernel(log_re, log_im, W, L)
+        if cast == "re":
+            return K.real
+        if kind == "re_re":
+            return K.real * K.real
+        if kind == "half":
+            return K.real * K.imag / 2
+        if kind == "conj":
+            return -K.real * K.imag
+        if kind == "abs2":
+            return np.abs(K) ** 2 / 2
+        return K.real * K.imag
+
+    def direct(u, log_re, log_im, W, D, bidirectional=False, cast="re"):
+        u = np.asarray(u, dtype=np.float64)
+        Bsz, H, L = u.shape
+        ndir = 2 if bidirectional else 1
+        y = u * np.asarray(D, dtype=np.float64).sum(0)[None, :, None]
+        for d in range(ndir):
+            for h in range(H):
+                k = kernel_cast(log_re[d, h], log_im[d, h], W[d, h], L, cast)
+                for b in range(Bsz):
+                    if d == 0:
+                        y[b, h] += np.convolve(u[b, h], k)[:L]
+                    else:
+                        y[b, h] += np.convolve(u[b, h][::-1], k)[:L][::-1]
+        return y
+
+    return types.SimpleNamespace(kernel_cast=kernel_cast, direct=direct)
+
+
+@pytest.mark.parametrize("kind", ["re_re", "half", "conj", "abs2"])
+def test_prod_pins_reject_planted_mistake(kind):
+    m = _prod_mutant(kind)
+    failed = [p.__name__ for p in PROD_PINS if not p(m)]
+    assert failed, f"no prod pin caught the planted mistake '{kind}'"
+
+
+def test_prod_mutant_harness_is_faithful():
+    m = _prod_mutant("none")
+    assert all(p(m) for p in PROD_PINS)
