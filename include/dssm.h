@@ -64,6 +64,13 @@ typedef enum {
   DSSM_OP_SCAN = 2   /* dssm_forward_scan */
 } dssm_op;
 
+/* How the complex kernel K is cast to the real kernel the convolution applies
+ * (DLR page, section 2 for the real cast; section 2.1 for DLR-prod). */
+typedef enum {
+  DSSM_CAST_RE = 0,    /* Re K_j */
+  DSSM_CAST_RE_IM = 1  /* Re K_j * Im K_j (DLR-prod) */
+} dssm_cast;
+
 /* Shape of a DLR bank: batch B, channels H, modes N, length L. */
 typedef struct {
   int B, H, N, L;
@@ -103,11 +110,21 @@ int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes);
  *   complex_out = 1: K is [ndir, H, L, 2] float32 holding K (re, im).
  * Powers are formed from lambda^r (r < 64) and anchors W lambda^(64q) that
  * are computed in float64 and rounded once to float32; the sum over modes is
- * a float32 matrix-core contraction.  B and p->D are ignored (D may be NULL);
- * the workspace size is 0 (ws may be NULL).
+ * a matrix-core contraction on split operands (fp16 hi + lo, three products,
+ * float32 accumulation; the anchors scaled by a power of two first), ~22
+ * significant bits per operand.  B and p->D are ignored (D may be NULL); the
+ * workspace size is 0 (ws may be NULL).
  * Requires 1 <= N <= 4096, 1 <= L <= 2^24. */
 int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_out,
                     float* K, void* ws, size_t ws_bytes, void* stream);
+
+/* The real kernel a cast applies: K [ndir, H, L] float32 holding Re K_j
+ * (cast = DSSM_CAST_RE, as dssm_gen_kernel with complex_out = 0) or
+ * Re K_j * Im K_j (cast = DSSM_CAST_RE_IM, the DLR-prod kernel of the DLR page,
+ * section 2.1), K as in dssm_gen_kernel.  Any other cast returns
+ * DSSM_ERR_INVALID_ARG.  Other arguments and limits as dssm_gen_kernel. */
+int dssm_gen_kernel_cast(const dssm_dlr_params* p, const dssm_shape* s, int cast, float* K,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /* Layer forward by the convolution view: y [B, H, L] from u [B, H, L].
  * Generates Re K, takes its spectrum on a zero-padded circle of length 2M
@@ -122,13 +139,28 @@ int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_o
 int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                      float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* dssm_forward_fft with the kernel cast `cast` in place of Re K: with
+ * DSSM_CAST_RE_IM each direction's convolution applies Re K_j * Im K_j (the
+ * DLR-prod layer of the DLR page, sections 2.1 and 3); DSSM_CAST_RE is
+ * dssm_forward_fft.  Any other cast returns DSSM_ERR_INVALID_ARG.  The
+ * workspace is dssm_workspace_size(DSSM_OP_FFT, s).  DLR-prod has no
+ * recurrence entry point: as a recurrence it is a DLR of N^2 modes
+ * lambda_n lambda_m. */
+int dssm_forward_fft_cast(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                          int cast, float* y, void* ws, size_t ws_bytes, void* stream);
+
 /* Layer forward by the recurrence view: x_k = lambda x_{k-1} + u_k (x_{-1} = 0,
  * every mode driven by u), y_k = Re(sum_n W_n x_{k,n}) + D u_k; the backward
  * direction runs over k = L-1 .. 0 and is added ("The Annotated S4", Part 1,
  * "Discrete-time SSM: the recurrent representation"; the diagonal parallel
  * scan of "Simplified State Space Layers for Sequence Modeling", section 2.2).
- * Time is split into segments, one per lane; segment carries are combined with
- * powers of lambda computed in float64.  Accepts any L >= 1. */
+ * For N <= 64 (and B H <= 2^24) the map is computed by chunks of 64 steps:
+ * within a chunk as dense contractions on the matrix cores (the Toeplitz
+ * product of the taps plus the contribution of the carried state, on split
+ * fp16 operands scaled by powers of two), across chunks by the state
+ * recurrence; otherwise time is split into segments, one per lane, whose
+ * carries are combined with powers of lambda computed in float64.  Accepts
+ * any L >= 1. */
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                       float* y, void* ws, size_t ws_bytes, void* stream);
 

@@ -18,11 +18,13 @@ DSSM_ERR_WORKSPACE = -3
 DSSM_ERR_HIP = -4
 
 OP_GEN, OP_FFT, OP_SCAN = 0, 1, 2
+CAST_RE, CAST_RE_IM = 0, 1  # Re K, or Re K * Im K (DLR-prod)
 
 # Every function the header declares (checked by the ABI tests).
 EXPORTS = [
     "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
-    "dssm_gen_kernel", "dssm_forward_fft", "dssm_forward_scan",
+    "dssm_gen_kernel", "dssm_gen_kernel_cast", "dssm_forward_fft", "dssm_forward_fft_cast",
+    "dssm_forward_scan",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
     "dssm_forward_scan_state", "dssm_step",
     "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed",
@@ -78,6 +80,12 @@ def lib():
     L.dssm_gen_kernel.restype = ctypes.c_int
     L.dssm_gen_kernel.argtypes = [ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), ctypes.c_int,
                                   vp, vp, sz, vp]
+    L.dssm_gen_kernel_cast.restype = ctypes.c_int
+    L.dssm_gen_kernel_cast.argtypes = [ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
+                                       ctypes.c_int, vp, vp, sz, vp]
+    L.dssm_forward_fft_cast.restype = ctypes.c_int
+    L.dssm_forward_fft_cast.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
+                                        ctypes.c_int, vp, vp, sz, vp]
     for name in ("dssm_forward_fft", "dssm_forward_scan"):
         f = getattr(L, name)
         f.restype = ctypes.c_int
@@ -194,7 +202,25 @@ def gen_kernel(log_re, log_im, W, L, complex_out=False, out=None, workspace=None
     return out
 
 
-def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream, events=None):
+def gen_kernel_cast(log_re, log_im, W, L, cast=CAST_RE, out=None, workspace=None, stream=None):
+    """The real kernel of a cast: Re K (CAST_RE) or Re K * Im K (CAST_RE_IM,
+    DLR-prod), [ndir,H,L] f32."""
+    torch = _torch()
+    ndir, H, N = log_re.shape
+    shape = Shape(1, H, N, L, ndir - 1)
+    p, keep = _params(log_re, log_im, W, None, ndir, H, N)
+    if out is None:
+        out = torch.empty(ndir, H, L, dtype=torch.float32, device=log_re.device)
+    o = _dev_f32(out, "out")
+    ws, nbytes = _workspace(OP_GEN, shape, workspace, log_re.device)
+    check(lib().dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(shape), int(cast),
+                                     o.data_ptr(), ws.data_ptr(), nbytes, _stream(stream)))
+    del keep
+    return out
+
+
+def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream, events=None,
+             cast=None):
     torch = _torch()
     uu = _dev_f32(u, "u")
     if uu.dim() != 3:
@@ -208,8 +234,10 @@ def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, strea
         y = torch.empty_like(uu)
     yy = _dev_f32(y, "y")
     ws, nbytes = _workspace(op, shape, workspace, uu.device)
-    args = [uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape), yy.data_ptr(), ws.data_ptr(),
-            nbytes, _stream(stream)]
+    args = [uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape)]
+    if cast is not None:
+        args.append(int(cast))
+    args += [yy.data_ptr(), ws.data_ptr(), nbytes, _stream(stream)]
     if events is not None:
         arr = (ctypes.c_void_p * len(events))(*events)
         args += [arr, len(events)]
@@ -222,6 +250,14 @@ def forward_fft(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace=
     """Layer forward by the FFT convolution view.  u [B,H,L] f32 -> y [B,H,L]."""
     return _forward(lib().dssm_forward_fft, OP_FFT, u, log_re, log_im, W, D, bidirectional, y,
                     workspace, stream)
+
+
+def forward_fft_cast(u, log_re, log_im, W, D, cast, bidirectional=False, y=None, workspace=None,
+                     stream=None):
+    """Layer forward by the FFT convolution view with the kernel cast `cast`
+    (CAST_RE: as forward_fft; CAST_RE_IM: DLR-prod)."""
+    return _forward(lib().dssm_forward_fft_cast, OP_FFT, u, log_re, log_im, W, D, bidirectional, y,
+                    workspace, stream, cast=cast)
 
 
 def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace=None, stream=None):

@@ -159,23 +159,48 @@ int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes) {
   return ok();
 }
 
-int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_out, float* K,
-                    void* ws, size_t ws_bytes, void* stream) {
+static int gen_impl(const dssm_dlr_params* p, const dssm_shape* s, int out, float* K, void* ws,
+                    size_t ws_bytes, void* stream) {
   bool empty = false;
   int rc = check_shape(DSSM_OP_GEN, s, &empty);
   if (rc) return rc;
-  if (complex_out != 0 && complex_out != 1)
-    return fail(DSSM_ERR_INVALID_ARG, "complex_out must be 0 or 1");
   if (empty) return ok();
   if ((rc = check_params(p, false))) return rc;
   if (!K || !aligned16(K)) return fail(DSSM_ERR_INVALID_ARG, "K is NULL or not 16-byte aligned");
   Layout l;
   if ((rc = check_ws(DSSM_OP_GEN, s, ws, ws_bytes, &l))) return rc;
   if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, (1 + s->bidirectional) * s->H, s->N,
-                                 s->L, complex_out, K, static_cast<hipStream_t>(stream)),
+                                 s->L, out, K, static_cast<hipStream_t>(stream)),
                       "gen launch")))
     return rc;
   return ok();
+}
+
+int dssm_gen_kernel(const dssm_dlr_params* p, const dssm_shape* s, int complex_out, float* K,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (complex_out != 0 && complex_out != 1) {
+    bool empty = false;
+    const int rc = check_shape(DSSM_OP_GEN, s, &empty);
+    if (rc) return rc;
+    return fail(DSSM_ERR_INVALID_ARG, "complex_out must be 0 or 1");
+  }
+  return gen_impl(p, s, complex_out ? kGenComplex : kGenRe, K, ws, ws_bytes, stream);
+}
+
+static int check_cast(int cast) {
+  if (cast != DSSM_CAST_RE && cast != DSSM_CAST_RE_IM)
+    return fail(DSSM_ERR_INVALID_ARG, "cast must be DSSM_CAST_RE (0) or DSSM_CAST_RE_IM (1), got %d",
+                cast);
+  return DSSM_OK;
+}
+
+int dssm_gen_kernel_cast(const dssm_dlr_params* p, const dssm_shape* s, int cast, float* K,
+                         void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_GEN, s, &empty);
+  if (rc) return rc;
+  if ((rc = check_cast(cast))) return rc;
+  return gen_impl(p, s, cast == DSSM_CAST_RE_IM ? kGenReIm : kGenRe, K, ws, ws_bytes, stream);
 }
 
 // A kernel's start/stop pair is both handles or neither (kernel untimed).
@@ -202,10 +227,11 @@ static KEvents kev(void* const* events, int k) {
 // that the GPU stamps at the start and the end of each kernel.
 static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                         float* y, void* ws, size_t ws_bytes, void* stream, void* const* events,
-                        int n_events) {
+                        int n_events, int cast = DSSM_CAST_RE) {
   bool empty = false;
   int rc = check_shape(op, s, &empty);
   if (rc) return rc;
+  if ((rc = check_cast(cast))) return rc;
   const int want = 4;
   if (events && n_events != want)
     return fail(DSSM_ERR_INVALID_ARG, "n_events must be %d (got %d)", want, n_events);
@@ -224,8 +250,9 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
     float2* spec = at<float2>(ws, l.spec);
     const KEvents e0 = kev(events, 0);  // parameters -> spectrum: generator + spectrum
     float* reK = at<float>(ws, l.reK);
-    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndir * s->H, s->N, s->L, 0, reK,
-                                   st, KEvents{e0.start, nullptr}),
+    const int gen_out = cast == DSSM_CAST_RE_IM ? kGenReIm : kGenRe;
+    if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndir * s->H, s->N, s->L, gen_out,
+                                   reK, st, KEvents{e0.start, nullptr}),
                         "gen launch")))
       return rc;
     if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st,
@@ -263,6 +290,11 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
 int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
                      void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
+}
+
+int dssm_forward_fft_cast(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                          int cast, float* y, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, ws_bytes, stream, nullptr, 0, cast);
 }
 
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,

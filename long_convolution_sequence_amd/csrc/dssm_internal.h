@@ -42,10 +42,12 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Kernel generation (eig_gen.hip)
 // ---------------------------------------------------------------------------
 // K[dh, j] = sum_n W[dh,n] lambda[dh,n]^j for j < L, from the parameters
-// directly (float64 powers, float32 matrix-core contraction over the modes).
-// complex_out = 0: Re K into float [ndh, L]; 1: (Re, Im) into float2 [ndh, L].
+// directly (float64 powers, split-fp16 matrix-core contraction over the modes).
+// out = kGenRe: Re K into float [ndh, L]; kGenComplex: (Re, Im) into float2
+// [ndh, L]; kGenReIm: Re K * Im K into float [ndh, L].
+constexpr int kGenRe = 0, kGenComplex = 1, kGenReIm = 2;
 hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, int ndh, int N,
-                      int L, int complex_out, float* K, hipStream_t st, KEvents ev = {});
+                      int L, int out, float* K, hipStream_t st, KEvents ev = {});
 
 // ---------------------------------------------------------------------------
 // FFT convolution (fft.hip)

@@ -52,7 +52,9 @@ __device__ __forceinline__ double2 zpow(double2 x, int e) {
   return a;
 }
 
-template <bool kComplex>
+// Output kOut: 0 = Re K, 1 = K (re, im), 2 = Re K Im K (the DLR-prod cast of
+// the DLR page, section 2.1).
+template <int kOut>
 __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ log_re,
                                                      const float* __restrict__ log_im,
                                                      const float2* __restrict__ W, int N, int L,
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
   const int dh = blockIdx.y;
   const int Q = (L + kAnchor - 1) / kAnchor;
   const int q0 = blockIdx.x * kQW;
+  constexpr bool kComplex = kOut != 0;  // the imaginary part is formed too
 
   f4 tot[4], toti[4];
 #pragma unroll
@@ -166,7 +169,13 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
   // tot[rt][v]: r = 16 rt + 4 g + v, q = q0 + 16 w + lane % 16; j = 64 q + r.
   // Positions at or beyond L fall outside the buffer range and are dropped.
   const int q = q0 + 16 * w + (lane & 15);
-  if (kComplex) {
+  if (kOut == 2) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tot[rt][v] *= toti[rt][v];
+  }
+  if (kOut == 1) {
     const BufRes kb = buf_res(K + (size_t)dh * L * 2, 8u * (unsigned)L);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -198,14 +207,16 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
 }  // namespace
 
 hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, int ndh, int N,
-                      int L, int complex_out, float* K, hipStream_t st, KEvents ev) {
+                      int L, int out, float* K, hipStream_t st, KEvents ev) {
   const int Q = (L + kAnchor - 1) / kAnchor;
   const dim3 grid((unsigned)((Q + kQW - 1) / kQW), (unsigned)ndh);
   const float2* w2 = reinterpret_cast<const float2*>(W);
-  if (complex_out)
-    launch_k(gen_kernel<true>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
+  if (out == kGenComplex)
+    launch_k(gen_kernel<1>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
+  else if (out == kGenReIm)
+    launch_k(gen_kernel<2>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
   else
-    launch_k(gen_kernel<false>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
+    launch_k(gen_kernel<0>, grid, dim3(256), st, ev, log_re, log_im, w2, N, L, K);
   return hipGetLastError();
 }
 

@@ -244,3 +244,42 @@ def test_step_rejects_bad_arguments():
     assert call(_params({"D": None}), good) == bd.DSSM_ERR_INVALID_ARG
     assert call(_params({"W": FAKE + 4}), good) == bd.DSSM_ERR_INVALID_ARG
     assert call(None, bd.Shape(0, 3, 4, 1, 0)) == 0
+
+
+def _call_cast(cast, shape, params=None, u=FAKE * 2, y=FAKE * 3, ws=FAKE * 4, nbytes=1 << 40):
+    p = _params() if params is None else params
+    return bd.lib().dssm_forward_fft_cast(u, ctypes.byref(p), ctypes.byref(shape), cast, y, ws,
+                                          nbytes, None)
+
+
+def test_fft_cast_validation():
+    good = bd.Shape(2, 3, 4, 32, 0)
+    for bad in (-1, 2, 7):
+        assert _call_cast(bad, good) == bd.DSSM_ERR_INVALID_ARG
+        assert b"cast" in bd.lib().dssm_last_error()
+    # the checks of dssm_forward_fft apply to both casts
+    for cast in (bd.CAST_RE, bd.CAST_RE_IM):
+        assert _call_cast(cast, good, u=None) == bd.DSSM_ERR_INVALID_ARG
+        assert _call_cast(cast, good, u=FAKE * 2, y=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG
+        assert _call_cast(cast, good, nbytes=16) == bd.DSSM_ERR_WORKSPACE
+        assert _call_cast(cast, good, params=_params({"W": None})) == bd.DSSM_ERR_INVALID_ARG
+        assert _call_cast(cast, bd.Shape(1, 1, 4, 16385, 0)) == bd.DSSM_ERR_UNSUPPORTED
+        assert _call_cast(cast, bd.Shape(0, 3, 4, 32, 0)) == 0  # empty: a no-op
+
+
+def test_gen_cast_validation():
+    L = bd.lib()
+    good = bd.Shape(1, 3, 4, 32, 0)
+    p = _params()
+    for bad in (-1, 2):
+        assert L.dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(good), bad, FAKE * 3, None, 0,
+                                      None) == bd.DSSM_ERR_INVALID_ARG
+    for cast in (bd.CAST_RE, bd.CAST_RE_IM):
+        assert L.dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(good), cast, None, None, 0,
+                                      None) == bd.DSSM_ERR_INVALID_ARG
+        assert L.dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(good), cast, FAKE * 3 + 4,
+                                      None, 0, None) == bd.DSSM_ERR_INVALID_ARG
+        assert L.dssm_gen_kernel_cast(None, ctypes.byref(good), cast, FAKE * 3, None, 0,
+                                      None) == bd.DSSM_ERR_INVALID_ARG
+        assert L.dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(bd.Shape(1, 3, 4, 0, 0)), cast,
+                                      None, None, 0, None) == 0
