@@ -16,6 +16,9 @@ pages define, in float64, from the float32 input values promoted exactly:
   bidirectional sum; computed twice, as an O(L^2) direct sum
   and as a sequential recurrence; and the recurrence continued from a given
   state (streaming / one-token decode), returning the state it ends in.
+* ``dlr_grad`` -- the gradients of that layer map at an output cotangent
+  (du, d log_re, d log_im, dW, dD), from the chain rule on the same
+  definitions.
 * ``s5``   -- the multi-input multi-output diagonal SSM of "Simplified State
   Space Layers for Sequence Modeling", section 3, computed as a sequential
   recurrence and as a direct causal sum over a prefix.
@@ -33,4 +36,5 @@ from .dlr import (  # noqa: F401
     dlr_recurrence,
     dlr_recurrence_state,
 )
+from .dlr_grad import dlr_backward  # noqa: F401
 from .s5 import s5_recurrence, s5_direct_prefix  # noqa: F401
