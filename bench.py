@@ -151,6 +151,43 @@ def time_s5(steps, warmup, hip):
     }
 
 
+def time_backward(dev, us, ys, bi, steps, warmup):
+    """Timed gradient passes (dssm_backward) of the layer on the bench workload,
+    with a seeded output cotangent; wall clock between two synchronisations."""
+    import torch
+    from long_convolution_sequence_amd import binding as bd
+
+    R = len(us)
+    B, H, L = us[0].shape
+    N = dev["log_re"].shape[-1]
+    dy = torch.randn(B, H, L, generator=torch.Generator().manual_seed(7)).cuda()
+    shape = bd.Shape(B, H, N, L, int(bool(bi)))
+    need = ctypes_size(bd, bd.OP_BWD, shape)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for k in range(warmup):
+        bd.backward(us[k % R], dy, dev["log_re"], dev["log_im"], dev["W"], dev["D"],
+                    bidirectional=bi, du=ys[k % R], workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        bd.backward(us[k % R], dy, dev["log_re"], dev["log_im"], dev["W"], dev["D"],
+                    bidirectional=bi, du=ys[k % R], workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    elems = B * H * L
+    return {"ms_per_step": ms, "elements_per_s": elems / (ms * 1e-3), "workspace_bytes": need,
+            "note": "du and the four parameter gradients for f = sum(dy y); kernels: generator, "
+                    "conjugate spectrum + convolution for du, per-row spectra + convolutions for "
+                    "the lagged correlations, parameter reductions"}
+
+
+def ctypes_size(bd, op, shape):
+    import ctypes
+    out = ctypes.c_size_t(0)
+    bd.check(bd.lib().dssm_workspace_size(op, ctypes.byref(shape), ctypes.byref(out)))
+    return max(out.value, 256)
+
+
 def time_copy(src, dst, reps, hip):
     """A plain device copy of `src` into `dst` (torch's copy kernel): the
     practically attainable HBM rate, and the calibration kernel of known size
@@ -320,6 +357,7 @@ def main():
             "rotated_sets": a.rotate,
             "device_copy": copy,
             "s5_path": time_s5(max(2, a.scan_steps), 2, hip),
+            "backward": time_backward(dev, us, ys, bi, max(2, a.scan_steps), 2),
         },
     }
     if not a.no_cpu_baseline:

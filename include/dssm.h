@@ -61,7 +61,8 @@ typedef enum {
 typedef enum {
   DSSM_OP_GEN = 0,   /* dssm_gen_kernel */
   DSSM_OP_FFT = 1,   /* dssm_forward_fft */
-  DSSM_OP_SCAN = 2   /* dssm_forward_scan */
+  DSSM_OP_SCAN = 2,  /* dssm_forward_scan */
+  DSSM_OP_BWD = 3    /* dssm_backward */
 } dssm_op;
 
 /* How the complex kernel K is cast to the real kernel the convolution applies
@@ -89,6 +90,17 @@ typedef struct {
   const float* W;
   const float* D;
 } dssm_dlr_params;
+
+/* Gradients of the DLR parameters (device pointers, float32, 16-byte
+ * aligned), laid out as the parameters of dssm_dlr_params:
+ *   dlog_re [ndir, H, N], dlog_im [ndir, H, N], dW [ndir, H, N, 2]
+ *   (d f / d Re W, d f / d Im W), dD [ndir, H]. */
+typedef struct {
+  float* dlog_re;
+  float* dlog_im;
+  float* dW;
+  float* dD;
+} dssm_dlr_grads;
 
 /* Library version (DSSM_VERSION of the build). */
 int dssm_version(void);
@@ -148,6 +160,29 @@ int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape*
  * lambda_n lambda_m. */
 int dssm_forward_fft_cast(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                           int cast, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradients of the layer map (the map of dssm_forward_fft / dssm_forward_scan,
+ * which is the same map) for the scalar f = sum(dy * y): the input gradient
+ * du [B, H, L] and the parameter gradients g (DLR page, section 2: K_j =
+ * sum_n W_n lambda_n^j, lambda = exp(-log_re^2 + i log_im), dK_j / dlambda =
+ * j W lambda^(j-1)).  With the kernel cotangents
+ *   G_f[h,j] = sum_{b,k} dy[b,h,k] u[b,h,k-j],  G_b[h,j] = sum_{b,k} dy[b,h,k] u[b,h,k+j]:
+ *   du     = the transposed layer operator applied to dy (the convolution with
+ *            the conjugate spectrum: correlation with Re K_f, convolution with
+ *            Re K_b, plus (D_f + D_b) dy);
+ *   dW     = sum_j G_j conj(lambda^j);   with Z = sum_j j G_j W lambda^j:
+ *   dlog_re = -2 log_re Re Z,  dlog_im = -Im Z;   dD_d = sum_{b,k} dy u.
+ * The cotangents are lagged correlations computed with the FFT convolution
+ * kernels (one transform per row of u and of dy); the sums over j run in
+ * float32 over 64-tap blocks combined with float64 powers lambda^(64 q).
+ * u, dy, du: [B, H, L] float32, 16-byte aligned; du must not alias u or dy.
+ * Workspace: dssm_workspace_size(DSSM_OP_BWD, s).  Requires L <= 16384 (as
+ * dssm_forward_fft) and B H <= 2^26.  With B = 0 or L = 0 the parameter
+ * gradients are set to zero (u, dy, du, ws unused); with H = 0 nothing is
+ * done. */
+int dssm_backward(const float* u, const float* dy, const dssm_dlr_params* p,
+                  const dssm_shape* s, float* du, const dssm_dlr_grads* g, void* ws,
+                  size_t ws_bytes, void* stream);
 
 /* Layer forward by the recurrence view: x_k = lambda x_{k-1} + u_k (x_{-1} = 0,
  * every mode driven by u), y_k = Re(sum_n W_n x_{k,n}) + D u_k; the backward

@@ -17,18 +17,23 @@ DSSM_ERR_UNSUPPORTED = -2
 DSSM_ERR_WORKSPACE = -3
 DSSM_ERR_HIP = -4
 
-OP_GEN, OP_FFT, OP_SCAN = 0, 1, 2
+OP_GEN, OP_FFT, OP_SCAN, OP_BWD = 0, 1, 2, 3
 CAST_RE, CAST_RE_IM = 0, 1  # Re K, or Re K * Im K (DLR-prod)
 
 # Every function the header declares (checked by the ABI tests).
 EXPORTS = [
     "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
     "dssm_gen_kernel", "dssm_gen_kernel_cast", "dssm_forward_fft", "dssm_forward_fft_cast",
-    "dssm_forward_scan",
+    "dssm_forward_scan", "dssm_backward",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
     "dssm_forward_scan_state", "dssm_step",
     "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed",
 ]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [("dlog_re", ctypes.c_void_p), ("dlog_im", ctypes.c_void_p),
+                ("dW", ctypes.c_void_p), ("dD", ctypes.c_void_p)]
 
 
 class Shape(ctypes.Structure):
@@ -83,6 +88,9 @@ def lib():
     L.dssm_gen_kernel_cast.restype = ctypes.c_int
     L.dssm_gen_kernel_cast.argtypes = [ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
                                        ctypes.c_int, vp, vp, sz, vp]
+    L.dssm_backward.restype = ctypes.c_int
+    L.dssm_backward.argtypes = [vp, vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp,
+                                ctypes.POINTER(Grads), vp, sz, vp]
     L.dssm_forward_fft_cast.restype = ctypes.c_int
     L.dssm_forward_fft_cast.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
                                         ctypes.c_int, vp, vp, sz, vp]
@@ -258,6 +266,38 @@ def forward_fft_cast(u, log_re, log_im, W, D, cast, bidirectional=False, y=None,
     (CAST_RE: as forward_fft; CAST_RE_IM: DLR-prod)."""
     return _forward(lib().dssm_forward_fft_cast, OP_FFT, u, log_re, log_im, W, D, bidirectional, y,
                     workspace, stream, cast=cast)
+
+
+def backward(u, dy, log_re, log_im, W, D, bidirectional=False, du=None, workspace=None,
+             stream=None):
+    """Gradients of f = sum(dy * y) for the layer map: returns du [B,H,L] f32
+    and a dict dlog_re, dlog_im [ndir,H,N] f32, dW [ndir,H,N] c64
+    (d/d Re W + i d/d Im W), dD [ndir,H] f32."""
+    torch = _torch()
+    uu = _dev_f32(u, "u")
+    gg = _dev_f32(dy, "dy")
+    if uu.dim() != 3 or gg.shape != uu.shape:
+        raise ValueError("u and dy must be [B, H, L] of the same shape")
+    B, H, L = uu.shape
+    ndir = 2 if bidirectional else 1
+    N = log_re.shape[-1]
+    shape = Shape(B, H, N, L, int(bool(bidirectional)))
+    p, keep = _params(log_re, log_im, W, D, ndir, H, N)
+    if du is None:
+        du = torch.empty_like(uu)
+    dd = _dev_f32(du, "du")
+    dev_ = uu.device
+    out = dict(dlog_re=torch.empty(ndir, H, N, device=dev_), dlog_im=torch.empty(ndir, H, N, device=dev_),
+               dW=torch.empty(ndir, H, N, dtype=torch.complex64, device=dev_),
+               dD=torch.empty(ndir, H, device=dev_))
+    g = Grads(out["dlog_re"].data_ptr(), out["dlog_im"].data_ptr(), out["dW"].data_ptr(),
+              out["dD"].data_ptr())
+    ws, nbytes = _workspace(OP_BWD, shape, workspace, dev_)
+    check(lib().dssm_backward(uu.data_ptr(), gg.data_ptr(), ctypes.byref(p), ctypes.byref(shape),
+                              dd.data_ptr(), ctypes.byref(g), ws.data_ptr(), nbytes,
+                              _stream(stream)))
+    del keep
+    return du, out
 
 
 def forward_scan(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace=None, stream=None):

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdssm.so")
-SOURCES = ["api.hip", "chunk.hip", "eig_gen.hip", "fft.hip", "scan.hip", "s5.hip"]
+SOURCES = ["api.hip", "chunk.hip", "eig_gen.hip", "fft.hip", "grad.hip", "scan.hip", "s5.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

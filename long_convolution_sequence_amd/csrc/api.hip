@@ -50,7 +50,7 @@ int check_shape(int op, const dssm_shape* s, bool* empty) {
   if (s->N < 1) return fail(DSSM_ERR_INVALID_ARG, "N must be >= 1 (got %d)", s->N);
   if (s->bidirectional != 0 && s->bidirectional != 1)
     return fail(DSSM_ERR_INVALID_ARG, "bidirectional must be 0 or 1 (got %d)", s->bidirectional);
-  if (op != DSSM_OP_GEN && op != DSSM_OP_FFT && op != DSSM_OP_SCAN)
+  if (op != DSSM_OP_GEN && op != DSSM_OP_FFT && op != DSSM_OP_SCAN && op != DSSM_OP_BWD)
     return fail(DSSM_ERR_INVALID_ARG, "unknown op %d", op);
   const int ndir = 1 + s->bidirectional;
   if (s->N > kMaxN) return fail(DSSM_ERR_UNSUPPORTED, "N=%d exceeds %d", s->N, kMaxN);
@@ -60,6 +60,11 @@ int check_shape(int op, const dssm_shape* s, bool* empty) {
   if (op == DSSM_OP_FFT && s->L > kMaxFFTL)
     return fail(DSSM_ERR_UNSUPPORTED, "FFT path needs L <= %d (got %d); use the scan path",
                 kMaxFFTL, s->L);
+  if (op == DSSM_OP_BWD && s->L > kMaxFFTL)
+    return fail(DSSM_ERR_UNSUPPORTED, "the backward pass needs L <= %d (got %d)", kMaxFFTL, s->L);
+  if (op == DSSM_OP_BWD && (long)s->B * s->H > (1L << 26))
+    return fail(DSSM_ERR_UNSUPPORTED, "B*H=%ld too large for the backward pass",
+                (long)s->B * s->H);
   if ((long)s->B * s->H * s->L > (1L << 40))
     return fail(DSSM_ERR_UNSUPPORTED, "B*H*L too large");
   const bool no_rows = (op == DSSM_OP_GEN) ? false : (s->B == 0);
@@ -87,7 +92,7 @@ bool use_chunk(const dssm_shape* s) {
 
 // Workspace layout, every region aligned to 256 bytes.
 struct Layout {
-  size_t reK = 0, spec = 0, consts = 0, carry = 0, total = 0;
+  size_t reK = 0, spec = 0, consts = 0, carry = 0, spec_rows = 0, corr = 0, parts = 0, total = 0;
 };
 
 Layout layout(int op, const dssm_shape* s) {
@@ -105,6 +110,19 @@ Layout layout(int op, const dssm_shape* s) {
     const size_t M = (size_t)1 << log2m;
     l.reK = take(ndh * L * sizeof(float));
     l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
+  }
+  if (op == DSSM_OP_BWD) {
+    // the layer's (conjugate) spectrum for du, the spectra of the B H rows of u
+    // (or dy) and the lagged correlations of every row, per direction, then the
+    // partial parameter sums
+    const int log2m = fft_log2m(s->L);
+    const size_t M = (size_t)1 << log2m;
+    const size_t rows = (size_t)s->B * s->H;
+    l.reK = take(ndh * L * sizeof(float));
+    l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
+    l.spec_rows = take(rows * 2 * M * sizeof(float2));
+    l.corr = take((size_t)(1 + s->bidirectional) * rows * L * sizeof(float));
+    l.parts = take(ndh * (size_t)grad_splits(s->L) * N * 2 * 2 * sizeof(double));
   }
   if (op == DSSM_OP_SCAN) {
     const ScanPlan plan = scan_plan(s->B, s->L);
@@ -295,6 +313,69 @@ int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape*
 int dssm_forward_fft_cast(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                           int cast, float* y, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, ws_bytes, stream, nullptr, 0, cast);
+}
+
+int dssm_backward(const float* u, const float* dy, const dssm_dlr_params* p, const dssm_shape* s,
+                  float* du, const dssm_dlr_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_BWD, s, &empty);
+  if (rc) return rc;
+  if (s->H == 0) return ok();
+  if ((rc = check_params(p, true))) return rc;
+  if (!g) return fail(DSSM_ERR_INVALID_ARG, "grads is NULL");
+  if (!g->dlog_re || !g->dlog_im || !g->dW || !g->dD)
+    return fail(DSSM_ERR_INVALID_ARG, "a gradient pointer is NULL");
+  if (!aligned16(g->dlog_re) || !aligned16(g->dlog_im) || !aligned16(g->dW) || !aligned16(g->dD))
+    return fail(DSSM_ERR_INVALID_ARG, "gradient pointers must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ndir = 1 + s->bidirectional;
+  if (empty) {  // no rows or no steps: the parameter gradients are zero
+    if ((rc = hip_check(launch_zero_grads(g->dlog_re, g->dlog_im, g->dW, g->dD, ndir * s->H, s->N,
+                                          st),
+                        "zero launch")))
+      return rc;
+    return ok();
+  }
+  if (!u || !dy || !du || !aligned16(u) || !aligned16(dy) || !aligned16(du))
+    return fail(DSSM_ERR_INVALID_ARG, "u, dy or du is NULL or not 16-byte aligned");
+  if (du == u || du == dy) return fail(DSSM_ERR_INVALID_ARG, "du must not alias u or dy");
+  Layout l;
+  if ((rc = check_ws(DSSM_OP_BWD, s, ws, ws_bytes, &l))) return rc;
+  const int log2m = fft_log2m(s->L);
+  const int rows = s->B * s->H;
+  float* reK = at<float>(ws, l.reK);
+  float2* spec = at<float2>(ws, l.spec);
+  float2* spec_rows = at<float2>(ws, l.spec_rows);
+  float* corr = at<float>(ws, l.corr);
+  // du: the transposed operator, i.e. the layer's spectrum conjugated
+  if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndir * s->H, s->N, s->L, kGenRe, reK,
+                                 st),
+                      "gen launch")))
+    return rc;
+  if ((rc = hip_check(launch_spectrum(reK, p->D, ndir, s->H, s->L, log2m, spec, st, {}, 1),
+                      "spectrum launch")))
+    return rc;
+  if ((rc = hip_check(launch_conv(dy, spec, s->B, s->H, s->L, log2m, du, st), "conv launch")))
+    return rc;
+  // kernel cotangents: corr_f[b,h,j] = sum_i u[i] dy[i + j] (every row its own
+  // correlation: u's conjugate spectrum applied to dy); corr_b swaps u and dy
+  for (int d = 0; d < ndir; ++d) {
+    const float* kern = d == 0 ? u : dy;
+    const float* x = d == 0 ? dy : u;
+    float* out = corr + (size_t)d * rows * s->L;
+    if ((rc = hip_check(launch_spectrum(kern, nullptr, 1, rows, s->L, log2m, spec_rows, st, {}, 1),
+                        "row spectrum launch")))
+      return rc;
+    if ((rc = hip_check(launch_conv(x, spec_rows, 1, rows, s->L, log2m, out, st),
+                        "row correlation launch")))
+      return rc;
+  }
+  if ((rc = hip_check(launch_grad_params(corr, s->B, s->H, s->L, p->log_re, p->log_im, p->W, s->N,
+                                         ndir, at<void>(ws, l.parts), g->dlog_re, g->dlog_im,
+                                         g->dW, g->dD, st),
+                      "gradient launch")))
+    return rc;
+  return ok();
 }
 
 int dssm_forward_scan(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,

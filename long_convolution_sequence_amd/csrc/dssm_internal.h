@@ -57,9 +57,10 @@ hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, 
 // position 16 t + r is stored at r M/16 + t), scaled by 1/(2M).  half 0 holds
 // the even bins of the 2M-point transform of the zero-padded real kernel,
 // half 1 the odd bins.  For ndir = 2 the backward kernel enters conjugated.
-// sum_d D[d,h] is added to every bin (the feed-through as tap 0).
+// sum_d D[d,h] is added to every bin (the feed-through as tap 0); D may be
+// NULL.  conj != 0 writes the conjugate table (the transposed operator).
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
-                           float2* spec, hipStream_t st, KEvents ev = {});
+                           float2* spec, hipStream_t st, KEvents ev = {}, int conj = 0);
 
 // y[b,h,:L] = first L samples of the 2M-circular convolution of u[b,h,:] with
 // the kernel whose spectrum is spec[h] (D u included through tap 0).
@@ -67,6 +68,20 @@ hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, 
                        hipStream_t st, KEvents ev = {});
 
 int fft_log2m(int L);  // log2 of M = max(16, next power of two >= L)
+
+// ---------------------------------------------------------------------------
+// Parameter gradients from kernel cotangents (grad.hip)
+// ---------------------------------------------------------------------------
+// corr [ndir][B][H][L]: per row, the lagged correlation whose batch sum is
+// d f / d Re K_d[h, j].  parts: grad_splits(L) * ndir * H * N * 2 double2.
+int grad_splits(int L);
+hipError_t launch_grad_params(const float* corr, int B, int H, int L, const float* log_re,
+                              const float* log_im, const float* W, int N, int ndir, void* parts,
+                              float* dlog_re, float* dlog_im, float* dW, float* dD,
+                              hipStream_t st);
+// The four gradient arrays of ndh = ndir H channels set to zero.
+hipError_t launch_zero_grads(float* dlog_re, float* dlog_im, float* dW, float* dD, int ndh, int N,
+                             hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Recurrence scan (scan.hip)

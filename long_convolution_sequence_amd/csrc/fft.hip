@@ -547,7 +547,7 @@ __device__ __forceinline__ int pos_of_freq(int k) {
 // convolution's transform (top bit of its last digit), and its twiddle is -w.
 template <int LOG2M>
 __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t, float deff,
-                                             float2* out) {
+                                             float sg, float2* out) {
   using C = Cfg<LOG2M - 1, 16>;
   using CM = Cfg<LOG2M, 16>;
   constexpr int M = CM::M, S = C::M;
@@ -571,8 +571,8 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
     const float2 o = make_float2(A.y + B.y, B.x - A.x);
     const float2 w = cmul(wt, g_twiddle[kr * (DSSM_TWN / M)]);
     const float2 wo = cmul(w, o);
-    out[(size_t)r * CM::T + t] = make_float2(e.x + wo.x + deff, e.y + wo.y);
-    out[(size_t)(r | RB) * CM::T + t] = make_float2(e.x - wo.x + deff, e.y - wo.y);
+    out[(size_t)r * CM::T + t] = make_float2(e.x + wo.x + deff, sg * (e.y + wo.y));
+    out[(size_t)(r | RB) * CM::T + t] = make_float2(e.x - wo.x + deff, sg * (e.y - wo.y));
   }
 }
 
@@ -584,6 +584,8 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
 // the constant D: adding it to every bin makes the convolution produce y + D u.
 // The backward DLR is a correlation with Re K_b, whose spectrum is the
 // conjugate (no wrap-around reaches the first L outputs on a 2M circle).
+// With conj != 0 the conjugate of the whole table is written (the transposed
+// operator, for gradients); D may be NULL (no feed-through).
 //
 // Both real sequences of a channel ride in ONE complex transform, and the two
 // real spectra are separated afterwards from the bins k and -k (the Hermitian
@@ -603,7 +605,7 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
 template <int LOG2M, bool PACK>
 __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spectrum_kernel(
     const float* __restrict__ reK, const float* __restrict__ D, int ndir, int H, int L,
-    float2* __restrict__ spec) {
+    float2* __restrict__ spec, int conj) {
   using C = Cfg<PACK ? LOG2M - 1 : LOG2M, 16>;  // the transform computed here
   using CM = Cfg<LOG2M, 16>;                     // the convolution's transform
   constexpr int M = CM::M, S = C::M;
@@ -657,7 +659,9 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
   if (!active) return;
 
   float deff = 0.f;
-  for (int d = 0; d < ndir; ++d) deff += D[(size_t)d * H + h];
+  if (D)
+    for (int d = 0; d < ndir; ++d) deff += D[(size_t)d * H + h];
+  const float sg = conj ? -1.f : 1.f;
   deff *= 1.0f / (2.0f * (float)M);
   float2* out = spec + ((size_t)h * 2 + half) * M;
   // Outputs of this thread: t = lt + T_S i (all the convolution's t), every r.
@@ -669,7 +673,7 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
     const int t = lt + C::T * i;
     const int kt = freq_of_pos<CM>(16 * t);
     if constexpr (PACK) {
-      pack_outputs<LOG2M>(lds, half, t, deff, out);
+      pack_outputs<LOG2M>(lds, half, t, deff, sg, out);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -679,7 +683,7 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
         const float2 B = lds[C::pad(pos_of_freq<C>(k2))];
         // (A + conj B) + i (conj A - B)
         out[(size_t)r * CM::T + t] =
-            make_float2(A.x + B.x + A.y + B.y + deff, A.y - B.y + A.x - B.x);
+            make_float2(A.x + B.x + A.y + B.y + deff, sg * (A.y - B.y + A.x - B.x));
       }
     }
   }
@@ -835,12 +839,12 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
 
 template <int LOG2M, bool PACK>
 hipError_t spectrum_launch2(const float* reK, const float* D, int ndir, int H, int L,
-                            float2* spec, hipStream_t st, KEvents ev) {
+                            float2* spec, hipStream_t st, KEvents ev, int conj) {
   using C = Cfg<PACK ? LOG2M - 1 : LOG2M, 16>;
   const int nprob = 2 * H;
   const int nblk = (nprob + C::G - 1) / C::G;
   launch_k(spectrum_kernel<LOG2M, PACK>, dim3(nblk), dim3(C::WG), st, ev, reK, D, ndir, H, L,
-           spec);
+           spec, conj);
   return hipGetLastError();
 }
 
@@ -848,11 +852,11 @@ hipError_t spectrum_launch2(const float* reK, const float* D, int ndir, int H, i
 // allows it; two directions pack forward and backward kernels.
 template <int LOG2M>
 hipError_t spectrum_launch(const float* reK, const float* D, int ndir, int H, int L, float2* spec,
-                           hipStream_t st, KEvents ev) {
+                           hipStream_t st, KEvents ev, int conj) {
   if constexpr (LOG2M >= 5) {
-    if (ndir == 1) return spectrum_launch2<LOG2M, true>(reK, D, ndir, H, L, spec, st, ev);
+    if (ndir == 1) return spectrum_launch2<LOG2M, true>(reK, D, ndir, H, L, spec, st, ev, conj);
   }
-  return spectrum_launch2<LOG2M, false>(reK, D, ndir, H, L, spec, st, ev);
+  return spectrum_launch2<LOG2M, false>(reK, D, ndir, H, L, spec, st, ev, conj);
 }
 
 template <int LOG2M>
@@ -877,11 +881,11 @@ int fft_log2m(int L) {
 
 
 hipError_t launch_spectrum(const float* reK, const float* D, int ndir, int H, int L, int log2m,
-                           float2* spec, hipStream_t st, KEvents ev) {
+                           float2* spec, hipStream_t st, KEvents ev, int conj) {
   switch (log2m) {
 #define X(n) \
   case n:    \
-    return spectrum_launch<n>(reK, D, ndir, H, L, spec, st, ev);
+    return spectrum_launch<n>(reK, D, ndir, H, L, spec, st, ev, conj);
     DSSM_FFT_CASES(X)
 #undef X
     default:

@@ -283,3 +283,38 @@ def test_gen_cast_validation():
                                       None) == bd.DSSM_ERR_INVALID_ARG
         assert L.dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(bd.Shape(1, 3, 4, 0, 0)), cast,
                                       None, None, 0, None) == 0
+
+
+def test_backward_validation():
+    L = bd.lib()
+    good = bd.Shape(2, 3, 4, 32, 0)
+    p = _params()
+    g = bd.Grads(FAKE * 5, FAKE * 5 + 4096, FAKE * 5 + 8192, FAKE * 5 + 16384)
+
+    def call(shape=good, params=p, grads=g, u=FAKE * 2, dy=FAKE * 6, du=FAKE * 3, ws=FAKE * 4,
+             nbytes=1 << 40):
+        return L.dssm_backward(u, dy, ctypes.byref(params) if params is not None else None,
+                               ctypes.byref(shape) if shape is not None else None, du,
+                               ctypes.byref(grads) if grads is not None else None, ws, nbytes,
+                               None)
+
+    assert call(shape=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(params=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(grads=None) == bd.DSSM_ERR_INVALID_ARG
+    for k in ("dlog_re", "dlog_im", "dW", "dD"):
+        bad = bd.Grads(g.dlog_re, g.dlog_im, g.dW, g.dD)
+        setattr(bad, k, None)
+        assert call(grads=bad) == bd.DSSM_ERR_INVALID_ARG
+        setattr(bad, k, getattr(g, k) + 4)
+        assert call(grads=bad) == bd.DSSM_ERR_INVALID_ARG
+    assert call(u=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(dy=FAKE * 6 + 8) == bd.DSSM_ERR_INVALID_ARG
+    assert call(du=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG  # du aliases u
+    assert call(du=FAKE * 6) == bd.DSSM_ERR_INVALID_ARG  # du aliases dy
+    assert call(nbytes=16) == bd.DSSM_ERR_WORKSPACE
+    assert call(shape=bd.Shape(1, 1, 4, 16385, 0)) == bd.DSSM_ERR_UNSUPPORTED
+    assert call(shape=bd.Shape(2, 0, 4, 32, 0)) == 0  # H = 0: nothing to do
+    rc, n = _ws(bd.OP_BWD, 4, 128, 64, 16384)
+    rc1, n1 = _ws(bd.OP_FFT, 4, 128, 64, 16384)
+    assert rc == 0 and rc1 == 0 and n > n1
+    assert _ws(bd.OP_BWD, 1, 1, 1, 16385)[0] == bd.DSSM_ERR_UNSUPPORTED
