@@ -194,6 +194,8 @@ EDGE = [
     # the chunked matrix-core scan serves N <= 64: both sides of that limit, a
     # length that leaves a partial chunk and a partial block, reversed too
     (2, 3, 64, 4159, 1), (2, 3, 65, 999, 1), (3, 2, 33, 63, 1),
+    # one direction, long transforms: several mode chunks, ragged lengths, one mode
+    (2, 2, 100, 6000, 0), (1, 2, 130, 4500, 0), (2, 3, 8, 4097, 0), (1, 2, 1, 16384, 0),
 ]
 
 
