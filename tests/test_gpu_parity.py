@@ -196,6 +196,8 @@ EDGE = [
     (2, 3, 64, 4159, 1), (2, 3, 65, 999, 1), (3, 2, 33, 63, 1),
     # one direction, long transforms: several mode chunks, ragged lengths, one mode
     (2, 2, 100, 6000, 0), (1, 2, 130, 4500, 0), (2, 3, 8, 4097, 0), (1, 2, 1, 16384, 0),
+    # more convolution workgroups (one per row pair) than the device holds at once
+    (6, 100, 8, 16384, 0), (1, 300, 8, 16384, 0),
 ]
 
 
