@@ -13,15 +13,19 @@
 //   Z_n  = W_n V1_n,  d f / d log_re = -2 log_re Re Z_n,  d f / d log_im = -Im Z_n,
 //   d f / d D = G[0]                      (sum over b and k of dy u).
 //
-// How: j = 64 q + r.  A workgroup takes one (direction, channel) and every
-// kSplit-th tile of 64 anchors q; it stages G for a tile in LDS (summing the
-// batch rows as it loads them) and the powers lambda^r (r < 64, float64 chains
-// rounded once) for a chunk of 64 modes; thread (mode n, part p) sums
-// s0 = sum_r G[q][r] lambda^r and s1 = sum_r r G[q][r] lambda^r over its anchors
-// q = p, p + 4, ... in float32, and accumulates V0 += mu^q s0 and
-// V1 += mu^q (64 q s0 + s1) in float64, with mu^q = lambda^(64 q) by float64
-// products.  The parts are combined in LDS and the kSplit partial sums of a
-// (direction, channel) by a second kernel, which also forms the gradients.
+// How: j = 64 q + r, so V0_n = sum_q mu_n^q S0[q][n] and
+// V1_n = sum_q mu_n^q (64 q S0[q][n] + S1[q][n]) with mu = lambda^64 and
+//   S0[q][n] = sum_r G[q][r] lambda_n^r,   S1[q][n] = sum_r r G[q][r] lambda_n^r:
+// two real products (Q x 64) x (64 x 2N) with the same right operand, run on
+// the matrix cores in float32 (v_mfma_f32_16x16x4_f32: exact products,
+// float32 sums, as a float32 dot product).  A workgroup takes one (direction,
+// channel) and a contiguous range of 16-anchor tiles; it stages G for them in
+// LDS (summing the batch rows as it loads them).  Wave w takes modes
+// 16 w .. 16 w + 15 of a chunk of 64: its right operands (Re and Im of
+// lambda^r, r < 64, float64 chains rounded once) stay in registers, and each
+// lane adds its four anchors' mu^q S terms into float64 sums (mu^q by float64
+// products).  The kSplit partial sums of a (direction, channel) are combined,
+// and the gradients formed, by a second kernel.
 #include <algorithm>
 
 #include "dssm_internal.h"
@@ -29,8 +33,23 @@
 namespace dssm {
 namespace {
 
-constexpr int kGM = 64;     // modes per chunk
-constexpr int kGTile = 64;  // anchors per LDS tile
+constexpr int kGM = 64;       // modes per chunk (4 waves x 16)
+constexpr int kQT = 16;       // anchors per matrix tile
+constexpr int kMaxTiles = 4;  // tiles per workgroup
+constexpr int kGS = kAnchor + 4;  // LDS row stride of G (floats)
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+// Raw buffer over `bytes` bytes at `base`: loads at or past the end read zero.
+__device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float buf_load(BufRes r, int voff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
 
 __device__ __forceinline__ double2 zmul(double2 a, double2 b) {
   return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
@@ -45,94 +64,136 @@ __device__ __forceinline__ double2 zpow(double2 x, long e) {
   return a;
 }
 
+__device__ __forceinline__ double shfl_xor_d(double v, int m) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(b & 0xffffffffLL), m), hi = __shfl_xor((int)(b >> 32), m);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Tiles of 16 anchors, and the workgroups (splits) sharing them, for length L.
+__host__ __device__ __forceinline__ int anchor_tiles(int L) {
+  const int Q = (L + kAnchor - 1) / kAnchor;
+  return (Q + kQT - 1) / kQT;
+}
+
 // Partial sums V0, V1 of (direction d, channel h, split s) for all modes:
 // parts[(((d * H + h) * S + s) * N + n) * 2 + {0, 1}].
+// Matrix layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, g = l / 16):
+// A[i][k = g], B[k = g][j = i], D[i][j]: lane j + 16 (i / 4), element i % 4.
+// Instruction ks (< 16) of a tile covers r = 16 g + ks on lane group g.
 __global__ __launch_bounds__(256) void grad_vander_kernel(
     const float* __restrict__ corr, int B, int H, int L, const float* __restrict__ log_re,
     const float* __restrict__ log_im, int N, int d, int S, double2* __restrict__ parts) {
-  __shared__ float G[kGTile][kAnchor];
-  __shared__ float2 P[kAnchor][kGM];
-  __shared__ double2 red[4][kGM][2];
-  const int t = threadIdx.x, n = t & 63, part = t >> 6;
+  __shared__ float G[kMaxTiles * kQT][kGS];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int j = lane & 15, g = lane >> 4;
   const int h = blockIdx.x / S, s = blockIdx.x % S;
-  const int Q = (L + kAnchor - 1) / kAnchor;
-  const int ntile = (Q + kGTile - 1) / kGTile;
+  const int ntile = anchor_tiles(L);
+  const int per = (ntile + S - 1) / S;
+  const int tile0 = s * per, tiles = max(0, min(per, ntile - tile0));
+
+  // stage G[q][r] = sum_b corr[b][h][64 q + r] for this split's anchors:
+  // thread t sums the floats t + 256 i (i < 16) of every row, the loads of
+  // four rows in flight together (raw buffers: offsets past the row's end
+  // read zero)
+  {
+    constexpr int kV = kMaxTiles * kQT * kAnchor / 256;  // floats per thread
+    static_assert(kV * 256 == kMaxTiles * kQT * kAnchor, "staging split");
+    const long j0 = (long)tile0 * kQT * kAnchor;
+    const int nval = (int)std::min<long>((long)tiles * kQT * kAnchor, std::max<long>(0, L - j0));
+    float acc[kV];
+#pragma unroll
+    for (int i = 0; i < kV; ++i) acc[i] = 0.f;
+    for (int b0 = 0; b0 < B; b0 += 4) {
+      float x[4][kV];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int b = b0 + bb;
+        const BufRes row = buf_res(corr + ((size_t)(b < B ? b : 0) * H + h) * L + j0,
+                                   b < B ? 4u * (unsigned)nval : 0u);
+#pragma unroll
+        for (int i = 0; i < kV; ++i) x[bb][i] = buf_load(row, 4 * (t + 256 * i));
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int i = 0; i < kV; ++i) acc[i] += x[bb][i];
+    }
+#pragma unroll
+    for (int i = 0; i < kV; ++i) {
+      const int e = t + 256 * i;
+      G[e / kAnchor][e % kAnchor] = acc[i];
+    }
+  }
+  __syncthreads();
 
   for (int n0 = 0; n0 < N; n0 += kGM) {
-    const int nn = min(kGM, N - n0);
-    // lambda of mode n (zero beyond N), its powers r = 16 part .. + 15 into P
+    const int n = n0 + 16 * w + j;  // this lane's mode (column)
     double2 lam = make_double2(0.0, 0.0);
-    if (n < nn) {
-      const size_t i = ((size_t)d * H + h) * N + n0 + n;
+    if (n < N) {
+      const size_t i = ((size_t)d * H + h) * N + n;
       const double re = (double)log_re[i];
       double sn, cs;
       sincos((double)log_im[i], &sn, &cs);
       const double m = exp(-re * re);
       lam = make_double2(m * cs, m * sn);
     }
-    __syncthreads();  // the previous chunk's P and G are read
+    // right operands: Re and Im of lambda^(16 g + ks), ks < 16
+    float bre[16], bim[16];
     {
-      double2 x = zpow(lam, 16 * part);
-      for (int r = 16 * part; r < 16 * part + 16; ++r) {
-        P[r][n] = make_float2((float)x.x, (float)x.y);
+      double2 x = zpow(lam, 16 * g);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        bre[ks] = (float)x.x;
+        bim[ks] = (float)x.y;
         x = zmul(x, lam);
       }
     }
     const double2 mu = zpow(lam, kAnchor);
-    const double2 mu4 = zpow(mu, 4);
-    const double2 muT = zpow(mu, (long)kGTile * S);  // from one of this workgroup's tiles to the next
-    double2 mq0 = zpow(mu, (long)kGTile * s + part);  // mu^q of this thread's first anchor
+    const double2 mu16 = zpow(mu, kQT);
+    // mu^q for this lane's first anchor row of the first tile: q = 16 tile0 + 4 g
+    double2 mq = zpow(mu, (long)kQT * tile0 + 4 * g);
     double2 v0 = make_double2(0.0, 0.0), v1 = v0;
-    for (int tile = s; tile < ntile; tile += S) {
-      __syncthreads();  // P written (first tile) / the previous tile's G read
-      // stage G[q][r] = sum_b corr[b][h][64 q + r] for the tile's anchors
-      for (int e = t; e < kGTile * kAnchor; e += 256) {
-        const long j = (long)tile * kGTile * kAnchor + e;
-        float g = 0.f;
-        if (j < L)
-          for (int b = 0; b < B; ++b) g += corr[((size_t)b * H + h) * L + j];
-        G[e / kAnchor][e % kAnchor] = g;
+    for (int tt = 0; tt < tiles; ++tt) {
+      f4 s0r = {0.f, 0.f, 0.f, 0.f}, s0i = s0r, s1r = s0r, s1i = s0r;
+      const float* grow = &G[tt * kQT + j][16 * g];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const float a = grow[ks];
+        const float ar = a * (float)(16 * g + ks);
+        s0r = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bre[ks], s0r, 0, 0, 0);
+        s0i = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bim[ks], s0i, 0, 0, 0);
+        s1r = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, bre[ks], s1r, 0, 0, 0);
+        s1i = __builtin_amdgcn_mfma_f32_16x16x4f32(ar, bim[ks], s1i, 0, 0, 0);
       }
-      __syncthreads();
-      double2 mq = mq0;
-      for (int qi = part; qi < kGTile; qi += 4) {
-        float2 s0 = make_float2(0.f, 0.f), s1 = s0;
-#pragma unroll 8
-        for (int r = 0; r < kAnchor; ++r) {
-          const float g = G[qi][r];
-          const float2 p = P[r][n];
-          const float gr = g * (float)r;
-          s0.x = fmaf(g, p.x, s0.x);
-          s0.y = fmaf(g, p.y, s0.y);
-          s1.x = fmaf(gr, p.x, s1.x);
-          s1.y = fmaf(gr, p.y, s1.y);
-        }
-        const double q64 = 64.0 * (double)((long)tile * kGTile + qi);
-        const double2 a0 = make_double2((double)s0.x, (double)s0.y);
-        const double2 a1 = make_double2(q64 * a0.x + (double)s1.x, q64 * a0.y + (double)s1.y);
-        const double2 t0 = zmul(mq, a0), t1 = zmul(mq, a1);
+      // rows 4 g + v of the tile: anchor q = 16 (tile0 + tt) + 4 g + v
+      double2 m = mq;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const double q64 = 64.0 * (double)(kQT * (tile0 + tt) + 4 * g + v);
+        const double2 a0 = make_double2((double)s0r[v], (double)s0i[v]);
+        const double2 a1 = make_double2(q64 * a0.x + (double)s1r[v], q64 * a0.y + (double)s1i[v]);
+        const double2 t0 = zmul(m, a0), t1 = zmul(m, a1);
         v0.x += t0.x;
         v0.y += t0.y;
         v1.x += t1.x;
         v1.y += t1.y;
-        mq = zmul(mq, mu4);
+        m = zmul(m, mu);
       }
-      mq0 = zmul(mq0, muT);
+      mq = zmul(mq, mu16);
     }
-    red[part][n][0] = v0;
-    red[part][n][1] = v1;
-    __syncthreads();
-    if (part == 0 && n < nn) {
-      double2 a = red[0][n][0], c = red[0][n][1];
-      for (int p2 = 1; p2 < 4; ++p2) {
-        a.x += red[p2][n][0].x;
-        a.y += red[p2][n][0].y;
-        c.x += red[p2][n][1].x;
-        c.y += red[p2][n][1].y;
-      }
-      double2* o = parts + ((((size_t)d * H + h) * S + s) * N + n0 + n) * 2;
-      o[0] = a;
-      o[1] = c;
+    // sum the four lane groups (anchor rows) of each mode
+#pragma unroll
+    for (int msk = 16; msk <= 32; msk <<= 1) {
+      v0.x += shfl_xor_d(v0.x, msk);
+      v0.y += shfl_xor_d(v0.y, msk);
+      v1.x += shfl_xor_d(v1.x, msk);
+      v1.y += shfl_xor_d(v1.y, msk);
+    }
+    if (g == 0 && n < N) {
+      double2* o = parts + ((((size_t)d * H + h) * S + s) * N + n) * 2;
+      o[0] = v0;
+      o[1] = v1;
     }
   }
 }
@@ -190,9 +251,8 @@ hipError_t launch_zero_grads(float* dlog_re, float* dlog_im, float* dW, float* d
 }
 
 int grad_splits(int L) {
-  const int Q = (L + kAnchor - 1) / kAnchor;
-  const int ntile = (Q + kGTile - 1) / kGTile;
-  return ntile < 4 ? ntile : 4;
+  const int ntile = anchor_tiles(L);
+  return std::max(1, (ntile + kMaxTiles - 1) / kMaxTiles);
 }
 
 hipError_t launch_grad_params(const float* corr, int B, int H, int L, const float* log_re,
