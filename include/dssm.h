@@ -172,9 +172,11 @@ int dssm_forward_fft_cast(const float* u, const dssm_dlr_params* p, const dssm_s
  *            Re K_b, plus (D_f + D_b) dy);
  *   dW     = sum_j G_j conj(lambda^j);   with Z = sum_j j G_j W lambda^j:
  *   dlog_re = -2 log_re Re Z,  dlog_im = -Im Z;   dD_d = sum_{b,k} dy u.
- * The cotangents are lagged correlations computed with the FFT convolution
- * kernels (one transform per row of u and of dy); the sums over j run in
- * float32 over 64-tap blocks combined with float64 powers lambda^(64 q).
+ * The cotangents are lagged correlations summed over the batch in the
+ * frequency domain (one transform per pair (u_b, dy_b) and half of the 2L
+ * circle, one inverse per channel and half, both directions from the same
+ * inverse); the sums over j run on float32 matrix products over 64-tap
+ * blocks combined with float64 powers lambda^(64 q).
  * u, dy, du: [B, H, L] float32, 16-byte aligned; du must not alias u or dy.
  * Workspace: dssm_workspace_size(DSSM_OP_BWD, s).  Requires L <= 16384 (as
  * dssm_forward_fft) and B H <= 2^26.  With B = 0 or L = 0 the parameter

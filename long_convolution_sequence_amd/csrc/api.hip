@@ -92,7 +92,7 @@ bool use_chunk(const dssm_shape* s) {
 
 // Workspace layout, every region aligned to 256 bytes.
 struct Layout {
-  size_t reK = 0, spec = 0, consts = 0, carry = 0, spec_rows = 0, corr = 0, parts = 0, total = 0;
+  size_t reK = 0, spec = 0, consts = 0, carry = 0, corr = 0, parts = 0, total = 0;
 };
 
 Layout layout(int op, const dssm_shape* s) {
@@ -112,16 +112,13 @@ Layout layout(int op, const dssm_shape* s) {
     l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
   }
   if (op == DSSM_OP_BWD) {
-    // the layer's (conjugate) spectrum for du, the spectra of the B H rows of u
-    // (or dy) and the lagged correlations of every row, per direction, then the
-    // partial parameter sums
+    // the layer's (conjugate) spectrum for du, the two halves of the
+    // batch-summed lagged correlations, then the partial parameter sums
     const int log2m = fft_log2m(s->L);
     const size_t M = (size_t)1 << log2m;
-    const size_t rows = (size_t)s->B * s->H;
     l.reK = take(ndh * L * sizeof(float));
     l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
-    l.spec_rows = take(rows * 2 * M * sizeof(float2));
-    l.corr = take((size_t)(1 + s->bidirectional) * rows * L * sizeof(float));
+    l.corr = take((size_t)s->H * 2 * M * sizeof(float));
     l.parts = take(ndh * (size_t)grad_splits(s->L) * N * 2 * 2 * sizeof(double));
   }
   if (op == DSSM_OP_SCAN) {
@@ -342,10 +339,8 @@ int dssm_backward(const float* u, const float* dy, const dssm_dlr_params* p, con
   Layout l;
   if ((rc = check_ws(DSSM_OP_BWD, s, ws, ws_bytes, &l))) return rc;
   const int log2m = fft_log2m(s->L);
-  const int rows = s->B * s->H;
   float* reK = at<float>(ws, l.reK);
   float2* spec = at<float2>(ws, l.spec);
-  float2* spec_rows = at<float2>(ws, l.spec_rows);
   float* corr = at<float>(ws, l.corr);
   // du: the transposed operator, i.e. the layer's spectrum conjugated
   if ((rc = hip_check(launch_gen(p->log_re, p->log_im, p->W, ndir * s->H, s->N, s->L, kGenRe, reK,
@@ -357,22 +352,13 @@ int dssm_backward(const float* u, const float* dy, const dssm_dlr_params* p, con
     return rc;
   if ((rc = hip_check(launch_conv(dy, spec, s->B, s->H, s->L, log2m, du, st), "conv launch")))
     return rc;
-  // kernel cotangents: corr_f[b,h,j] = sum_i u[i] dy[i + j] (every row its own
-  // correlation: u's conjugate spectrum applied to dy); corr_b swaps u and dy
-  for (int d = 0; d < ndir; ++d) {
-    const float* kern = d == 0 ? u : dy;
-    const float* x = d == 0 ? dy : u;
-    float* out = corr + (size_t)d * rows * s->L;
-    if ((rc = hip_check(launch_spectrum(kern, nullptr, 1, rows, s->L, log2m, spec_rows, st, {}, 1),
-                        "row spectrum launch")))
-      return rc;
-    if ((rc = hip_check(launch_conv(x, spec_rows, 1, rows, s->L, log2m, out, st),
-                        "row correlation launch")))
-      return rc;
-  }
-  if ((rc = hip_check(launch_grad_params(corr, s->B, s->H, s->L, p->log_re, p->log_im, p->W, s->N,
-                                         ndir, at<void>(ws, l.parts), g->dlog_re, g->dlog_im,
-                                         g->dW, g->dD, st),
+  // kernel cotangents of both directions: the lagged correlations of u and
+  // dy, summed over the batch in the frequency domain
+  if ((rc = hip_check(launch_corr(u, dy, s->B, s->H, s->L, log2m, corr, st), "corr launch")))
+    return rc;
+  if ((rc = hip_check(launch_grad_params(corr, 1 << log2m, s->H, s->L, p->log_re, p->log_im, p->W,
+                                         s->N, ndir, at<void>(ws, l.parts), g->dlog_re,
+                                         g->dlog_im, g->dW, g->dD, st),
                       "gradient launch")))
     return rc;
   return ok();

@@ -837,6 +837,103 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
                    active, lt, lds_all + gi * C::LDSN, tab, y, [] {});
 }
 
+// Kernel cotangents of the gradients: the lagged correlations of the row
+// pairs (u_b, dy_b) of channel h, summed over the batch in the frequency
+// domain, on one half of the 2M circle ("Simplifying and Understanding State
+// Space Models with Diagonal Linear RNNs", section 2: the convolution view;
+// the correlation is the transposed Toeplitz product).  With
+// C(m) = sum_b DY_b(m) conj U_b(m) and c = IDFT_2M(C):
+//   G_f[j] = sum_b sum_i u_b[i] dy_b[i + j] = c[j],
+//   G_b[j] = sum_b sum_i dy_b[i] u_b[i + j] = c[2M - j]   (0 <= j < L).
+// One workgroup per (channel, half): for each b it transforms
+// z = u_b + i dy_b (even bins: z; odd bins: z t, t[n] = exp(-i pi n / M)),
+// meets each bin Z[m] with Z[-m] in LDS and adds
+//   DY conj U = Im(Z[m] Z[-m]) / 2 - i (|Z[m]|^2 - |Z[-m]|^2) / 4
+// (with the inverse's 1/2M) to its registers; after the batch it inverts its
+// half and stores part[h][half][n] (n < M): the real part of the half's
+// inverse, the odd half multiplied by conj t[n] first.  Then
+//   c[n] = part[h][0][n] + part[h][1][n],  c[n + M] = part[h][0][n] - part[h][1][n].
+template <int LOG2M>
+__global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void corr_kernel(
+    const float* __restrict__ u, const float* __restrict__ dy, int B, int H, int L,
+    float* __restrict__ part) {
+  using C = Cfg<LOG2M, 16>;
+  constexpr int M = C::M;
+  __shared__ float2 lds_all[C::G * C::LDSN];
+  __shared__ float2 tab[TwTab<C>::kAlloc];
+  twtab_init<C>(tab);  // published by the first barrier
+  const int lt = threadIdx.x % C::T;
+  const int gi = threadIdx.x / C::T;
+  float2* lds = lds_all + gi * C::LDSN;
+  // the two halves of a channel, which read the same rows, share an XCD
+  const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
+  const bool active = prob < 2 * H;
+  const int h = active ? (prob >> 1) : 0;
+  const int half = prob & 1;
+  const int kt = freq_of_pos<C>(C::PT * lt);  // bins of this thread: kt | freq_of_pos(r)
+  const float c1 = 0.25f / (float)M, c2 = 0.125f / (float)M;
+
+  float2 acc[C::PT];
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) acc[r] = make_float2(0.f, 0.f);
+  for (int b = 0; b < B; ++b) {
+    float2 v[C::PT];
+    {
+      const BufRes ur = buf_res(u + ((size_t)b * H + h) * L, active ? 4u * L : 0u);
+      const BufRes dr = buf_res(dy + ((size_t)b * H + h) * L, active ? 4u * L : 0u);
+      const int lo = opaque(lt);
+#pragma unroll
+      for (int r = 0; r < C::PT; ++r) {
+        const int o = 4 * nat<C>(lo, r);
+        v[r] = make_float2(buf_load_f32(ur, o, 0), buf_load_f32(dr, o, 0));
+      }
+    }
+    if (half) {  // z t
+      const float2 tl = g_twiddle[lt * (DSSM_TWN / (2 * M))];
+      odd_twiddle_fixed<C, false>(v);
+#pragma unroll
+      for (int r = 0; r < C::PT; ++r) v[r] = cmul(v[r], tl);
+    }
+    forward1<C>(v, lds, lt, tab);
+    // bins to LDS at their positions, then each meets its mirror bin
+    wave_sync();
+    lds_write<C, C::NP - 1>(lds, lt, v);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) {
+      const int k = kt | freq_of_pos<C>(r);
+      const int k2 = half ? (M - 1 - k) : ((M - k) & (M - 1));
+      const float2 zm = lds[C::pad(pos_of_freq<C>(k2))];
+      const float2 z = v[r];
+      acc[r].x = fmaf(c1, fmaf(z.x, zm.y, z.y * zm.x), acc[r].x);
+      acc[r].y = fmaf(-c2, (fmaf(z.x, z.x, z.y * z.y) - fmaf(zm.x, zm.x, zm.y * zm.y)), acc[r].y);
+    }
+    __syncthreads();  // mirror reads done before the next row's exchange
+  }
+  inv_head<C>(acc, lds, lt, tab);
+  inverse_finish<C>(acc, lds, lt);
+  const int lte = opaque(lt);
+  if (half) {  // conj t[n]
+    const float2 tlc = cconj(g_twiddle[lte * (DSSM_TWN / (2 * M))]);
+    odd_twiddle_fixed<C, true>(acc);
+#pragma unroll
+    for (int r = 0; r < C::PT; ++r) acc[r] = cmul(acc[r], tlc);
+  }
+  const BufRes pr = buf_res(part + ((size_t)h * 2 + half) * M, active ? 4u * M : 0u);
+#pragma unroll
+  for (int r = 0; r < C::PT; ++r) buf_store_f32(pr, 4 * nat<C>(lte, r), 0, acc[r].x);
+}
+
+template <int LOG2M>
+hipError_t corr_launch(const float* u, const float* dy, int B, int H, int L, float* part,
+                       hipStream_t st) {
+  using C = Cfg<LOG2M, 16>;
+  const int nprob = 2 * H;
+  const int nblk = (nprob + C::G - 1) / C::G;
+  launch_k(corr_kernel<LOG2M>, dim3(nblk), dim3(C::WG), st, KEvents{}, u, dy, B, H, L, part);
+  return hipGetLastError();
+}
+
 template <int LOG2M, bool PACK>
 hipError_t spectrum_launch2(const float* reK, const float* D, int ndir, int H, int L,
                             float2* spec, hipStream_t st, KEvents ev, int conj) {
@@ -899,6 +996,19 @@ hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, 
 #define X(n) \
   case n:    \
     return conv_launch<n>(u, spec, B, H, L, y, st, ev);
+    DSSM_FFT_CASES(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_corr(const float* u, const float* dy, int B, int H, int L, int log2m,
+                       float* part, hipStream_t st) {
+  switch (log2m) {
+#define X(n) \
+  case n:    \
+    return corr_launch<n>(u, dy, B, H, L, part, st);
     DSSM_FFT_CASES(X)
 #undef X
     default:

@@ -7,7 +7,9 @@
 // j W lambda^(j-1) in its vanishing-gradient paragraph): for the scalar
 // f = sum(dy y) and one direction d of channel h, with the kernel cotangent
 // G[j] = d f / d Re K_j (the lagged correlation of dy and u summed over the
-// batch, computed by the convolution kernels),
+// batch; the correlation kernel leaves its halves in part[h][2][M]:
+// G_f[j] = part[h][0][j] + part[h][1][j], and G_b[j] = part[h][0][M - j] -
+// part[h][1][M - j] for j >= 1, G_b[0] = G_f[0]),
 //   V0_n = sum_j G[j] lambda_n^j,   V1_n = sum_j j G[j] lambda_n^j,
 //   dW_n = conj(V0_n)                     (d f / d Re W + i d f / d Im W),
 //   Z_n  = W_n V1_n,  d f / d log_re = -2 log_re Re Z_n,  d f / d log_im = -Im Z_n,
@@ -82,7 +84,7 @@ __host__ __device__ __forceinline__ int anchor_tiles(int L) {
 // A[i][k = g], B[k = g][j = i], D[i][j]: lane j + 16 (i / 4), element i % 4.
 // Instruction ks (< 16) of a tile covers r = 16 g + ks on lane group g.
 __global__ __launch_bounds__(256) void grad_vander_kernel(
-    const float* __restrict__ corr, int B, int H, int L, const float* __restrict__ log_re,
+    const float* __restrict__ part, int M, int H, int L, const float* __restrict__ log_re,
     const float* __restrict__ log_im, int N, int d, int S, double2* __restrict__ parts) {
   __shared__ float G[kMaxTiles * kQT][kGS];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -92,37 +94,31 @@ __global__ __launch_bounds__(256) void grad_vander_kernel(
   const int per = (ntile + S - 1) / S;
   const int tile0 = s * per, tiles = max(0, min(per, ntile - tile0));
 
-  // stage G[q][r] = sum_b corr[b][h][64 q + r] for this split's anchors:
-  // thread t sums the floats t + 256 i (i < 16) of every row, the loads of
-  // four rows in flight together (raw buffers: offsets past the row's end
-  // read zero)
+  // stage G[q][r] = G_d[64 q + r] for this split's anchors from the two
+  // correlation halves (raw buffers: offsets outside them read zero; the
+  // backward direction reads them mirrored, M - j)
   {
     constexpr int kV = kMaxTiles * kQT * kAnchor / 256;  // floats per thread
     static_assert(kV * 256 == kMaxTiles * kQT * kAnchor, "staging split");
     const long j0 = (long)tile0 * kQT * kAnchor;
     const int nval = (int)std::min<long>((long)tiles * kQT * kAnchor, std::max<long>(0, L - j0));
-    float acc[kV];
+    const BufRes pe = buf_res(part + (size_t)h * 2 * M, 4u * (unsigned)M);
+    const BufRes po = buf_res(part + ((size_t)h * 2 + 1) * M, 4u * (unsigned)M);
+    float x[2][kV];
 #pragma unroll
-    for (int i = 0; i < kV; ++i) acc[i] = 0.f;
-    for (int b0 = 0; b0 < B; b0 += 4) {
-      float x[4][kV];
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int b = b0 + bb;
-        const BufRes row = buf_res(corr + ((size_t)(b < B ? b : 0) * H + h) * L + j0,
-                                   b < B ? 4u * (unsigned)nval : 0u);
-#pragma unroll
-        for (int i = 0; i < kV; ++i) x[bb][i] = buf_load(row, 4 * (t + 256 * i));
-      }
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-        for (int i = 0; i < kV; ++i) acc[i] += x[bb][i];
+    for (int i = 0; i < kV; ++i) {
+      const int e = t + 256 * i;
+      const int jj = (int)j0 + e;
+      // past the split's range: an offset beyond the halves (reads zero)
+      const int src = e >= nval ? M : (d == 0 || jj == 0 ? jj : M - jj);
+      x[0][i] = buf_load(pe, 4 * src);
+      x[1][i] = buf_load(po, 4 * src);
     }
 #pragma unroll
     for (int i = 0; i < kV; ++i) {
       const int e = t + 256 * i;
-      G[e / kAnchor][e % kAnchor] = acc[i];
+      const int jj = (int)j0 + e;
+      G[e / kAnchor][e % kAnchor] = (d == 0 || jj == 0) ? x[0][i] + x[1][i] : x[0][i] - x[1][i];
     }
   }
   __syncthreads();
@@ -203,7 +199,7 @@ __global__ __launch_bounds__(256) void grad_vander_kernel(
 __global__ __launch_bounds__(256) void grad_combine_kernel(
     const double2* __restrict__ parts, int S, int ndir, int H, int N,
     const float* __restrict__ log_re, const float2* __restrict__ W,
-    const float* __restrict__ corr, int B, int L, float* __restrict__ dlog_re,
+    const float* __restrict__ part, int M, float* __restrict__ dlog_re,
     float* __restrict__ dlog_im, float2* __restrict__ dW, float* __restrict__ dD) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long total = (long)ndir * H * N;
@@ -223,12 +219,9 @@ __global__ __launch_bounds__(256) void grad_combine_kernel(
   dW[i] = make_float2((float)v0.x, (float)-v0.y);
   dlog_re[i] = (float)(-2.0 * (double)log_re[i] * z.x);
   dlog_im[i] = (float)(-z.y);
-  if (n == 0) {
-    const int d = (int)(dh / H), h = (int)(dh % H);
-    const float* c = corr + (size_t)d * B * H * L;
-    double g = 0.0;
-    for (int b = 0; b < B; ++b) g += (double)c[((size_t)b * H + h) * L];
-    dD[dh] = (float)g;
+  if (n == 0) {  // lag 0, the same for both directions
+    const int h = (int)(dh % H);
+    dD[dh] = part[(size_t)h * 2 * M] + part[((size_t)h * 2 + 1) * M];
   }
 }
 
@@ -255,19 +248,19 @@ int grad_splits(int L) {
   return std::max(1, (ntile + kMaxTiles - 1) / kMaxTiles);
 }
 
-hipError_t launch_grad_params(const float* corr, int B, int H, int L, const float* log_re,
+hipError_t launch_grad_params(const float* part, int M, int H, int L, const float* log_re,
                               const float* log_im, const float* W, int N, int ndir, void* parts,
                               float* dlog_re, float* dlog_im, float* dW, float* dD,
                               hipStream_t st) {
   const int S = grad_splits(L);
   double2* pp = static_cast<double2*>(parts);
   for (int d = 0; d < ndir; ++d)
-    launch_k(grad_vander_kernel, dim3((unsigned)(H * S)), dim3(256), st, KEvents{},
-             corr + (size_t)d * B * H * L, B, H, L, log_re, log_im, N, d, S, pp);
+    launch_k(grad_vander_kernel, dim3((unsigned)(H * S)), dim3(256), st, KEvents{}, part, M, H, L,
+             log_re, log_im, N, d, S, pp);
   const long total = (long)ndir * H * N;
   launch_k(grad_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), st, KEvents{},
            static_cast<const double2*>(pp), S, ndir, H, N, log_re,
-           reinterpret_cast<const float2*>(W), corr, B, L, dlog_re, dlog_im,
+           reinterpret_cast<const float2*>(W), part, M, dlog_re, dlog_im,
            reinterpret_cast<float2*>(dW), dD);
   return hipGetLastError();
 }
