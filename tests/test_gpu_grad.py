@@ -43,6 +43,8 @@ def check(x, dy, bi, what, hs=None):
 SHAPES = [  # (B, H, N, L, bi)
     (2, 3, 8, 300, 0), (2, 3, 8, 300, 1), (3, 2, 64, 2000, 0), (2, 2, 64, 4097, 1),
     (1, 2, 100, 777, 1), (2, 3, 16, 17, 0), (3, 2, 8, 1, 1), (5, 2, 16, 16384, 0),
+    # many batch rows summed in the frequency domain, both directions, ragged L
+    (9, 2, 16, 5000, 1), (4, 300, 8, 1024, 1),
 ]
 
 
