@@ -12,9 +12,10 @@ does not hold the step's inputs from an earlier step.
 Prints ONE JSON line: value = elements (B*H*L) per second over the timed
 steps (wall clock between two device synchronisations), the per-kernel
 durations from the start/stop HIP events the GPU stamps around each kernel, the
-roofline of the dominant kernel (the convolution) on algorithmic bytes
-(u read + y write = 8 bytes per element), and the float64 oracle timed on
-the host as the CPU baseline.
+roofline of the dominant kernel (the convolution: bound by the vector ALU,
+on its algorithmic flops, with its HBM rate on algorithmic bytes, u read + y
+write = 8 bytes per element, beside it), and the float64 oracle timed on the
+host as the CPU baseline.
 """
 import argparse
 import json
@@ -27,6 +28,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# FP32 vector peak without packed FP32 (disabled in this build): 256 CUs x 4
+# SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz.  The published 157.3 TFLOP/s
+# counts packed FMAs (two per lane per clock).
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 METRIC = "SSM layer fwd elements/s (B·H·L) and achieved HBM GB/s vs peak, L=16384"
 WORKLOAD = "long_sequence"
 
@@ -316,13 +321,13 @@ def main():
 
     elems = B * H * L
     alg_bytes = 8 * elems  # u read + y write, float32
-    achieved = alg_bytes / (conv_ms * 1e-3) / 1e9
-    # convolution flops on the 2M = 32768 circle: 4 complex transforms of
-    # M = 16384 points per pair of rows, counted as 5 M log2 M each, plus the
-    # spectrum product (6 flops per bin) and the odd-bin twiddles
-    M = 1 << max(4, (L - 1).bit_length())
-    pairs = H * ((B + 1) // 2)
-    conv_flop = pairs * (4 * 5 * M * np.log2(M) + 2 * 6 * M + 4 * 6 * M)
+    hbm_gbs = alg_bytes / (conv_ms * 1e-3) / 1e9
+    # algorithmic flops of the convolution per (b, h) row: two real FFTs of
+    # n = 2L points (2 n log2 n - 4 n each), the spectrum product on L + 1
+    # bins (6 each) and the D skip (2 per element)
+    n = 2 * L
+    alg_flop = B * H * (2 * (2 * n * np.log2(n) - 4 * n) + 6 * (L + 1) + 2 * L)
+    tflops = alg_flop / (conv_ms * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": elems / (ms * 1e-3),
@@ -338,21 +343,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "B": B, "H": H, "N": N, "L": L,
                    "bidirectional": bool(bi), "path": "fft", "parallelism": "none"},
+        # The convolution is bound by the vector ALU (non-packed FP32): its
+        # VALU instructions alone take ~25 of its ~42 us, its algorithmic
+        # bytes 8.4 us at the HBM peak.  The HBM figures of the metric ride
+        # along (hbm_*).
         "roofline": {
-            "bound": "hbm",
+            "bound": "alu",
             "kernel": "conv_kernel<14> (FFT convolution)",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
+            "achieved": tflops,
+            "peak": ALU_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / ALU_PEAK_TFLOPS,
             "traffic": measured_traffic(),
+            "alg_flop_per_launch": alg_flop,
+            "frac_of_published_packed_fp32": tflops / 157.3,
+            "hbm_achieved_gbs": hbm_gbs,
+            "hbm_peak_gbs": HBM_PEAK_GBS,
+            "hbm_frac": hbm_gbs / HBM_PEAK_GBS,
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_ms": conv_ms,
         },
         "extra": {
             "stage_ms_breakdown": {"kernel_spectrum": stages[0], "conv": stages[1]},
             "full_call_hbm_gbs": alg_bytes / (ms * 1e-3) / 1e9,
-            "conv_fp32_tflops_est": conv_flop / (conv_ms * 1e-3) / 1e12,
             "scan_path": scan_path_summary(B, H, N, L, bi, ms_scan, scan_ms, stages_scan),
             "rotated_sets": a.rotate,
             "device_copy": copy,
