@@ -725,12 +725,11 @@ constexpr int conv_pt() { return 16; }
 // h by one workgroup (C::G problems per workgroup when a transform is
 // smaller than a wave).  Both halves of the 2M spectrum are transformed:
 // ve = z (even bins), vo = z t (odd bins), where z = u[b1] + i u[b2].
-// `ready()` is called by every thread before the spectrum is first read.
-template <int LOG2M, class Ready>
+template <int LOG2M>
 __device__ __forceinline__ void conv_body(const float* __restrict__ u,
                                           const float2* __restrict__ spec, int B, int H, int L,
                                           int h, int pr, bool active, int lt, float2* lds,
-                                          const float2* tab, float* __restrict__ y, Ready ready) {
+                                          const float2* tab, float* __restrict__ y) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   const int b1 = 2 * pr, b2 = 2 * pr + 1;
   const bool has2 = active && b2 < B;
@@ -782,7 +781,6 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
     lds_read<C, 1>(lds, lt, ve);
     fwd_tail<C, 1>(ve, lds, lt, tab);
   }
-  ready();
   load_spec(0, sv);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], sv[r]);
@@ -834,7 +832,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
   const bool active = prob < H * npairs;
   conv_body<LOG2M>(u, spec, B, H, L, active ? prob / npairs : 0, active ? prob % npairs : 0,
-                   active, lt, lds_all + gi * C::LDSN, tab, y, [] {});
+                   active, lt, lds_all + gi * C::LDSN, tab, y);
 }
 
 // Kernel cotangents of the gradients: the lagged correlations of the row
