@@ -132,6 +132,72 @@ __global__ __launch_bounds__(256) void s5_pack_kernel(const float2* __restrict__
   }
 }
 
+// The same fragments and exponents for K <= kPackLdsK, with one read of the
+// matrices: workgroup (row tile it, kind, k group g) stages the tile's 16
+// rows (all K) in LDS, takes each row's maximum there, and writes the
+// fragments of k steps kPackKS g .. + kPackKS - 1 (the row maxima are formed
+// redundantly by the k groups of a tile; the k group 0 writes the exponents).
+constexpr int kPackLdsK = 1024;
+constexpr int kPackKS = 2;  // k steps (of 32) per workgroup
+__global__ __launch_bounds__(256) void s5_pack_lds_kernel(const float2* __restrict__ Bbar,
+                                                          const float2* __restrict__ C, int H,
+                                                          int P, half8* __restrict__ apk_in,
+                                                          int* __restrict__ rexp_in,
+                                                          half8* __restrict__ apk_out,
+                                                          int* __restrict__ rexp_out) {
+  __shared__ float A[16][kPackLdsK + 4];
+  __shared__ float red[16][17];
+  __shared__ int rexp_s[16];
+  const int kind = blockIdx.y;
+  const int M = kind == 0 ? 2 * P : H;
+  const int K = kind == 0 ? H : 2 * P;
+  const int it = blockIdx.x, g = blockIdx.z;
+  const int KS = (K + 31) / 32;
+  if (16 * it >= M || kPackKS * g >= KS) return;  // the whole workgroup
+  const int KP = 32 * KS;  // staged row length (zero past K)
+  const int t = threadIdx.x;
+  // stage: thread (row t / 16, c = t % 16) takes columns c + 16 q, sixteen
+  // loads in flight per round
+  {
+    const int r = t >> 4, c = t & 15;
+    for (int q0 = 0; 16 * q0 < KP; q0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = a_elem(kind, Bbar, C, H, P, 16 * it + r, c + 16 * (q0 + q));
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (16 * (q0 + q) < KP) A[r][c + 16 * (q0 + q)] = v[q];
+    }
+  }
+  __syncthreads();
+  {
+    const int r = t & 15, part = t >> 4;
+    float m = 0.f;
+    for (int k = part; k < KP; k += 16) m = fmaxf(m, fabsf(A[r][k]));
+    red[r][part] = m;
+  }
+  __syncthreads();
+  if (t < 16) {
+    float mm = 0.f;
+    for (int q = 0; q < 16; ++q) mm = fmaxf(mm, red[t][q]);
+    rexp_s[t] = scale_exp(mm);
+    if (g == 0) (kind == 0 ? rexp_in : rexp_out)[16 * it + t] = rexp_s[t];
+  }
+  __syncthreads();
+  const int ks = kPackKS * g + (t >> 6);
+  if (t < 64 * kPackKS && ks < KS) {
+    const int l = t & 63, i = l & 15, k0 = 32 * ks + 8 * (l >> 4);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = A[i][k0 + e];
+    half8 hi, lo;
+    split8(v, hi, lo, rexp_s[i]);
+    half8* out = (kind == 0 ? apk_in : apk_out) + (size_t)it * KS * 2 * 64;
+    out[(size_t)(ks * 2) * 64 + l] = hi;
+    out[(size_t)(ks * 2 + 1) * 64 + l] = lo;
+  }
+}
+
 // out[b][i][j] = sum_k A[i][k] Bm[b][k][j]  (+ D[i] u[b][i][j] when kAddDu);
 // Bm [B][K][L] row-major, out [B][M][L].  Computed transposed, outT = Bm^T A^T,
 // so each lane's four results are consecutive time steps (16-byte stores).
@@ -668,6 +734,14 @@ S5Layout s5_layout(int B, int H, int P, int L) {
 hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, void* apk_in,
                           int* rexp_in, void* apk_out, int* rexp_out, hipStream_t st, KEvents ev) {
   const int tiles = (std::max(2 * P, H) + 15) / 16;
+  const int kmax = std::max(2 * P, H);  // the larger K of the two kinds
+  if (kmax <= kPackLdsK) {
+    const int groups = ((kmax + 31) / 32 + kPackKS - 1) / kPackKS;
+    launch_k(s5_pack_lds_kernel, dim3((unsigned)tiles, 2, (unsigned)groups), dim3(256), st, ev,
+             reinterpret_cast<const float2*>(Bbar), reinterpret_cast<const float2*>(C), H, P,
+             static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out);
+    return hipGetLastError();
+  }
   launch_k(s5_pack_kernel, dim3((unsigned)tiles, 2), dim3(256), st, ev,
            reinterpret_cast<const float2*>(Bbar), reinterpret_cast<const float2*>(C), H, P,
            static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out);

@@ -39,6 +39,8 @@ S5_EDGE = [
     # contractions over several 256-deep k chunks and several 256-row blocks,
     # ragged row counts inside a wave's 64 rows, ragged time tail
     (1, 600, 140, 3001), (2, 72, 300, 515),
+    # more than 1024 input channels: the fragments packed without LDS staging
+    (1, 1100, 8, 70),
 ]
 
 
