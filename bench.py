@@ -118,8 +118,11 @@ def time_path(path, dev, us, ys, ws, steps, warmup, bi, hip, breakdown_steps=20)
     return (t1 - t0) * 1e3 / steps, dom, stages
 
 
-def time_s5(steps, warmup, hip):
-    """Timed S5 layer forwards on the S5 workload (B=4, H=256, P=128, L=16384)."""
+def time_s5(steps, warmup, hip, rotate=5, breakdown_steps=10):
+    """Timed S5 layer forwards on the S5 workload (B=4, H=256, P=128, L=16384):
+    plain calls over `rotate` input/output sets (5 x 2 x 67 MB, beyond the
+    256 MB MALL) for the wall clock, then `breakdown_steps` more with each of
+    the four kernels stamped by GPU events for the per-kernel times."""
     import numpy as np
     import torch
     from long_convolution_sequence_amd import binding as bd
@@ -128,19 +131,28 @@ def time_s5(steps, warmup, hip):
     c = inputs.config("s5_mimo")
     x = inputs.inputs_for(c)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
-    y = torch.empty_like(t["u"])
+    us = [t["u"]] + [t["u"].clone() for _ in range(rotate - 1)]
+    ys = [torch.empty_like(t["u"]) for _ in range(rotate)]
     ws = torch.empty(bd.s5_workspace_size(c["B"], c["H"], c["P"], c["L"]), dtype=torch.uint8,
                      device="cuda")
-    for _ in range(warmup):
-        bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], y=y, workspace=ws)
-    evs = [hip.create(8) for _ in range(steps)]
+
+    def call(k, evs=None):
+        bd.s5_forward(us[k % rotate], t["lam"], t["Bbar"], t["C"], t["D"], y=ys[k % rotate],
+                      workspace=ws, events=evs)
+
+    for k in range(warmup):
+        call(k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], y=y, workspace=ws, events=evs[k])
+        call(k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    st = [sum(hip.ms(e[2 * i], e[2 * i + 1]) for e in evs) / steps for i in range(4)]
+    evs = [hip.create(8) for _ in range(breakdown_steps)]
+    for k in range(breakdown_steps):
+        call(k, evs[k])
+    torch.cuda.synchronize()
+    st = [sum(hip.ms(e[2 * i], e[2 * i + 1]) for e in evs) / breakdown_steps for i in range(4)]
     for e in evs:
         hip.destroy(e)
     ms = (t1 - t0) * 1e3 / steps
@@ -148,7 +160,7 @@ def time_s5(steps, warmup, hip):
     gemm_flop = 2.0 * (2 * P) * H * L * B  # one projection
     return {
         "workload": "s5_mimo", "B": B, "H": H, "P": P, "L": L,
-        "ms_per_step": ms, "elements_per_s": B * H * L / (ms * 1e-3),
+        "ms_per_step": ms, "elements_per_s": B * H * L / (ms * 1e-3), "rotated_sets": rotate,
         "stage_ms": {"pack": st[0], "proj_in": st[1], "scan": st[2], "proj_out": st[3]},
         "proj_in_fp32_tflops": gemm_flop / (st[1] * 1e-3) / 1e12,
         "proj_out_fp32_tflops": gemm_flop / (st[3] * 1e-3) / 1e12,
