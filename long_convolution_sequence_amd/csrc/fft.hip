@@ -576,6 +576,32 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
   }
 }
 
+// Raw buffer resource over `bytes` bytes at `base`.  The hardware range
+// check of raw buffers returns zero for loads at or beyond `bytes` and drops
+// such stores, so a row's tail and an inactive problem (bytes = 0) need no
+// branches; one SGPR descriptor plus one lane offset addresses all of a
+// thread's strided accesses.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float buf_load_f32(BufRes r, int voff, int soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ float2 buf_load_f32x2(BufRes r, int voff, int soff) {
+  const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+}
+
+__device__ __forceinline__ void buf_store_f32(BufRes r, int voff, int soff, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+
 // Spectrum of the kernel, in the convolution's layout:
 //   spec[h, half, e] = ( X[2 k + half] + D_f + D_b ) / (2M),   e = r T + t,
 //   k = frequency of the convolution's transform position 16 t + r,
@@ -628,18 +654,22 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
   {
     const float* kf = reK + (size_t)h * L;
     const float* kb = reK + ((size_t)(ndir - 1) * H + h) * L;
+    // raw buffers over the rows: samples at or past L read zero
+    const BufRes rf = buf_res(kf, active ? 4u * L : 0u);
+    const BufRes rb = buf_res(kb, active && ndir == 2 ? 4u * L : 0u);
+    const int lo = opaque(lt);
+    if (PACK && (L & 1) == 0) {  // (K[2n], K[2n+1]) as one 8-byte load, wholly in or out of range
 #pragma unroll
-    for (int r = 0; r < C::PT; ++r) {
-      const int n = nat<C>(lt, r);
-      float a = 0.f, b = 0.f;
-      if (PACK) {
-        if (active && 2 * n < L) a = kf[2 * n];
-        if (active && 2 * n + 1 < L) b = kf[2 * n + 1];
-      } else if (active && n < L) {
-        a = kf[n];
-        if (ndir == 2) b = kb[n];
+      for (int r = 0; r < C::PT; ++r) v[r] = buf_load_f32x2(rf, 8 * nat<C>(lo, r), 0);
+    } else {
+#pragma unroll
+      for (int r = 0; r < C::PT; ++r) {
+        const int n = nat<C>(lo, r);
+        if (PACK)
+          v[r] = make_float2(buf_load_f32(rf, 8 * n, 0), buf_load_f32(rf, 8 * n + 4, 0));
+        else
+          v[r] = make_float2(buf_load_f32(rf, 4 * n, 0), buf_load_f32(rb, 4 * n, 0));
       }
-      v[r] = make_float2(a, b);
     }
   }
   if (half) {  // z t_S, t_S[n] = exp(-i pi n / S)
@@ -687,32 +717,6 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
       }
     }
   }
-}
-
-// Raw buffer resource over `bytes` bytes at `base`.  The hardware range
-// check of raw buffers returns zero for loads at or beyond `bytes` and drops
-// such stores, so a row's tail and an inactive problem (bytes = 0) need no
-// branches; one SGPR descriptor plus one lane offset addresses all of a
-// thread's strided accesses.
-typedef __amdgpu_buffer_rsrc_t BufRes;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ BufRes buf_res(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ float buf_load_f32(BufRes r, int voff, int soff) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
-}
-
-__device__ __forceinline__ float2 buf_load_f32x2(BufRes r, int voff, int soff) {
-  const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-  return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
-}
-
-__device__ __forceinline__ void buf_store_f32(BufRes r, int voff, int soff, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
 }
 
 // Points per thread of the convolution.  16 (1024 threads at M = 16384, four
