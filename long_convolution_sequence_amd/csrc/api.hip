@@ -118,7 +118,7 @@ Layout layout(int op, const dssm_shape* s) {
     const size_t M = (size_t)1 << log2m;
     l.reK = take(ndh * L * sizeof(float));
     l.spec = take((size_t)s->H * 2 * M * sizeof(float2));
-    l.corr = take((size_t)s->H * 2 * M * sizeof(float));
+    l.corr = take((size_t)corr_groups(s->B, s->H) * s->H * 2 * M * sizeof(float));
     l.parts = take(ndh * (size_t)grad_splits(s->L) * N * 2 * 2 * sizeof(double));
   }
   if (op == DSSM_OP_SCAN) {
@@ -356,7 +356,8 @@ int dssm_backward(const float* u, const float* dy, const dssm_dlr_params* p, con
   // dy, summed over the batch in the frequency domain
   if ((rc = hip_check(launch_corr(u, dy, s->B, s->H, s->L, log2m, corr, st), "corr launch")))
     return rc;
-  if ((rc = hip_check(launch_grad_params(corr, 1 << log2m, s->H, s->L, p->log_re, p->log_im, p->W,
+  if ((rc = hip_check(launch_grad_params(corr, 1 << log2m, corr_groups(s->B, s->H), s->H, s->L,
+                                         p->log_re, p->log_im, p->W,
                                          s->N, ndir, at<void>(ws, l.parts), g->dlog_re,
                                          g->dlog_im, g->dW, g->dD, st),
                       "gradient launch")))

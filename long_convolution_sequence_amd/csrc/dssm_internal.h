@@ -69,20 +69,21 @@ hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, 
 
 int fft_log2m(int L);  // log2 of M = max(16, next power of two >= L)
 
-// Kernel cotangents for the gradients, summed over the batch: part [H][2][M]
-// floats such that, for j < L,
-//   sum_b sum_i u[b,h,i] dy[b,h,i+j] = part[h][0][j] + part[h][1][j],
-//   sum_b sum_i dy[b,h,i] u[b,h,i+j] = part[h][0][M-j] - part[h][1][M-j] (j >= 1).
+// Kernel cotangents for the gradients, summed over the batch: part [G][H][2][M]
+// floats (G = corr_groups(B, H) batch groups) such that, for j < L,
+//   sum_b sum_i u[b,h,i] dy[b,h,i+j] = sum_g part[g][h][0][j] + part[g][h][1][j],
+//   sum_b sum_i dy[b,h,i] u[b,h,i+j] = sum_g part[g][h][0][M-j] - part[g][h][1][M-j] (j >= 1).
+int corr_groups(int B, int H);
 hipError_t launch_corr(const float* u, const float* dy, int B, int H, int L, int log2m,
                        float* part, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Parameter gradients from kernel cotangents (grad.hip)
 // ---------------------------------------------------------------------------
-// part [H][2][M]: the halves of the batch-summed lagged correlations
+// part [G][H][2][M]: the halves of the batch-summed lagged correlations
 // (launch_corr).  parts: grad_splits(L) * ndir * H * N * 2 double2.
 int grad_splits(int L);
-hipError_t launch_grad_params(const float* part, int M, int H, int L, const float* log_re,
+hipError_t launch_grad_params(const float* part, int M, int G, int H, int L, const float* log_re,
                               const float* log_im, const float* W, int N, int ndir, void* parts,
                               float* dlog_re, float* dlog_im, float* dW, float* dD,
                               hipStream_t st);

@@ -855,9 +855,12 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
 // half and stores part[h][half][n] (n < M): the real part of the half's
 // inverse, the odd half multiplied by conj t[n] first.  Then
 //   c[n] = part[h][0][n] + part[h][1][n],  c[n + M] = part[h][0][n] - part[h][1][n].
+// With G > 1 batch groups (few channels, many rows) workgroup (g, h, half)
+// takes rows b = g, g + G, ... and stores part[g][h][half][n]; the groups'
+// parts add up (the map from the rows to c is linear).
 template <int LOG2M>
 __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void corr_kernel(
-    const float* __restrict__ u, const float* __restrict__ dy, int B, int H, int L,
+    const float* __restrict__ u, const float* __restrict__ dy, int B, int H, int L, int G,
     float* __restrict__ part) {
   using C = Cfg<LOG2M, 16>;
   constexpr int M = C::M;
@@ -869,8 +872,9 @@ __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void corr_kernel(
   float2* lds = lds_all + gi * C::LDSN;
   // the two halves of a channel, which read the same rows, share an XCD
   const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
-  const bool active = prob < 2 * H;
-  const int h = active ? (prob >> 1) : 0;
+  const bool active = prob < 2 * H * G;
+  const int grp = active ? prob / (2 * H) : 0;
+  const int h = active ? (prob % (2 * H)) >> 1 : 0;
   const int half = prob & 1;
   const int kt = freq_of_pos<C>(C::PT * lt);  // bins of this thread: kt | freq_of_pos(r)
   const float c1 = 0.25f / (float)M, c2 = 0.125f / (float)M;
@@ -878,7 +882,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void corr_kernel(
   float2 acc[C::PT];
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) acc[r] = make_float2(0.f, 0.f);
-  for (int b = 0; b < B; ++b) {
+  for (int b = grp; b < B; b += G) {
     float2 v[C::PT];
     {
       const BufRes ur = buf_res(u + ((size_t)b * H + h) * L, active ? 4u * L : 0u);
@@ -921,18 +925,19 @@ __global__ __launch_bounds__((Cfg<LOG2M, 16>::WG)) void corr_kernel(
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) acc[r] = cmul(acc[r], tlc);
   }
-  const BufRes pr = buf_res(part + ((size_t)h * 2 + half) * M, active ? 4u * M : 0u);
+  const BufRes pr = buf_res(part + (((size_t)grp * H + h) * 2 + half) * M, active ? 4u * M : 0u);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) buf_store_f32(pr, 4 * nat<C>(lte, r), 0, acc[r].x);
 }
 
 template <int LOG2M>
-hipError_t corr_launch(const float* u, const float* dy, int B, int H, int L, float* part,
+hipError_t corr_launch(const float* u, const float* dy, int B, int H, int L, int G, float* part,
                        hipStream_t st) {
   using C = Cfg<LOG2M, 16>;
-  const int nprob = 2 * H;
-  const int nblk = (nprob + C::G - 1) / C::G;
-  launch_k(corr_kernel<LOG2M>, dim3(nblk), dim3(C::WG), st, KEvents{}, u, dy, B, H, L, part);
+  const long nprob = 2L * H * G;
+  const long nblk = (nprob + C::G - 1) / C::G;
+  launch_k(corr_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), st, KEvents{}, u, dy, B, H, L, G,
+           part);
   return hipGetLastError();
 }
 
@@ -1005,12 +1010,20 @@ hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, 
   }
 }
 
+int corr_groups(int B, int H) {
+  // enough (channel, half, group) workgroups for the 256 CUs, at most one
+  // group per row; a fixed count, so workspace sizes do not depend on the device
+  const long want = (256 + 2L * H - 1) / (2L * H);
+  return (int)std::max(1L, std::min<long>(B, want));
+}
+
 hipError_t launch_corr(const float* u, const float* dy, int B, int H, int L, int log2m,
                        float* part, hipStream_t st) {
+  const int G = corr_groups(B, H);
   switch (log2m) {
 #define X(n) \
   case n:    \
-    return corr_launch<n>(u, dy, B, H, L, part, st);
+    return corr_launch<n>(u, dy, B, H, L, G, part, st);
     DSSM_FFT_CASES(X)
 #undef X
     default:

@@ -84,7 +84,7 @@ __host__ __device__ __forceinline__ int anchor_tiles(int L) {
 // A[i][k = g], B[k = g][j = i], D[i][j]: lane j + 16 (i / 4), element i % 4.
 // Instruction ks (< 16) of a tile covers r = 16 g + ks on lane group g.
 __global__ __launch_bounds__(256) void grad_vander_kernel(
-    const float* __restrict__ part, int M, int H, int L, const float* __restrict__ log_re,
+    const float* __restrict__ part, int M, int NG, int H, int L, const float* __restrict__ log_re,
     const float* __restrict__ log_im, int N, int d, int S, double2* __restrict__ parts) {
   __shared__ float G[kMaxTiles * kQT][kGS];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -95,30 +95,39 @@ __global__ __launch_bounds__(256) void grad_vander_kernel(
   const int tile0 = s * per, tiles = max(0, min(per, ntile - tile0));
 
   // stage G[q][r] = G_d[64 q + r] for this split's anchors from the two
-  // correlation halves (raw buffers: offsets outside them read zero; the
-  // backward direction reads them mirrored, M - j)
+  // correlation halves of every batch group (raw buffers: offsets outside
+  // them read zero; the backward direction reads them mirrored, M - j)
   {
     constexpr int kV = kMaxTiles * kQT * kAnchor / 256;  // floats per thread
     static_assert(kV * 256 == kMaxTiles * kQT * kAnchor, "staging split");
     const long j0 = (long)tile0 * kQT * kAnchor;
     const int nval = (int)std::min<long>((long)tiles * kQT * kAnchor, std::max<long>(0, L - j0));
-    const BufRes pe = buf_res(part + (size_t)h * 2 * M, 4u * (unsigned)M);
-    const BufRes po = buf_res(part + ((size_t)h * 2 + 1) * M, 4u * (unsigned)M);
-    float x[2][kV];
+    float acc[kV];
 #pragma unroll
-    for (int i = 0; i < kV; ++i) {
-      const int e = t + 256 * i;
-      const int jj = (int)j0 + e;
-      // past the split's range: an offset beyond the halves (reads zero)
-      const int src = e >= nval ? M : (d == 0 || jj == 0 ? jj : M - jj);
-      x[0][i] = buf_load(pe, 4 * src);
-      x[1][i] = buf_load(po, 4 * src);
+    for (int i = 0; i < kV; ++i) acc[i] = 0.f;
+    for (int grp = 0; grp < NG; ++grp) {
+      const BufRes pe = buf_res(part + ((size_t)grp * H + h) * 2 * M, 4u * (unsigned)M);
+      const BufRes po = buf_res(part + (((size_t)grp * H + h) * 2 + 1) * M, 4u * (unsigned)M);
+      float x[2][kV];
+#pragma unroll
+      for (int i = 0; i < kV; ++i) {
+        const int e = t + 256 * i;
+        const int jj = (int)j0 + e;
+        // past the split's range: an offset beyond the halves (reads zero)
+        const int src = e >= nval ? M : (d == 0 || jj == 0 ? jj : M - jj);
+        x[0][i] = buf_load(pe, 4 * src);
+        x[1][i] = buf_load(po, 4 * src);
+      }
+#pragma unroll
+      for (int i = 0; i < kV; ++i) {
+        const int jj = (int)j0 + t + 256 * i;
+        acc[i] += (d == 0 || jj == 0) ? x[0][i] + x[1][i] : x[0][i] - x[1][i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < kV; ++i) {
       const int e = t + 256 * i;
-      const int jj = (int)j0 + e;
-      G[e / kAnchor][e % kAnchor] = (d == 0 || jj == 0) ? x[0][i] + x[1][i] : x[0][i] - x[1][i];
+      G[e / kAnchor][e % kAnchor] = acc[i];
     }
   }
   __syncthreads();
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(256) void grad_vander_kernel(
 __global__ __launch_bounds__(256) void grad_combine_kernel(
     const double2* __restrict__ parts, int S, int ndir, int H, int N,
     const float* __restrict__ log_re, const float2* __restrict__ W,
-    const float* __restrict__ part, int M, float* __restrict__ dlog_re,
+    const float* __restrict__ part, int M, int NG, float* __restrict__ dlog_re,
     float* __restrict__ dlog_im, float2* __restrict__ dW, float* __restrict__ dD) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const long total = (long)ndir * H * N;
@@ -221,7 +230,10 @@ __global__ __launch_bounds__(256) void grad_combine_kernel(
   dlog_im[i] = (float)(-z.y);
   if (n == 0) {  // lag 0, the same for both directions
     const int h = (int)(dh % H);
-    dD[dh] = part[(size_t)h * 2 * M] + part[((size_t)h * 2 + 1) * M];
+    float g = 0.f;
+    for (int grp = 0; grp < NG; ++grp)
+      g += part[((size_t)grp * H + h) * 2 * M] + part[(((size_t)grp * H + h) * 2 + 1) * M];
+    dD[dh] = g;
   }
 }
 
@@ -248,19 +260,19 @@ int grad_splits(int L) {
   return std::max(1, (ntile + kMaxTiles - 1) / kMaxTiles);
 }
 
-hipError_t launch_grad_params(const float* part, int M, int H, int L, const float* log_re,
+hipError_t launch_grad_params(const float* part, int M, int NG, int H, int L, const float* log_re,
                               const float* log_im, const float* W, int N, int ndir, void* parts,
                               float* dlog_re, float* dlog_im, float* dW, float* dD,
                               hipStream_t st) {
   const int S = grad_splits(L);
   double2* pp = static_cast<double2*>(parts);
   for (int d = 0; d < ndir; ++d)
-    launch_k(grad_vander_kernel, dim3((unsigned)(H * S)), dim3(256), st, KEvents{}, part, M, H, L,
-             log_re, log_im, N, d, S, pp);
+    launch_k(grad_vander_kernel, dim3((unsigned)(H * S)), dim3(256), st, KEvents{}, part, M, NG, H,
+             L, log_re, log_im, N, d, S, pp);
   const long total = (long)ndir * H * N;
   launch_k(grad_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), st, KEvents{},
            static_cast<const double2*>(pp), S, ndir, H, N, log_re,
-           reinterpret_cast<const float2*>(W), part, M, dlog_re, dlog_im,
+           reinterpret_cast<const float2*>(W), part, M, NG, dlog_re, dlog_im,
            reinterpret_cast<float2*>(dW), dD);
   return hipGetLastError();
 }
