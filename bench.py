@@ -28,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# FP32 vector peak without packed FP32 (disabled in this build): 256 CUs x 4
+# FP32 vector peak without packed FP32 (the library is compiled without it): 256 CUs x 4
 # SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz.  The published 157.3 TFLOP/s
 # counts packed FMAs (two per lane per clock).
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12

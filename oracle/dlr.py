@@ -17,7 +17,7 @@ survives, and what this module follows, is:
 * the bidirectional form as the sum of two independent DLRs, one per direction
   (section 2, bidirectionality paragraph).
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
 
 * the recurrence is  x_k = Lambda x_{k-1} + 1 u_k,  x_{-1} = 0,
   y_k = Re <w, x_k>  -- the only recurrence with unit input weights whose

@@ -8,7 +8,7 @@ linear recurrence x_k = A_bar x_{k-1} + B_bar u_k computed by a scan) and
 section 3 (the S5 layer: one diagonal state of size P shared by all H inputs,
 learnable B~ in C^{PxH}, C~ in C^{HxP}, diagonal real D).
 
-Readings where the page is silent (each listed in the design doc): the discrete
+Readings where the page is silent: the discrete
 diagonal Lambda_bar and B_bar are given directly (no discretisation is applied
 here), the initial state is zero, and the real output is Re(C~ x_k) + D * u_k
 with no factor of two.
