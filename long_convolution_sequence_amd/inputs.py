@@ -132,3 +132,33 @@ def dlr_state(B, H, N, seed=0, scale=3.0):
     re = rng.normal(0.0, sd, size=(B, H, N))
     im = rng.normal(0.0, sd, size=(B, H, N))
     return (re + 1j * im).astype(np.complex64)
+
+
+def s5_tv_inputs(B, H, P, L, seed=4, step_range=(0.5, 1.5)):
+    """Seeded continuous-time S5 parameters, per-step step sizes and input.
+
+    Returns a dict with u [B,H,L] f32, lam_c [P] c64 (-0.5 + i pi p),
+    delta [P] f32 (log-uniform in [1e-3, 1e-1]), Bt [P,H] c64, C [H,P] c64,
+    D [H] f32 and step [B,L] f32 (uniform in step_range: irregular sampling
+    around the nominal step).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    log_dt = rng.uniform(np.log(1e-3), np.log(1e-1), size=P)
+    lam_c = -0.5 + 1j * np.pi * np.arange(P)
+    s = np.sqrt(1.0 / (2.0 * H))
+    b_re = rng.normal(0.0, s, size=(P, H))
+    b_im = rng.normal(0.0, s, size=(P, H))
+    c_re = rng.normal(0.0, s, size=(H, P))
+    c_im = rng.normal(0.0, s, size=(H, P))
+    D = rng.normal(0.0, 1.0, size=H)
+    u = rng.normal(0.0, 1.0, size=(B, H, L))
+    step = rng.uniform(step_range[0], step_range[1], size=(B, L))
+    return dict(
+        u=u.astype(np.float32),
+        lam_c=lam_c.astype(np.complex64),
+        delta=np.exp(log_dt).astype(np.float32),
+        Bt=(b_re + 1j * b_im).astype(np.complex64),
+        C=(c_re + 1j * c_im).astype(np.complex64),
+        D=D.astype(np.float32),
+        step=step.astype(np.float32),
+    )

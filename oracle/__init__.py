@@ -21,7 +21,8 @@ pages define, in float64, from the float32 input values promoted exactly:
   definitions.
 * ``s5``   -- the multi-input multi-output diagonal SSM of "Simplified State
   Space Layers for Sequence Modeling", section 3, computed as a sequential
-  recurrence and as a direct causal sum over a prefix.
+  recurrence and as a direct causal sum over a prefix; and its continuous-time
+  form with a step size that changes from step to step (zero-order hold).
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (closed forms, a library DFT, brute-force
@@ -37,4 +38,4 @@ from .dlr import (  # noqa: F401
     dlr_recurrence_state,
 )
 from .dlr_grad import dlr_backward  # noqa: F401
-from .s5 import s5_recurrence, s5_direct_prefix  # noqa: F401
+from .s5 import s5_recurrence, s5_direct_prefix, s5_recurrence_tv  # noqa: F401

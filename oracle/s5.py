@@ -64,3 +64,55 @@ def s5_direct_prefix(u, lam, Bbar, C, D, Lp):
         for b in range(Bsz):
             x[b, p] = np.convolve(v[b, p], powers)[:L]
     return np.einsum("hp,bpl->bhl", Cc, x).real + D[None, :, None] * u
+
+
+def _expm1c(z):
+    """exp(z) - 1 for complex z without cancellation near z = 0:
+    (expm1(a) cos b - 2 sin^2(b/2)) + i exp(a) sin b, z = a + ib."""
+    a, b = z.real, z.imag
+    return (np.expm1(a) * np.cos(b) - 2.0 * np.sin(0.5 * b) ** 2) + 1j * (np.exp(a) * np.sin(b))
+
+
+def s5_recurrence_tv(u, lam_c, Bt, C, D, delta, step):
+    """S5 with continuous-time parameters and a step size that changes from step
+    to step ("Simplified State Space Layers for Sequence Modeling", section 3:
+    a diagonal continuous-time system with a learnable timescale per state,
+    discretised by zero-order hold; irregularly sampled sequences are handled by
+    supplying a different timescale to the discretisation at each step).
+
+    Reading where the page is silent (its discretisation equations were lost):
+    the timescale of state p at step k of batch row b is step[b, k] * delta[p]
+    (a per-step time increment relative to the nominal step, scaling the
+    learnt per-state timescale), and zero-order hold gives, with
+    z = lam_c[p] * step[b, k] * delta[p],
+        Lambda_bar = exp(z),   B_bar row p = (exp(z) - 1) / lam_c[p] * Bt[p, :]
+    ((exp(z) - 1) / lam_c -> step * delta as lam_c -> 0); then
+        x_k = Lambda_bar x_{k-1} + B_bar u_k,  y_k = Re(C x_k) + D * u_k,  x_{-1} = 0.
+
+    Layouts: u [B, H, L] real; lam_c [P] complex; Bt [P, H] complex;
+    C [H, P] complex; D [H] real; delta [P] real; step [B, L] real.
+    """
+    u = np.asarray(u).astype(np.float64)
+    lam = np.asarray(lam_c).astype(np.complex128)
+    Bb = np.asarray(Bt).astype(np.complex128)
+    Cc = np.asarray(C).astype(np.complex128)
+    D = np.asarray(D).astype(np.float64)
+    dl = np.asarray(delta).astype(np.float64)
+    st = np.asarray(step).astype(np.float64)
+    Bsz, H, L = u.shape
+    P = lam.shape[0]
+    x = np.zeros((Bsz, P), dtype=np.complex128)
+    y = np.empty((Bsz, H, L), dtype=np.float64)
+    BbT = Bb.T.copy()
+    CT = Cc.T.copy()
+    zero = lam == 0
+    inv = np.where(zero, 0.0, 1.0 / np.where(zero, 1.0, lam))
+    for k in range(L):
+        uk = u[:, :, k]
+        dt = st[:, k][:, None] * dl[None, :]  # [B, P]
+        z = lam[None, :] * dt
+        a = np.exp(z)
+        beta = np.where(zero[None, :], dt, _expm1c(z) * inv[None, :])
+        x = a * x + beta * (uk @ BbT)
+        y[:, :, k] = (x @ CT).real + D[None, :] * uk
+    return y
