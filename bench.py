@@ -168,6 +168,40 @@ def time_s5(steps, warmup, hip, rotate=5, breakdown_steps=10):
     }
 
 
+def time_s5_tv(steps, warmup, rotate=5):
+    """Timed forwards of the continuous-time S5 layer with irregular per-step
+    step sizes (uniform in [0.5, 1.5]) on the S5 workload shape: plain calls
+    over `rotate` input/output sets, wall clock."""
+    import numpy as np
+    import torch
+    from long_convolution_sequence_amd import binding as bd
+    from long_convolution_sequence_amd import inputs
+
+    c = inputs.config("s5_mimo")
+    x = inputs.s5_tv_inputs(c["B"], c["H"], c["P"], c["L"], seed=c["seed"])
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    us = [t["u"]] + [t["u"].clone() for _ in range(rotate - 1)]
+    ys = [torch.empty_like(t["u"]) for _ in range(rotate)]
+    ws = torch.empty(bd.s5_workspace_size(c["B"], c["H"], c["P"], c["L"]), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(k):
+        bd.s5_forward_tv(us[k % rotate], t["lam_c"], t["Bt"], t["C"], t["D"], t["delta"],
+                         t["step"], y=ys[k % rotate], workspace=ws)
+
+    for k in range(warmup):
+        call(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        call(k)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    B, H, L = c["B"], c["H"], c["L"]
+    return {"workload": "s5_mimo shape, continuous-time, steps ~ U(0.5, 1.5)",
+            "ms_per_step": ms, "elements_per_s": B * H * L / (ms * 1e-3), "rotated_sets": rotate}
+
+
 def time_backward(dev, us, ys, bi, steps, warmup):
     """Timed gradient passes (dssm_backward) of the layer on the bench workload,
     with a seeded output cotangent; wall clock between two synchronisations."""
@@ -382,6 +416,7 @@ def main():
             "rotated_sets": a.rotate,
             "device_copy": copy,
             "s5_path": time_s5(max(2, a.scan_steps), 2, hip),
+            "s5_tv_path": time_s5_tv(max(2, a.scan_steps), 2),
             "backward": time_backward(dev, us, ys, bi, max(2, a.scan_steps), 2),
         },
     }

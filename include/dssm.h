@@ -269,6 +269,35 @@ int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes);
 int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* S5 in continuous time with a step size that changes from step to step
+ * ("Simplified State Space Layers for Sequence Modeling", section 3: a
+ * diagonal continuous-time system with a learnable timescale per state,
+ * discretised by zero-order hold; irregularly sampled sequences are handled
+ * by supplying a different timescale to the discretisation at each step).
+ * The timescale of state p at step k of batch row b is step[b, k] * delta[p];
+ * with z = lambda_c[p] step[b, k] delta[p]:
+ *   x_k = exp(z) x_{k-1} + (exp(z) - 1) / lambda_c[p] (Btilde u_k)_p,
+ *   y_k = Re(C x_k) + D u_k,   x_{-1} = 0
+ * ((exp(z) - 1) / lambda_c is step delta where lambda_c = 0).  Layouts:
+ *   lambda_c [P, 2] complex (continuous-time), Btilde [P, H, 2] complex,
+ *   C [H, P, 2] complex, D [H] float32, delta [P] float32,
+ *   step [B, L] float32 (the caller's time increments over the nominal step;
+ *   0 is allowed: the state is then carried over unchanged).
+ * The projections are those of dssm_s5_forward (Btilde in place of Bbar);
+ * the scan forms z in float64 and the discretised values in float32.  Same
+ * shape limits, workspace (dssm_s5_workspace_size) and conventions as
+ * dssm_s5_forward; step must be 16-byte aligned. */
+typedef struct {
+  const float* lambda_c;
+  const float* Btilde;
+  const float* C;
+  const float* D;
+  const float* delta;
+} dssm_s5_tv_params;
+
+int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5_shape* s,
+                       const float* step, float* y, void* ws, size_t ws_bytes, void* stream);
+
 /* Timing variant of dssm_s5_forward (n_events = 8): start/stop pairs of the
  * four kernels, in order: packing of Bbar and C, input projection, scan,
  * output projection (same event conventions as the DLR timing variants). */

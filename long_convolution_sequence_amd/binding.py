@@ -27,7 +27,7 @@ EXPORTS = [
     "dssm_forward_scan", "dssm_backward",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
     "dssm_forward_scan_state", "dssm_step",
-    "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed",
+    "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed", "dssm_s5_forward_tv",
 ]
 
 
@@ -54,6 +54,11 @@ class S5Shape(ctypes.Structure):
 class S5Params(ctypes.Structure):
     _fields_ = [("lam", ctypes.c_void_p), ("Bbar", ctypes.c_void_p), ("C", ctypes.c_void_p),
                 ("D", ctypes.c_void_p)]
+
+
+class S5TVParams(ctypes.Structure):
+    _fields_ = [("lam_c", ctypes.c_void_p), ("Bt", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("D", ctypes.c_void_p), ("delta", ctypes.c_void_p)]
 
 
 class DSSMError(RuntimeError):
@@ -116,6 +121,9 @@ def lib():
     L.dssm_s5_forward_timed.restype = ctypes.c_int
     L.dssm_s5_forward_timed.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape), vp,
                                         vp, sz, vp, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.dssm_s5_forward_tv.restype = ctypes.c_int
+    L.dssm_s5_forward_tv.argtypes = [vp, ctypes.POINTER(S5TVParams), ctypes.POINTER(S5Shape), vp,
+                                     vp, vp, sz, vp]
     _lib = L
     return L
 
@@ -410,6 +418,42 @@ def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=N
     else:
         arr = (ctypes.c_void_p * len(events))(*events)
         check(lib().dssm_s5_forward_timed(*(args + [arr, len(events)])))
+    return y
+
+
+def s5_forward_tv(u, lam_c, Bt, C, D, delta, step, y=None, workspace=None, stream=None):
+    """Continuous-time S5 layer forward with a step size per (b, k).  u [B,H,L]
+    f32, lam_c [P] c64, Bt [P,H] c64, C [H,P] c64, D [H] f32, delta [P] f32,
+    step [B,L] f32 -> y [B,H,L] f32."""
+    torch = _torch()
+    uu = _dev_f32(u, "u")
+    if uu.dim() != 3:
+        raise ValueError("u must be [B, H, L]")
+    B, H, L = uu.shape
+    lm = _dev_f32(lam_c, "lam_c")
+    P = lm.numel() // 2
+    bb = _dev_f32(Bt, "Bt")
+    cc = _dev_f32(C, "C")
+    dd = _dev_f32(D, "D")
+    dl = _dev_f32(delta, "delta")
+    ss = _dev_f32(step, "step")
+    if bb.numel() != 2 * P * H or cc.numel() != 2 * H * P or dd.numel() != H:
+        raise ValueError("Bt must be [P,H], C [H,P] complex and D [H]")
+    if dl.numel() != P or ss.numel() != B * L:
+        raise ValueError("delta must be [P] and step [B, L]")
+    shape = S5Shape(B, H, P, L, 0)
+    prm = S5TVParams(lm.data_ptr(), bb.data_ptr(), cc.data_ptr(), dd.data_ptr(), dl.data_ptr())
+    if y is None:
+        y = torch.empty_like(uu)
+    yy = _dev_f32(y, "y")
+    need = ctypes.c_size_t(0)
+    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=uu.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    check(lib().dssm_s5_forward_tv(uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape),
+                                   ss.data_ptr(), yy.data_ptr(), workspace.data_ptr(), nbytes,
+                                   _stream(stream)))
     return y
 
 

@@ -507,6 +507,52 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   return ok();
 }
 
+int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5_shape* s,
+                       const float* step, float* y, void* ws, size_t ws_bytes, void* stream) {
+  bool empty = false;
+  int rc = s5_check_shape(s, &empty);
+  if (rc) return rc;
+  if (empty) return ok();
+  if (!p) return fail(DSSM_ERR_INVALID_ARG, "params is NULL");
+  if (!p->lambda_c || !p->Btilde || !p->C || !p->D || !p->delta)
+    return fail(DSSM_ERR_INVALID_ARG, "a parameter pointer is NULL");
+  if (!aligned16(p->lambda_c) || !aligned16(p->Btilde) || !aligned16(p->C) || !aligned16(p->D) ||
+      !aligned16(p->delta))
+    return fail(DSSM_ERR_INVALID_ARG, "parameter pointers must be 16-byte aligned");
+  if (!u || !y || !step || !aligned16(u) || !aligned16(y) || !aligned16(step))
+    return fail(DSSM_ERR_INVALID_ARG, "u, step or y is NULL or not 16-byte aligned");
+  if (u == y || step == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u or step");
+  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L);
+  if (ws_bytes < l.total)
+    return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, l.total);
+  if (!ws) return fail(DSSM_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(DSSM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* apk_in = at<unsigned char>(ws, l.apk_in);
+  void* apk_out = at<unsigned char>(ws, l.apk_out);
+  int* rexp_in = at<int>(ws, l.rexp_in);
+  int* rexp_out = at<int>(ws, l.rexp_out);
+  float* v = at<float>(ws, l.v);
+  float* x = at<float>(ws, l.x);
+  if ((rc = hip_check(launch_s5_pack(p->Btilde, p->C, s->H, s->P, apk_in, rexp_in, apk_out,
+                                     rexp_out, st),
+                      "s5 pack")))
+    return rc;
+  if ((rc = hip_check(launch_s5_proj_in(apk_in, rexp_in, u, s->B, s->H, s->P, s->L, v, st),
+                      "s5 proj_in")))
+    return rc;
+  if ((rc = hip_check(launch_s5_scan_tv(p->lambda_c, p->delta, step, v, s->B, s->P, s->L, x, st),
+                      "s5 scan")))
+    return rc;
+  if ((rc = hip_check(launch_s5_proj_out(apk_out, rexp_out, x, p->D, u, s->B, s->H, s->P, s->L,
+                                         y, st),
+                      "s5 proj_out")))
+    return rc;
+  return ok();
+}
+
 int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes) {
   if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
   bool empty = false;

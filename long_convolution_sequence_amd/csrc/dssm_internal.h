@@ -150,6 +150,11 @@ hipError_t launch_s5_proj_in(const void* apk_in, const int* rexp_in, const float
 // x [B][P][2][L]: x_k = lambda x_{k-1} + v_k
 hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int L, float* x,
                           hipStream_t st, KEvents ev = {});
+// x [B][P][2][L] for the continuous-time system with per-step step sizes:
+// x_k = exp(z) x_{k-1} + (exp(z) - 1) / lam_c v_k, z = lam_c[p] step[b,k] delta[p]
+hipError_t launch_s5_scan_tv(const float* lam_c, const float* delta, const float* step,
+                            const float* v, int B, int P, int L, float* x, hipStream_t st,
+                            KEvents ev = {});
 // y [B][H][L] = Re(C x) + D u
 hipError_t launch_s5_proj_out(const void* apk_out, const int* rexp_out, const float* x,
                               const float* D, const float* u, int B, int H, int P, int L, float* y,

@@ -705,6 +705,147 @@ __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restric
   }
 }
 
+// The same recurrence for a continuous-time system with a step size that
+// changes from step to step ("Simplified State Space Layers for Sequence
+// Modeling", section 3: zero-order hold of a diagonal system with a timescale
+// per state; a different timescale supplied at each step for irregular
+// sampling): with z = lam_c[p] step[b,k] delta[p],
+//   x_k = exp(z) x_{k-1} + (exp(z) - 1) / lam_c[p] v_k     (v = B~ u)
+// ((exp(z) - 1) / lam_c -> step delta as lam_c -> 0).  The per-step
+// multipliers differ, so the carries use the general associative pair
+// (A, X) o (A', X') = (A' A, A' X + X'): each lane folds its 16 steps into
+// (A, X), a wave combines its lanes by shuffles, the four waves through LDS,
+// and the tile's total carries into the next tile.  z is formed in float64 and
+// its phase reduced to [-pi, pi] there; the exponential, the sine and cosine
+// and exp(z) - 1 (as expm1(a) cos b - (1 - cos b) + i e^a sin b, 1 - cos b
+// without cancellation) then run in float32.
+// (ir, ii) = 1 / lam_c; lam_zero: lam_c = 0 (then the gain is the step length).
+__device__ __forceinline__ void zoh_step(float lr, float li, float ir, float ii, bool lam_zero,
+                                         double ld, float s, float2& a, float2& beta) {
+  const double dt = ld * (double)s;
+  const double zr = (double)lr * dt, zi = (double)li * dt;
+  // phase reduced to [-pi, pi] in float64
+  const double kTwoPi = 6.283185307179586476925286766559;
+  const double kInvTwoPi = 0.15915494309189533576888376337251;
+  const double red = zi - kTwoPi * rint(zi * kInvTwoPi);
+  const float b = (float)red;
+  float sn, cs;
+  sincosf(b, &sn, &cs);
+  const float em1r = expm1f((float)zr);
+  const float e = 1.f + em1r;
+  a = make_float2(e * cs, e * sn);
+  // 1 - cos b without cancellation: sin^2 b / (1 + cos b) for cos b > 0
+  const float omc = cs > 0.f ? sn * sn * __builtin_amdgcn_rcpf(1.f + cs) : 1.f - cs;
+  const float2 em1 = make_float2(em1r * cs - omc, e * sn);
+  beta = lam_zero ? make_float2((float)dt, 0.f)
+                  : make_float2(em1.x * ir - em1.y * ii, em1.x * ii + em1.y * ir);
+}
+
+__global__ __launch_bounds__(kLanes) void s5_scan_tv_kernel(const float2* __restrict__ lam_c,
+                                                            const float* __restrict__ delta,
+                                                            const float* __restrict__ step,
+                                                            const float* __restrict__ v, int P,
+                                                            int L, float* __restrict__ x) {
+  __shared__ float sre[kPadT], sim[kPadT], sst[kPadT];
+  __shared__ float2 bA[4], bX[4];  // per-wave inclusive totals
+  __shared__ float2 carry;
+  const int p = blockIdx.x % P;
+  const int b = blockIdx.x / P;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const float2 lm = lam_c[p];
+  const double ld = (double)delta[p];
+  const float den = lm.x * lm.x + lm.y * lm.y;
+  const bool lam_zero = !(den > 0.f);
+  const float ir = lam_zero ? 0.f : lm.x / den, ii = lam_zero ? 0.f : -lm.y / den;
+  if (t == 0) carry = make_float2(0.f, 0.f);
+
+  const float* vre = v + ((size_t)b * P + p) * 2 * L;
+  const float* vim = vre + L;
+  const float* srow = step + (size_t)b * L;
+  float* xre = x + ((size_t)b * P + p) * 2 * L;
+  float* xim = xre + L;
+
+  for (int base = 0; base < L; base += kTile) {
+    const int n = min(kTile, L - base);
+    for (int e = t; e < kTile; e += kLanes) {  // stage the tile (zero beyond L)
+      const bool in = e < n;
+      sre[tpad(e)] = in ? vre[base + e] : 0.f;
+      sim[tpad(e)] = in ? vim[base + e] : 0.f;
+      sst[tpad(e)] = in ? srow[base + e] : 0.f;
+    }
+    __syncthreads();
+    float2 va[kSeg], vb[kSeg];  // multipliers, input gains times inputs
+    float2 A = make_float2(1.f, 0.f), X = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      const int q = 17 * t + i;  // tpad(16 t + i)
+      float2 a, beta;
+      zoh_step(lm.x, lm.y, ir, ii, lam_zero, ld, sst[q], a, beta);
+      va[i] = a;
+      vb[i] = cm(beta, make_float2(sre[q], sim[q]));
+      const float2 m = cm(a, X);
+      X = make_float2(m.x + vb[i].x, m.y + vb[i].y);
+      A = cm(a, A);
+    }
+    // inclusive scan inside the wave: earlier (A', X') then this lane's (A, X)
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int o = 1 << j;
+      const int src = max(lane - o, 0);
+      const float2 pA = make_float2(__shfl(A.x, src), __shfl(A.y, src));
+      const float2 pX = make_float2(__shfl(X.x, src), __shfl(X.y, src));
+      if (lane >= o) {
+        const float2 m = cm(A, pX);
+        X = make_float2(m.x + X.x, m.y + X.y);
+        A = cm(A, pA);
+      }
+    }
+    if (lane == 63) {
+      bA[w] = A;
+      bX[w] = X;
+    }
+    __syncthreads();
+    const float2 cin = carry;
+    // prefix of the earlier waves, then the carried state
+    float2 wA = make_float2(1.f, 0.f), wX = make_float2(0.f, 0.f);
+    for (int k = 0; k < w; ++k) {
+      const float2 m = cm(bA[k], wX);
+      wX = make_float2(m.x + bX[k].x, m.y + bX[k].y);
+      wA = cm(bA[k], wA);
+    }
+    {
+      const float2 m = cm(wA, cin);
+      wX = make_float2(wX.x + m.x, wX.y + m.y);  // state entering wave w
+    }
+    {
+      const float2 m = cm(A, wX);
+      X = make_float2(X.x + m.x, X.y + m.y);  // state after this lane's steps
+    }
+    float2 xin;  // state before this lane's steps
+    {
+      const float2 q = make_float2(__shfl(X.x, max(lane - 1, 0)), __shfl(X.y, max(lane - 1, 0)));
+      xin = lane == 0 ? wX : q;
+    }
+    __syncthreads();  // everyone has read `carry`, the totals and its inputs
+    if (t == kLanes - 1) carry = X;
+    float2 st = xin;
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      const float2 m = cm(va[i], st);
+      st = make_float2(m.x + vb[i].x, m.y + vb[i].y);
+      const int q = 17 * t + i;
+      sre[q] = st.x;
+      sim[q] = st.y;
+    }
+    __syncthreads();
+    for (int e = t; e < n; e += kLanes) {
+      xre[base + e] = sre[tpad(e)];
+      xim[base + e] = sim[tpad(e)];
+    }
+    __syncthreads();  // the tile's buffers are read before the next tile's staging
+  }
+}
+
 }  // namespace
 
 S5Layout s5_layout(int B, int H, int P, int L) {
@@ -791,6 +932,14 @@ hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int
                           hipStream_t st, KEvents ev) {
   launch_k(s5_scan_kernel, dim3((unsigned)(B * P)), dim3(kLanes), st, ev,
            reinterpret_cast<const float2*>(lambda), v, P, L, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_s5_scan_tv(const float* lam_c, const float* delta, const float* step,
+                            const float* v, int B, int P, int L, float* x, hipStream_t st,
+                            KEvents ev) {
+  launch_k(s5_scan_tv_kernel, dim3((unsigned)(B * P)), dim3(kLanes), st, ev,
+           reinterpret_cast<const float2*>(lam_c), delta, step, v, P, L, x);
   return hipGetLastError();
 }
 

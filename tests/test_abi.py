@@ -171,6 +171,23 @@ def test_s5_workspace_and_validation():
     assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
 
 
+def test_s5_tv_validation():
+    fn = bd.lib().dssm_s5_forward_tv
+    good = bd.S5Shape(2, 3, 4, 32, 0)
+    prm = bd.S5TVParams(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288, FAKE + 16384)
+    call = lambda p, s, u=FAKE * 2, st=FAKE * 5, y=FAKE * 3, ws=FAKE * 4, n=1 << 40: fn(
+        u, ctypes.byref(p) if p is not None else None, ctypes.byref(s), st, y, ws, n, None)
+    assert call(None, good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(bd.S5TVParams(FAKE, FAKE, FAKE, FAKE, None), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(bd.S5TVParams(FAKE, FAKE, FAKE, FAKE, FAKE + 4), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, st=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, st=FAKE * 5 + 8) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, y=FAKE * 5) == bd.DSSM_ERR_INVALID_ARG  # aliases step
+    assert call(prm, good, n=64) == bd.DSSM_ERR_WORKSPACE
+    assert call(prm, bd.S5Shape(2, 3, 4, 32, 1)) == bd.DSSM_ERR_UNSUPPORTED
+    assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
+
+
 @pytest.mark.parametrize("name,n", [("dssm_forward_fft_timed", 4), ("dssm_forward_scan_timed", 4)])
 def test_timed_variants_validate_events(name, n):
     fn = getattr(bd.lib(), name)
