@@ -113,7 +113,9 @@ const char* dssm_last_error(void);
 
 /* Bytes of workspace needed by `op` for shape `s` (host only; launches
  * nothing).  Returns DSSM_ERR_INVALID_ARG / DSSM_ERR_UNSUPPORTED exactly
- * when the corresponding compute call would. */
+ * when the corresponding compute call would.  Limits common to the DLR calls:
+ * 1 <= N <= 4096, H (1 + bidirectional) <= 65535, B H L <= 2^40 and
+ * B H (1 + bidirectional) <= 2^31 - 1. */
 int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes);
 
 /* Kernel generation: K[d,h,j] = sum_n W[d,h,n] lambda[d,h,n]^j for 0 <= j < L

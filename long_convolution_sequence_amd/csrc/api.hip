@@ -67,6 +67,10 @@ int check_shape(int op, const dssm_shape* s, bool* empty) {
                 (long)s->B * s->H);
   if ((long)s->B * s->H * s->L > (1L << 40))
     return fail(DSSM_ERR_UNSUPPORTED, "B*H*L too large");
+  // rows (and the workgroups of the per-row kernels) are counted in int
+  if ((long)s->B * s->H * ndir > (long)INT32_MAX)
+    return fail(DSSM_ERR_UNSUPPORTED, "B*H*ndir=%ld exceeds 2^31 - 1",
+                (long)s->B * s->H * ndir);
   const bool no_rows = (op == DSSM_OP_GEN) ? false : (s->B == 0);
   *empty = no_rows || s->H == 0 || s->L == 0;
   return DSSM_OK;

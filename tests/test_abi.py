@@ -71,6 +71,10 @@ def test_workspace_size_limits_and_empty():
     assert _ws(bd.OP_FFT, 1, 1, 1, 16385)[0] == bd.DSSM_ERR_UNSUPPORTED
     assert _ws(bd.OP_SCAN, 1, 1, 1, 1 << 20)[0] == 0
     assert _ws(bd.OP_SCAN, 1, 1, 1, (1 << 24) + 1)[0] == bd.DSSM_ERR_UNSUPPORTED
+    # more rows than an int counts
+    assert _ws(bd.OP_SCAN, 1 << 21, 1 << 10, 1, 1)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _ws(bd.OP_FFT, (1 << 30), 2, 1, 1)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _ws(bd.OP_FFT, (1 << 30) - 1, 2, 1, 1)[0] == 0
     for op in (bd.OP_FFT, bd.OP_SCAN):
         assert _ws(op, 0, 4, 4, 8) == (0, 0)
         assert _ws(op, 2, 0, 4, 8) == (0, 0)
