@@ -715,33 +715,58 @@ __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restric
 // multipliers differ, so the carries use the general associative pair
 // (A, X) o (A', X') = (A' A, A' X + X'): each lane folds its 16 steps into
 // (A, X), a wave combines its lanes by shuffles, the four waves through LDS,
-// and the tile's total carries into the next tile.  z is formed in float64 and
-// its phase reduced to [-pi, pi] there; the exponential, the sine and cosine
-// and exp(z) - 1 (as expm1(a) cos b - (1 - cos b) + i e^a sin b, 1 - cos b
-// without cancellation) then run in float32.
+// and the tile's total carries into the next tile; the next tile's inputs are
+// loaded while the current one's carries and outputs are formed.  z is formed in float64 and its
+// phase reduced there to a quadrant and a remainder in [-pi/4, pi/4]; the
+// exponential, the sine and cosine and exp(z) - 1 (as expm1(a) cos b -
+// (1 - cos b) + i e^a sin b, 1 - cos b without cancellation) then run in
+// float32.
+
+// sin and cos of x = q pi/2 + r, |r| <= pi/4, from the Taylor series of sin r
+// (to r^9) and cos r (to r^10): truncation below 3e-9 relative on that range;
+// the quadrant q (mod 4) swaps the pair and flips signs, without branches.
+__device__ __forceinline__ void sincos_quadrant(float r, int q, float& sn, float& cs) {
+  const float r2 = r * r;
+  float ps = fmaf(r2, 1.f / 362880.f, -1.f / 5040.f);
+  ps = fmaf(ps, r2, 1.f / 120.f);
+  ps = fmaf(ps, r2, -1.f / 6.f);
+  const float s = fmaf(ps * r2, r, r);
+  float pc = fmaf(r2, -1.f / 3628800.f, 1.f / 40320.f);
+  pc = fmaf(pc, r2, -1.f / 720.f);
+  pc = fmaf(pc, r2, 1.f / 24.f);
+  pc = fmaf(pc, r2, -0.5f);
+  const float c = fmaf(pc, r2, 1.f);
+  const bool odd = (q & 1) != 0;
+  // q = 0: (s, c); 1: (c, -s); 2: (-s, -c); 3: (-c, s)
+  sn = __int_as_float(__float_as_int(odd ? c : s) ^ ((q & 2) << 30));
+  cs = __int_as_float(__float_as_int(odd ? s : c) ^ (((q + 1) & 2) << 30));
+}
+
 // (ir, ii) = 1 / lam_c; lam_zero: lam_c = 0 (then the gain is the step length).
 __device__ __forceinline__ void zoh_step(float lr, float li, float ir, float ii, bool lam_zero,
                                          double ld, float s, float2& a, float2& beta) {
   const double dt = ld * (double)s;
   const double zr = (double)lr * dt, zi = (double)li * dt;
-  // phase reduced to [-pi, pi] in float64
-  const double kTwoPi = 6.283185307179586476925286766559;
-  const double kInvTwoPi = 0.15915494309189533576888376337251;
-  const double red = zi - kTwoPi * rint(zi * kInvTwoPi);
-  const float b = (float)red;
+  // phase: quadrant q and remainder |r| <= pi/4 in float64
+  const double kHalfPi = 1.5707963267948966192313216916398;
+  const double kInvHalfPi = 0.63661977236758134307553505349006;
+  const double q = rint(zi * kInvHalfPi);
+  const double q4 = fma(-4.0, floor(q * 0.25), q);  // q mod 4, exact
   float sn, cs;
-  sincosf(b, &sn, &cs);
+  sincos_quadrant((float)fma(-q, kHalfPi, zi), (int)q4, sn, cs);
   const float em1r = expm1f((float)zr);
   const float e = 1.f + em1r;
   a = make_float2(e * cs, e * sn);
-  // 1 - cos b without cancellation: sin^2 b / (1 + cos b) for cos b > 0
-  const float omc = cs > 0.f ? sn * sn * __builtin_amdgcn_rcpf(1.f + cs) : 1.f - cs;
+  // 1 - cos b without cancellation: sin^2 b / (1 + cos b) for cos b > 0, both
+  // forms evaluated and one selected
+  const float omc_pos = sn * sn * __builtin_amdgcn_rcpf(1.f + fmaxf(cs, 0.f));
+  const float omc = cs > 0.f ? omc_pos : 1.f - cs;
   const float2 em1 = make_float2(em1r * cs - omc, e * sn);
   beta = lam_zero ? make_float2((float)dt, 0.f)
                   : make_float2(em1.x * ir - em1.y * ii, em1.x * ii + em1.y * ir);
 }
 
-__global__ __launch_bounds__(kLanes) void s5_scan_tv_kernel(const float2* __restrict__ lam_c,
+__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(2))) void s5_scan_tv_kernel(const float2* __restrict__ lam_c,
                                                             const float* __restrict__ delta,
                                                             const float* __restrict__ step,
                                                             const float* __restrict__ v, int P,
@@ -765,13 +790,28 @@ __global__ __launch_bounds__(kLanes) void s5_scan_tv_kernel(const float2* __rest
   float* xre = x + ((size_t)b * P + p) * 2 * L;
   float* xim = xre + L;
 
+  // the next tile's elements t + kLanes i (zero beyond L)
+  float nre[kSeg], nim[kSeg], nst[kSeg];
+  auto fetch = [&](int at) {
+    const int m = min(kTile, L - at);
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {
+      const int e = t + kLanes * i;
+      const bool in = e < m;
+      nre[i] = in ? vre[at + e] : 0.f;
+      nim[i] = in ? vim[at + e] : 0.f;
+      nst[i] = in ? srow[at + e] : 0.f;
+    }
+  };
+  fetch(0);
   for (int base = 0; base < L; base += kTile) {
     const int n = min(kTile, L - base);
-    for (int e = t; e < kTile; e += kLanes) {  // stage the tile (zero beyond L)
-      const bool in = e < n;
-      sre[tpad(e)] = in ? vre[base + e] : 0.f;
-      sim[tpad(e)] = in ? vim[base + e] : 0.f;
-      sst[tpad(e)] = in ? srow[base + e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kSeg; ++i) {  // stage the tile
+      const int q = tpad(t + kLanes * i);
+      sre[q] = nre[i];
+      sim[q] = nim[i];
+      sst[q] = nst[i];
     }
     __syncthreads();
     float2 va[kSeg], vb[kSeg];  // multipliers, input gains times inputs
@@ -787,6 +827,9 @@ __global__ __launch_bounds__(kLanes) void s5_scan_tv_kernel(const float2* __rest
       X = make_float2(m.x + vb[i].x, m.y + vb[i].y);
       A = cm(a, A);
     }
+    // the next tile's loads overlap the carries, the outputs and the stores
+    // (issued after the steps' arithmetic, whose temporaries need the registers)
+    if (base + kTile < L) fetch(base + kTile);
     // inclusive scan inside the wave: earlier (A', X') then this lane's (A, X)
 #pragma unroll
     for (int j = 0; j < 6; ++j) {
