@@ -35,6 +35,7 @@
 //   a depth <= 5 product tree; the table (exact float32 roundings of float64
 //   values) is built into the library.
 #include <algorithm>
+#include <type_traits>
 
 #include "dssm_internal.h"
 #include "twiddle_table.inc"
@@ -538,6 +539,37 @@ __device__ __forceinline__ int pos_of_freq(int k) {
   return P * C::RLAST + (k >> (4 * (C::NP - 1)));
 }
 
+// Storage of a spectrum half (the kernel is real, so its 2M-point spectrum is
+// Hermitian: X[-m] = conj X[m]).  With 16 points per thread the position
+// 16 t + r of the convolution's transform holds frequency k, whose low digit
+// (k mod 16, the first pass's index) is the position's top four bits.
+// * Odd half, bins X[2k+1]: the partner of k is M - 1 - k, the complement of
+//   every bit, hence of every position bit: thread T - 1 - t, register 15 - r.
+// * Even half, bins X[2k]: the partner of k is -k mod M.  For k mod 16 = j != 0
+//   that is 16 - j in the low digit and the complement of the rest, i.e.
+//   thread (16 - j) Q + (Q - 1 - (t mod Q)), register 15 - r, Q = T / 16, where
+//   j = t / Q.  The threads t < Q (k mod 16 = 0, the self-paired bins 0 and
+//   M/2 among them) keep all 16 bins.
+// Stored: registers r < 8 of every thread at slot r T + t, and for the even
+// half registers r >= 8 of the threads t < Q at slot (23 - r) T + t: M/2 + M/32
+// of the M slots of the even half, M/2 of the odd half.  Every other bin is the
+// conjugate of a stored partner.  A reader's slot for register r >= 8 is then
+// (15 - r) T + (a per-thread part): one lane offset, per-register scalar
+// offsets.  Transforms below 256 points (T < 16) store every bin at r T + t.
+template <int LOG2M>
+struct SpecStore {
+  using CM = Cfg<LOG2M, 16>;
+  static constexpr bool kHerm = CM::T >= 16;
+  static constexpr int Q = CM::T / 16;
+  // whether bin (t, r) of `half` is stored, and its slot
+  __device__ static __forceinline__ bool stored(int half, int t, int r) {
+    return !kHerm || r < 8 || (half == 0 && t < Q);
+  }
+  __device__ static __forceinline__ int slot(int t, int r) {
+    return (!kHerm || r < 8) ? r * CM::T + t : (23 - r) * CM::T + t;
+  }
+};
+
 // Separated outputs of a PACK spectrum half for the convolution's column t
 // (its 16 rows): lds holds the bins of the M/2-point transform of the packed
 // z (or z exp(-2 pi i n / M) for half 1) at their transform positions.
@@ -550,6 +582,7 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
                                              float sg, float2* out) {
   using C = Cfg<LOG2M - 1, 16>;
   using CM = Cfg<LOG2M, 16>;
+  using SS = SpecStore<LOG2M>;
   constexpr int M = CM::M, S = C::M;
   constexpr int RB = CM::RLAST / 2;
   const int kt = freq_of_pos<CM>(16 * t);
@@ -560,6 +593,8 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     if (r & RB) continue;
+    const bool st0 = SS::stored(half, t, r), st1 = SS::stored(half, t, r | RB);
+    if (!st0 && !st1) continue;
     const int kr = freq_of_pos<CM>(r);
     const int k1 = kt1 | (kr & (S - 1));
     const int pa = pt + pos_of_freq<C>(kr & (S - 1));  // disjoint bit fields
@@ -571,8 +606,8 @@ __device__ __forceinline__ void pack_outputs(const float2* lds, int half, int t,
     const float2 o = make_float2(A.y + B.y, B.x - A.x);
     const float2 w = cmul(wt, g_twiddle[kr * (DSSM_TWN / M)]);
     const float2 wo = cmul(w, o);
-    out[(size_t)r * CM::T + t] = make_float2(e.x + wo.x + deff, sg * (e.y + wo.y));
-    out[(size_t)(r | RB) * CM::T + t] = make_float2(e.x - wo.x + deff, sg * (e.y - wo.y));
+    if (st0) out[SS::slot(t, r)] = make_float2(e.x + wo.x + deff, sg * (e.y + wo.y));
+    if (st1) out[SS::slot(t, r | RB)] = make_float2(e.x - wo.x + deff, sg * (e.y - wo.y));
   }
 }
 
@@ -603,7 +638,9 @@ __device__ __forceinline__ void buf_store_f32(BufRes r, int voff, int soff, floa
 }
 
 // Spectrum of the kernel, in the convolution's layout:
-//   spec[h, half, e] = ( X[2 k + half] + D_f + D_b ) / (2M),   e = r T + t,
+//   spec[h, half, e] = ( X[2 k + half] + D_f + D_b ) / (2M),
+//   e = SpecStore slot of (t, r) for the stored bins (the others are the
+//   conjugates of stored partners and are not written),
 //   k = frequency of the convolution's transform position 16 t + r,
 //   X = DFT_2M( pad(Re K_f) ) + conj( DFT_2M( pad(Re K_b) ) ).
 // The feed-through D u is the convolution with D at tap 0, whose transform is
@@ -707,12 +744,13 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        if (!SpecStore<LOG2M>::stored(half, t, r)) continue;
         const int k = kt | freq_of_pos<CM>(r);  // output bin X[2k + half]
         const int k2 = half ? (M - 1 - k) : ((M - k) & (M - 1));
         const float2 A = lds[C::pad(pos_of_freq<C>(k))];
         const float2 B = lds[C::pad(pos_of_freq<C>(k2))];
         // (A + conj B) + i (conj A - B)
-        out[(size_t)r * CM::T + t] =
+        out[SpecStore<LOG2M>::slot(t, r)] =
             make_float2(A.x + B.x + A.y + B.y + deff, sg * (A.y - B.y + A.x - B.x));
       }
     }
@@ -751,14 +789,41 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
       v[r] = make_float2(buf_load_f32(ur1, o, 0), buf_load_f32(ur2, o, 0));
     }
   };
-  // spectrum bin at position PT lt + r lives at r T + lt (as the spectrum
-  // kernels, which use the same PT, store it); always in range
+  // spectrum bin at position PT lt + r: stored at slot r T + lt, or the
+  // conjugate of a stored partner (SpecStore, shared with spectrum_kernel,
+  // which uses the same PT); every access in range
   static_assert(C::PT == Cfg<LOG2M, 16>::PT, "spectrum layout is shared with spectrum_kernel");
+  using SS = SpecStore<LOG2M>;
   const BufRes sr = buf_res(spec + (size_t)h * 2 * C::M, 2u * C::M * 8u);
-  auto load_spec = [&](int half, float2* v) {
-    const int o = 8 * opaque(lt);
+  auto load_spec = [&](auto half_c, float2* v) {
+    constexpr int half = decltype(half_c)::value;
+    const int lto = opaque(lt);
+    const int o = 8 * lto;
 #pragma unroll
-    for (int r = 0; r < C::PT; ++r) v[r] = buf_load_f32x2(sr, o, 8 * (half * C::M + r * C::T));
+    for (int r = 0; r < (SS::kHerm ? 8 : C::PT); ++r)
+      v[r] = buf_load_f32x2(sr, o, 8 * (half * C::M + r * C::T));
+    if constexpr (SS::kHerm) {
+      // registers 8..15 at slot (15 - r) T + lane part: odd half, thread
+      // T-1-lt conjugated; even half, the thread's own slots (lt < Q: lane
+      // part 8T + lt) or the partner thread's, conjugated
+      if constexpr (half == 1) {
+        const int op = 8 * (C::T - 1 - lto);
+#pragma unroll
+        for (int r = 8; r < C::PT; ++r)
+          v[r] = cconj(buf_load_f32x2(sr, op, 8 * (C::M + (15 - r) * C::T)));
+      } else {
+        constexpr int Q = SS::Q;
+        // partner thread (16 - j) Q + (Q - 1 - (lt mod Q)) = 17 Q - 1 - lt
+        const bool own = lto < Q;
+        const int op = 8 * (own ? 8 * C::T + lto : 17 * Q - 1 - lto);
+        const float sgn = own ? 1.f : -1.f;
+#pragma unroll
+        for (int r = 8; r < C::PT; ++r) {
+          const float2 s = buf_load_f32x2(sr, op, 8 * (15 - r) * C::T);
+          v[r] = make_float2(s.x, sgn * s.y);
+        }
+      }
+    }
   };
 
   float2 ve[C::PT], vo[C::PT], sv[C::PT];
@@ -785,7 +850,7 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
     lds_read<C, 1>(lds, lt, ve);
     fwd_tail<C, 1>(ve, lds, lt, tab);
   }
-  load_spec(0, sv);
+  load_spec(std::integral_constant<int, 0>{}, sv);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], sv[r]);
   inv_head<C>(ve, lds, lt, tab);
@@ -798,7 +863,7 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
     lds_read<C, 1>(lds, lt, vo);
     fwd_tail<C, 1>(vo, lds, lt, tab);
   }
-  load_spec(1, sv);
+  load_spec(std::integral_constant<int, 1>{}, sv);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], sv[r]);
   inv_head<C>(vo, lds, lt, tab);
