@@ -558,7 +558,10 @@ __device__ __forceinline__ float2 cm(float2 a, float2 b) {
 // x[b,p,:] = scan of v[b,p,:] with multiplier lambda[p]; planar re/im rows.
 // Each tile of 4096 steps is staged through LDS (coalesced float4 global
 // accesses; lane l then owns steps 16 l .. 16 l + 15, padded one slot per 16
-// so the per-lane reads are conflict-free).
+// so the per-lane reads are conflict-free).  With L a multiple of 4 the next
+// tile is loaded into registers once the current one is in LDS and its
+// segments' end states are formed, so the loads overlap the carries, the
+// outputs and the stores of the current tile.
 constexpr int kPadT = kTile + kTile / 16;
 __device__ __forceinline__ int tpad(int e) { return e + (e >> 4); }
 
@@ -592,19 +595,32 @@ __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restric
   float* xim = xre + L;
   const bool vec = (L & 3) == 0;
 
+  // float4 groups e = 4 (t + kLanes k) of the next tile (zero beyond L; with
+  // L a multiple of 4 a group lies wholly inside or outside)
+  constexpr int kG = kTile / (4 * kLanes);
+  float4 nre[kG], nim[kG];
+  auto fetch = [&](int at) {
+    const int m = min(kTile, L - at);
+#pragma unroll
+    for (int k = 0; k < kG; ++k) {
+      const int e = 4 * (t + kLanes * k);
+      nre[k] = nim[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e < m) {
+        nre[k] = *reinterpret_cast<const float4*>(vre + at + e);
+        nim[k] = *reinterpret_cast<const float4*>(vim + at + e);
+      }
+    }
+  };
+  if (vec) fetch(0);
+
   for (int base = 0; base < L; base += kTile) {
     const int n = min(kTile, L - base);
     // stage the tile (zero beyond L)
     if (vec) {
 #pragma unroll
-      for (int k = 0; k < kTile / (4 * kLanes); ++k) {
-        const int e = 4 * (t + kLanes * k);
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
-        if (e < n) {
-          a = *reinterpret_cast<const float4*>(vre + base + e);
-          c = *reinterpret_cast<const float4*>(vim + base + e);
-        }
-        const int q = tpad(e);  // e is a multiple of 4: the 4 slots stay contiguous
+      for (int k = 0; k < kG; ++k) {
+        const int q = tpad(4 * (t + kLanes * k));  // the 4 slots stay contiguous
+        const float4 a = nre[k], c = nim[k];
         sre[q] = a.x; sre[q + 1] = a.y; sre[q + 2] = a.z; sre[q + 3] = a.w;
         sim[q] = c.x; sim[q + 1] = c.y; sim[q + 2] = c.z; sim[q + 3] = c.w;
       }
@@ -628,6 +644,7 @@ __global__ __launch_bounds__(kLanes) void s5_scan_kernel(const float2* __restric
       const float2 m = cm(lm, s);
       s = make_float2(m.x + vv[i].x, m.y + vv[i].y);
     }
+    if (vec && base + kTile < L) fetch(base + kTile);
     const float2 cin = carry;
     if (t == 0) {  // the tile's first segment starts from the carried state
       const float2 m = cm(mu[0], cin);
