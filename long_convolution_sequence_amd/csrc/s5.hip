@@ -53,16 +53,18 @@ constexpr int kBTS = kKC + 8;  // LDS row stride (fp16) of the transposed B tile
 // Element A[i][k] of a contraction (zero outside M x K):
 // kind 0: A = [Re Bbar; Im Bbar] interleaved by p (M = 2P rows, K = H)
 // kind 1: A = [Re C, -Im C] interleaved by p      (M = H rows,  K = 2P)
+// Branch-free: the load always reads an in-range element (clamped indices)
+// and the result is selected afterwards, so a thread's loads of several
+// elements are all in flight together instead of one round trip each.
 __device__ __forceinline__ float a_elem(int kind, const float2* __restrict__ Bbar,
                                         const float2* __restrict__ C, int H, int P, int i, int k) {
-  if (kind == 0) {
-    if (i >= 2 * P || k >= H) return 0.f;
-    const float2 v = Bbar[(size_t)(i >> 1) * H + k];
-    return (i & 1) ? v.y : v.x;
-  }
-  if (i >= H || k >= 2 * P) return 0.f;
-  const float2 v = C[(size_t)i * P + (k >> 1)];
-  return (k & 1) ? -v.y : v.x;
+  const bool k0 = kind == 0;
+  const bool in = k0 ? (i < 2 * P && k < H) : (i < H && k < 2 * P);
+  const size_t idx = k0 ? (size_t)min(i >> 1, P - 1) * H + min(k, H - 1)
+                        : (size_t)min(i, H - 1) * P + min(k >> 1, P - 1);
+  const float2 v = (k0 ? Bbar : C)[idx];
+  const float e = k0 ? ((i & 1) ? v.y : v.x) : ((k & 1) ? -v.y : v.x);
+  return in ? e : 0.f;
 }
 
 // A^T as the B operand of v_mfma_f32_16x16x32_f16, split: for row tile it
