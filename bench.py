@@ -118,6 +118,29 @@ def time_path(path, dev, us, ys, ws, steps, warmup, bi, hip, breakdown_steps=20)
     return (t1 - t0) * 1e3 / steps, dom, stages
 
 
+def time_plain(dev, us, ys, ws, steps, bi):
+    """Wall ms per layer forward (FFT view) by plain calls with no event stamps,
+    for comparison with the timed region, whose convolution launch carries a
+    GPU event pair on every step."""
+    import torch
+    from long_convolution_sequence_amd import binding as bd
+
+    R = len(us)
+
+    def call(k):
+        bd.forward_fft(us[k % R], dev["log_re"], dev["log_im"], dev["W"], dev["D"],
+                       bidirectional=bi, y=ys[k % R], workspace=ws)
+
+    for k in range(3):
+        call(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        call(k)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 def time_s5(steps, warmup, hip, rotate=5, breakdown_steps=10):
     """Timed S5 layer forwards on the S5 workload (B=4, H=256, P=128, L=16384):
     plain calls over `rotate` input/output sets (5 x 2 x 67 MB, beyond the
@@ -411,6 +434,7 @@ def main():
         },
         "extra": {
             "stage_ms_breakdown": {"kernel_spectrum": stages[0], "conv": stages[1]},
+            "fft_plain_calls_ms_per_step": time_plain(dev, us, ys, ws_fft, a.steps, bi),
             "full_call_hbm_gbs": alg_bytes / (ms * 1e-3) / 1e9,
             "scan_path": scan_path_summary(B, H, N, L, bi, ms_scan, scan_ms, stages_scan),
             "rotated_sets": a.rotate,
