@@ -229,7 +229,9 @@ int dssm_forward_scan_state(const float* u, const dssm_dlr_params* p, const dssm
  * s->L must be 1 and s->bidirectional 0.  lambda is formed in float64 and
  * rounded once to float32 per call; a run of k steps is the float32 chain of
  * k products, so its error grows with k like any float32 recurrence.  No
- * workspace. */
+ * workspace.  Requires B H <= 262140 (one wave per (b, h), four per
+ * workgroup, at most 65535 workgroups); larger B H returns
+ * DSSM_ERR_UNSUPPORTED. */
 int dssm_step(const float* u_t, const dssm_dlr_params* p, const dssm_shape* s, float* x,
               float* y_t, void* stream);
 
@@ -246,9 +248,13 @@ int dssm_step(const float* u_t, const dssm_dlr_params* p, const dssm_shape* s, f
  *   Bbar   [P, H, 2] complex
  *   C      [H, P, 2] complex
  *   D      [H]       float32
- * The projections run on the matrix cores in float32 (a dense contraction
- * over H and over 2P); the recurrence is a segmented complex scan whose
- * carries use powers of lambda computed in float64.  bidirectional = 1 is
+ * The projections are dense contractions (over H, and over 2P) on the
+ * matrix cores with split operands: each float32 operand is written as an
+ * fp16 hi part plus an fp16 lo part after a power-of-two scale per row (or
+ * per time step), and three fp16 products (hi.hi + hi.lo + lo.hi) are
+ * accumulated in float32, about 22 significant bits per operand.  The
+ * recurrence is a segmented complex scan whose carries use powers of lambda
+ * computed in float64.  bidirectional = 1 is
  * DSSM_ERR_UNSUPPORTED (the pages define no bidirectional S5).
  * Requires 1 <= P <= 4096, L <= 2^24, B <= 65535.
  * ------------------------------------------------------------------------ */

@@ -149,7 +149,9 @@ def _torch():
     return torch
 
 
-def _dev_f32(t, name):
+def _dev_f32(t, name, numel=None, device=None):
+    """t as a contiguous float32 device tensor (complex64 viewed as pairs),
+    with `numel` float32 elements and on `device` when those are given."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
@@ -161,6 +163,10 @@ def _dev_f32(t, name):
         raise ValueError("%s must be a device tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d float32 elements, expected %d" % (name, t.numel(), numel))
     return t
 
 
@@ -170,30 +176,43 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(op, shape, workspace, device):
+def _on_stream(stream):
+    """Context for the binding's own allocations (workspace, default outputs):
+    made on the stream the kernels run on, so the caching allocator does not
+    hand their memory to another stream's allocation while those kernels may
+    still use it."""
+    import contextlib
+
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _workspace(op, shape, workspace, device, stream=None):
     torch = _torch()
     need = ctypes.c_size_t(0)
     check(lib().dssm_workspace_size(op, ctypes.byref(shape), ctypes.byref(need)))
     if workspace is None:
-        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=device)
+        with _on_stream(stream):
+            workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=device)
+    elif workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def _params(log_re, log_im, W, D, ndir, H, N):
-    lr = _dev_f32(log_re, "log_re")
-    li = _dev_f32(log_im, "log_im")
-    w = _dev_f32(W, "W")
+def _empty(shape, dtype, device, stream):
+    torch = _torch()
+    with _on_stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _params(log_re, log_im, W, D, ndir, H, N, device):
+    n = ndir * H * N
+    lr = _dev_f32(log_re, "log_re", n, device)
+    li = _dev_f32(log_im, "log_im", n, device)
+    w = _dev_f32(W, "W", 2 * n, device)
     if D is None:  # generator only
-        if lr.numel() != ndir * H * N or li.numel() != ndir * H * N or w.numel() != 2 * ndir * H * N:
-            raise ValueError("parameter sizes do not match [ndir, H, N]")
         return DLRParams(lr.data_ptr(), li.data_ptr(), w.data_ptr(), None), (lr, li, w)
-    d = _dev_f32(D, "D")
-    if lr.numel() != ndir * H * N or li.numel() != ndir * H * N:
-        raise ValueError("log_re/log_im must have ndir*H*N elements")
-    if w.numel() != 2 * ndir * H * N:
-        raise ValueError("W must have ndir*H*N complex elements")
-    if d.numel() != ndir * H:
-        raise ValueError("D must have ndir*H elements")
+    d = _dev_f32(D, "D", ndir * H, device)
     keep = (lr, li, w, d)
     return DLRParams(lr.data_ptr(), li.data_ptr(), w.data_ptr(), d.data_ptr()), keep
 
@@ -203,15 +222,13 @@ def gen_kernel(log_re, log_im, W, L, complex_out=False, out=None, workspace=None
     W [ndir,H,N] c64.  Returns Re K [ndir,H,L] f32 or K [ndir,H,L] c64."""
     torch = _torch()
     ndir, H, N = log_re.shape
+    dev = log_re.device
     shape = Shape(1, H, N, L, ndir - 1)
-    p, keep = _params(log_re, log_im, W, None, ndir, H, N)
+    p, keep = _params(log_re, log_im, W, None, ndir, H, N, dev)
     if out is None:
-        if complex_out:
-            out = torch.empty(ndir, H, L, dtype=torch.complex64, device=log_re.device)
-        else:
-            out = torch.empty(ndir, H, L, dtype=torch.float32, device=log_re.device)
-    o = _dev_f32(out, "out")
-    ws, nbytes = _workspace(OP_GEN, shape, workspace, log_re.device)
+        out = _empty((ndir, H, L), torch.complex64 if complex_out else torch.float32, dev, stream)
+    o = _dev_f32(out, "out", ndir * H * L * (2 if complex_out else 1), dev)
+    ws, nbytes = _workspace(OP_GEN, shape, workspace, dev, stream)
     check(lib().dssm_gen_kernel(ctypes.byref(p), ctypes.byref(shape), int(bool(complex_out)),
                                 o.data_ptr(), ws.data_ptr(), nbytes, _stream(stream)))
     del keep
@@ -223,33 +240,40 @@ def gen_kernel_cast(log_re, log_im, W, L, cast=CAST_RE, out=None, workspace=None
     DLR-prod), [ndir,H,L] f32."""
     torch = _torch()
     ndir, H, N = log_re.shape
+    dev = log_re.device
     shape = Shape(1, H, N, L, ndir - 1)
-    p, keep = _params(log_re, log_im, W, None, ndir, H, N)
+    p, keep = _params(log_re, log_im, W, None, ndir, H, N, dev)
     if out is None:
-        out = torch.empty(ndir, H, L, dtype=torch.float32, device=log_re.device)
-    o = _dev_f32(out, "out")
-    ws, nbytes = _workspace(OP_GEN, shape, workspace, log_re.device)
+        out = _empty((ndir, H, L), torch.float32, dev, stream)
+    o = _dev_f32(out, "out", ndir * H * L, dev)
+    ws, nbytes = _workspace(OP_GEN, shape, workspace, dev, stream)
     check(lib().dssm_gen_kernel_cast(ctypes.byref(p), ctypes.byref(shape), int(cast),
                                      o.data_ptr(), ws.data_ptr(), nbytes, _stream(stream)))
     del keep
     return out
 
 
+def _rows(u, name="u"):
+    uu = _dev_f32(u, name)
+    if uu.dim() != 3:
+        raise ValueError("%s must be [B, H, L]" % name)
+    return uu
+
+
 def _forward(fn, op, u, log_re, log_im, W, D, bidirectional, y, workspace, stream, events=None,
              cast=None):
     torch = _torch()
-    uu = _dev_f32(u, "u")
-    if uu.dim() != 3:
-        raise ValueError("u must be [B, H, L]")
+    uu = _rows(u)
     B, H, L = uu.shape
+    dev = uu.device
     ndir = 2 if bidirectional else 1
     N = log_re.shape[-1]
     shape = Shape(B, H, N, L, int(bool(bidirectional)))
-    p, keep = _params(log_re, log_im, W, D, ndir, H, N)
+    p, keep = _params(log_re, log_im, W, D, ndir, H, N, dev)
     if y is None:
-        y = torch.empty_like(uu)
-    yy = _dev_f32(y, "y")
-    ws, nbytes = _workspace(op, shape, workspace, uu.device)
+        y = _empty(uu.shape, torch.float32, dev, stream)
+    yy = _dev_f32(y, "y", uu.numel(), dev)
+    ws, nbytes = _workspace(op, shape, workspace, dev, stream)
     args = [uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape)]
     if cast is not None:
         args.append(int(cast))
@@ -282,25 +306,24 @@ def backward(u, dy, log_re, log_im, W, D, bidirectional=False, du=None, workspac
     and a dict dlog_re, dlog_im [ndir,H,N] f32, dW [ndir,H,N] c64
     (d/d Re W + i d/d Im W), dD [ndir,H] f32."""
     torch = _torch()
-    uu = _dev_f32(u, "u")
-    gg = _dev_f32(dy, "dy")
-    if uu.dim() != 3 or gg.shape != uu.shape:
-        raise ValueError("u and dy must be [B, H, L] of the same shape")
+    uu = _rows(u)
+    dev = uu.device
+    gg = _dev_f32(dy, "dy", uu.numel(), dev)
     B, H, L = uu.shape
     ndir = 2 if bidirectional else 1
     N = log_re.shape[-1]
     shape = Shape(B, H, N, L, int(bool(bidirectional)))
-    p, keep = _params(log_re, log_im, W, D, ndir, H, N)
+    p, keep = _params(log_re, log_im, W, D, ndir, H, N, dev)
     if du is None:
-        du = torch.empty_like(uu)
-    dd = _dev_f32(du, "du")
-    dev_ = uu.device
-    out = dict(dlog_re=torch.empty(ndir, H, N, device=dev_), dlog_im=torch.empty(ndir, H, N, device=dev_),
-               dW=torch.empty(ndir, H, N, dtype=torch.complex64, device=dev_),
-               dD=torch.empty(ndir, H, device=dev_))
+        du = _empty(uu.shape, torch.float32, dev, stream)
+    dd = _dev_f32(du, "du", uu.numel(), dev)
+    out = dict(dlog_re=_empty((ndir, H, N), torch.float32, dev, stream),
+               dlog_im=_empty((ndir, H, N), torch.float32, dev, stream),
+               dW=_empty((ndir, H, N), torch.complex64, dev, stream),
+               dD=_empty((ndir, H), torch.float32, dev, stream))
     g = Grads(out["dlog_re"].data_ptr(), out["dlog_im"].data_ptr(), out["dW"].data_ptr(),
               out["dD"].data_ptr())
-    ws, nbytes = _workspace(OP_BWD, shape, workspace, dev_)
+    ws, nbytes = _workspace(OP_BWD, shape, workspace, dev, stream)
     check(lib().dssm_backward(uu.data_ptr(), gg.data_ptr(), ctypes.byref(p), ctypes.byref(shape),
                               dd.data_ptr(), ctypes.byref(g), ws.data_ptr(), nbytes,
                               _stream(stream)))
@@ -319,20 +342,17 @@ def forward_scan_state(u, log_re, log_im, W, D, x, y=None, workspace=None, strea
     state x [B,H,N] c64 (updated in place to the state after the last step).
     u [B,H,L] f32 -> y [B,H,L]."""
     torch = _torch()
-    uu = _dev_f32(u, "u")
-    if uu.dim() != 3:
-        raise ValueError("u must be [B, H, L]")
+    uu = _rows(u)
     B, H, L = uu.shape
+    dev = uu.device
     N = log_re.shape[-1]
     shape = Shape(B, H, N, L, 0)
-    p, keep = _params(log_re, log_im, W, D, 1, H, N)
-    xx = _dev_f32(x, "x")
-    if xx.numel() != 2 * B * H * N:
-        raise ValueError("x must be [B, H, N] complex")
+    p, keep = _params(log_re, log_im, W, D, 1, H, N, dev)
+    xx = _dev_f32(x, "x", 2 * B * H * N, dev)
     if y is None:
-        y = torch.empty_like(uu)
-    yy = _dev_f32(y, "y")
-    ws, nbytes = _workspace(OP_SCAN, shape, workspace, uu.device)
+        y = _empty(uu.shape, torch.float32, dev, stream)
+    yy = _dev_f32(y, "y", uu.numel(), dev)
+    ws, nbytes = _workspace(OP_SCAN, shape, workspace, dev, stream)
     check(lib().dssm_forward_scan_state(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape),
                                         xx.data_ptr(), yy.data_ptr(), ws.data_ptr(), nbytes,
                                         _stream(stream)))
@@ -348,15 +368,14 @@ def step(u_t, log_re, log_im, W, D, x, y=None, stream=None):
     if uu.dim() != 2:
         raise ValueError("u_t must be [B, H]")
     B, H = uu.shape
+    dev = uu.device
     N = log_re.shape[-1]
     shape = Shape(B, H, N, 1, 0)
-    p, keep = _params(log_re, log_im, W, D, 1, H, N)
-    xx = _dev_f32(x, "x")
-    if xx.numel() != 2 * B * H * N:
-        raise ValueError("x must be [B, H, N] complex")
+    p, keep = _params(log_re, log_im, W, D, 1, H, N, dev)
+    xx = _dev_f32(x, "x", 2 * B * H * N, dev)
     if y is None:
-        y = torch.empty_like(uu)
-    yy = _dev_f32(y, "y")
+        y = _empty(uu.shape, torch.float32, dev, stream)
+    yy = _dev_f32(y, "y", uu.numel(), dev)
     check(lib().dssm_step(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape), xx.data_ptr(),
                           yy.data_ptr(), _stream(stream)))
     del keep
@@ -384,35 +403,40 @@ def s5_workspace_size(B, H, P, L):
     return out.value
 
 
+def _s5_workspace(shape, workspace, device, stream):
+    torch = _torch()
+    need = ctypes.c_size_t(0)
+    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    if workspace is None:
+        with _on_stream(stream):
+            workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=device)
+    elif workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=None):
     """S5 layer forward.  u [B,H,L] f32, lam [P] c64, Bbar [P,H] c64,
     C [H,P] c64, D [H] f32 -> y [B,H,L] f32.  events: optional 8 raw
     hipEvent_t handles, a start/stop pair per kernel (pack, proj_in, scan,
     proj_out)."""
     torch = _torch()
-    uu = _dev_f32(u, "u")
-    if uu.dim() != 3:
-        raise ValueError("u must be [B, H, L]")
+    uu = _rows(u)
     B, H, L = uu.shape
-    lm = _dev_f32(lam, "lam")
+    dev = uu.device
+    lm = _dev_f32(lam, "lam", device=dev)
     P = lm.numel() // 2
-    bb = _dev_f32(Bbar, "Bbar")
-    cc = _dev_f32(C, "C")
-    dd = _dev_f32(D, "D")
-    if bb.numel() != 2 * P * H or cc.numel() != 2 * H * P or dd.numel() != H:
-        raise ValueError("Bbar must be [P,H], C [H,P] complex and D [H]")
+    bb = _dev_f32(Bbar, "Bbar", 2 * P * H, dev)
+    cc = _dev_f32(C, "C", 2 * H * P, dev)
+    dd = _dev_f32(D, "D", H, dev)
     shape = S5Shape(B, H, P, L, 0)
     prm = S5Params(lm.data_ptr(), bb.data_ptr(), cc.data_ptr(), dd.data_ptr())
     if y is None:
-        y = torch.empty_like(uu)
-    yy = _dev_f32(y, "y")
-    need = ctypes.c_size_t(0)
-    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=uu.device)
-    nbytes = workspace.numel() * workspace.element_size()
+        y = _empty(uu.shape, torch.float32, dev, stream)
+    yy = _dev_f32(y, "y", uu.numel(), dev)
+    ws, nbytes = _s5_workspace(shape, workspace, dev, stream)
     args = [uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape), yy.data_ptr(),
-            workspace.data_ptr(), nbytes, _stream(stream)]
+            ws.data_ptr(), nbytes, _stream(stream)]
     if events is None:
         check(lib().dssm_s5_forward(*args))
     else:
@@ -426,33 +450,24 @@ def s5_forward_tv(u, lam_c, Bt, C, D, delta, step, y=None, workspace=None, strea
     f32, lam_c [P] c64, Bt [P,H] c64, C [H,P] c64, D [H] f32, delta [P] f32,
     step [B,L] f32 -> y [B,H,L] f32."""
     torch = _torch()
-    uu = _dev_f32(u, "u")
-    if uu.dim() != 3:
-        raise ValueError("u must be [B, H, L]")
+    uu = _rows(u)
     B, H, L = uu.shape
-    lm = _dev_f32(lam_c, "lam_c")
+    dev = uu.device
+    lm = _dev_f32(lam_c, "lam_c", device=dev)
     P = lm.numel() // 2
-    bb = _dev_f32(Bt, "Bt")
-    cc = _dev_f32(C, "C")
-    dd = _dev_f32(D, "D")
-    dl = _dev_f32(delta, "delta")
-    ss = _dev_f32(step, "step")
-    if bb.numel() != 2 * P * H or cc.numel() != 2 * H * P or dd.numel() != H:
-        raise ValueError("Bt must be [P,H], C [H,P] complex and D [H]")
-    if dl.numel() != P or ss.numel() != B * L:
-        raise ValueError("delta must be [P] and step [B, L]")
+    bb = _dev_f32(Bt, "Bt", 2 * P * H, dev)
+    cc = _dev_f32(C, "C", 2 * H * P, dev)
+    dd = _dev_f32(D, "D", H, dev)
+    dl = _dev_f32(delta, "delta", P, dev)
+    ss = _dev_f32(step, "step", B * L, dev)
     shape = S5Shape(B, H, P, L, 0)
     prm = S5TVParams(lm.data_ptr(), bb.data_ptr(), cc.data_ptr(), dd.data_ptr(), dl.data_ptr())
     if y is None:
-        y = torch.empty_like(uu)
-    yy = _dev_f32(y, "y")
-    need = ctypes.c_size_t(0)
-    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
-    if workspace is None:
-        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=uu.device)
-    nbytes = workspace.numel() * workspace.element_size()
+        y = _empty(uu.shape, torch.float32, dev, stream)
+    yy = _dev_f32(y, "y", uu.numel(), dev)
+    ws, nbytes = _s5_workspace(shape, workspace, dev, stream)
     check(lib().dssm_s5_forward_tv(uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape),
-                                   ss.data_ptr(), yy.data_ptr(), workspace.data_ptr(), nbytes,
+                                   ss.data_ptr(), yy.data_ptr(), ws.data_ptr(), nbytes,
                                    _stream(stream)))
     return y
 
