@@ -27,7 +27,9 @@
  *   only enqueues kernels on `stream` and returns; it never synchronises.
  * - Ownership: the caller allocates and owns every buffer, including the
  *   workspace `ws` of at least the size reported by dssm_workspace_size().
- *   The library allocates no device memory and keeps no pointer after return.
+ *   The library allocates no device memory and keeps no pointer after return
+ *   (the one exception: the fixed per-device scratch array of
+ *   dssm_forward_fft_noalloc, part of the library's device image).
  *   Outputs must not alias inputs.  The workspace may be reused by later calls
  *   on the same stream; concurrent calls need distinct workspaces.
  * - Errors: every call returns a dssm_status.  Arguments are validated on the
@@ -35,7 +37,9 @@
  *   enqueued (except DSSM_ERR_HIP, reported by the launch itself).  No call
  *   aborts or throws.  dssm_last_error() gives a per-thread message.
  * - Thread safety: calls may be made from several threads; the only mutable
- *   library state is the per-thread last-error message.
+ *   library state is the per-thread last-error message and the per-device
+ *   scratch address of dssm_forward_fft_noalloc (looked up once under a
+ *   lock; see that call for the race between overlapping calls). 
  */
 #ifndef DSSM_H
 #define DSSM_H
@@ -46,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DSSM_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define DSSM_VERSION 10100 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 typedef enum {
@@ -152,6 +156,23 @@ int dssm_gen_kernel_cast(const dssm_dlr_params* p, const dssm_shape* s, int cast
  * returns DSSM_ERR_UNSUPPORTED (use dssm_forward_scan). */
 int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
                      float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* dssm_forward_fft without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace of dssm_forward_fft (the
+ * real kernel rows and the spectrum table) lives in a device array inside the
+ * library, 64 MiB per device, held by each device from the library's first
+ * call on it until the process ends; the call itself allocates and frees
+ * nothing.  Shapes whose workspace, dssm_workspace_size(DSSM_OP_FFT, s), is
+ * larger than 64 MiB return DSSM_ERR_UNSUPPORTED before anything is
+ * enqueued (for example B=4, H=128, L=16384 needs 42 MB; H=256, L=16384 needs
+ * 84 MB and is refused).  Every call on one device uses that device's one
+ * array: calls that overlap in time on the same device (different streams,
+ * or threads) race and give wrong results; serialise them.  Results are the
+ * same as dssm_forward_fft's.  Other arguments, conventions and limits as
+ * dssm_forward_fft. */
+int dssm_forward_fft_noalloc(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                             float* y, void* stream);
 
 /* dssm_forward_fft with the kernel cast `cast` in place of Re K: with
  * DSSM_CAST_RE_IM each direction's convolution applies Re K_j * Im K_j (the

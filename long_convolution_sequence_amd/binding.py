@@ -23,7 +23,8 @@ CAST_RE, CAST_RE_IM = 0, 1  # Re K, or Re K * Im K (DLR-prod)
 # Every function the header declares (checked by the ABI tests).
 EXPORTS = [
     "dssm_version", "dssm_status_string", "dssm_last_error", "dssm_workspace_size",
-    "dssm_gen_kernel", "dssm_gen_kernel_cast", "dssm_forward_fft", "dssm_forward_fft_cast",
+    "dssm_gen_kernel", "dssm_gen_kernel_cast", "dssm_forward_fft", "dssm_forward_fft_noalloc",
+    "dssm_forward_fft_cast",
     "dssm_forward_scan", "dssm_backward",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
     "dssm_forward_scan_state", "dssm_step",
@@ -108,6 +109,9 @@ def lib():
         f.restype = ctypes.c_int
         f.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, sz, vp,
                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.dssm_forward_fft_noalloc.restype = ctypes.c_int
+    L.dssm_forward_fft_noalloc.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
+                                           vp, vp]
     L.dssm_forward_scan_state.restype = ctypes.c_int
     L.dssm_forward_scan_state.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape),
                                           vp, vp, vp, sz, vp]
@@ -290,6 +294,24 @@ def forward_fft(u, log_re, log_im, W, D, bidirectional=False, y=None, workspace=
     """Layer forward by the FFT convolution view.  u [B,H,L] f32 -> y [B,H,L]."""
     return _forward(lib().dssm_forward_fft, OP_FFT, u, log_re, log_im, W, D, bidirectional, y,
                     workspace, stream)
+
+
+def forward_fft_noalloc(u, log_re, log_im, W, D, y, bidirectional=False, stream=None):
+    """forward_fft into the caller's y with the library's fixed per-device
+    scratch array as workspace: nothing is allocated, here or in the library.
+    Calls that overlap in time on one device race on that array."""
+    uu = _rows(u)
+    B, H, L = uu.shape
+    dev = uu.device
+    ndir = 2 if bidirectional else 1
+    N = log_re.shape[-1]
+    shape = Shape(B, H, N, L, int(bool(bidirectional)))
+    p, keep = _params(log_re, log_im, W, D, ndir, H, N, dev)
+    yy = _dev_f32(y, "y", uu.numel(), dev)
+    check(lib().dssm_forward_fft_noalloc(uu.data_ptr(), ctypes.byref(p), ctypes.byref(shape),
+                                         yy.data_ptr(), _stream(stream)))
+    del keep
+    return y
 
 
 def forward_fft_cast(u, log_re, log_im, W, D, cast, bidirectional=False, y=None, workspace=None,

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/dssm.h"
@@ -309,6 +310,61 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
 int dssm_forward_fft(const float* u, const dssm_dlr_params* p, const dssm_shape* s, float* y,
                      void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
+}
+
+// Scratch memory of dssm_forward_fft_noalloc: the workspace of the FFT view
+// (the real kernel rows and the spectrum table) as a file-scope device array.
+// Each device holds its own copy, from the library's first use on it until
+// the process ends.  Host code never passes the symbol itself to a kernel:
+// the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call per device, then cached).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (int rc = hip_check(hipGetDevice(&dev), "hipGetDevice")) return rc;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSSM_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (int rc = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress"))
+      return rc;
+    if (!ptr) return fail(DSSM_ERR_HIP, "hipGetSymbolAddress returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSSM_OK;
+}
+}  // namespace
+
+int dssm_forward_fft_noalloc(const float* u, const dssm_dlr_params* p, const dssm_shape* s,
+                             float* y, void* stream) {
+  bool empty = false;
+  int rc = check_shape(DSSM_OP_FFT, s, &empty);
+  if (rc) return rc;
+  if (empty) return ok();
+  const size_t need = layout(DSSM_OP_FFT, s).total;
+  if (need > kScratchBytes)
+    return fail(DSSM_ERR_UNSUPPORTED,
+                "the allocation-free forward needs %zu bytes of scratch for this shape; its "
+                "maximum is %zu (use dssm_forward_fft with a caller workspace)",
+                need, kScratchBytes);
+  // argument errors are reported before the device is touched
+  if ((rc = check_params(p, true))) return rc;
+  if (!u || !y || !aligned16(u) || !aligned16(y))
+    return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
+  if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return forward_impl(DSSM_OP_FFT, u, p, s, y, ws, kScratchBytes, stream, nullptr, 0);
 }
 
 int dssm_forward_fft_cast(const float* u, const dssm_dlr_params* p, const dssm_shape* s,

@@ -339,3 +339,28 @@ def test_backward_validation():
     rc1, n1 = _ws(bd.OP_FFT, 4, 128, 64, 16384)
     assert rc == 0 and rc1 == 0 and n > n1
     assert _ws(bd.OP_BWD, 1, 1, 1, 16385)[0] == bd.DSSM_ERR_UNSUPPORTED
+
+
+def test_noalloc_forward_host_validation():
+    """dssm_forward_fft_noalloc refuses, before touching the device, argument
+    errors and shapes whose workspace exceeds its 64 MiB scratch array."""
+    fn = bd.lib().dssm_forward_fft_noalloc
+
+    def call(params, shape, u=FAKE * 2, y=FAKE * 3):
+        return fn(u, ctypes.byref(params) if params is not None else None,
+                  ctypes.byref(shape) if shape is not None else None, y, None)
+
+    good = bd.Shape(2, 3, 4, 32, 0)
+    assert call(_params(), None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(None, good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(_params({"W": FAKE + 4}), good) == bd.DSSM_ERR_INVALID_ARG
+    assert call(_params(), good, u=None) == bd.DSSM_ERR_INVALID_ARG
+    assert call(_params(), good, u=FAKE * 2, y=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG
+    assert call(_params(), bd.Shape(2, 3, 4, 16385, 0)) == bd.DSSM_ERR_UNSUPPORTED
+    # 84 MB of workspace (> 64 MiB): refused; 42 MB (the long-sequence shape) fits
+    big = bd.Shape(1, 256, 8, 16384, 0)
+    assert _ws(bd.OP_FFT, 1, 256, 8, 16384)[1] > 64 << 20
+    assert call(_params(), big) == bd.DSSM_ERR_UNSUPPORTED
+    assert b"scratch" in bd.lib().dssm_last_error()
+    assert _ws(bd.OP_FFT, 4, 128, 64, 16384)[1] <= 64 << 20
+    assert call(None, bd.Shape(0, 3, 4, 32, 0)) == 0  # empty: a no-op
