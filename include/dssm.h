@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DSSM_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define DSSM_VERSION 10200 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 typedef enum {
@@ -63,11 +63,21 @@ typedef enum {
 
 /* Operations, for dssm_workspace_size(). */
 typedef enum {
-  DSSM_OP_GEN = 0,   /* dssm_gen_kernel */
-  DSSM_OP_FFT = 1,   /* dssm_forward_fft */
-  DSSM_OP_SCAN = 2,  /* dssm_forward_scan */
-  DSSM_OP_BWD = 3    /* dssm_backward */
+  DSSM_OP_GEN = 0,     /* dssm_gen_kernel */
+  DSSM_OP_FFT = 1,     /* dssm_forward_fft */
+  DSSM_OP_SCAN = 2,    /* dssm_forward_scan */
+  DSSM_OP_BWD = 3,     /* dssm_backward */
+  DSSM_OP_S5_SCAN = 4, /* dssm_s5_forward, method DSSM_S5_SCAN (shape N = state size P) */
+  DSSM_OP_S5_FFT = 5   /* dssm_s5_forward, method DSSM_S5_FFT (shape N = state size P) */
 } dssm_op;
+
+/* How dssm_s5_forward runs the state recurrence ("Simplified State Space
+ * Layers for Sequence Modeling", section 2.3: the recurrent mode and the
+ * convolution mode of a linear time-invariant system give the same map). */
+typedef enum {
+  DSSM_S5_SCAN = 0, /* the recurrence as a parallel scan over time */
+  DSSM_S5_FFT = 1   /* per state, the convolution with lambda_p^j by FFT */
+} dssm_s5_method;
 
 /* How the complex kernel K is cast to the real kernel the convolution applies
  * (DLR page, section 2 for the real cast; section 2.1 for DLR-prod). */
@@ -119,7 +129,9 @@ const char* dssm_last_error(void);
  * nothing).  Returns DSSM_ERR_INVALID_ARG / DSSM_ERR_UNSUPPORTED exactly
  * when the corresponding compute call would.  Limits common to the DLR calls:
  * 1 <= N <= 4096, H (1 + bidirectional) <= 65535, B H L <= 2^40 and
- * B H (1 + bidirectional) <= 2^31 - 1. */
+ * B H (1 + bidirectional) <= 2^31 - 1.  For DSSM_OP_S5_SCAN / DSSM_OP_S5_FFT
+ * the shape is read as the S5 shape {B, H, P = N, L, bidirectional} and the
+ * result is dssm_s5_workspace_size() of that method. */
 int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes);
 
 /* Kernel generation: K[d,h,j] = sum_n W[d,h,n] lambda[d,h,n]^j for 0 <= j < L
@@ -274,8 +286,17 @@ int dssm_step(const float* u_t, const dssm_dlr_params* p, const dssm_shape* s, f
  * fp16 hi part plus an fp16 lo part after a power-of-two scale per row (or
  * per time step), and three fp16 products (hi.hi + hi.lo + lo.hi) are
  * accumulated in float32, about 22 significant bits per operand.  The
- * recurrence is a segmented complex scan whose carries use powers of lambda
- * computed in float64.  bidirectional = 1 is
+ * state recurrence runs by `method`:
+ *   DSSM_S5_SCAN: a segmented complex scan whose carries use powers of lambda
+ *     computed in float64 (section 2.2, the parallel scan);
+ *   DSSM_S5_FFT: per state p and batch row b, the causal convolution
+ *     x_p = (lambda_p^j)_j * v_p (section 2.3, the convolution mode), by a
+ *     complex FFT on a zero-padded circle of length 2M (M = the smallest
+ *     power of two >= max(L, 16)); the spectrum of the powers,
+ *     (1 - (lambda w^m)^M) / (1 - lambda w^m) with w = exp(-i pi / M), is
+ *     evaluated in float64 and rounded once.  Requires L <= 16384 (longer L:
+ *     DSSM_ERR_UNSUPPORTED); its workspace adds P x 2M complex values.
+ * Any other method returns DSSM_ERR_INVALID_ARG.  bidirectional = 1 is
  * DSSM_ERR_UNSUPPORTED (the pages define no bidirectional S5).
  * Requires 1 <= P <= 4096, L <= 2^24, B <= 65535.
  * ------------------------------------------------------------------------ */
@@ -291,12 +312,14 @@ typedef struct {
   const float* D;
 } dssm_s5_params;
 
-/* Bytes of workspace dssm_s5_forward needs (host only). */
-int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes);
+/* Bytes of workspace dssm_s5_forward needs with `method` (host only);
+ * dssm_s5_forward_tv takes the DSSM_S5_SCAN size. */
+int dssm_s5_workspace_size(const dssm_s5_shape* s, int method, size_t* bytes);
 
-/* y [B, H, L] from u [B, H, L]; same conventions as the DLR calls. */
-int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
-                    void* ws, size_t ws_bytes, void* stream);
+/* y [B, H, L] from u [B, H, L] by `method` (a dssm_s5_method); same
+ * conventions as the DLR calls. */
+int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, int method,
+                    float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* S5 in continuous time with a step size that changes from step to step
  * ("Simplified State Space Layers for Sequence Modeling", section 3: a
@@ -314,7 +337,7 @@ int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape
  *   0 is allowed: the state is then carried over unchanged).
  * The projections are those of dssm_s5_forward (Btilde in place of Bbar);
  * the scan forms z in float64 and the discretised values in float32.  Same
- * shape limits, workspace (dssm_s5_workspace_size) and conventions as
+ * shape limits, workspace (dssm_s5_workspace_size, DSSM_S5_SCAN) and conventions as
  * dssm_s5_forward; step must be 16-byte aligned. */
 typedef struct {
   const float* lambda_c;
@@ -328,10 +351,12 @@ int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5
                        const float* step, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Timing variant of dssm_s5_forward (n_events = 8): start/stop pairs of the
- * four kernels, in order: packing of Bbar and C, input projection, scan,
- * output projection (same event conventions as the DLR timing variants). */
+ * four stages, in order: packing of Bbar and C, input projection, the state
+ * recurrence (the scan kernel, or the spectrum and convolution kernels of
+ * DSSM_S5_FFT), output projection (same event conventions as the DLR timing
+ * variants). */
 int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s,
-                          float* y, void* ws, size_t ws_bytes, void* stream,
+                          int method, float* y, void* ws, size_t ws_bytes, void* stream,
                           void* const* events, int n_events);
 
 /* Timing variants: identical results to dssm_forward_fft / dssm_forward_scan;

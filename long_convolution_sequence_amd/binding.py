@@ -17,7 +17,8 @@ DSSM_ERR_UNSUPPORTED = -2
 DSSM_ERR_WORKSPACE = -3
 DSSM_ERR_HIP = -4
 
-OP_GEN, OP_FFT, OP_SCAN, OP_BWD = 0, 1, 2, 3
+OP_GEN, OP_FFT, OP_SCAN, OP_BWD, OP_S5_SCAN, OP_S5_FFT = 0, 1, 2, 3, 4, 5
+S5_SCAN, S5_FFT = 0, 1  # how the S5 state recurrence runs: scan, or per-state FFT convolution
 CAST_RE, CAST_RE_IM = 0, 1  # Re K, or Re K * Im K (DLR-prod)
 
 # Every function the header declares (checked by the ABI tests).
@@ -118,13 +119,15 @@ def lib():
     L.dssm_step.restype = ctypes.c_int
     L.dssm_step.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, vp]
     L.dssm_s5_workspace_size.restype = ctypes.c_int
-    L.dssm_s5_workspace_size.argtypes = [ctypes.POINTER(S5Shape), ctypes.POINTER(sz)]
+    L.dssm_s5_workspace_size.argtypes = [ctypes.POINTER(S5Shape), ctypes.c_int,
+                                         ctypes.POINTER(sz)]
     L.dssm_s5_forward.restype = ctypes.c_int
-    L.dssm_s5_forward.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape), vp, vp,
-                                  sz, vp]
+    L.dssm_s5_forward.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape),
+                                  ctypes.c_int, vp, vp, sz, vp]
     L.dssm_s5_forward_timed.restype = ctypes.c_int
-    L.dssm_s5_forward_timed.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape), vp,
-                                        vp, sz, vp, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    L.dssm_s5_forward_timed.argtypes = [vp, ctypes.POINTER(S5Params), ctypes.POINTER(S5Shape),
+                                        ctypes.c_int, vp, vp, sz, vp,
+                                        ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     L.dssm_s5_forward_tv.restype = ctypes.c_int
     L.dssm_s5_forward_tv.argtypes = [vp, ctypes.POINTER(S5TVParams), ctypes.POINTER(S5Shape), vp,
                                      vp, vp, sz, vp]
@@ -418,17 +421,17 @@ def forward_timed(path, u, log_re, log_im, W, D, events, bidirectional=False, y=
                     events=list(events))
 
 
-def s5_workspace_size(B, H, P, L):
+def s5_workspace_size(B, H, P, L, method=S5_SCAN):
     shape = S5Shape(B, H, P, L, 0)
     out = ctypes.c_size_t(0)
-    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
+    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), int(method), ctypes.byref(out)))
     return out.value
 
 
-def _s5_workspace(shape, workspace, device, stream):
+def _s5_workspace(shape, workspace, device, stream, method=S5_SCAN):
     torch = _torch()
     need = ctypes.c_size_t(0)
-    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), int(method), ctypes.byref(need)))
     if workspace is None:
         with _on_stream(stream):
             workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=device)
@@ -437,11 +440,13 @@ def _s5_workspace(shape, workspace, device, stream):
     return workspace, workspace.numel() * workspace.element_size()
 
 
-def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=None):
+def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=None,
+               method=S5_SCAN):
     """S5 layer forward.  u [B,H,L] f32, lam [P] c64, Bbar [P,H] c64,
-    C [H,P] c64, D [H] f32 -> y [B,H,L] f32.  events: optional 8 raw
-    hipEvent_t handles, a start/stop pair per kernel (pack, proj_in, scan,
-    proj_out)."""
+    C [H,P] c64, D [H] f32 -> y [B,H,L] f32.  method: S5_SCAN (the
+    recurrence as a scan) or S5_FFT (per state, the convolution with
+    lambda^j by FFT).  events: optional 8 raw hipEvent_t handles, a
+    start/stop pair per stage (pack, proj_in, recurrence, proj_out)."""
     torch = _torch()
     uu = _rows(u)
     B, H, L = uu.shape
@@ -456,8 +461,8 @@ def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=N
     if y is None:
         y = _empty(uu.shape, torch.float32, dev, stream)
     yy = _dev_f32(y, "y", uu.numel(), dev)
-    ws, nbytes = _s5_workspace(shape, workspace, dev, stream)
-    args = [uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape), yy.data_ptr(),
+    ws, nbytes = _s5_workspace(shape, workspace, dev, stream, method)
+    args = [uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape), int(method), yy.data_ptr(),
             ws.data_ptr(), nbytes, _stream(stream)]
     if events is None:
         check(lib().dssm_s5_forward(*args))

@@ -170,8 +170,15 @@ const char* dssm_status_string(int status) {
 
 const char* dssm_last_error(void) { return g_last_error.c_str(); }
 
+static int s5_workspace(const dssm_s5_shape* s, int method, size_t* bytes);
+
 int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes) {
   if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
+  if (op == DSSM_OP_S5_SCAN || op == DSSM_OP_S5_FFT) {  // N is the state size P
+    if (!s) return fail(DSSM_ERR_INVALID_ARG, "shape is NULL");
+    const dssm_s5_shape s5{s->B, s->H, s->N, s->L, s->bidirectional};
+    return s5_workspace(&s5, op == DSSM_OP_S5_FFT ? DSSM_S5_FFT : DSSM_S5_SCAN, bytes);
+  }
   bool empty = false;
   int rc = check_shape(op, s, &empty);
   if (rc) return rc;
@@ -518,11 +525,32 @@ static int s5_check_shape(const dssm_s5_shape* s, bool* empty) {
   return DSSM_OK;
 }
 
-static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
-                   void* ws, size_t ws_bytes, void* stream, void* const* events, int n_events) {
+static int s5_check_method(int method, const dssm_s5_shape* s) {
+  if (method != DSSM_S5_SCAN && method != DSSM_S5_FFT)
+    return fail(DSSM_ERR_INVALID_ARG, "method must be DSSM_S5_SCAN (0) or DSSM_S5_FFT (1), got %d",
+                method);
+  if (method == DSSM_S5_FFT && s->L > kMaxFFTL)
+    return fail(DSSM_ERR_UNSUPPORTED,
+                "the S5 convolution view needs L <= %d (got %d); use DSSM_S5_SCAN", kMaxFFTL, s->L);
+  return DSSM_OK;
+}
+
+static int s5_workspace(const dssm_s5_shape* s, int method, size_t* bytes) {
   bool empty = false;
   int rc = s5_check_shape(s, &empty);
   if (rc) return rc;
+  if ((rc = s5_check_method(method, s))) return rc;
+  *bytes = empty ? 0 : s5_layout(s->B, s->H, s->P, s->L, method == DSSM_S5_FFT).total;
+  return ok();
+}
+
+static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, int method,
+                   float* y, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                   int n_events) {
+  bool empty = false;
+  int rc = s5_check_shape(s, &empty);
+  if (rc) return rc;
+  if ((rc = s5_check_method(method, s))) return rc;
   if (events && n_events != 8)
     return fail(DSSM_ERR_INVALID_ARG, "n_events must be 8 (got %d)", n_events);
   if (empty) return ok();
@@ -535,7 +563,8 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
     return fail(DSSM_ERR_INVALID_ARG, "u or y is NULL or not 16-byte aligned");
   if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
   if ((rc = check_events(events, n_events))) return rc;
-  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L);
+  const bool fft = method == DSSM_S5_FFT;
+  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L, fft);
   if (ws_bytes < l.total)
     return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 ws_bytes, l.total);
@@ -557,9 +586,24 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
            launch_s5_proj_in(apk_in, rexp_in, u, s->B, s->H, s->P, s->L, v, st, kev(events, 1)),
            "s5 proj_in")))
     return rc;
-  if ((rc = hip_check(launch_s5_scan(p->lambda, v, s->B, s->P, s->L, x, st, kev(events, 2)),
-                      "s5 scan")))
+  if (fft) {
+    // x_p = (lambda_p^j) * v_p: the spectrum of the powers, then the
+    // convolution of every complex row (stage 2 spans both kernels)
+    const KEvents e2 = kev(events, 2);
+    const int log2m = fft_log2m(s->L);
+    float2* spec = at<float2>(ws, l.spec);
+    if ((rc = hip_check(launch_s5_spectrum(p->lambda, s->P, log2m, spec, st,
+                                           KEvents{e2.start, nullptr}),
+                        "s5 spectrum")))
+      return rc;
+    if ((rc = hip_check(launch_s5_conv(v, spec, s->B, s->P, s->L, log2m, x, st,
+                                       KEvents{nullptr, e2.stop}),
+                        "s5 conv")))
+      return rc;
+  } else if ((rc = hip_check(launch_s5_scan(p->lambda, v, s->B, s->P, s->L, x, st, kev(events, 2)),
+                             "s5 scan"))) {
     return rc;
+  }
   if ((rc = hip_check(launch_s5_proj_out(apk_out, rexp_out, x, p->D, u, s->B, s->H, s->P, s->L,
                                          y, st, kev(events, 3)),
                       "s5 proj_out")))
@@ -613,25 +657,21 @@ int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5
   return ok();
 }
 
-int dssm_s5_workspace_size(const dssm_s5_shape* s, size_t* bytes) {
+int dssm_s5_workspace_size(const dssm_s5_shape* s, int method, size_t* bytes) {
   if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
-  bool empty = false;
-  int rc = s5_check_shape(s, &empty);
-  if (rc) return rc;
-  *bytes = empty ? 0 : s5_layout(s->B, s->H, s->P, s->L).total;
-  return ok();
+  return s5_workspace(s, method, bytes);
 }
 
-int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, float* y,
-                    void* ws, size_t ws_bytes, void* stream) {
-  return s5_impl(u, p, s, y, ws, ws_bytes, stream, nullptr, 0);
+int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, int method,
+                    float* y, void* ws, size_t ws_bytes, void* stream) {
+  return s5_impl(u, p, s, method, y, ws, ws_bytes, stream, nullptr, 0);
 }
 
 int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s,
-                          float* y, void* ws, size_t ws_bytes, void* stream, void* const* events,
-                          int n_events) {
+                          int method, float* y, void* ws, size_t ws_bytes, void* stream,
+                          void* const* events, int n_events) {
   if (!events) return fail(DSSM_ERR_INVALID_ARG, "events is NULL");
-  return s5_impl(u, p, s, y, ws, ws_bytes, stream, events, n_events);
+  return s5_impl(u, p, s, method, y, ws, ws_bytes, stream, events, n_events);
 }
 
 }  // extern "C"

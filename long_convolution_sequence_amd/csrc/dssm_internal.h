@@ -69,6 +69,16 @@ hipError_t launch_conv(const float* u, const float2* spec, int B, int H, int L, 
 
 int fft_log2m(int L);  // log2 of M = max(16, next power of two >= L)
 
+// S5 convolution view: spec [P][2][M] float2 (full storage, the bin at
+// position 16 t + r of half `half` at slot r M/16 + t) holds the spectrum of
+// lambda_p^j (j < M) on the 2M circle, scaled by 1/(2M), in float64 rounded
+// once.  launch_s5_conv: x [B][P][2][L] (real row, imaginary row) = the
+// causal convolution of v [B][P][2][L] with lambda_p^j.
+hipError_t launch_s5_spectrum(const float* lambda, int P, int log2m, float2* spec,
+                              hipStream_t st, KEvents ev = {});
+hipError_t launch_s5_conv(const float* v, const float2* spec, int B, int P, int L, int log2m,
+                          float* x, hipStream_t st, KEvents ev = {});
+
 // Kernel cotangents for the gradients, summed over the batch: part [G][H][2][M]
 // floats (G = corr_groups(B, H) batch groups) such that, for j < L,
 //   sum_b sum_i u[b,h,i] dy[b,h,i+j] = sum_g part[g][h][0][j] + part[g][h][1][j],
@@ -135,9 +145,10 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
 // S5 multi-input multi-output diagonal SSM (s5.hip)
 // ---------------------------------------------------------------------------
 struct S5Layout {
-  size_t apk_in = 0, rexp_in = 0, apk_out = 0, rexp_out = 0, v = 0, x = 0, total = 0;
+  size_t apk_in = 0, rexp_in = 0, apk_out = 0, rexp_out = 0, v = 0, x = 0, spec = 0, total = 0;
 };
-S5Layout s5_layout(int B, int H, int P, int L);
+// with_spec: the convolution view's spectrum table [P][2][M] float2 as well
+S5Layout s5_layout(int B, int H, int P, int L, bool with_spec = false);
 
 // Bbar [P,H] c64, C [H,P] c64 -> split MFMA fragment tables (16-byte aligned)
 // and per-row scale exponents.

@@ -763,21 +763,27 @@ __global__ __launch_bounds__((Cfg<PACK ? LOG2M - 1 : LOG2M, 16>::WG)) void spect
 template <int LOG2M>
 constexpr int conv_pt() { return 16; }
 
-// Convolution of a pair of batch rows (b1 = 2 pr, b2 = 2 pr + 1) of channel
-// h by one workgroup (C::G problems per workgroup when a transform is
-// smaller than a wave).  Both halves of the 2M spectrum are transformed:
-// ve = z (even bins), vo = z t (odd bins), where z = u[b1] + i u[b2].
-template <int LOG2M>
-__device__ __forceinline__ void conv_body(const float* __restrict__ u,
-                                          const float2* __restrict__ spec, int B, int H, int L,
-                                          int h, int pr, bool active, int lt, float2* lds,
-                                          const float2* tab, float* __restrict__ y) {
+// Convolution of a pair of real rows (r1, r2: 4 L bytes each; r2 is absent
+// when len2 = 0 and reads as zero) with one kernel spectrum, by one workgroup
+// (C::G problems per workgroup when a transform is smaller than a wave).
+// Both halves of the 2M spectrum are transformed: ve = z (even bins),
+// vo = z t (odd bins), where z = r1 + i r2; outputs go to the rows o1, o2
+// (o2 dropped when len2 = 0).  FULL selects the spectrum storage: every bin
+// at slot r T + t (a complex kernel, whose spectrum has no symmetry), or the
+// Hermitian half storage of SpecStore (a real kernel).  With a real kernel
+// the real and imaginary parts of the result are the two rows' convolutions;
+// with a complex one, z = Re + i Im of one complex row and the result is its
+// convolution, real part to o1 and imaginary part to o2.
+template <int LOG2M, bool FULL>
+__device__ __forceinline__ void conv_rows(const float* __restrict__ r1,
+                                          const float* __restrict__ r2, unsigned len1,
+                                          unsigned len2, const float2* __restrict__ spec_h,
+                                          int lt, float2* lds, const float2* tab,
+                                          float* __restrict__ o1, float* __restrict__ o2) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
-  const int b1 = 2 * pr, b2 = 2 * pr + 1;
-  const bool has2 = active && b2 < B;
   // rows as buffers: element n of register r sits at byte 4 n, n = lt + T(...)
-  const BufRes ur1 = buf_res(u + ((size_t)b1 * H + h) * L, active ? 4u * L : 0u);
-  const BufRes ur2 = buf_res(u + ((size_t)(has2 ? b2 : b1) * H + h) * L, has2 ? 4u * L : 0u);
+  const BufRes ur1 = buf_res(r1, len1);
+  const BufRes ur2 = buf_res(r2, len2);
 
   // The whole element offset goes in the range-checked lane offset (the
   // scalar offset is added after the check).
@@ -789,20 +795,21 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
       v[r] = make_float2(buf_load_f32(ur1, o, 0), buf_load_f32(ur2, o, 0));
     }
   };
-  // spectrum bin at position PT lt + r: stored at slot r T + lt, or the
-  // conjugate of a stored partner (SpecStore, shared with spectrum_kernel,
-  // which uses the same PT); every access in range
+  // spectrum bin at position PT lt + r: stored at slot r T + lt, or (half
+  // storage) the conjugate of a stored partner (SpecStore, shared with
+  // spectrum_kernel, which uses the same PT); every access in range
   static_assert(C::PT == Cfg<LOG2M, 16>::PT, "spectrum layout is shared with spectrum_kernel");
   using SS = SpecStore<LOG2M>;
-  const BufRes sr = buf_res(spec + (size_t)h * 2 * C::M, 2u * C::M * 8u);
+  constexpr bool kHerm = SS::kHerm && !FULL;
+  const BufRes sr = buf_res(spec_h, 2u * C::M * 8u);
   auto load_spec = [&](auto half_c, float2* v) {
     constexpr int half = decltype(half_c)::value;
     const int lto = opaque(lt);
     const int o = 8 * lto;
 #pragma unroll
-    for (int r = 0; r < (SS::kHerm ? 8 : C::PT); ++r)
+    for (int r = 0; r < (kHerm ? 8 : C::PT); ++r)
       v[r] = buf_load_f32x2(sr, o, 8 * (half * C::M + r * C::T));
-    if constexpr (SS::kHerm) {
+    if constexpr (kHerm) {
       // registers 8..15 at slot (15 - r) T + lane part: odd half, thread
       // T-1-lt conjugated; even half, the thread's own slots (lt < Q: lane
       // part 8T + lt) or the partner thread's, conjugated
@@ -878,8 +885,8 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) ve[r] = cadd(ve[r], cmul(vo[r], tlc));
   }
-  const BufRes yr1 = buf_res(y + ((size_t)b1 * H + h) * L, active ? 4u * L : 0u);
-  const BufRes yr2 = buf_res(y + ((size_t)(has2 ? b2 : b1) * H + h) * L, has2 ? 4u * L : 0u);
+  const BufRes yr1 = buf_res(o1, len1);
+  const BufRes yr2 = buf_res(o2, len2);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) {
     const int o = 4 * nat<C>(lte, r);
@@ -888,6 +895,9 @@ __device__ __forceinline__ void conv_body(const float* __restrict__ u,
   }
 }
 
+// DLR convolution: workgroup problem = (channel h, row pair pr), the batch
+// rows b1 = 2 pr and b2 = 2 pr + 1 of u [B, H, L] riding in one complex
+// sequence, with the channel's real-kernel spectrum (Hermitian half storage).
 template <int LOG2M>
 __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kernel(
     const float* __restrict__ u, const float2* __restrict__ spec, int B, int H, int L, int npairs,
@@ -900,8 +910,114 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   const int gi = threadIdx.x / C::T;
   const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
   const bool active = prob < H * npairs;
-  conv_body<LOG2M>(u, spec, B, H, L, active ? prob / npairs : 0, active ? prob % npairs : 0,
-                   active, lt, lds_all + gi * C::LDSN, tab, y);
+  const int h = active ? prob / npairs : 0;
+  const int pr = active ? prob % npairs : 0;
+  const int b1 = 2 * pr, b2 = 2 * pr + 1;
+  const bool has2 = active && b2 < B;
+  const size_t o1 = ((size_t)b1 * H + h) * L;
+  const size_t o2 = ((size_t)(has2 ? b2 : b1) * H + h) * L;
+  conv_rows<LOG2M, false>(u + o1, u + o2, active ? 4u * L : 0u, has2 ? 4u * L : 0u,
+                          spec + (size_t)h * 2 * C::M, lt, lds_all + gi * C::LDSN, tab, y + o1,
+                          y + o2);
+}
+
+// S5 convolution view: workgroup problem = one complex row (b, p) of
+// v [B][P][2][L] (real row, imaginary row), convolved with the spectrum of
+// lambda_p^j (full storage) into x [B][P][2][L].  Problems are numbered
+// p-major, so the rows that read one spectrum share an XCD's L2.
+template <int LOG2M>
+__global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void s5_conv_kernel(
+    const float* __restrict__ v, const float2* __restrict__ spec, int B, int P, int L,
+    float* __restrict__ x) {
+  using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
+  __shared__ float2 lds_all[C::G * C::LDSN];
+  __shared__ float2 tab[TwTab<C>::kAlloc];
+  twtab_init<C>(tab);
+  const int lt = threadIdx.x % C::T;
+  const int gi = threadIdx.x / C::T;
+  const int prob = xcd_grouped(blockIdx.x, gridDim.x) * C::G + gi;
+  const bool active = prob < B * P;
+  const int p = active ? prob / B : 0;
+  const int b = active ? prob % B : 0;
+  const size_t o = ((size_t)b * P + p) * 2 * L;
+  const unsigned len = active ? 4u * L : 0u;
+  conv_rows<LOG2M, true>(v + o, v + o + L, len, len, spec + (size_t)p * 2 * C::M, lt,
+                         lds_all + gi * C::LDSN, tab, x + o, x + o + L);
+}
+
+// Spectrum of the kernel kappa[j] = lambda_p^j (0 <= j < M, zero on the upper
+// half of the 2M circle) in the convolution's full storage, scaled by 1/(2M):
+//   spec[p, half, r T + t] = S[2 k + half],  k = frequency of position 16 t + r,
+//   S[m] = (1/2M) sum_{j<M} (lambda w^m)^j = (1/2M) (1 - z^M) / (1 - z),
+//   z = lambda w^m, w = exp(-i pi / M), z^M = (-1)^m lambda^M.
+// Every output sample x_k = sum_{j<=k} lambda^j v_{k-j} (k < L <= M) is then
+// the k-th sample of the 2M-circular convolution, as the taps j >= M never
+// meet a nonzero input there ("Simplified State Space Layers for Sequence
+// Modeling", section 2.3: the convolution kernel of a diagonal linear system
+// is the powers of its eigenvalues).  float64 throughout, rounded once: near
+// z = 1 (|lambda| close to 1 with a phase close to a bin's) the quotient is
+// taken as expm1(M d) / expm1(d), d = log z, which has no cancellation.
+__device__ __forceinline__ double2 zdiv(double2 a, double2 b) {
+  const double den = b.x * b.x + b.y * b.y;
+  return make_double2((a.x * b.x + a.y * b.y) / den, (a.y * b.x - a.x * b.y) / den);
+}
+
+// exp(d) - 1 for complex d = (x, y), without cancellation at small |d|:
+// Re = expm1(x) cos y - 2 sin^2(y / 2), Im = exp(x) sin y.
+__device__ __forceinline__ double2 zexpm1(double x, double y) {
+  double sh, ch;
+  sincos(0.5 * y, &sh, &ch);
+  const double s = 2.0 * sh * ch, c = 1.0 - 2.0 * sh * sh;
+  return make_double2(expm1(x) * c - 2.0 * sh * sh, exp(x) * s);
+}
+
+template <int LOG2M>
+__global__ __launch_bounds__(256) void s5_spec_kernel(const float2* __restrict__ lam, int P,
+                                                       float2* __restrict__ spec) {
+  using CM = Cfg<LOG2M, 16>;
+  constexpr int M = CM::M;
+  const int p = blockIdx.y;
+  const float2 lf = lam[p];
+  const double lre = (double)lf.x, lim = (double)lf.y;
+  // log lambda: log |lambda| = log1p(|lambda|^2 - 1) / 2 (the squares of the
+  // float32 parts are exact in float64, so |lambda|^2 - 1 is formed exactly
+  // up to one rounding), arg lambda
+  const double a2m1 = (lre * lre - 1.0) + lim * lim;
+  const double lmag = 0.5 * log1p(a2m1), larg = atan2(lim, lre);
+  // lambda^M = exp(M log lambda); the phase M arg is reduced by sincos itself
+  double sM, cM;
+  sincos((double)M * larg, &sM, &cM);
+  const double eM = exp((double)M * lmag);
+  const double2 lamM = make_double2(eM * cM, eM * sM);
+  const double scale = 1.0 / (2.0 * M);
+  float2* out = spec + (size_t)p * 2 * M;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < 2 * M; e += gridDim.x * blockDim.x) {
+    const int half = e / M, slot = e % M;
+    const int t = slot % CM::T, r = slot / CM::T;
+    const int k = freq_of_pos<CM>(16 * t + r);
+    const int m = 2 * k + half;
+    double sw, cw;
+    sincospi(-(double)m / (double)M, &sw, &cw);  // w^m = exp(-i pi m / M)
+    const double2 z = make_double2(lre * cw - lim * sw, lre * sw + lim * cw);
+    const double2 omz = make_double2(1.0 - z.x, -z.y);
+    double2 q;
+    if (omz.x * omz.x + omz.y * omz.y >= 1e-6) {
+      const double sg = (m & 1) ? -1.0 : 1.0;  // z^M = (-1)^m lambda^M
+      q = zdiv(make_double2(1.0 - sg * lamM.x, -sg * lamM.y), omz);
+    } else {
+      // d = log z = log lambda - i pi m / M, imaginary part reduced to [-pi, pi]
+      double dy = larg - M_PI * ((double)m / (double)M);
+      dy -= 2.0 * M_PI * rint(dy / (2.0 * M_PI));
+      const double2 den = zexpm1(lmag, dy);
+      if (den.x == 0.0 && den.y == 0.0) {
+        q = make_double2((double)M, 0.0);  // z = 1: the sum of M ones
+      } else {
+        // M d: its phase M dy reduced by sincos inside zexpm1
+        q = zdiv(zexpm1((double)M * lmag, (double)M * dy), den);
+      }
+    }
+    out[e] = make_float2((float)(q.x * scale), (float)(q.y * scale));
+  }
 }
 
 // Kernel cotangents of the gradients: the lagged correlations of the row
@@ -1040,7 +1156,52 @@ hipError_t conv_launch(const float* u, const float2* spec, int B, int H, int L, 
   return hipGetLastError();
 }
 
+template <int LOG2M>
+hipError_t s5_spec_launch(const float* lambda, int P, float2* spec, hipStream_t st, KEvents ev) {
+  constexpr int M = 1 << LOG2M;
+  const int per = std::max(1, 2 * M / 256);
+  launch_k(s5_spec_kernel<LOG2M>, dim3((unsigned)std::min(per, 64), (unsigned)P), dim3(256), st,
+           ev, reinterpret_cast<const float2*>(lambda), P, spec);
+  return hipGetLastError();
+}
+
+template <int LOG2M>
+hipError_t s5_conv_launch(const float* v, const float2* spec, int B, int P, int L, float* x,
+                          hipStream_t st, KEvents ev) {
+  using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
+  const long nprob = (long)B * P;
+  const long nblk = (nprob + C::G - 1) / C::G;
+  launch_k(s5_conv_kernel<LOG2M>, dim3((unsigned)nblk), dim3(C::WG), st, ev, v, spec, B, P, L, x);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_s5_spectrum(const float* lambda, int P, int log2m, float2* spec,
+                              hipStream_t st, KEvents ev) {
+  switch (log2m) {
+#define X(n) \
+  case n:    \
+    return s5_spec_launch<n>(lambda, P, spec, st, ev);
+    DSSM_FFT_CASES(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_s5_conv(const float* v, const float2* spec, int B, int P, int L, int log2m,
+                          float* x, hipStream_t st, KEvents ev) {
+  switch (log2m) {
+#define X(n) \
+  case n:    \
+    return s5_conv_launch<n>(v, spec, B, P, L, x, st, ev);
+    DSSM_FFT_CASES(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 int fft_log2m(int L) {
   int l = 4;

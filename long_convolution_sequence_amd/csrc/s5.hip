@@ -910,7 +910,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(2))) voi
 
 }  // namespace
 
-S5Layout s5_layout(int B, int H, int P, int L) {
+S5Layout s5_layout(int B, int H, int P, int L, bool with_spec) {
   S5Layout l;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -930,6 +930,7 @@ S5Layout s5_layout(int B, int H, int P, int L) {
   l.rexp_out = take((size_t)((H + 15) / 16) * 16 * sizeof(int));
   l.v = take((size_t)B * P * 2 * L * sizeof(float));
   l.x = take((size_t)B * P * 2 * L * sizeof(float));
+  if (with_spec) l.spec = take((size_t)P * 2 * ((size_t)1 << fft_log2m(L)) * sizeof(float2));
   l.total = off;
   return l;
 }

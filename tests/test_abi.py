@@ -145,25 +145,33 @@ def test_error_message_is_per_call():
     assert bd.lib().dssm_last_error() == b""
 
 
-def _s5ws(B, H, P, L, bi=0):
+def _s5ws(B, H, P, L, bi=0, method=bd.S5_SCAN):
     s = bd.S5Shape(B, H, P, L, bi)
     out = ctypes.c_size_t(0)
-    return bd.lib().dssm_s5_workspace_size(ctypes.byref(s), ctypes.byref(out)), out.value
+    return bd.lib().dssm_s5_workspace_size(ctypes.byref(s), method, ctypes.byref(out)), out.value
 
 
-def test_s5_workspace_and_validation():
-    assert _s5ws(4, 256, 128, 16384)[0] == 0
-    assert _s5ws(-1, 2, 2, 8)[0] == bd.DSSM_ERR_INVALID_ARG
-    assert _s5ws(1, 2, 0, 8)[0] == bd.DSSM_ERR_INVALID_ARG
-    assert _s5ws(1, 2, 2, 8, 1)[0] == bd.DSSM_ERR_UNSUPPORTED
-    assert _s5ws(1, 2, 2, 8, 5)[0] == bd.DSSM_ERR_INVALID_ARG
-    assert _s5ws(1, 2, 5000, 8)[0] == bd.DSSM_ERR_UNSUPPORTED
-    assert _s5ws(0, 2, 2, 8) == (0, 0)
+@pytest.mark.parametrize("method", [bd.S5_SCAN, bd.S5_FFT])
+def test_s5_workspace_and_validation(method):
+    ws = lambda *a, **k: _s5ws(*a, method=method, **k)
+    assert ws(4, 256, 128, 16384)[0] == 0
+    assert ws(-1, 2, 2, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert ws(1, 2, 0, 8)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert ws(1, 2, 2, 8, 1)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert ws(1, 2, 2, 8, 5)[0] == bd.DSSM_ERR_INVALID_ARG
+    assert ws(1, 2, 5000, 8)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert ws(0, 2, 2, 8) == (0, 0)
+    # the generic query with N read as P gives the same sizes
+    op = bd.OP_S5_FFT if method == bd.S5_FFT else bd.OP_S5_SCAN
+    s = bd.Shape(4, 256, 128, 16384, 0)
+    out = ctypes.c_size_t(0)
+    assert bd.lib().dssm_workspace_size(op, ctypes.byref(s), ctypes.byref(out)) == 0
+    assert out.value == ws(4, 256, 128, 16384)[1]
     fn = bd.lib().dssm_s5_forward
     good = bd.S5Shape(2, 3, 4, 32, 0)
     prm = bd.S5Params(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
-    call = lambda p, s, u=FAKE * 2, y=FAKE * 3, ws=FAKE * 4, n=1 << 40: fn(
-        u, ctypes.byref(p) if p is not None else None, ctypes.byref(s), y, ws, n, None)
+    call = lambda p, s, u=FAKE * 2, y=FAKE * 3, ws=FAKE * 4, n=1 << 40, m=method: fn(
+        u, ctypes.byref(p) if p is not None else None, ctypes.byref(s), m, y, ws, n, None)
     assert call(None, good) == bd.DSSM_ERR_INVALID_ARG
     assert call(bd.S5Params(None, FAKE, FAKE, FAKE), good) == bd.DSSM_ERR_INVALID_ARG
     assert call(bd.S5Params(FAKE + 8, FAKE, FAKE, FAKE), good) == bd.DSSM_ERR_INVALID_ARG
@@ -172,7 +180,21 @@ def test_s5_workspace_and_validation():
     assert call(prm, good, n=64) == bd.DSSM_ERR_WORKSPACE
     assert call(prm, good, ws=FAKE * 4 + 16) == bd.DSSM_ERR_INVALID_ARG
     assert call(prm, bd.S5Shape(2, 3, 4, 32, 1)) == bd.DSSM_ERR_UNSUPPORTED
+    assert call(prm, good, m=2) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, m=-1) == bd.DSSM_ERR_INVALID_ARG
     assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
+
+
+def test_s5_method_limits():
+    # the convolution view stops at L = 16384 (one compute unit's LDS); the scan does not
+    assert _s5ws(1, 2, 2, 16385, method=bd.S5_SCAN)[0] == 0
+    assert _s5ws(1, 2, 2, 16385, method=bd.S5_FFT)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _s5ws(1, 2, 2, 16384, method=bd.S5_FFT)[0] == 0
+    assert _s5ws(1, 2, 2, 8, method=7)[0] == bd.DSSM_ERR_INVALID_ARG
+    # the FFT view adds the spectrum table, P x 2M complex values
+    n_scan = _s5ws(4, 256, 128, 16384, method=bd.S5_SCAN)[1]
+    n_fft = _s5ws(4, 256, 128, 16384, method=bd.S5_FFT)[1]
+    assert n_fft - n_scan >= 128 * 2 * 16384 * 8
 
 
 def test_s5_tv_validation():
@@ -210,12 +232,14 @@ def test_timed_variants_validate_events(name, n):
     assert fn(*(small + [half, n])) == bd.DSSM_ERR_WORKSPACE
 
 
-def test_s5_timed_validates_events():
+@pytest.mark.parametrize("method", [bd.S5_SCAN, bd.S5_FFT])
+def test_s5_timed_validates_events(method):
     fn = bd.lib().dssm_s5_forward_timed
     good = bd.S5Shape(2, 3, 4, 32, 0)
     prm = bd.S5Params(FAKE, FAKE + 4096, FAKE + 8192, FAKE + 12288)
     evs = (ctypes.c_void_p * 8)(*([FAKE] * 8))
-    args = [FAKE * 2, ctypes.byref(prm), ctypes.byref(good), FAKE * 3, FAKE * 4, 1 << 40, None]
+    args = [FAKE * 2, ctypes.byref(prm), ctypes.byref(good), method, FAKE * 3, FAKE * 4, 1 << 40,
+            None]
     assert fn(*(args + [None, 8])) == bd.DSSM_ERR_INVALID_ARG
     assert fn(*(args + [evs, 5])) == bd.DSSM_ERR_INVALID_ARG
     bad = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))

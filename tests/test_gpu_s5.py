@@ -13,19 +13,24 @@ from test_gpu_parity import assert_close, say, _torch
 pytestmark = pytest.mark.gpu
 
 
-def run_s5(x):
+METHODS = {"scan": bd.S5_SCAN, "fft": bd.S5_FFT}
+
+
+def run_s5(x, method="scan"):
     torch = _torch()
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
-    y = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"])
+    y = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], method=METHODS[method])
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
-def test_s5_workload_full_size():
+@pytest.mark.parametrize("method", ["scan", "fft"])
+def test_s5_workload_full_size(method):
     c = inputs.config("s5_mimo")
-    say("case: s5 workload B=%d H=%d P=%d L=%d" % (c["B"], c["H"], c["P"], c["L"]))
+    say("case: s5 workload B=%d H=%d P=%d L=%d method=%s" % (c["B"], c["H"], c["P"], c["L"],
+                                                            method))
     x = inputs.inputs_for(c)
-    y = run_s5(x)
+    y = run_s5(x, method)
     ref = oracle.s5_recurrence(x["u"], x["lam"], x["Bbar"], x["C"], x["D"])
     assert_close(y, ref, "s5/full")
     refp = oracle.s5_direct_prefix(x["u"], x["lam"], x["Bbar"], x["C"], x["D"], 256)
@@ -44,12 +49,13 @@ S5_EDGE = [
 ]
 
 
+@pytest.mark.parametrize("method", ["scan", "fft"])
 @pytest.mark.parametrize("shape", S5_EDGE, ids=["B%dH%dP%dL%d" % s for s in S5_EDGE])
-def test_s5_edge_shapes(shape):
+def test_s5_edge_shapes(shape, method):
     B, H, P, L = shape
-    say("case: s5 edge B=%d H=%d P=%d L=%d" % shape)
+    say("case: s5 edge B=%d H=%d P=%d L=%d method=%s" % (shape + (method,)))
     x = inputs.s5_inputs(B, H, P, L, seed=500 + H + P + L)
-    y = run_s5(x)
+    y = run_s5(x, method)
     ref = oracle.s5_recurrence(x["u"], x["lam"], x["Bbar"], x["C"], x["D"])
     assert_close(y, ref, "s5/edge")
     if L <= 300:
@@ -57,7 +63,8 @@ def test_s5_edge_shapes(shape):
         assert_close(y, refd, "s5/edge/direct")
 
 
-def test_s5_reduces_to_dlr_bank_on_device():
+@pytest.mark.parametrize("method", ["scan", "fft"])
+def test_s5_reduces_to_dlr_bank_on_device(method):
     """P = H, Bbar = I, C = diag(w): the S5 layer equals H scalar DLRs; the
     device S5 path must agree with the device DLR paths on it."""
     torch = _torch()
@@ -67,8 +74,9 @@ def test_s5_reduces_to_dlr_bank_on_device():
     w = (rng.normal(size=H) + 1j * rng.normal(size=H)).astype(np.complex64)
     D = rng.normal(size=H).astype(np.float32)
     u = rng.normal(size=(B, H, L)).astype(np.float32)
-    say("case: s5 reduction to DLR bank")
-    y = run_s5(dict(u=u, lam=lam, Bbar=np.eye(H, dtype=np.complex64), C=np.diag(w).astype(np.complex64), D=D))
+    say("case: s5 reduction to DLR bank method=%s" % method)
+    y = run_s5(dict(u=u, lam=lam, Bbar=np.eye(H, dtype=np.complex64), C=np.diag(w).astype(np.complex64), D=D),
+               method)
     ref = oracle.s5_recurrence(u, lam, np.eye(H), np.diag(w), D)
     assert_close(y, ref, "s5/reduction")
 
@@ -79,10 +87,11 @@ def test_s5_reduces_to_dlr_bank_on_device():
 S5_MAGS = [("u", -70), ("u", 60), ("BC", 40), ("BC", -40)]
 
 
+@pytest.mark.parametrize("method", ["scan", "fft"])
 @pytest.mark.parametrize("what,k", S5_MAGS, ids=["%s2^%d" % m for m in S5_MAGS])
-def test_s5_magnitudes(what, k):
+def test_s5_magnitudes(what, k, method):
     B, H, P, L = 2, 40, 24, 2000
-    say("case: s5 magnitudes %s x 2^%d" % (what, k))
+    say("case: s5 magnitudes %s x 2^%d method=%s" % (what, k, method))
     x = inputs.s5_inputs(B, H, P, L, seed=717)
     ref = oracle.s5_recurrence(x["u"], x["lam"], x["Bbar"], x["C"], x["D"])
     xs = dict(x)
@@ -92,20 +101,22 @@ def test_s5_magnitudes(what, k):
     else:
         xs["Bbar"] = (x["Bbar"] * np.float32(np.ldexp(1.0, k))).astype(np.complex64)
         xs["C"] = (x["C"] * np.float32(np.ldexp(1.0, -k))).astype(np.complex64)
-    y = run_s5(xs)
+    y = run_s5(xs, method)
     assert np.all(np.isfinite(y))
     assert_close(y, ref, "s5/magnitudes")
 
 
-def test_s5_timed_matches_untimed():
+@pytest.mark.parametrize("method", ["scan", "fft"])
+def test_s5_timed_matches_untimed(method):
     torch = _torch()
     x = inputs.s5_inputs(2, 24, 9, 3000, seed=17)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
-    say("case: s5 timed variant B=2 H=24 P=9 L=3000")
-    y0 = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"])
+    say("case: s5 timed variant B=2 H=24 P=9 L=3000 method=%s" % method)
+    m = METHODS[method]
+    y0 = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], method=m)
     hip = bd.HipEvents()
     evs = hip.create(8)
-    y1 = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], events=evs)
+    y1 = bd.s5_forward(t["u"], t["lam"], t["Bbar"], t["C"], t["D"], events=evs, method=m)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     for k in range(4):
@@ -113,10 +124,12 @@ def test_s5_timed_matches_untimed():
     hip.destroy(evs)
 
 
-def test_s5_empty_is_noop():
+@pytest.mark.parametrize("method", ["scan", "fft"])
+def test_s5_empty_is_noop(method):
     torch = _torch()
     x = inputs.s5_inputs(1, 3, 2, 8, seed=1)
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
-    y = bd.s5_forward(torch.zeros(0, 3, 8, device="cuda"), t["lam"], t["Bbar"], t["C"], t["D"])
+    y = bd.s5_forward(torch.zeros(0, 3, 8, device="cuda"), t["lam"], t["Bbar"], t["C"], t["D"],
+                      method=METHODS[method])
     torch.cuda.synchronize()
     assert y.shape == (0, 3, 8)
