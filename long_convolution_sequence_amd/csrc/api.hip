@@ -97,7 +97,7 @@ bool use_chunk(const dssm_shape* s) {
 
 // Workspace layout, every region aligned to 256 bytes.
 struct Layout {
-  size_t reK = 0, spec = 0, consts = 0, carry = 0, corr = 0, parts = 0, total = 0;
+  size_t reK = 0, spec = 0, consts = 0, carry = 0, corr = 0, parts = 0, chunk = 0, total = 0;
 };
 
 Layout layout(int op, const dssm_shape* s) {
@@ -126,7 +126,10 @@ Layout layout(int op, const dssm_shape* s) {
     l.corr = take((size_t)corr_groups(s->B, s->H) * s->H * 2 * M * sizeof(float));
     l.parts = take(ndh * (size_t)grad_splits(s->L) * N * 2 * 2 * sizeof(double));
   }
-  if (op == DSSM_OP_SCAN) {
+  if (op == DSSM_OP_SCAN && use_chunk(s)) {
+    // segment states of the chunked form (none unless the sequence is split)
+    l.chunk = take(chunk_workspace(s->B, s->H, s->N, s->L, 1 + s->bidirectional));
+  } else if (op == DSSM_OP_SCAN) {
     const ScanPlan plan = scan_plan(s->B, s->L);
     l.consts = take(ndh * N * plan.nconst * sizeof(float));
     l.carry = take((size_t)s->B * s->H * N * sizeof(float2));
@@ -296,7 +299,8 @@ static int forward_impl(int op, const float* u, const dssm_dlr_params* p, const 
     if (e0.start && (rc = hip_check(hipEventRecord(e0.start, st), "event record"))) return rc;
     if (e0.stop && (rc = hip_check(hipEventRecord(e0.stop, st), "event record"))) return rc;
     if ((rc = hip_check(launch_chunk(u, p->log_re, p->log_im, p->W, p->D, s->B, s->H, s->N, s->L,
-                                     ndir, y, st, kev(events, 1)),
+                                     ndir, y, nullptr, nullptr, at<void>(ws, l.chunk), st,
+                                     kev(events, 1)),
                         "chunk launch")))
       return rc;
   } else {
@@ -453,6 +457,13 @@ int dssm_forward_scan_state(const float* u, const dssm_dlr_params* p, const dssm
   Layout l;
   if ((rc = check_ws(DSSM_OP_SCAN, s, ws, ws_bytes, &l))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (use_chunk(s)) {  // the chunked form, from the state in x and back into it
+    if ((rc = hip_check(launch_chunk(u, p->log_re, p->log_im, p->W, p->D, s->B, s->H, s->N, s->L,
+                                     1, y, x, x, at<void>(ws, l.chunk), st),
+                        "chunk launch")))
+      return rc;
+    return ok();
+  }
   const ScanPlan plan = scan_plan(s->B, s->L);
   float* consts = at<float>(ws, l.consts);
   if ((rc = hip_check(launch_scan_consts(p->log_re, p->log_im, p->W, s->H, s->N, plan, consts, st),

@@ -31,6 +31,8 @@
 //   chunk recurrence (a wave per quarter of the block, a lane per mode;
 //   quarters combined with lambda^(16T)), GEMM3 -> y.  The next block's input
 //   is requested before the current block is computed.
+#include <algorithm>
+
 #include "dssm_internal.h"
 #include "mfma_split.h"
 
@@ -89,6 +91,7 @@ struct BlockLds {
   float2 E[4][kModes];
   int eU[kCB];  // scale exponent of each chunk's input (U rows)
   int eS[4];    // scale exponent of the carried states of each quarter
+  float2 Xl[kModes];  // the state entering the sequence's last chunk (end-state capture)
 };
 constexpr int kLdsBytes = sizeof(TablesLds) > sizeof(BlockLds) ? sizeof(TablesLds) : sizeof(BlockLds);
 
@@ -226,46 +229,84 @@ __device__ __forceinline__ void build_operands(
   __syncthreads();
 }
 
-// One (channel h, batch row b) per workgroup.  The second direction (if any)
-// runs in reversed time t' = Lp - 1 - t (Lp = chunks x T) and adds to y.
+// What one launch of the chunked kernel does (all pointers device memory):
+//   directions d in [dir0, dir0 + ndir_wg), each in its own time order
+//   (d = 1: reversed time t' = Lp - 1 - t, Lp = chunks x T);
+//   workgroup = (channel h, group of rpw batch rows, segment s), segments of
+//   seg_blocks blocks of processing time;
+//   the state entering the segment: x0 [B,H,N] (one direction, segment 0),
+//   or cin [ndir][B][H][nseg][N], or zero;
+//   outputs: y stored (add = 0, first direction of the workgroup) or added
+//   (add = 1, and every later direction); none when state_only;
+//   sout [ndir][B][H][nseg][N]: the state leaving each segment (state_only);
+//   xend [B,H,N]: the state after step L - 1 (one direction).
+struct ChunkArgs {
+  const float* u;
+  const float* log_re;
+  const float* log_im;
+  const float2* W;
+  const float* D;
+  float* y;
+  const float2* x0;
+  float2* xend;
+  const float2* cin;
+  float2* sout;
+  int B, H, N, L, ndir;
+  int dir0, ndir_wg, rpw, nseg, seg_blocks;
+  int add, state_only;
+};
+
+// float64 lambda of mode n of direction d, channel h (zero for n >= N).
+__device__ __forceinline__ double2 lambda64(const ChunkArgs& a, int d, int h, int n) {
+  if (n >= a.N) return make_double2(0.0, 0.0);
+  const size_t i = ((size_t)d * a.H + h) * a.N + n;
+  const double re = (double)a.log_re[i];
+  double sn, cs;
+  sincos((double)a.log_im[i], &sn, &cs);
+  const double m = exp(-re * re);
+  return make_double2(m * cs, m * sn);
+}
+
 template <bool VEC>
-__global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__ u,
-                                                    const float* __restrict__ log_re,
-                                                    const float* __restrict__ log_im,
-                                                    const float2* __restrict__ W,
-                                                    const float* __restrict__ D, int B, int H,
-                                                    int N, int L, int ndir,
-                                                    float* __restrict__ y) {
+__global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   TablesLds& tl = *reinterpret_cast<TablesLds*>(lds_raw);
   BlockLds& bl = *reinterpret_cast<BlockLds*>(lds_raw);
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
+  const int B = a.B, H = a.H, L = a.L;
+  const int ngrp = (B + a.rpw - 1) / a.rpw;
   const int wg = xcd_grouped(blockIdx.x, gridDim.x);
-  const int h = wg / B, b = wg % B;
+  const int seg = wg % a.nseg;
+  const int h = (wg / a.nseg) / ngrp, grp = (wg / a.nseg) % ngrp;
+  const int b0 = grp * a.rpw, b1 = min(B, b0 + a.rpw);
   const int nchunk = (L + kT - 1) / kT;
   const int nblk = (nchunk + kCB - 1) / kCB;
+  const int blk0 = seg * a.seg_blocks, blk1 = min(nblk, blk0 + a.seg_blocks);
   const int Lp = nchunk * kT;  // padded length (reversed-time origin)
-  const float* ur = u + ((size_t)b * H + h) * L;
-  float* yr = y + ((size_t)b * H + h) * L;
-  const BufRes ubuf = buf_res(ur, 4u * (unsigned)L);
-  const BufRes ybuf = buf_res(yr, 4u * (unsigned)L);
+  const int cl = nchunk - 1;   // the last chunk (holds step L - 1)
+  const bool last_seg = blk1 == nblk;
+  if (a.state_only && last_seg) return;  // (whole workgroup) no later segment needs its state
+  unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
 
-  for (int d = 0; d < ndir; ++d) {
+  for (int dd = 0; dd < a.ndir_wg; ++dd) {
+    const int d = a.dir0 + dd;
     const bool rev = d == 1;
+    const bool add = a.add || dd > 0;
     // element e of block blk in processing time -> sequence position (out of
     // range, hence zero on load and dropped on store, beyond the sequence)
     auto pos = [&](int blk, int e) {
       const int q = blk * kCB * kT + e;
       return rev ? Lp - 1 - q : q;
     };
-    // input of block blk: thread t takes elements 4 t + 1024 q + c4 (c4 < 4, q < 4)
-    auto load_block = [&](int blk, float* v) {
+    // input of block blk of row b: thread t takes elements 4 t + 1024 q + c4 (c4 < 4, q < 4)
+    auto load_block = [&](int b, int blk, float* v) {
+      const BufRes ub = buf_res(a.u + ((size_t)b * H + h) * L, 4u * (unsigned)L);
       if (VEC && !rev) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4 x =
-              __builtin_amdgcn_raw_buffer_load_b128(ubuf, 4 * pos(blk, 4 * t + 1024 * q), 0, 0);
+              __builtin_amdgcn_raw_buffer_load_b128(ub, 4 * pos(blk, 4 * t + 1024 * q), 0, 0);
           v[4 * q + 0] = __uint_as_float(x.x);
           v[4 * q + 1] = __uint_as_float(x.y);
           v[4 * q + 2] = __uint_as_float(x.z);
@@ -275,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-              ubuf, 4 * pos(blk, 4 * t + 1024 * q + 3), 0, 0);
+              ub, 4 * pos(blk, 4 * t + 1024 * q + 3), 0, 0);
           v[4 * q + 0] = __uint_as_float(x.w);
           v[4 * q + 1] = __uint_as_float(x.z);
           v[4 * q + 2] = __uint_as_float(x.y);
@@ -285,227 +326,394 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const float* __restrict__
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int e = 4 * t + 1024 * (q >> 2) + (q & 3);
-          v[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ubuf, 4 * pos(blk, e), 0, 0));
+          v[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ub, 4 * pos(blk, e), 0, 0));
         }
       }
     };
     float un[16];
-    load_block(0, un);  // in flight while the operands are formed
+    load_block(b0, blk0, un);  // in flight while the operands are formed
     half8 a1[8], a3[12];
     float2 lamT, lam16T;
     int eT, eW;
-    build_operands(log_re, log_im, W, D, ndir, H, N, d, h, tl, a1, a3, lamT, lam16T, eT, eW);
-    float2 carry = make_float2(0.f, 0.f);  // state entering the block, mode = lane
-    unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
+    build_operands(a.log_re, a.log_im, a.W, a.D, a.ndir, H, a.N, d, h, tl, a1, a3, lamT, lam16T,
+                   eT, eW);
 
-    for (int blk = 0; blk < nblk; ++blk) {
-      __syncthreads();  // the previous block's readers of U and S are done
-      // 1. input to LDS, split: element e = 4 t + 1024 q + c4 -> chunk e / 64, step e % 64;
-      //    the 16 lanes of a DPP row hold one chunk, scaled by 2^eU[chunk]
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * t + 1024 * q;
-        const int c = e >> 6, j = e & 63;
-        const int sc = scale_exp(row_max16(amax4(un + 4 * q)));
-        if ((lane & 15) == 0) bl.eU[c] = sc;
-        half4 vh, vl;
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          _Float16 a, b;
-          split16(__builtin_amdgcn_ldexpf(un[4 * q + c4], sc), a, b);
-          vh[c4] = a;
-          vl[c4] = b;
-        }
-        *reinterpret_cast<half4*>(bl.Uh + c * kUS + j) = vh;
-        *reinterpret_cast<half4*>(bl.Ul + c * kUS + j) = vl;
+    for (int b = b0; b < b1; ++b) {
+      const size_t row = (size_t)b * H + h;
+      const BufRes ybuf = buf_res(a.y + row * L, 4u * (unsigned)L);
+      // the state entering the segment, mode = lane (every wave keeps it)
+      float2 carry = make_float2(0.f, 0.f);
+      if (lane < a.N) {
+        if (a.cin)
+          carry = a.cin[((((size_t)d * B + b) * H + h) * a.nseg + seg) * a.N + lane];
+        else if (a.x0 && seg == 0)
+          carry = a.x0[row * a.N + lane];
       }
-      __builtin_amdgcn_sched_barrier(0);
-      load_block(blk + 1, un);  // in flight during this block (zeros beyond the sequence)
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      // 2. chunk states: S1[c][r] = sum_j A1[r][j] U[j][c]; this wave: rows 32 w .. +31,
-      //    in two halves of 32 columns (fewer accumulators live)
+
+      for (int blk = blk0; blk < blk1; ++blk) {
+        __syncthreads();  // the previous block's readers of U and S are done
+        // 1. input to LDS, split: element e = 4 t + 1024 q + c4 -> chunk e / 64, step e % 64;
+        //    the 16 lanes of a DPP row hold one chunk, scaled by 2^eU[chunk]
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        f4 acc[2][2];
+        for (int q = 0; q < 4; ++q) {
+          const int e = 4 * t + 1024 * q;
+          const int c = e >> 6, j = e & 63;
+          const int sc = scale_exp(row_max16(amax4(un + 4 * q)));
+          if ((lane & 15) == 0) bl.eU[c] = sc;
+          half4 vh, vl;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const int c = 32 * ch + 16 * ct + (lane & 15);
-            const int k = 32 * ks + 8 * (lane >> 4);
-            const half8 bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
-            const half8 blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-              const half8 ah = a1[(rt * 2 + ks) * 2], al = a1[(rt * 2 + ks) * 2 + 1];
-              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[rt][ct], 0, 0, 0);
-              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc[rt][ct], 0, 0, 0);
-              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[rt][ct], 0, 0, 0);
-            }
+          for (int c4 = 0; c4 < 4; ++c4) {
+            _Float16 p, r;
+            split16(__builtin_amdgcn_ldexpf(un[4 * q + c4], sc), p, r);
+            vh[c4] = p;
+            vl[c4] = r;
           }
+          *reinterpret_cast<half4*>(bl.Uh + c * kUS + j) = vh;
+          *reinterpret_cast<half4*>(bl.Ul + c * kUS + j) = vl;
         }
-        // acc[rt][ct][v]: row r = 32 w + 16 rt + 4 (lane / 16) + v, column c = 32 ch + 16 ct + lane % 16
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            const int c = 32 * ch + 16 * ct + (lane & 15);
-            const int r = 32 * w + 16 * rt + 4 * (lane >> 4);
-            *reinterpret_cast<f4*>(bl.S1 + c * kS1S + r) = acc[rt][ct];
-          }
-      }
-      __syncthreads();
-      // 3. chunk recurrence: wave w takes chunks 16 w .. 16 w + 15, lane = mode.  The
-      //    wave reads its rows' S1 values before it writes S over them.
-      {
-        const int n = lane;
-        float2 sv[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {  // chunk states, unscaled (S1 carries 2^eU)
-          const float2 v = *reinterpret_cast<const float2*>(bl.S1 + (16 * w + c) * kS1S + 2 * n);
-          const int ec = -bl.eU[16 * w + c];
-          sv[c] = make_float2(__builtin_amdgcn_ldexpf(v.x, ec), __builtin_amdgcn_ldexpf(v.y, ec));
-        }
-        float2 e = make_float2(0.f, 0.f);
-#pragma unroll
-        for (int c = 0; c < 16; ++c) e = cfma(lamT, e, sv[c]);
-        bl.E[w][n] = e;
+        __builtin_amdgcn_sched_barrier(0);
+        // in flight during this block: the next block of this row, or the
+        // first block of the next row (zeros beyond the sequence)
+        if (blk + 1 < blk1) load_block(b, blk + 1, un);
+        else if (b + 1 < b1) load_block(b + 1, blk0, un);
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        float2 cin = carry;  // state entering quarter w
-        for (int q = 0; q < w; ++q) cin = cfma(lam16T, cin, bl.E[q][n]);
-        float2 cnext = carry;  // state leaving the block (every wave keeps it)
+        // 2. chunk states: S1[c][r] = sum_j A1[r][j] U[j][c]; this wave: rows 32 w .. +31,
+        //    in two halves of 32 columns (fewer accumulators live)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) cnext = cfma(lam16T, cnext, bl.E[q][n]);
-        carry = cnext;
-        float2 st = cin;
-        float m = 0.f;
+        for (int ch = 0; ch < 2; ++ch) {
+          f4 acc[2][2];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {  // sv[c] becomes the state entering chunk 16 w + c
-          const float2 nx = cfma(lamT, st, sv[c]);
-          sv[c] = st;
-          m = fmaxf(m, fmaxf(fabsf(st.x), fabsf(st.y)));
-          st = nx;
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const int c = 32 * ch + 16 * ct + (lane & 15);
+              const int k = 32 * ks + 8 * (lane >> 4);
+              const half8 bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
+              const half8 blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
+#pragma unroll
+              for (int rt = 0; rt < 2; ++rt) {
+                const half8 ah = a1[(rt * 2 + ks) * 2], al = a1[(rt * 2 + ks) * 2 + 1];
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc[rt][ct], 0, 0, 0);
+                acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[rt][ct], 0, 0, 0);
+              }
+            }
+          }
+          // acc[rt][ct][v]: row r = 32 w + 16 rt + 4 (lane / 16) + v, column c = 32 ch + 16 ct + lane % 16
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const int c = 32 * ch + 16 * ct + (lane & 15);
+              const int r = 32 * w + 16 * rt + 4 * (lane >> 4);
+              *reinterpret_cast<f4*>(bl.S1 + c * kS1S + r) = acc[rt][ct];
+            }
         }
-        const int es = scale_exp(wave_max(m));  // one exponent for the quarter's states
-        if (lane == 0) bl.eS[w] = es;
+        __syncthreads();
+        // 3. chunk recurrence: wave w takes chunks 16 w .. 16 w + 15, lane = mode.  The
+        //    wave reads its rows' S1 values before it writes S over them.
+        {
+          const int n = lane;
+          float2 sv[16];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          half2v hi, lo;
-          _Float16 a, b;
-          split16(__builtin_amdgcn_ldexpf(sv[c].x, es), a, b);
-          hi[0] = a;
-          lo[0] = b;
-          split16(__builtin_amdgcn_ldexpf(sv[c].y, es), a, b);
-          hi[1] = a;
-          lo[1] = b;
-          unsigned char* row = srow + (16 * w + c) * kSRow;
-          *reinterpret_cast<half2v*>(row + 4 * n) = hi;
-          *reinterpret_cast<half2v*>(row + kSLo + 4 * n) = lo;
+          for (int c = 0; c < 16; ++c) {  // chunk states, unscaled (S1 carries 2^eU)
+            const float2 v = *reinterpret_cast<const float2*>(bl.S1 + (16 * w + c) * kS1S + 2 * n);
+            const int ec = -bl.eU[16 * w + c];
+            sv[c] = make_float2(__builtin_amdgcn_ldexpf(v.x, ec), __builtin_amdgcn_ldexpf(v.y, ec));
+          }
+          float2 e = make_float2(0.f, 0.f);
+#pragma unroll
+          for (int c = 0; c < 16; ++c) e = cfma(lamT, e, sv[c]);
+          bl.E[w][n] = e;
+          __syncthreads();
+          float2 cin = carry;  // state entering quarter w
+          for (int q = 0; q < w; ++q) cin = cfma(lam16T, cin, bl.E[q][n]);
+          float2 cnext = carry;  // state leaving the block (every wave keeps it)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cnext = cfma(lam16T, cnext, bl.E[q][n]);
+          carry = cnext;
+          float2 st = cin;
+          float m = 0.f;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {  // sv[c] becomes the state entering chunk 16 w + c
+            const float2 nx = cfma(lamT, st, sv[c]);
+            sv[c] = st;
+            m = fmaxf(m, fmaxf(fabsf(st.x), fabsf(st.y)));
+            st = nx;
+          }
+          // the state entering the sequence's last chunk, kept for the end state
+          if (a.xend && last_seg) {
+            const int cloc = cl - blk * kCB - 16 * w;
+            if (cloc >= 0 && cloc < 16) {
+              float2 s0 = sv[0];
+#pragma unroll
+              for (int c = 1; c < 16; ++c)
+                if (c == cloc) s0 = sv[c];
+              bl.Xl[n] = s0;
+            }
+          }
+          const int es = scale_exp(wave_max(m));  // one exponent for the quarter's states
+          if (lane == 0) bl.eS[w] = es;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            half2v hi, lo;
+            _Float16 p, r;
+            split16(__builtin_amdgcn_ldexpf(sv[c].x, es), p, r);
+            hi[0] = p;
+            lo[0] = r;
+            split16(__builtin_amdgcn_ldexpf(sv[c].y, es), p, r);
+            hi[1] = p;
+            lo[1] = r;
+            unsigned char* rw = srow + (16 * w + c) * kSRow;
+            *reinterpret_cast<half2v*>(rw + 4 * n) = hi;
+            *reinterpret_cast<half2v*>(rw + kSLo + 4 * n) = lo;
+          }
         }
-      }
-      __syncthreads();
-      // 4. outputs: Y[i][c] = sum_k A3[i][k] [U; S][k][c]; this wave: rows 16 w .. +15,
-      //    in two halves of 32 columns.  The U part (k < T) and the S part are
-      //    accumulated apart: each carries its own scale.
+        if (a.state_only) continue;  // the segment's end state is all this pass needs
+        __syncthreads();
+        // 4. outputs: Y[i][c] = sum_k A3[i][k] [U; S][k][c]; this wave: rows 16 w .. +15,
+        //    in two halves of 32 columns.  The U part (k < T) and the S part are
+        //    accumulated apart: each carries its own scale.
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        f4 accU[2], accS[2];
-        accU[0] = accU[1] = accS[0] = accS[1] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int ch = 0; ch < 2; ++ch) {
+          f4 accU[2], accS[2];
+          accU[0] = accU[1] = accS[0] = accS[1] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 6; ++ks) {
-          __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
-          const half8 ah = a3[ks * 2], al = a3[ks * 2 + 1];
+          for (int ks = 0; ks < 6; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
+            const half8 ah = a3[ks * 2], al = a3[ks * 2 + 1];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              const int c = 32 * ch + 16 * ct + (lane & 15);
+              half8 bh, blo;
+              if (ks < 2) {
+                const int k = 32 * ks + 8 * (lane >> 4);
+                bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
+                blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
+              } else {
+                const int k = 32 * (ks - 2) + 8 * (lane >> 4);
+                const unsigned char* rw = srow + c * kSRow;
+                bh = *reinterpret_cast<const half8*>(rw + 2 * k);
+                blo = *reinterpret_cast<const half8*>(rw + kSLo + 2 * k);
+              }
+              f4& acc = ks < 2 ? accU[ct] : accS[ct];
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+            }
+          }
+          // acc*[ct][v]: step i = 16 w + 4 (lane / 16) + v of chunk c = 32 ch + 16 ct + lane % 16
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             const int c = 32 * ch + 16 * ct + (lane & 15);
-            half8 bh, blo;
-            if (ks < 2) {
-              const int k = 32 * ks + 8 * (lane >> 4);
-              bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
-              blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
+            const int e0 = (blk * kCB + c) * kT + 16 * w + 4 * (lane >> 4);  // processing time
+            const int xu = -(eT + bl.eU[c]), xs = -(eW + bl.eS[c >> 4]);
+            f4 acc;
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4)
+              acc[v4] = __builtin_amdgcn_ldexpf(accU[ct][v4], xu) +
+                        __builtin_amdgcn_ldexpf(accS[ct][v4], xs);
+            if (VEC) {
+              // four consecutive processing times: one 16-byte group (ascending
+              // positions forward, descending reversed; 16-byte aligned as L % 4 == 0)
+              const int p0 = rev ? Lp - 4 - e0 : e0;
+              f4 o = rev ? f4{acc[3], acc[2], acc[1], acc[0]} : acc;
+              if (add) {
+                // added to the earlier direction's output (read past the L1, which
+                // may hold lines from before this workgroup's own stores)
+                const u32x4 old = __builtin_amdgcn_raw_buffer_load_b128(ybuf, 4 * p0, 0, 1);
+                o += f4{__uint_as_float(old.x), __uint_as_float(old.y), __uint_as_float(old.z),
+                        __uint_as_float(old.w)};
+              }
+              u32x4 ov;
+              ov.x = __float_as_uint(o[0]);
+              ov.y = __float_as_uint(o[1]);
+              ov.z = __float_as_uint(o[2]);
+              ov.w = __float_as_uint(o[3]);
+              __builtin_amdgcn_raw_buffer_store_b128(ov, ybuf, 4 * p0, 0, 0);
             } else {
-              const int k = 32 * (ks - 2) + 8 * (lane >> 4);
-              const unsigned char* row = srow + c * kSRow;
-              bh = *reinterpret_cast<const half8*>(row + 2 * k);
-              blo = *reinterpret_cast<const half8*>(row + kSLo + 2 * k);
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4) {
+                const int p = rev ? Lp - 1 - (e0 + v4) : e0 + v4;
+                float o = acc[v4];
+                if (add)
+                  o += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ybuf, 4 * p, 0, 1));
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ybuf, 4 * p, 0, 0);
+              }
             }
-            f4& acc = ks < 2 ? accU[ct] : accS[ct];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
           }
         }
-        // acc*[ct][v]: step i = 16 w + 4 (lane / 16) + v of chunk c = 32 ch + 16 ct + lane % 16
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int c = 32 * ch + 16 * ct + (lane & 15);
-          const int e0 = (blk * kCB + c) * kT + 16 * w + 4 * (lane >> 4);  // processing time
-          const int xu = -(eT + bl.eU[c]), xs = -(eW + bl.eS[c >> 4]);
-          f4 acc;
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4)
-            acc[v4] = __builtin_amdgcn_ldexpf(accU[ct][v4], xu) +
-                      __builtin_amdgcn_ldexpf(accS[ct][v4], xs);
-          if (!rev) {
-            if (VEC) {
-              u32x4 o;
-              o.x = __float_as_uint(acc[0]);
-              o.y = __float_as_uint(acc[1]);
-              o.z = __float_as_uint(acc[2]);
-              o.w = __float_as_uint(acc[3]);
-              __builtin_amdgcn_raw_buffer_store_b128(o, ybuf, 4 * e0, 0, 0);
-            } else {
-#pragma unroll
-              for (int v4 = 0; v4 < 4; ++v4)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[v4]), ybuf,
-                                                      4 * (e0 + v4), 0, 0);
-            }
-          } else {
-            // reversed time: element v4 sits at position Lp - 1 - (e0 + v4); added to
-            // the forward direction's output (read past the L1, which may hold lines
-            // from before this workgroup's own stores)
-#pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-              const int p = Lp - 1 - (e0 + v4);
-              const float o =
-                  __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ybuf, 4 * p, 0, 1));
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o + acc[v4]), ybuf,
-                                                    4 * p, 0, 0);
-            }
+      }
+      // the state leaving a segment that is not the last (all its chunks are real)
+      if (a.sout && !last_seg && w == 0 && lane < a.N)
+        a.sout[((((size_t)d * B + b) * H + h) * a.nseg + seg) * a.N + lane] = carry;
+      // the state after step L - 1: from the state entering the last chunk and
+      // that chunk's first L - 64 cl inputs (still in LDS: the row's last block
+      // holds the last chunk), advanced in float64 by one wave, lane = mode
+      if (a.xend && last_seg) {
+        __syncthreads();  // Xl written by the wave that held the last chunk
+        if (w == 0) {
+          const int c = cl - (nblk - 1) * kCB;  // the last chunk's index in its block
+          const double2 lam = lambda64(a, d, h, lane);
+          const float2 s0 = bl.Xl[lane];
+          double2 x = make_double2((double)s0.x, (double)s0.y);
+          const float inv = __builtin_amdgcn_ldexpf(1.f, -bl.eU[c]);
+          for (int j = 0; j < L - kT * cl; ++j) {
+            const float uj = ((float)bl.Uh[c * kUS + j] + (float)bl.Ul[c * kUS + j]) * inv;
+            x = make_double2(lam.x * x.x - lam.y * x.y + (double)uj, lam.x * x.y + lam.y * x.x);
           }
+          if (lane < a.N) a.xend[row * a.N + lane] = make_float2((float)x.x, (float)x.y);
         }
       }
     }
-    if (d + 1 < ndir) {
-      __threadfence();  // the forward direction's stores are visible to the reversed sweep
+    if (dd + 1 < a.ndir_wg) {
+      __threadfence();  // this direction's stores are visible to the next one's sweep
       __syncthreads();
     }
   }
+}
+
+// The state entering each segment from the states the segments leave when
+// started from zero: cin[s] = lambda^(S) cin[s-1] + sout[s-1] (S = the
+// segment's length in steps, lambda^S in float64), cin[0] = x0 or zero.  One
+// thread per (direction, row, channel, mode).
+__global__ __launch_bounds__(256) void chunk_carry_kernel(ChunkArgs a, int seg_len,
+                                                          float2* __restrict__ cin) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)a.ndir * a.B * a.H * a.N;
+  if (i >= total) return;
+  const int n = (int)(i % a.N);
+  const long r = i / a.N;  // (d, b, h)
+  const int h = (int)(r % a.H);
+  const int b = (int)((r / a.H) % a.B);
+  const int d = (int)(r / ((long)a.H * a.B));
+  const size_t i_par = ((size_t)d * a.H + h) * a.N + n;
+  // lambda^S = exp(S log lambda) in float64
+  const double re = (double)a.log_re[i_par];
+  const double mag = exp(-re * re * (double)seg_len);
+  double sn, cs;
+  sincos((double)a.log_im[i_par] * (double)seg_len, &sn, &cs);
+  const double2 lS = make_double2(mag * cs, mag * sn);
+  double2 x = make_double2(0.0, 0.0);
+  if (a.x0 && d == 0) {
+    const float2 v = a.x0[((size_t)b * a.H + h) * a.N + n];
+    x = make_double2((double)v.x, (double)v.y);
+  }
+  const size_t base = ((((size_t)d * a.B + b) * a.H + h) * a.nseg) * a.N + n;
+  for (int s = 0; s < a.nseg; ++s) {
+    cin[base + (size_t)s * a.N] = make_float2((float)x.x, (float)x.y);
+    if (s + 1 < a.nseg) {
+      const float2 o = a.sout[base + (size_t)s * a.N];
+      x = make_double2(lS.x * x.x - lS.y * x.y + (double)o.x, lS.x * x.y + lS.y * x.x + (double)o.y);
+    }
+  }
+}
+
+void launch_chunk_args(const ChunkArgs& a, hipStream_t st, KEvents ev) {
+  const long nwg = (long)a.H * ((a.B + a.rpw - 1) / a.rpw) * a.nseg;
+  // 16-byte accesses need a length that a 16-byte access never straddles (rows
+  // then also start 16-byte aligned)
+  if ((a.L % 4) == 0)
+    launch_k(chunk_kernel<true>, dim3((unsigned)nwg), dim3(256), st, ev, a);
+  else
+    launch_k(chunk_kernel<false>, dim3((unsigned)nwg), dim3(256), st, ev, a);
 }
 
 }  // namespace
 
 bool chunk_supported(int N) { return N >= 1 && N <= kModes; }
 
+ChunkPlan chunk_plan(int B, int H, int L, int ndir) {
+  ChunkPlan p;
+  const int nchunk = (L + kT - 1) / kT;
+  const int nblk = (nchunk + kCB - 1) / kCB;
+  const long rows = (long)B * H;
+  // enough workgroups for two per CU (the occupancy the kernel's registers
+  // allow) on 256 CUs: several batch rows of a channel share one workgroup's
+  // operands when rows are many; a long sequence is split into segments when
+  // rows are few
+  const long want = 512;
+  p.rpw = (int)std::max(1L, std::min<long>(B, rows / want));
+  p.nseg = 1;
+  p.seg_blocks = nblk;
+  if (rows * ndir < want && nblk > 1) {
+    const long segs = std::min<long>(nblk, (want + rows * ndir - 1) / (rows * ndir));
+    p.seg_blocks = (int)((nblk + segs - 1) / segs);
+    p.nseg = (nblk + p.seg_blocks - 1) / p.seg_blocks;
+  }
+  return p;
+}
+
+size_t chunk_workspace(int B, int H, int N, int L, int ndir) {
+  const ChunkPlan p = chunk_plan(B, H, L, ndir);
+  if (p.nseg == 1) return 0;
+  // sout and cin
+  return 2 * align_up((size_t)ndir * B * H * p.nseg * N * sizeof(float2), 256);
+}
+
 hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im, const float* W,
                         const float* D, int B, int H, int N, int L, int ndir, float* y,
-                        hipStream_t st, KEvents ev) {
-  const long nwg = (long)B * H;
-  const float2* w2 = reinterpret_cast<const float2*>(W);
-  // 16-byte accesses need a length that a 16-byte access never straddles (rows
-  // then also start 16-byte aligned)
-  if ((L % 4) == 0)
-    launch_k(chunk_kernel<true>, dim3((unsigned)nwg), dim3(256), st, ev, u, log_re, log_im, w2, D,
-             B, H, N, L, ndir, y);
-  else
-    launch_k(chunk_kernel<false>, dim3((unsigned)nwg), dim3(256), st, ev, u, log_re, log_im, w2, D,
-             B, H, N, L, ndir, y);
+                        const float* x0, float* xend, void* ws, hipStream_t st, KEvents ev) {
+  const ChunkPlan p = chunk_plan(B, H, L, ndir);
+  ChunkArgs a{};
+  a.u = u;
+  a.log_re = log_re;
+  a.log_im = log_im;
+  a.W = reinterpret_cast<const float2*>(W);
+  a.D = D;
+  a.y = y;
+  a.x0 = reinterpret_cast<const float2*>(x0);
+  a.xend = reinterpret_cast<float2*>(xend);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.L = L;
+  a.ndir = ndir;
+  a.rpw = p.rpw;
+  a.nseg = p.nseg;
+  a.seg_blocks = p.seg_blocks;
+  if (p.nseg == 1) {  // one pass over each row, every direction in one workgroup
+    a.dir0 = 0;
+    a.ndir_wg = ndir;
+    launch_chunk_args(a, st, ev);
+    return hipGetLastError();
+  }
+  // segments: (1) the state each segment leaves from zero, (2) the state each
+  // one enters, (3) the outputs from those states, one direction per launch
+  // (the reversed one adding into y)
+  const size_t part = align_up((size_t)ndir * B * H * p.nseg * N * sizeof(float2), 256);
+  float2* sout = static_cast<float2*>(ws);
+  float2* cin = reinterpret_cast<float2*>(static_cast<char*>(ws) + part);
+  const KEvents e_first{ev.start, nullptr}, e_last{nullptr, ev.stop};
+  ChunkArgs s1 = a;
+  s1.dir0 = 0;
+  s1.ndir_wg = ndir;
+  s1.state_only = 1;
+  s1.sout = sout;
+  s1.x0 = nullptr;  // every segment from zero here; x0 enters through the carries
+  s1.xend = nullptr;
+  launch_chunk_args(s1, st, e_first);
+  const long total = (long)ndir * B * H * N;
+  ChunkArgs s2 = a;
+  s2.sout = sout;
+  launch_k(chunk_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), st, KEvents{},
+           s2, p.seg_blocks * kCB * kT, cin);
+  for (int d = 0; d < ndir; ++d) {
+    ChunkArgs s3 = a;
+    s3.dir0 = d;
+    s3.ndir_wg = 1;
+    s3.add = d > 0;
+    s3.cin = cin;
+    s3.x0 = nullptr;
+    s3.xend = d == 0 ? a.xend : nullptr;
+    launch_chunk_args(s3, st, d + 1 == ndir ? e_last : KEvents{});
+  }
   return hipGetLastError();
 }
 

@@ -135,11 +135,22 @@ hipError_t launch_step(const float* u, const float* log_re, const float* log_im,
 // Chunked state-space form on the matrix cores (chunk.hip)
 // ---------------------------------------------------------------------------
 bool chunk_supported(int N);  // N <= 64 modes
-// y [B,H,L] from u [B,H,L] (operands formed in the kernel, no workspace); the
-// second direction (if any) in reversed time.
+// How a launch is organised: rpw batch rows of a channel per workgroup (the
+// operands built once), and nseg segments of seg_blocks blocks of 4096 steps
+// per row when rows are too few to fill the device.
+struct ChunkPlan {
+  int rpw = 1, nseg = 1, seg_blocks = 1;
+};
+ChunkPlan chunk_plan(int B, int H, int L, int ndir);
+// Workspace bytes of launch_chunk (0 unless the sequence is split).
+size_t chunk_workspace(int B, int H, int N, int L, int ndir);
+// y [B,H,L] from u [B,H,L]; the second direction (if any) in reversed time.
+// x0 [B,H,N] c64 (may be NULL): the state before step 0 (one direction);
+// xend [B,H,N] c64 (may be NULL): receives the state after step L-1 (one
+// direction); x0 and xend may be the same array.  ws: chunk_workspace bytes.
 hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im, const float* W,
                         const float* D, int B, int H, int N, int L, int ndir, float* y,
-                        hipStream_t st, KEvents ev = {});
+                        const float* x0, float* xend, void* ws, hipStream_t st, KEvents ev = {});
 
 // ---------------------------------------------------------------------------
 // S5 multi-input multi-output diagonal SSM (s5.hip)

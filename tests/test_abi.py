@@ -111,9 +111,11 @@ def test_forward_rejects_bad_arguments(name):
     assert _call(fn, _params(), good, y=None) == bd.DSSM_ERR_INVALID_ARG
     assert _call(fn, _params(), good, u=FAKE + 8) == bd.DSSM_ERR_INVALID_ARG
     assert _call(fn, _params(), good, u=FAKE * 2, y=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG
-    assert _call(fn, _params(), good, nbytes=16) == bd.DSSM_ERR_WORKSPACE
-    assert _call(fn, _params(), good, ws=None) == bd.DSSM_ERR_INVALID_ARG
-    assert _call(fn, _params(), good, ws=FAKE * 4 + 64) == bd.DSSM_ERR_INVALID_ARG
+    # a shape that needs a workspace on both paths (N > 64: the segmented scan)
+    wide = bd.Shape(2, 3, 100, 32, 0)
+    assert _call(fn, _params(), wide, nbytes=16) == bd.DSSM_ERR_WORKSPACE
+    assert _call(fn, _params(), wide, ws=None) == bd.DSSM_ERR_INVALID_ARG
+    assert _call(fn, _params(), wide, ws=FAKE * 4 + 64) == bd.DSSM_ERR_INVALID_ARG
     assert _call(fn, _params(), bd.Shape(2, 3, 4, 32, 3)) == bd.DSSM_ERR_INVALID_ARG
     # empty problems are valid no-ops (nothing is launched, nothing is read)
     assert _call(fn, None, bd.Shape(0, 3, 4, 32, 0)) == 0
@@ -228,7 +230,8 @@ def test_timed_variants_validate_events(name, n):
     # a NULL pair (kernel untimed) passes validation: the call then fails on
     # the workspace, which is checked after the events
     half = (ctypes.c_void_p * n)(*([None, None] + [FAKE] * (n - 2)))
-    small = [FAKE * 2, ctypes.byref(p), ctypes.byref(good), FAKE * 3, FAKE * 4, 8, None]
+    wide = bd.Shape(2, 3, 100, 32, 0)  # needs a workspace on both paths
+    small = [FAKE * 2, ctypes.byref(p), ctypes.byref(wide), FAKE * 3, FAKE * 4, 8, None]
     assert fn(*(small + [half, n])) == bd.DSSM_ERR_WORKSPACE
 
 
@@ -261,7 +264,7 @@ def test_stateful_forward_rejects_bad_arguments():
     assert call(p, good, x=FAKE * 5 + 8) == bd.DSSM_ERR_INVALID_ARG
     assert call(p, good, x=FAKE * 2) == bd.DSSM_ERR_INVALID_ARG  # aliases u
     assert call(p, good, x=FAKE * 3) == bd.DSSM_ERR_INVALID_ARG  # aliases y
-    assert call(p, good, n=16) == bd.DSSM_ERR_WORKSPACE
+    assert call(p, bd.Shape(2, 3, 100, 32, 0), n=16) == bd.DSSM_ERR_WORKSPACE  # segmented scan
     assert call(p, bd.Shape(2, 3, 4, 32, 1)) == bd.DSSM_ERR_UNSUPPORTED  # needs the future
     assert b"direction" in bd.lib().dssm_last_error()
     assert call(p, bd.Shape(2, 3, 4, 32, 2)) == bd.DSSM_ERR_INVALID_ARG

@@ -336,3 +336,44 @@ def test_empty_inputs_are_noops():
             y = f(u, lr.contiguous(), li.contiguous(), W.contiguous(), D.contiguous())
             assert y.shape == (B, H, L)
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------
+# The recurrence view's work split: several batch rows per workgroup (many
+# rows), and the sequence cut into segments whose entering states come from a
+# state-only pass and a carry combination (few rows, long sequences).
+# ----------------------------------------------------------------------------
+
+SPLIT = [  # (B, H, N, L, bi, re_scale): few rows -> segments
+    (1, 4, 64, 1 << 20, 0, 0.1),         # 256 blocks of 4096 steps, 128 segments of 2
+    (1, 2, 64, 1 << 19, 1, 0.1),         # both directions, 128 segments
+    (2, 3, 33, 5 * 4096 * 3 + 77, 1, 1.0),  # ragged last chunk and block, one block per segment
+    (1, 1, 16, 4096 * 2 + 1, 0, 1.0),    # the last segment holds one step
+    (3, 2, 64, 3 * 4096, 0, 0.1),        # length a whole number of blocks
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT, ids=["B%dH%dN%dL%dbi%d" % s[:5] for s in SPLIT])
+def test_scan_sequence_split(shape):
+    B, H, N, L, bi, rs = shape
+    say("case: scan split B=%d H=%d N=%d L=%d bi=%d" % shape[:5])
+    x = inputs.dlr_inputs(B, H, N, L, bidirectional=bool(bi), seed=1300 + L % 1000, re_scale=rs)
+    y = run("scan", x, bool(bi))
+    ref = oracle.dlr_recurrence(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], bool(bi))
+    assert_close(y, ref, "scan/split")
+
+
+ROWS = [  # (B, H, N, L, bi): many rows -> several batch rows per workgroup, ragged groups
+    (7, 300, 16, 500, 0), (9, 130, 64, 4096, 1), (16, 80, 8, 1000, 1), (5, 230, 64, 70, 0),
+]
+
+
+@pytest.mark.parametrize("shape", ROWS, ids=["B%dH%dN%dL%dbi%d" % s for s in ROWS])
+def test_scan_rows_per_workgroup(shape):
+    B, H, N, L, bi = shape
+    say("case: scan rows per workgroup B=%d H=%d N=%d L=%d bi=%d" % shape)
+    x = inputs.dlr_inputs(B, H, N, L, bidirectional=bool(bi), seed=1400 + H)
+    y = run("scan", x, bool(bi))
+    ref = oracle.dlr_recurrence(x["u"], x["log_re"], x["log_im"], x["W"], x["D"], bool(bi))
+    assert_close(y, ref, "scan/rows")
+    assert_close(run("fft", x, bool(bi)), ref, "fft/rows")

@@ -72,6 +72,10 @@ SHAPES = [
     # (B, H, N, L): single tile, ragged tails, several tiles
     (2, 3, 5, 37), (1, 2, 8, 1), (3, 2, 8, 2), (2, 2, 16, 255), (3, 2, 8, 257),
     (2, 3, 64, 1000), (1, 2, 7, 4097), (1, 2, 64, 16384), (2, 2, 7, 40000),
+    # the chunked form's organisations: segments with carried states (few rows,
+    # long sequence), several batch rows per workgroup (many rows); N > 64
+    # runs the segmented scan
+    (1, 3, 64, 100000), (2, 1, 16, 4096 * 3 + 5), (7, 300, 16, 300), (2, 2, 100, 3000),
 ]
 
 
