@@ -21,7 +21,8 @@ Prints ONE JSON line:
   launch stream, with the vector-ALU co-limit beside it;
 * extra.configs: every workload on both paths (the DLR workloads by the FFT
   and the recurrence views, the S5 workload by the scan and FFT methods),
-  plus the continuous-time S5, the gradients and a device copy;
+  plus the continuous-time S5, the gradients, the recurrence view's sequence
+  split on few long rows, streaming prefill and a device copy;
 * cpu_baseline: the float64 oracle on the host's cores (a process pool over
   channels), with the single-core figure, taken before the GPU is touched.
 """
@@ -364,6 +365,80 @@ def dlr_config(name, steps, hip):
     return out
 
 
+def scan_split(hip, reps=5):
+    """The recurrence view when rows are few and the sequence long (B=1, H=4,
+    N=64, L=2^20, one and two directions): the sequence cut into segments
+    (state-only pass, carry chain, output pass) against the walk of one
+    workgroup per row it replaces.  That walk is estimated from one row's
+    kernel time at one block (4096 steps) and at one chunk (64 steps): the
+    operand prologue plus blocks times the per-block time."""
+    import numpy as np
+    import torch
+
+    from long_convolution_sequence_amd import binding as bd
+    from long_convolution_sequence_amd import inputs
+
+    def kernel_ms(B, H, N, L, bi, seed):
+        x = inputs.dlr_inputs(B, H, N, L, bidirectional=bi, seed=seed, re_scale=0.1)
+        dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+        y = torch.empty_like(dev["u"])
+        ws = torch.empty(max(256, bd.workspace_size(bd.OP_SCAN, B, H, N, L, bi)),
+                         dtype=torch.uint8, device="cuda")
+
+        def call_timed(k, evs):
+            bd.forward_timed("scan", dev["u"], dev["log_re"], dev["log_im"], dev["W"], dev["D"],
+                             evs, bidirectional=bi, y=y, workspace=ws)
+
+        call_timed(0, [None] * 4)
+        return stage_times(call_timed, 2, reps, hip, only=1)[1]
+
+    out = {}
+    L = 1 << 20
+    one_blk = kernel_ms(1, 1, 64, 4096, False, 51)
+    one_chunk = kernel_ms(1, 1, 64, 64, False, 52)
+    per_blk = max(one_blk - one_chunk, 0.0)
+    for bi in (False, True):
+        ms = kernel_ms(1, 4, 64, L, bi, 53)
+        ndir = 2 if bi else 1
+        walk = ndir * (one_chunk + (L // 4096) * per_blk)
+        out["bidirectional" if bi else "unidirectional"] = {
+            "B": 1, "H": 4, "N": 64, "L": L, "kernels_ms": ms,
+            "elements_per_s": 4 * L / (ms * 1e-3),
+            "one_workgroup_per_row_walk_ms_estimate": walk,
+            "speedup_over_walk": walk / ms,
+        }
+    out["walk_estimate_from"] = {"one_row_one_block_ms": one_blk, "one_row_one_chunk_ms": one_chunk}
+    return out
+
+
+def stream_prefill(steps, hip):
+    """Streaming prefill on the long-sequence workload: dssm_forward_scan_state
+    from a random state (state read, outputs, last state written back)."""
+    import numpy as np
+    import torch
+
+    from long_convolution_sequence_amd import binding as bd
+    from long_convolution_sequence_amd import inputs
+
+    c = inputs.config("long_sequence")
+    B, H, N, L = c["B"], c["H"], c["N"], c["L"]
+    x = inputs.inputs_for(c)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    us, ys = rotated(dev["u"])
+    R = len(us)
+    x0 = torch.from_numpy(inputs.dlr_state(B, H, N, seed=3)).cuda()
+    ws = torch.empty(max(256, bd.workspace_size(bd.OP_SCAN, B, H, N, L)), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(k):
+        bd.forward_scan_state(us[k % R], dev["log_re"], dev["log_im"], dev["W"], dev["D"], x0,
+                              y=ys[k % R], workspace=ws)
+
+    ms = wall_ms(call, steps, 3)
+    return {"workload": "long_sequence", "ms_per_prefill": ms,
+            "elements_per_s": B * H * L / (ms * 1e-3), "path": "chunked form, state in and out"}
+
+
 def s5_config(steps, hip):
     """The S5 workload by both methods: plain-call wall ms over rotated sets and
     the four stages' stamped durations; errors against the float64 recurrence
@@ -607,6 +682,8 @@ def main():
                          for name in ("tiny", "image_length", "bidirectional", "long_sequence")}
         ex["configs"]["s5_mimo"] = s5_config(max(4, a.side_steps // 2), hip)
         ex["s5_tv_path"] = time_s5_tv(max(4, a.side_steps // 2))
+        ex["scan_sequence_split"] = scan_split(hip)
+        ex["streaming_prefill"] = stream_prefill(a.side_steps, hip)
         ex["backward"] = time_backward(dev, us, ys, bi, max(4, a.side_steps // 2))
     if cpu is not None:
         line["cpu_baseline"] = cpu

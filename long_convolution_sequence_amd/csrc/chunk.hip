@@ -267,7 +267,7 @@ __device__ __forceinline__ double2 lambda64(const ChunkArgs& a, int d, int h, in
   return make_double2(m * cs, m * sn);
 }
 
-template <bool VEC>
+template <bool VEC, bool STATE_ONLY, bool CAPTURE>
 __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   TablesLds& tl = *reinterpret_cast<TablesLds*>(lds_raw);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
   const int Lp = nchunk * kT;  // padded length (reversed-time origin)
   const int cl = nchunk - 1;   // the last chunk (holds step L - 1)
   const bool last_seg = blk1 == nblk;
-  if (a.state_only && last_seg) return;  // (whole workgroup) no later segment needs its state
+  if (STATE_ONLY && last_seg) return;  // (whole workgroup) no later segment needs its state
   unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
 
   for (int dd = 0; dd < a.ndir_wg; ++dd) {
@@ -299,9 +299,11 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
       const int q = blk * kCB * kT + e;
       return rev ? Lp - 1 - q : q;
     };
-    // input of block blk of row b: thread t takes elements 4 t + 1024 q + c4 (c4 < 4, q < 4)
-    auto load_block = [&](int b, int blk, float* v) {
-      const BufRes ub = buf_res(a.u + ((size_t)b * H + h) * L, 4u * (unsigned)L);
+    // input of block blk of row b: thread t takes elements 4 t + 1024 q + c4 (c4 < 4, q < 4);
+    // !valid: zeros (an empty buffer)
+    auto load_block = [&](int b, int blk, float* v, bool valid = true) {
+      const BufRes ub = buf_res(a.u + ((size_t)(valid ? b : 0) * H + h) * L,
+                                valid ? 4u * (unsigned)L : 0u);
       if (VEC && !rev) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -373,9 +375,11 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
         // in flight during this block: the next block of this row, or the
-        // first block of the next row (zeros beyond the sequence)
-        if (blk + 1 < blk1) load_block(b, blk + 1, un);
-        else if (b + 1 < b1) load_block(b + 1, blk0, un);
+        // first block of the next row (zeros beyond the sequence or the rows)
+        {
+          const bool same = blk + 1 < blk1;
+          load_block(same ? b : b + 1, same ? blk + 1 : blk0, un, same || b + 1 < b1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         // 2. chunk states: S1[c][r] = sum_j A1[r][j] U[j][c]; this wave: rows 32 w .. +31,
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
             st = nx;
           }
           // the state entering the sequence's last chunk, kept for the end state
-          if (a.xend && last_seg) {
+          if (CAPTURE && last_seg) {
             const int cloc = cl - blk * kCB - 16 * w;
             if (cloc >= 0 && cloc < 16) {
               float2 s0 = sv[0];
@@ -475,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
             *reinterpret_cast<half2v*>(rw + kSLo + 4 * n) = lo;
           }
         }
-        if (a.state_only) continue;  // the segment's end state is all this pass needs
+        if (STATE_ONLY) continue;  // the segment's end state is all this pass needs
         __syncthreads();
         // 4. outputs: Y[i][c] = sum_k A3[i][k] [U; S][k][c]; this wave: rows 16 w .. +15,
         //    in two halves of 32 columns.  The U part (k < T) and the S part are
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
       // the state after step L - 1: from the state entering the last chunk and
       // that chunk's first L - 64 cl inputs (still in LDS: the row's last block
       // holds the last chunk), advanced in float64 by one wave, lane = mode
-      if (a.xend && last_seg) {
+      if (CAPTURE && last_seg) {
         __syncthreads();  // Xl written by the wave that held the last chunk
         if (w == 0) {
           const int c = cl - (nblk - 1) * kCB;  // the last chunk's index in its block
@@ -580,38 +584,82 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
 }
 
 // The state entering each segment from the states the segments leave when
-// started from zero: cin[s] = lambda^(S) cin[s-1] + sout[s-1] (S = the
-// segment's length in steps, lambda^S in float64), cin[0] = x0 or zero.  One
-// thread per (direction, row, channel, mode).
-__global__ __launch_bounds__(256) void chunk_carry_kernel(ChunkArgs a, int seg_len,
+// started from zero: cin[s] = A cin[s-1] + sout[s-1] with A = lambda^S (S =
+// the segment's length in steps), cin[0] = x0 or zero, in float64.  A
+// parallel scan over the segments of one (direction, row, channel, mode):
+// thread j of a group of P2 lanes takes segments 16 j .. 16 j + 15 (its 16
+// loads issued together), forms their aggregate from zero, the lanes combine
+// the aggregates by a Hillis-Steele scan with the multipliers A^(16 2^k),
+// and each thread
+// replays its segments from the state entering its first one.  A is formed
+// from the float64 logarithm; its powers A^(16 2^k) by squaring.
+constexpr int kSegPerThread = 16;
+
+__device__ __forceinline__ double2 zfma(double2 m, double2 x, double2 c) {  // m x + c
+  return make_double2(fma(m.x, x.x, fma(-m.y, x.y, c.x)), fma(m.x, x.y, fma(m.y, x.x, c.y)));
+}
+
+__global__ __launch_bounds__(256) void chunk_carry_kernel(ChunkArgs a, int seg_len, int p2,
                                                           float2* __restrict__ cin) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)a.ndir * a.B * a.H * a.N;
-  if (i >= total) return;
-  const int n = (int)(i % a.N);
-  const long r = i / a.N;  // (d, b, h)
+  const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long pairs = (long)a.ndir * a.B * a.H * a.N;
+  const long pr = g / p2;  // (direction, row, channel, mode)
+  const int j = (int)(g % p2);
+  const bool active = pr < pairs;
+  const long pc = active ? pr : 0;
+  const int n = (int)(pc % a.N);
+  const long r = pc / a.N;  // (d, b, h)
   const int h = (int)(r % a.H);
   const int b = (int)((r / a.H) % a.B);
   const int d = (int)(r / ((long)a.H * a.B));
   const size_t i_par = ((size_t)d * a.H + h) * a.N + n;
-  // lambda^S = exp(S log lambda) in float64
-  const double re = (double)a.log_re[i_par];
-  const double mag = exp(-re * re * (double)seg_len);
-  double sn, cs;
-  sincos((double)a.log_im[i_par] * (double)seg_len, &sn, &cs);
-  const double2 lS = make_double2(mag * cs, mag * sn);
-  double2 x = make_double2(0.0, 0.0);
-  if (a.x0 && d == 0) {
-    const float2 v = a.x0[((size_t)b * a.H + h) * a.N + n];
-    x = make_double2((double)v.x, (double)v.y);
-  }
+  const double re = (double)a.log_re[i_par], im = (double)a.log_im[i_par];
+  // lambda^m = exp(m log lambda), log lambda = -re^2 + i im
+  auto lpow = [&](double m) {
+    double sn, cs;
+    sincos(im * m, &sn, &cs);
+    const double mag = exp(-re * re * m);
+    return make_double2(mag * cs, mag * sn);
+  };
+  const double2 A = lpow((double)seg_len);
+  // A^16 and its powers A^(16 2^k) by squaring (relative error ~2^k ulp of
+  // float64 after k squarings, k <= 9 here)
+  auto zsq = [](double2 z) { return make_double2(z.x * z.x - z.y * z.y, 2.0 * z.x * z.y); };
+  double2 A16 = zsq(zsq(zsq(zsq(A))));
   const size_t base = ((((size_t)d * a.B + b) * a.H + h) * a.nseg) * a.N + n;
-  for (int s = 0; s < a.nseg; ++s) {
-    cin[base + (size_t)s * a.N] = make_float2((float)x.x, (float)x.y);
-    if (s + 1 < a.nseg) {
-      const float2 o = a.sout[base + (size_t)s * a.N];
-      x = make_double2(lS.x * x.x - lS.y * x.y + (double)o.x, lS.x * x.y + lS.y * x.x + (double)o.y);
-    }
+  const int s0 = kSegPerThread * j;
+  float2 o[kSegPerThread];
+#pragma unroll
+  for (int k = 0; k < kSegPerThread; ++k) {  // segment s0 + k leaves o[k] (the last one: unused)
+    const int sg = s0 + k;
+    o[k] = (active && sg < a.nseg - 1) ? a.sout[base + (size_t)sg * a.N] : make_float2(0.f, 0.f);
+  }
+  double2 agg = make_double2(0.0, 0.0);  // the state leaving segment s0 + 15 from zero at s0
+#pragma unroll
+  for (int k = 0; k < kSegPerThread; ++k)
+    agg = zfma(A, agg, make_double2((double)o[k].x, (double)o[k].y));
+  double2 x0 = make_double2(0.0, 0.0);
+  if (active && a.x0 && d == 0) {
+    const float2 v = a.x0[((size_t)b * a.H + h) * a.N + n];
+    x0 = make_double2((double)v.x, (double)v.y);
+  }
+  // inclusive scan over j of v_j = A^16 v_{j-1} + agg_j, v_{-1} = x0
+  double2 v = j == 0 ? zfma(A16, x0, agg) : agg;
+  double2 m = A16;  // A^(16 2^k)
+  for (int k = 0; (1 << k) < p2; ++k) {
+    const int off = 1 << k;
+    const double2 up = make_double2(__shfl_up(v.x, off, p2), __shfl_up(v.y, off, p2));
+    if (j >= off) v = zfma(m, up, v);
+    m = zsq(m);
+  }
+  // the state entering segment s0
+  const double2 prev = make_double2(__shfl_up(v.x, 1, p2), __shfl_up(v.y, 1, p2));
+  double2 c = j == 0 ? x0 : prev;
+#pragma unroll
+  for (int k = 0; k < kSegPerThread; ++k) {
+    const int sg = s0 + k;
+    if (active && sg < a.nseg) cin[base + (size_t)sg * a.N] = make_float2((float)c.x, (float)c.y);
+    c = zfma(A, c, make_double2((double)o[k].x, (double)o[k].y));
   }
 }
 
@@ -619,10 +667,18 @@ void launch_chunk_args(const ChunkArgs& a, hipStream_t st, KEvents ev) {
   const long nwg = (long)a.H * ((a.B + a.rpw - 1) / a.rpw) * a.nseg;
   // 16-byte accesses need a length that a 16-byte access never straddles (rows
   // then also start 16-byte aligned)
-  if ((a.L % 4) == 0)
-    launch_k(chunk_kernel<true>, dim3((unsigned)nwg), dim3(256), st, ev, a);
-  else
-    launch_k(chunk_kernel<false>, dim3((unsigned)nwg), dim3(256), st, ev, a);
+  const dim3 g((unsigned)nwg), blk(256);
+  const bool vec = (a.L % 4) == 0;
+  if (a.state_only) {  // (no end state here)
+    if (vec) launch_k(chunk_kernel<true, true, false>, g, blk, st, ev, a);
+    else launch_k(chunk_kernel<false, true, false>, g, blk, st, ev, a);
+  } else if (a.xend) {
+    if (vec) launch_k(chunk_kernel<true, false, true>, g, blk, st, ev, a);
+    else launch_k(chunk_kernel<false, false, true>, g, blk, st, ev, a);
+  } else {
+    if (vec) launch_k(chunk_kernel<true, false, false>, g, blk, st, ev, a);
+    else launch_k(chunk_kernel<false, false, false>, g, blk, st, ev, a);
+  }
 }
 
 }  // namespace
@@ -699,11 +755,15 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
   s1.x0 = nullptr;  // every segment from zero here; x0 enters through the carries
   s1.xend = nullptr;
   launch_chunk_args(s1, st, e_first);
-  const long total = (long)ndir * B * H * N;
+  // lanes per (direction, row, channel, mode): a power of two covering the
+  // segments in groups of kSegPerThread (nseg <= 512, so at most 32)
+  int p2 = 1;
+  while (p2 * kSegPerThread < p.nseg) p2 *= 2;
+  const long threads = (long)ndir * B * H * N * p2;
   ChunkArgs s2 = a;
   s2.sout = sout;
-  launch_k(chunk_carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), st, KEvents{},
-           s2, p.seg_blocks * kCB * kT, cin);
+  launch_k(chunk_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), st,
+           KEvents{}, s2, p.seg_blocks * kCB * kT, p2, cin);
   for (int d = 0; d < ndir; ++d) {
     ChunkArgs s3 = a;
     s3.dir0 = d;
