@@ -231,7 +231,10 @@ __device__ __forceinline__ void build_operands(
 
 // What one launch of the chunked kernel does (all pointers device memory):
 //   directions d in [dir0, dir0 + ndir_wg), each in its own time order
-//   (d = 1: reversed time t' = Lp - 1 - t, Lp = chunks x T);
+//   (d = 1: reversed time t' = Lp - 1 - t, Lp = chunks x T); with dir_in_grid
+//   one direction per workgroup, dir0 + the workgroup's place in the grid
+//   divided by H x row groups x segments (state-only passes only: they write
+//   no outputs two directions could race on);
 //   workgroup = (channel h, group of rpw batch rows, segment s), segments of
 //   seg_blocks blocks of processing time;
 //   the state entering the segment: x0 [B,H,N] (one direction, segment 0),
@@ -254,6 +257,7 @@ struct ChunkArgs {
   int B, H, N, L, ndir;
   int dir0, ndir_wg, rpw, nseg, seg_blocks;
   int add, state_only;
+  int dir_in_grid;  // the workgroup's one direction is dir0 + its grid position / (H groups segments)
 };
 
 // float64 lambda of mode n of direction d, channel h (zero for n >= N).
@@ -276,7 +280,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
   const int lane = t & 63, w = t >> 6;
   const int B = a.B, H = a.H, L = a.L;
   const int ngrp = (B + a.rpw - 1) / a.rpw;
-  const int wg = xcd_grouped(blockIdx.x, gridDim.x);
+  const int wg_all = xcd_grouped(blockIdx.x, gridDim.x);
+  const int per_dir = H * ngrp * a.nseg;
+  const int wg = a.dir_in_grid ? wg_all % per_dir : wg_all;
+  const int dir0 = a.dir0 + (a.dir_in_grid ? wg_all / per_dir : 0);
   const int seg = wg % a.nseg;
   const int h = (wg / a.nseg) / ngrp, grp = (wg / a.nseg) % ngrp;
   const int b0 = grp * a.rpw, b1 = min(B, b0 + a.rpw);
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
   unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
 
   for (int dd = 0; dd < a.ndir_wg; ++dd) {
-    const int d = a.dir0 + dd;
+    const int d = dir0 + dd;
     const bool rev = d == 1;
     const bool add = a.add || dd > 0;
     // element e of block blk in processing time -> sequence position (out of
@@ -617,7 +624,7 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ChunkArgs a, int seg_l
   // lambda^m = exp(m log lambda), log lambda = -re^2 + i im
   auto lpow = [&](double m) {
     double sn, cs;
-    sincos(im * m, &sn, &cs);
+    sincos(fmod(im * m, 2.0 * M_PI), &sn, &cs);  // (a small argument: the fast reduction)
     const double mag = exp(-re * re * m);
     return make_double2(mag * cs, mag * sn);
   };
@@ -663,8 +670,8 @@ __global__ __launch_bounds__(256) void chunk_carry_kernel(ChunkArgs a, int seg_l
   }
 }
 
-void launch_chunk_args(const ChunkArgs& a, hipStream_t st, KEvents ev) {
-  const long nwg = (long)a.H * ((a.B + a.rpw - 1) / a.rpw) * a.nseg;
+void launch_chunk_args(const ChunkArgs& a, hipStream_t st, KEvents ev, int ndir_grid = 1) {
+  const long nwg = (long)ndir_grid * a.H * ((a.B + a.rpw - 1) / a.rpw) * a.nseg;
   // 16-byte accesses need a length that a 16-byte access never straddles (rows
   // then also start 16-byte aligned)
   const dim3 g((unsigned)nwg), blk(256);
@@ -698,8 +705,9 @@ ChunkPlan chunk_plan(int B, int H, int L, int ndir) {
   p.rpw = (int)std::max(1L, std::min<long>(B, rows / want));
   p.nseg = 1;
   p.seg_blocks = nblk;
-  if (rows * ndir < want && nblk > 1) {
-    const long segs = std::min<long>(nblk, (want + rows * ndir - 1) / (rows * ndir));
+  // (each launch of a split runs one direction, or the directions side by side)
+  if (rows < want && nblk > 1) {
+    const long segs = std::min<long>(nblk, (want + rows - 1) / rows);
     p.seg_blocks = (int)((nblk + segs - 1) / segs);
     p.nseg = (nblk + p.seg_blocks - 1) / p.seg_blocks;
   }
@@ -749,12 +757,13 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
   const KEvents e_first{ev.start, nullptr}, e_last{nullptr, ev.stop};
   ChunkArgs s1 = a;
   s1.dir0 = 0;
-  s1.ndir_wg = ndir;
+  s1.ndir_wg = 1;
+  s1.dir_in_grid = 1;  // the directions side by side (no outputs to share)
   s1.state_only = 1;
   s1.sout = sout;
   s1.x0 = nullptr;  // every segment from zero here; x0 enters through the carries
   s1.xend = nullptr;
-  launch_chunk_args(s1, st, e_first);
+  launch_chunk_args(s1, st, e_first, ndir);
   // lanes per (direction, row, channel, mode): a power of two covering the
   // segments in groups of kSegPerThread (nseg <= 512, so at most 32)
   int p2 = 1;
