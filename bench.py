@@ -439,6 +439,18 @@ def stream_prefill(steps, hip):
             "elements_per_s": B * H * L / (ms * 1e-3), "path": "chunked form, state in and out"}
 
 
+def _s5_fused_segments(B, H, P, L):
+    """Segments per batch row of the fused S5 scan (0 where the fused form does
+    not apply), as the library plans them: about 256 workgroups of whole
+    64-step tiles.  Used only to attribute the flops of the report."""
+    if not (P <= 128 and H <= 256 and H * L <= 1 << 29):
+        return 0
+    nt = -(-L // 64)
+    want = max(1, -(-256 // B))
+    seg_tiles = max(1, -(-nt // want))
+    return -(-nt // seg_tiles)
+
+
 def s5_config(steps, hip):
     """The S5 workload by both methods: plain-call wall ms over rotated sets and
     the four stages' stamped durations; errors against the float64 recurrence
@@ -461,7 +473,7 @@ def s5_config(steps, hip):
     gemm_flop = 2.0 * (2 * P) * H * L * B  # one projection, as float32 products
     out = {"workload": "s5_mimo", "B": B, "H": H, "P": P, "L": L, "elements": elems,
            "rotated_sets": R}
-    for name, method in (("scan", bd.S5_SCAN), ("fft", bd.S5_FFT)):
+    for name, method in (("scan", bd.S5_SCAN), ("fft", bd.S5_FFT), ("fused", bd.S5_FUSED)):
         ws = torch.empty(bd.s5_workspace_size(B, H, P, L, method), dtype=torch.uint8,
                          device="cuda")
 
@@ -482,15 +494,30 @@ def s5_config(steps, hip):
         out[name] = {
             "ms_per_forward": ms, "elements_per_s": elems / (ms * 1e-3),
             "layer_hbm_gbs": gbs, "layer_hbm_frac": frac,
-            "stage_ms": {"pack": st[0], "proj_in": st[1],
-                         ("scan" if name == "scan" else "spectrum+conv"): st[2],
-                         "proj_out": st[3]},
-            # the projections run 3 fp16 products per float32 product
-            "proj_in_mfma_f16_tflops_executed": 3 * gemm_flop / (st[1] * 1e-3) / 1e12,
-            "proj_out_mfma_f16_tflops_executed": 3 * gemm_flop / (st[3] * 1e-3) / 1e12,
             "mfma_f16_dense_peak_tflops": FP16_MFMA_PEAK_TFLOPS,
             "vs_oracle_batch_row_0": errors_vs(y, ref),
         }
+        if name == "fused":
+            # one kernel per pass: the state-only pass runs the input
+            # projection and the recurrence on every segment but the last;
+            # the output pass runs both projections and the recurrence (and
+            # joins the segment states)
+            f = 1.0 - 1.0 / _s5_fused_segments(B, H, P, L)
+            out[name]["form"] = "v and x on chip"
+            out[name]["stage_ms"] = {"pack": st[0], "state_only_pass": st[1],
+                                     "lambda_powers": st[2], "output_pass": st[3]}
+            # the projections run 3 fp16 products per float32 product
+            out[name]["state_pass_mfma_f16_tflops_executed"] = (
+                3 * gemm_flop * f / (st[1] * 1e-3) / 1e12)
+            out[name]["output_pass_mfma_f16_tflops_executed"] = (
+                2 * 3 * gemm_flop / (st[3] * 1e-3) / 1e12)
+        else:
+            out[name]["form"] = "v and x through HBM"
+            out[name]["stage_ms"] = {"pack": st[0], "proj_in": st[1],
+                                     ("scan" if name == "scan" else "spectrum+conv"): st[2],
+                                     "proj_out": st[3]}
+            out[name]["proj_in_mfma_f16_tflops_executed"] = 3 * gemm_flop / (st[1] * 1e-3) / 1e12
+            out[name]["proj_out_mfma_f16_tflops_executed"] = 3 * gemm_flop / (st[3] * 1e-3) / 1e12
     return out
 
 
@@ -508,7 +535,7 @@ def time_s5_tv(steps):
     t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
     us, ys = rotated(t["u"], 700 << 20)
     R = len(us)
-    ws = torch.empty(bd.s5_workspace_size(c["B"], c["H"], c["P"], c["L"]), dtype=torch.uint8,
+    ws = torch.empty(bd.s5_tv_workspace_size(c["B"], c["H"], c["P"], c["L"]), dtype=torch.uint8,
                      device="cuda")
 
     def call(k):

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DSSM_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define DSSM_VERSION 10300 /* major*10000 + minor*100 + patch */
 
 /* Status codes. */
 typedef enum {
@@ -67,8 +67,9 @@ typedef enum {
   DSSM_OP_FFT = 1,     /* dssm_forward_fft */
   DSSM_OP_SCAN = 2,    /* dssm_forward_scan */
   DSSM_OP_BWD = 3,     /* dssm_backward */
-  DSSM_OP_S5_SCAN = 4, /* dssm_s5_forward, method DSSM_S5_SCAN (shape N = state size P) */
-  DSSM_OP_S5_FFT = 5   /* dssm_s5_forward, method DSSM_S5_FFT (shape N = state size P) */
+  DSSM_OP_S5_SCAN = 4,  /* dssm_s5_forward, method DSSM_S5_SCAN (shape N = state size P) */
+  DSSM_OP_S5_FFT = 5,   /* dssm_s5_forward, method DSSM_S5_FFT (shape N = state size P) */
+  DSSM_OP_S5_FUSED = 6  /* dssm_s5_forward, method DSSM_S5_FUSED (shape N = state size P) */
 } dssm_op;
 
 /* How dssm_s5_forward runs the state recurrence ("Simplified State Space
@@ -76,7 +77,8 @@ typedef enum {
  * convolution mode of a linear time-invariant system give the same map). */
 typedef enum {
   DSSM_S5_SCAN = 0, /* the recurrence as a parallel scan over time */
-  DSSM_S5_FFT = 1   /* per state, the convolution with lambda_p^j by FFT */
+  DSSM_S5_FFT = 1,  /* per state, the convolution with lambda_p^j by FFT */
+  DSSM_S5_FUSED = 2 /* projections and recurrence in one pass over u (v, x on chip) */
 } dssm_s5_method;
 
 /* How the complex kernel K is cast to the real kernel the convolution applies
@@ -129,7 +131,7 @@ const char* dssm_last_error(void);
  * nothing).  Returns DSSM_ERR_INVALID_ARG / DSSM_ERR_UNSUPPORTED exactly
  * when the corresponding compute call would.  Limits common to the DLR calls:
  * 1 <= N <= 4096, H (1 + bidirectional) <= 65535, B H L <= 2^40 and
- * B H (1 + bidirectional) <= 2^31 - 1.  For DSSM_OP_S5_SCAN / DSSM_OP_S5_FFT
+ * B H (1 + bidirectional) <= 2^31 - 1.  For DSSM_OP_S5_SCAN / _FFT / _FUSED
  * the shape is read as the S5 shape {B, H, P = N, L, bidirectional} and the
  * result is dssm_s5_workspace_size() of that method. */
 int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes);
@@ -287,8 +289,16 @@ int dssm_step(const float* u_t, const dssm_dlr_params* p, const dssm_shape* s, f
  * per time step), and three fp16 products (hi.hi + hi.lo + lo.hi) are
  * accumulated in float32, about 22 significant bits per operand.  The
  * state recurrence runs by `method`:
- *   DSSM_S5_SCAN: a segmented complex scan whose carries use powers of lambda
- *     computed in float64 (section 2.2, the parallel scan);
+ *   DSSM_S5_SCAN: v and x in the workspace, a segmented complex scan
+ *     between the projections whose carries use powers of lambda computed in
+ *     float64 (section 2.2, the parallel scan);
+ *   DSSM_S5_FUSED: the same recurrence with v and x never written to memory:
+ *     per 64-step tile of a batch row, v = Bbar u, the tile's recurrence and
+ *     y = Re(C x) + D u in one kernel; the sequence of a row is cut into
+ *     segments whose entering states come from a state-only pass (the state
+ *     each segment leaves from zero), joined with powers of lambda in
+ *     float64.  Requires P <= 128, H <= 256 and H L <= 2^29 (otherwise
+ *     DSSM_ERR_UNSUPPORTED);
  *   DSSM_S5_FFT: per state p and batch row b, the causal convolution
  *     x_p = (lambda_p^j)_j * v_p (section 2.3, the convolution mode), by a
  *     complex FFT on a zero-padded circle of length 2M (M = the smallest
@@ -312,9 +322,15 @@ typedef struct {
   const float* D;
 } dssm_s5_params;
 
-/* Bytes of workspace dssm_s5_forward needs with `method` (host only);
- * dssm_s5_forward_tv takes the DSSM_S5_SCAN size. */
+/* Bytes of workspace dssm_s5_forward needs with `method` (host only).
+ * DSSM_S5_FUSED needs only the packed projections, the segment states and
+ * powers of lambda; the other methods add v and x (2 x B P L complex
+ * float32). */
 int dssm_s5_workspace_size(const dssm_s5_shape* s, int method, size_t* bytes);
+
+/* Bytes of workspace dssm_s5_forward_tv needs (host only): the packed
+ * projections, v and x.  Errors as dssm_s5_workspace_size. */
+int dssm_s5_tv_workspace_size(const dssm_s5_shape* s, size_t* bytes);
 
 /* y [B, H, L] from u [B, H, L] by `method` (a dssm_s5_method); same
  * conventions as the DLR calls. */
@@ -337,8 +353,8 @@ int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape
  *   0 is allowed: the state is then carried over unchanged).
  * The projections are those of dssm_s5_forward (Btilde in place of Bbar);
  * the scan forms z in float64 and the discretised values in float32.  Same
- * shape limits, workspace (dssm_s5_workspace_size, DSSM_S5_SCAN) and conventions as
- * dssm_s5_forward; step must be 16-byte aligned. */
+ * shape limits and conventions as dssm_s5_forward, workspace
+ * dssm_s5_tv_workspace_size; step must be 16-byte aligned. */
 typedef struct {
   const float* lambda_c;
   const float* Btilde;
@@ -354,7 +370,10 @@ int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5
  * four stages, in order: packing of Bbar and C, input projection, the state
  * recurrence (the scan kernel, or the spectrum and convolution kernels of
  * DSSM_S5_FFT), output projection (same event conventions as the DLR timing
- * variants). */
+ * variants).  For DSSM_S5_FUSED the last three pairs stamp the state-only
+ * pass, the kernel that forms the powers of lambda, and the output pass
+ * (which also joins the segment states); with one segment per row there is
+ * no state-only pass and its pair is recorded back to back. */
 int dssm_s5_forward_timed(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s,
                           int method, float* y, void* ws, size_t ws_bytes, void* stream,
                           void* const* events, int n_events);

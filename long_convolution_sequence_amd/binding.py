@@ -17,8 +17,10 @@ DSSM_ERR_UNSUPPORTED = -2
 DSSM_ERR_WORKSPACE = -3
 DSSM_ERR_HIP = -4
 
-OP_GEN, OP_FFT, OP_SCAN, OP_BWD, OP_S5_SCAN, OP_S5_FFT = 0, 1, 2, 3, 4, 5
-S5_SCAN, S5_FFT = 0, 1  # how the S5 state recurrence runs: scan, or per-state FFT convolution
+OP_GEN, OP_FFT, OP_SCAN, OP_BWD, OP_S5_SCAN, OP_S5_FFT, OP_S5_FUSED = 0, 1, 2, 3, 4, 5, 6
+# how the S5 state recurrence runs: scan between the projections, per-state FFT
+# convolution, or fused with both projections (v and x on chip)
+S5_SCAN, S5_FFT, S5_FUSED = 0, 1, 2
 CAST_RE, CAST_RE_IM = 0, 1  # Re K, or Re K * Im K (DLR-prod)
 
 # Every function the header declares (checked by the ABI tests).
@@ -29,7 +31,8 @@ EXPORTS = [
     "dssm_forward_scan", "dssm_backward",
     "dssm_forward_fft_timed", "dssm_forward_scan_timed",
     "dssm_forward_scan_state", "dssm_step",
-    "dssm_s5_workspace_size", "dssm_s5_forward", "dssm_s5_forward_timed", "dssm_s5_forward_tv",
+    "dssm_s5_workspace_size", "dssm_s5_tv_workspace_size", "dssm_s5_forward",
+    "dssm_s5_forward_timed", "dssm_s5_forward_tv",
 ]
 
 
@@ -118,6 +121,8 @@ def lib():
                                           vp, vp, vp, sz, vp]
     L.dssm_step.restype = ctypes.c_int
     L.dssm_step.argtypes = [vp, ctypes.POINTER(DLRParams), ctypes.POINTER(Shape), vp, vp, vp]
+    L.dssm_s5_tv_workspace_size.restype = ctypes.c_int
+    L.dssm_s5_tv_workspace_size.argtypes = [ctypes.POINTER(S5Shape), ctypes.POINTER(ctypes.c_size_t)]
     L.dssm_s5_workspace_size.restype = ctypes.c_int
     L.dssm_s5_workspace_size.argtypes = [ctypes.POINTER(S5Shape), ctypes.c_int,
                                          ctypes.POINTER(sz)]
@@ -428,10 +433,21 @@ def s5_workspace_size(B, H, P, L, method=S5_SCAN):
     return out.value
 
 
+def s5_tv_workspace_size(B, H, P, L):
+    shape = S5Shape(B, H, P, L, 0)
+    out = ctypes.c_size_t(0)
+    check(lib().dssm_s5_tv_workspace_size(ctypes.byref(shape), ctypes.byref(out)))
+    return out.value
+
+
 def _s5_workspace(shape, workspace, device, stream, method=S5_SCAN):
+    """method None: the size dssm_s5_forward_tv needs."""
     torch = _torch()
     need = ctypes.c_size_t(0)
-    check(lib().dssm_s5_workspace_size(ctypes.byref(shape), int(method), ctypes.byref(need)))
+    if method is None:
+        check(lib().dssm_s5_tv_workspace_size(ctypes.byref(shape), ctypes.byref(need)))
+    else:
+        check(lib().dssm_s5_workspace_size(ctypes.byref(shape), int(method), ctypes.byref(need)))
     if workspace is None:
         with _on_stream(stream):
             workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=device)
@@ -444,9 +460,12 @@ def s5_forward(u, lam, Bbar, C, D, y=None, workspace=None, stream=None, events=N
                method=S5_SCAN):
     """S5 layer forward.  u [B,H,L] f32, lam [P] c64, Bbar [P,H] c64,
     C [H,P] c64, D [H] f32 -> y [B,H,L] f32.  method: S5_SCAN (the
-    recurrence as a scan) or S5_FFT (per state, the convolution with
-    lambda^j by FFT).  events: optional 8 raw hipEvent_t handles, a
-    start/stop pair per stage (pack, proj_in, recurrence, proj_out)."""
+    recurrence as a scan between the projections), S5_FFT (per state, the
+    convolution with lambda^j by FFT) or S5_FUSED (projections and
+    recurrence in one pass, v and x on chip).  events: optional 8 raw
+    hipEvent_t handles, a start/stop pair per stage (pack, proj_in,
+    recurrence, proj_out; for S5_FUSED: pack, state-only pass, powers of
+    lambda, output pass)."""
     torch = _torch()
     uu = _rows(u)
     B, H, L = uu.shape
@@ -492,7 +511,7 @@ def s5_forward_tv(u, lam_c, Bt, C, D, delta, step, y=None, workspace=None, strea
     if y is None:
         y = _empty(uu.shape, torch.float32, dev, stream)
     yy = _dev_f32(y, "y", uu.numel(), dev)
-    ws, nbytes = _s5_workspace(shape, workspace, dev, stream)
+    ws, nbytes = _s5_workspace(shape, workspace, dev, stream, None)
     check(lib().dssm_s5_forward_tv(uu.data_ptr(), ctypes.byref(prm), ctypes.byref(shape),
                                    ss.data_ptr(), yy.data_ptr(), ws.data_ptr(), nbytes,
                                    _stream(stream)))

@@ -177,10 +177,15 @@ static int s5_workspace(const dssm_s5_shape* s, int method, size_t* bytes);
 
 int dssm_workspace_size(int op, const dssm_shape* s, size_t* bytes) {
   if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
-  if (op == DSSM_OP_S5_SCAN || op == DSSM_OP_S5_FFT) {  // N is the state size P
+  if (op == DSSM_OP_S5_SCAN || op == DSSM_OP_S5_FFT || op == DSSM_OP_S5_FUSED) {
+    // N is the state size P
     if (!s) return fail(DSSM_ERR_INVALID_ARG, "shape is NULL");
     const dssm_s5_shape s5{s->B, s->H, s->N, s->L, s->bidirectional};
-    return s5_workspace(&s5, op == DSSM_OP_S5_FFT ? DSSM_S5_FFT : DSSM_S5_SCAN, bytes);
+    return s5_workspace(&s5,
+                        op == DSSM_OP_S5_FFT     ? DSSM_S5_FFT
+                        : op == DSSM_OP_S5_FUSED ? DSSM_S5_FUSED
+                                                 : DSSM_S5_SCAN,
+                        bytes);
   }
   bool empty = false;
   int rc = check_shape(op, s, &empty);
@@ -536,10 +541,20 @@ static int s5_check_shape(const dssm_s5_shape* s, bool* empty) {
   return DSSM_OK;
 }
 
+static S5Form s5_form(int method) {
+  return method == DSSM_S5_FFT ? kS5Conv : method == DSSM_S5_FUSED ? kS5Fused : kS5Unfused;
+}
+
 static int s5_check_method(int method, const dssm_s5_shape* s) {
-  if (method != DSSM_S5_SCAN && method != DSSM_S5_FFT)
-    return fail(DSSM_ERR_INVALID_ARG, "method must be DSSM_S5_SCAN (0) or DSSM_S5_FFT (1), got %d",
+  if (method != DSSM_S5_SCAN && method != DSSM_S5_FFT && method != DSSM_S5_FUSED)
+    return fail(DSSM_ERR_INVALID_ARG,
+                "method must be DSSM_S5_SCAN (0), DSSM_S5_FFT (1) or DSSM_S5_FUSED (2), got %d",
                 method);
+  if (method == DSSM_S5_FUSED && !s5_fused_supported(s->H, s->P, s->L))
+    return fail(DSSM_ERR_UNSUPPORTED,
+                "the fused S5 form needs P <= 128, H <= 256 and H L <= 2^29 (got P=%d H=%d L=%d); "
+                "use DSSM_S5_SCAN",
+                s->P, s->H, s->L);
   if (method == DSSM_S5_FFT && s->L > kMaxFFTL)
     return fail(DSSM_ERR_UNSUPPORTED,
                 "the S5 convolution view needs L <= %d (got %d); use DSSM_S5_SCAN", kMaxFFTL, s->L);
@@ -551,7 +566,7 @@ static int s5_workspace(const dssm_s5_shape* s, int method, size_t* bytes) {
   int rc = s5_check_shape(s, &empty);
   if (rc) return rc;
   if ((rc = s5_check_method(method, s))) return rc;
-  *bytes = empty ? 0 : s5_layout(s->B, s->H, s->P, s->L, method == DSSM_S5_FFT).total;
+  *bytes = empty ? 0 : s5_layout(s->B, s->H, s->P, s->L, s5_form(method)).total;
   return ok();
 }
 
@@ -575,7 +590,7 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   if (u == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u");
   if ((rc = check_events(events, n_events))) return rc;
   const bool fft = method == DSSM_S5_FFT;
-  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L, fft);
+  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L, s5_form(method));
   if (ws_bytes < l.total)
     return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 ws_bytes, l.total);
@@ -589,10 +604,22 @@ static int s5_impl(const float* u, const dssm_s5_params* p, const dssm_s5_shape*
   int* rexp_out = at<int>(ws, l.rexp_out);
   float* v = at<float>(ws, l.v);
   float* x = at<float>(ws, l.x);
+  const bool fused = method == DSSM_S5_FUSED;
   if ((rc = hip_check(launch_s5_pack(p->Bbar, p->C, s->H, s->P, apk_in, rexp_in, apk_out,
-                                     rexp_out, st, kev(events, 0)),
+                                     rexp_out, st, kev(events, 0), fused),
                       "s5 pack")))
     return rc;
+  if (fused) {
+    // v and x on chip: the powers of lambda, the state-only pass, then the
+    // output pass (which joins the segment states)
+    if ((rc = hip_check(launch_s5_fused(apk_in, rexp_in, apk_out, rexp_out, p->lambda, p->D, u,
+                                        s->B, s->H, s->P, s->L, y, at<float2>(ws, l.sout),
+                                        at<unsigned char>(ws, l.fconst), st, kev(events, 2),
+                                        kev(events, 1), kev(events, 3)),
+                        "s5 fused")))
+      return rc;
+    return ok();
+  }
   if ((rc = hip_check(
            launch_s5_proj_in(apk_in, rexp_in, u, s->B, s->H, s->P, s->L, v, st, kev(events, 1)),
            "s5 proj_in")))
@@ -637,7 +664,7 @@ int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5
   if (!u || !y || !step || !aligned16(u) || !aligned16(y) || !aligned16(step))
     return fail(DSSM_ERR_INVALID_ARG, "u, step or y is NULL or not 16-byte aligned");
   if (u == y || step == y) return fail(DSSM_ERR_INVALID_ARG, "y must not alias u or step");
-  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L);
+  const S5Layout l = s5_layout(s->B, s->H, s->P, s->L, kS5Unfused);
   if (ws_bytes < l.total)
     return fail(DSSM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                 ws_bytes, l.total);
@@ -671,6 +698,15 @@ int dssm_s5_forward_tv(const float* u, const dssm_s5_tv_params* p, const dssm_s5
 int dssm_s5_workspace_size(const dssm_s5_shape* s, int method, size_t* bytes) {
   if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
   return s5_workspace(s, method, bytes);
+}
+
+int dssm_s5_tv_workspace_size(const dssm_s5_shape* s, size_t* bytes) {
+  if (!bytes) return fail(DSSM_ERR_INVALID_ARG, "bytes is NULL");
+  bool empty = false;
+  const int rc = s5_check_shape(s, &empty);
+  if (rc) return rc;
+  *bytes = empty ? 0 : s5_layout(s->B, s->H, s->P, s->L, kS5Unfused).total;
+  return ok();
 }
 
 int dssm_s5_forward(const float* u, const dssm_s5_params* p, const dssm_s5_shape* s, int method,

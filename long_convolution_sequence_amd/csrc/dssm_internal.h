@@ -156,16 +156,26 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
 // S5 multi-input multi-output diagonal SSM (s5.hip)
 // ---------------------------------------------------------------------------
 struct S5Layout {
-  size_t apk_in = 0, rexp_in = 0, apk_out = 0, rexp_out = 0, v = 0, x = 0, spec = 0, total = 0;
+  size_t apk_in = 0, rexp_in = 0, apk_out = 0, rexp_out = 0, v = 0, x = 0, spec = 0, sout = 0,
+         fconst = 0, total = 0;
 };
-// with_spec: the convolution view's spectrum table [P][2][M] float2 as well
-S5Layout s5_layout(int B, int H, int P, int L, bool with_spec = false);
+// Which regions a call needs besides the packed fragments:
+//   kS5Unfused: v and x (the scan between the projections, also with a step
+//     size per step);
+//   kS5Conv: v, x and the convolution view's spectrum table [P][2][M] float2;
+//   kS5Fused: the fused form's segment states and powers of lambda (the
+//     fragments in its layout; requires s5_fused_supported).
+enum S5Form { kS5Unfused = 1, kS5Conv = 2, kS5Fused = 3 };
+S5Layout s5_layout(int B, int H, int P, int L, S5Form form);
 
 // Bbar [P,H] c64, C [H,P] c64 -> split MFMA fragment tables (16-byte aligned)
 // and per-row scale exponents.
+// fused: the layout of the fused form: Bbar's rows in its order (per 32
+// rows, the real then the imaginary rows of 16 states; 32 ceil(P / 16) rows),
+// both kinds zero-padded to 32 s5_fused_ks(H, P) columns.
 hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, void* apk_in,
                           int* rexp_in, void* apk_out, int* rexp_out, hipStream_t st,
-                          KEvents ev = {});
+                          KEvents ev = {}, bool fused = false);
 // v [B][P][2][L] = Bbar u
 hipError_t launch_s5_proj_in(const void* apk_in, const int* rexp_in, const float* u, int B, int H,
                              int P, int L, float* v, hipStream_t st, KEvents ev = {});
@@ -177,6 +187,25 @@ hipError_t launch_s5_scan(const float* lambda, const float* v, int B, int P, int
 hipError_t launch_s5_scan_tv(const float* lam_c, const float* delta, const float* step,
                             const float* v, int B, int P, int L, float* x, hipStream_t st,
                             KEvents ev = {});
+// The fused form (P <= 128, H <= 256, H L <= 2^29): y from u through the
+// packed Bbar (fused row order) and C fragments, v and x kept on chip, the
+// sequence of each batch row in nseg segments of seg_tiles 64-step tiles;
+// sout: [B][nseg][P] c64 scratch; consts: P (32 + 16 nseg) bytes (powers of
+// lambda).  Three launches, each stamped by its own event pair: the powers of
+// lambda, a state-only pass, then the output pass that also joins the segment
+// states (no state-only pass when nseg == 1: its pair is stamped back to back).
+bool s5_fused_supported(int H, int P, int L);
+// k steps (of 32) both fused products are padded to: 2, 4 or 8
+int s5_fused_ks(int H, int P);
+struct S5FusedPlan {
+  int nseg = 1, seg_tiles = 1;
+};
+S5FusedPlan s5_fused_plan(int B, int L);
+hipError_t launch_s5_fused(const void* apk_in, const int* rexp_in, const void* apk_out,
+                           const int* rexp_out, const float* lambda, const float* D,
+                           const float* u, int B, int H, int P, int L, float* y, float2* sout,
+                           void* consts, hipStream_t st, KEvents ev_consts = {},
+                           KEvents ev_state = {}, KEvents ev_out = {});
 // y [B][H][L] = Re(C x) + D u
 hipError_t launch_s5_proj_out(const void* apk_out, const int* rexp_out, const float* x,
                               const float* D, const float* u, int B, int H, int P, int L, float* y,

@@ -26,6 +26,7 @@
 //     Hillis-Steele scan with multipliers lambda^(16 2^j) from float64, tiles
 //     of 4096 steps chained by the carried state.
 #include <algorithm>
+#include <climits>
 
 #include "dssm_internal.h"
 #include "mfma_split.h"
@@ -53,17 +54,21 @@ constexpr int kBTS = kKC + 8;  // LDS row stride (fp16) of the transposed B tile
 // Element A[i][k] of a contraction (zero outside M x K):
 // kind 0: A = [Re Bbar; Im Bbar] interleaved by p (M = 2P rows, K = H)
 // kind 1: A = [Re C, -Im C] interleaved by p      (M = H rows,  K = 2P)
+// kind 2: Bbar in the fused form's row order (M = 32 ceil(P / 16) rows,
+//         K = H): row i is Re (bit 4 of i clear) or Im of Bbar[16 (i / 32) + i % 16, :]
 // Branch-free: the load always reads an in-range element (clamped indices)
 // and the result is selected afterwards, so a thread's loads of several
 // elements are all in flight together instead of one round trip each.
 __device__ __forceinline__ float a_elem(int kind, const float2* __restrict__ Bbar,
                                         const float2* __restrict__ C, int H, int P, int i, int k) {
-  const bool k0 = kind == 0;
-  const bool in = k0 ? (i < 2 * P && k < H) : (i < H && k < 2 * P);
-  const size_t idx = k0 ? (size_t)min(i >> 1, P - 1) * H + min(k, H - 1)
+  const bool k0 = kind != 1;
+  const int pb = kind == 2 ? 16 * (i >> 5) + (i & 15) : i >> 1;  // state of a Bbar row
+  const bool imb = kind == 2 ? ((i >> 4) & 1) : (i & 1);         // its imaginary part
+  const bool in = k0 ? (pb < P && k < H) : (i < H && k < 2 * P);
+  const size_t idx = k0 ? (size_t)min(pb, P - 1) * H + min(k, H - 1)
                         : (size_t)min(i, H - 1) * P + min(k >> 1, P - 1);
   const float2 v = (k0 ? Bbar : C)[idx];
-  const float e = k0 ? ((i & 1) ? v.y : v.x) : ((k & 1) ? -v.y : v.x);
+  const float e = k0 ? (imb ? v.y : v.x) : ((k & 1) ? -v.y : v.x);
   return in ? e : 0.f;
 }
 
@@ -78,15 +83,15 @@ __global__ __launch_bounds__(256) void s5_pack_kernel(const float2* __restrict__
                                                       half8* __restrict__ apk_in,
                                                       int* __restrict__ rexp_in,
                                                       half8* __restrict__ apk_out,
-                                                      int* __restrict__ rexp_out) {
+                                                      int* __restrict__ rexp_out, int fused, int kpad) {
   __shared__ float red[16][17];
   __shared__ int rexp_s[16];
-  const int kind = blockIdx.y;
-  const int M = kind == 0 ? 2 * P : H;
-  const int K = kind == 0 ? H : 2 * P;
+  const int kind = blockIdx.y == 1 ? 1 : (fused ? 2 : 0);
+  const int M = kind == 0 ? 2 * P : kind == 2 ? 64 * ((32 * ((P + 15) / 16) + 63) / 64) : H;
+  const int K = kind == 1 ? 2 * P : H;
   const int it = blockIdx.x;
   if (16 * it >= M) return;
-  const int KS = (K + 31) / 32;
+  const int KS = kpad > 0 ? kpad : (K + 31) / 32;  // k steps (zero past K)
   const int t = threadIdx.x, r = t & 15, part = t >> 4;
   // row maxima: thread (r, part) scans k = part, part + 16, ... (16 independent
   // loads in flight per step: one step covers K = 256)
@@ -105,10 +110,10 @@ __global__ __launch_bounds__(256) void s5_pack_kernel(const float2* __restrict__
     float mm = 0.f;
     for (int q = 0; q < 16; ++q) mm = fmaxf(mm, red[t][q]);
     rexp_s[t] = scale_exp(mm);
-    (kind == 0 ? rexp_in : rexp_out)[16 * it + t] = rexp_s[t];
+    (kind != 1 ? rexp_in : rexp_out)[16 * it + t] = rexp_s[t];
   }
   __syncthreads();
-  half8* out = (kind == 0 ? apk_in : apk_out) + (size_t)it * KS * 2 * 64;
+  half8* out = (kind != 1 ? apk_in : apk_out) + (size_t)it * KS * 2 * 64;
   // fragments: two (k step, lane) entries per thread and step, all 16 loads
   // issued before the first is used
   for (int idx0 = t; idx0 < KS * 64; idx0 += 512) {
@@ -146,15 +151,15 @@ __global__ __launch_bounds__(256) void s5_pack_lds_kernel(const float2* __restri
                                                           int P, half8* __restrict__ apk_in,
                                                           int* __restrict__ rexp_in,
                                                           half8* __restrict__ apk_out,
-                                                          int* __restrict__ rexp_out) {
+                                                          int* __restrict__ rexp_out, int fused, int kpad) {
   __shared__ float A[16][kPackLdsK + 4];
   __shared__ float red[16][17];
   __shared__ int rexp_s[16];
-  const int kind = blockIdx.y;
-  const int M = kind == 0 ? 2 * P : H;
-  const int K = kind == 0 ? H : 2 * P;
+  const int kind = blockIdx.y == 1 ? 1 : (fused ? 2 : 0);
+  const int M = kind == 0 ? 2 * P : kind == 2 ? 64 * ((32 * ((P + 15) / 16) + 63) / 64) : H;
+  const int K = kind == 1 ? 2 * P : H;
   const int it = blockIdx.x, g = blockIdx.z;
-  const int KS = (K + 31) / 32;
+  const int KS = kpad > 0 ? kpad : (K + 31) / 32;  // k steps (zero past K)
   if (16 * it >= M || kPackKS * g >= KS) return;  // the whole workgroup
   const int KP = 32 * KS;  // staged row length (zero past K)
   const int t = threadIdx.x;
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(256) void s5_pack_lds_kernel(const float2* __restri
     float mm = 0.f;
     for (int q = 0; q < 16; ++q) mm = fmaxf(mm, red[t][q]);
     rexp_s[t] = scale_exp(mm);
-    if (g == 0) (kind == 0 ? rexp_in : rexp_out)[16 * it + t] = rexp_s[t];
+    if (g == 0) (kind != 1 ? rexp_in : rexp_out)[16 * it + t] = rexp_s[t];
   }
   __syncthreads();
   const int ks = kPackKS * g + (t >> 6);
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256) void s5_pack_lds_kernel(const float2* __restri
     for (int e = 0; e < 8; ++e) v[e] = A[i][k0 + e];
     half8 hi, lo;
     split8(v, hi, lo, rexp_s[i]);
-    half8* out = (kind == 0 ? apk_in : apk_out) + (size_t)it * KS * 2 * 64;
+    half8* out = (kind != 1 ? apk_in : apk_out) + (size_t)it * KS * 2 * 64;
     out[(size_t)(ks * 2) * 64 + l] = hi;
     out[(size_t)(ks * 2 + 1) * 64 + l] = lo;
   }
@@ -908,9 +913,597 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused S5 form (P <= 128, H <= 256): per 64-step tile of one batch row,
+// v = Bbar u on the matrix cores, the recurrence on the tile in registers, and
+// y = Re(C x) + D u on the matrix cores, so v and x never leave the CU.  The
+// sequence of a batch row is cut into segments of whole tiles (one workgroup
+// each).  A state-only pass (the input projection and the recurrence from
+// zero) leaves the state at the end of every segment but the last; the output
+// pass forms the state entering its segment from those (float64 Horner steps
+// with lambda^S, S the steps of a segment) and runs the whole tile pipeline.
+//
+// One workgroup of 4 waves per CU, one wave per SIMD (so a wave may hold up to
+// 512 registers: accumulators and operands of 16 independent products, and in
+// the state-only pass the input projection's fragments).  LDS: the fp32 u tile
+// [H][64] (filled by buffer-to-LDS loads one tile ahead, so u needs no
+// registers in flight), the staged right-hand operand [64 steps][256 k] as
+// fp16 hi and lo (u, then x), per-step maxima and exponents.  Wave w owns 64
+// rows of each product: for the input projection the real and the imaginary
+// rows of states 32 w .. 32 w + 31, 16 states per 32 rows (the packed Bbar
+// takes that row order), so after the product lane (q, g) holds v of states
+// 32 w + q and 32 w + 16 + q at the 16 consecutive steps 16 g .. 16 g + 15 of
+// the tile (the staged operand's rows are read in that time order).  The
+// recurrence: a float32 chain of 16 steps from zero per lane and state, the
+// four quarters joined with lambda^16, lambda^32, lambda^48 (float64, rounded
+// once), each step completed by lambda^(j+1) times its quarter's entering
+// state, the tile's last state by lambda^64.  The output projection's operand
+// x is scaled per step (the largest magnitude over all 2P rows, across the
+// waves through LDS) and split into fp16 hi and lo like u.
+// ---------------------------------------------------------------------------
+constexpr int kFT = kColsWG;  // steps per tile
+
+struct S5FusedArgs {
+  const half8* apk_in;  // Bbar as A in the fused row order (s5_fused_rows), K = H
+  const int* rexp_in;
+  const half8* apk_out;  // C as A: M = H rows, K = 2P
+  const int* rexp_out;
+  const float* u;
+  const float2* lam;
+  const float* D;
+  float* y;
+  float2* sout;  // [B][nseg][P]: the state leaving each segment but the last
+  const float4* lp;     // [P][2]: lambda^16, lambda^32 | lambda^48, lambda^64
+  const double2* apow;  // [P][nseg]: lambda^(S n), S the steps of a segment
+  int B, H, P, L, nseg, seg_tiles;
+};
+
+__device__ __forceinline__ float2 cmad(float2 m, float2 x, float2 c) {  // m x + c
+  return make_float2(fmaf(m.x, x.x, fmaf(-m.y, x.y, c.x)), fmaf(m.x, x.y, fmaf(m.y, x.x, c.y)));
+}
+
+// lambda^k from the float64 logarithm of lambda (lambda != 0).
+__device__ __forceinline__ double2 lam_pow_d(float2 lm, double k) {
+  const double lr = (double)lm.x, li = (double)lm.y;
+  const double lmag = 0.5 * log1p((lr * lr - 1.0) + li * li);
+  double sn, cs;
+  sincos(fmod(k * atan2(li, lr), 2.0 * M_PI), &sn, &cs);
+  const double m = exp(k * lmag);
+  return make_double2(m * cs, m * sn);
+}
+__device__ __forceinline__ float2 lam_pow64(float2 lm, double k) {
+  const double2 z = lam_pow_d(lm, k);
+  return make_float2((float)z.x, (float)z.y);
+}
+
+// Per-call constants of the fused form (float64 from the logarithm of lambda,
+// rounded once): lp[p] = lambda^16, lambda^32, lambda^48, lambda^64 (the
+// recurrence on a tile); apow[p][n] = lambda^(S n) for n < nseg (joining the
+// segment states; lambda^0 = 1).
+__global__ __launch_bounds__(256) void s5_fused_consts_kernel(const float2* __restrict__ lam,
+                                                              int P, int nseg, double S,
+                                                              float4* __restrict__ lp,
+                                                              double2* __restrict__ apow) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long na = (long)P * nseg;
+  if (i < na) {
+    const int p = (int)(i / nseg), n = (int)(i % nseg);
+    const float2 lm = lam[p];
+    const bool nz = lm.x != 0.f || lm.y != 0.f;
+    apow[i] = n == 0 ? make_double2(1.0, 0.0)
+                     : (nz ? lam_pow_d(lm, S * (double)n) : make_double2(0.0, 0.0));
+  } else if (i < na + P) {
+    const int p = (int)(i - na);
+    const float2 lm = lam[p];
+    float2 l16 = make_float2(0.f, 0.f), l32 = l16, l48 = l16, l64 = l16;
+    if (lm.x != 0.f || lm.y != 0.f) {
+      l16 = lam_pow64(lm, 16.0);
+      l32 = lam_pow64(lm, 32.0);
+      l48 = lam_pow64(lm, 48.0);
+      l64 = lam_pow64(lm, 64.0);
+    }
+    lp[2 * p] = make_float4(l16.x, l16.y, l32.x, l32.y);
+    lp[2 * p + 1] = make_float4(l48.x, l48.y, l64.x, l64.y);
+  }
+}
+
+// One dword per lane from a raw buffer into LDS at lds + 4 lane (zero where
+// the lane's offset is past the buffer).  Issued from inline assembly so the
+// compiler tracks no LDS write by it: every reader of that LDS is ordered by
+// an explicit vmcnt(0) wait and a barrier.
+__device__ __forceinline__ void dma_dword(BufRes rs, unsigned lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rs)
+               : "memory");
+}
+
+// 16-byte chunk c (8 halves of k) of the staged operand's row `step`, swizzled
+// so that a k step's matrix-core reads and the staging writes meet every LDS
+// bank equally often.
+__device__ __forceinline__ int sw_chunk(int step, int c) { return c ^ ((step >> 4) << 2); }
+// Float index of u[k][j] within row k of the u tile (16-byte slots swizzled by k).
+__device__ __forceinline__ int u_slot(int k, int j) { return (((j >> 2) ^ (k & 15)) << 2) | (j & 3); }
+
+__device__ __forceinline__ int opaque_s(int x) {  // a scalar the optimiser recomputes at its use
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// KS: k steps (of 32) of both products, the fragments zero-padded to 32 KS;
+// FI: 16-row tiles per wave of each product (2: 8 waves, 4: 4 waves)
+template <bool STATE_ONLY, int KS, int FI>
+__global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArgs a) {
+  constexpr int kFW = 16 / FI;  // waves (256 rows of each product)
+  constexpr int kFI = FI;
+  constexpr int kFR = 16 * FI;  // rows per wave
+  constexpr int NS = FI / 2;    // states per lane
+  __shared__ __attribute__((aligned(16))) _Float16 Sh[kFT][kBTS];  // staged operand, hi
+  __shared__ __attribute__((aligned(16))) _Float16 Sl[kFT][kBTS];  // staged operand, lo
+  __shared__ __attribute__((aligned(16))) float U[kRowsWG][kFT];   // u tile, fp32
+  __shared__ float cmax[kFW][kFT];
+  __shared__ __attribute__((aligned(16))) int cexp[kFT];
+  __shared__ float2 cin_s[128];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int q = lane & 15, g = lane >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int H = a.H, P = a.P, L = a.L;
+  const int M1 = 32 * ((P + 15) / 16), K1 = H, M2 = H;
+  const int nt = (L + kFT - 1) / kFT;
+  const int wg = blockIdx.x;
+  const int b = wg / a.nseg, seg = wg % a.nseg;
+  const int tile0 = seg * a.seg_tiles, tile1 = min(nt, tile0 + a.seg_tiles);
+  if (STATE_ONLY && tile1 == nt) return;  // (whole workgroup) no later segment needs its state
+  const int i0 = kFR * wu;                // this wave's first row (both products)
+  const float* ub = a.u + (size_t)b * H * L;
+
+  // this lane's states (rows of the input projection: it = 2 s Re, 2 s + 1 Im)
+  int ps[NS];
+  bool pin[NS];
+  float2 lm[NS], l16[NS], l32[NS], l48[NS], l64[NS];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) {
+    ps[s2] = 16 * (NS * wu + s2) + q;
+    pin[s2] = ps[s2] < P;
+    lm[s2] = l16[s2] = l32[s2] = l48[s2] = l64[s2] = make_float2(0.f, 0.f);
+    if (pin[s2]) {
+      lm[s2] = a.lam[ps[s2]];
+      const float4 c0 = a.lp[2 * ps[s2]], c1 = a.lp[2 * ps[s2] + 1];
+      l16[s2] = make_float2(c0.x, c0.y);
+      l32[s2] = make_float2(c0.z, c0.w);
+      l48[s2] = make_float2(c1.x, c1.y);
+      l64[s2] = make_float2(c1.z, c1.w);
+    }
+  }
+  // per-row scale exponents of this wave's rows of each product, D of its output rows
+  int rx1[kFI], rx2[kFI];
+  float dd[kFI];
+#pragma unroll
+  for (int it = 0; it < kFI; ++it) {
+    const int i = i0 + 16 * it + q;
+    rx1[it] = i0 < M1 ? a.rexp_in[min(i, M1 - 1)] : 0;
+    rx2[it] = !STATE_ONLY && i0 < M2 ? a.rexp_out[min(i, M2 - 1)] : 0;
+    dd[it] = !STATE_ONLY && i0 < M2 ? a.D[min(i, M2 - 1)] : 0.f;
+  }
+
+  // the state entering this segment (output pass):
+  //   x_in(seg) = sum_{m < seg} lambda^(S (seg - 1 - m)) sout[m],
+  // thread (state t / NP, part t % NP) sums a part of the terms in float64; its
+  // first 16 terms are loaded before the first u tile (memory returns in order)
+  constexpr int NP = kFW / 2;  // threads per state (128 states)
+  const int cst = t / NP, cpart = t % NP;
+  int cm0 = 0, cm1 = 0;
+  float2 co[16];
+  double2 cc[16];
+  const float2* cso = a.sout + (size_t)b * a.nseg * P + cst;
+  const double2* cap = a.apow + (size_t)cst * a.nseg + (seg - 1);
+  auto carry_load = [&](int m) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int mm = min(m + e, cm1 - 1);  // in range; terms past cm1 zeroed below
+      co[e] = cso[(size_t)mm * P];
+      cc[e] = cap[-mm];
+    }
+  };
+  double2 h = make_double2(0.0, 0.0);
+  auto carry_add = [&](int m) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const double2 c = m + e < cm1 ? cc[e] : make_double2(0.0, 0.0);
+      h = make_double2(fma(c.x, (double)co[e].x, fma(-c.y, (double)co[e].y, h.x)),
+                       fma(c.x, (double)co[e].y, fma(c.y, (double)co[e].x, h.y)));
+    }
+  };
+  const bool cany = !STATE_ONLY && cst < P && seg > 0;
+  if (cany) {
+    const int cs = (seg + NP - 1) / NP;
+    cm0 = min(seg, cpart * cs);
+    cm1 = min(seg, cm0 + cs);
+    if (cm0 < cm1) carry_load(cm0);
+  }
+
+  // u tile jb into U: wave w fills rows k = w + W i, lane l dword l of the row
+  // (the column whose slot is l / 4); columns past L take an offset beyond the
+  // buffer (zero).  The batch row's u is one buffer (H L floats < 2^31 bytes).
+  // Rows k = w + W i have k % 16 = w + W (i % FI): FI lane patterns.
+  const BufRes ubuf = buf_res_uniform(ub, 4u * (unsigned)(H * L));
+  int upat[FI];
+#pragma unroll
+  for (int r = 0; r < FI; ++r) upat[r] = (((lane >> 2) ^ (wu + kFW * r)) << 2) | (lane & 3);
+  auto issue_u = [&](int jb) {
+    int o[FI];
+#pragma unroll
+    for (int r = 0; r < FI; ++r) {
+      const int j = jb * kFT + upat[r];
+      o[r] = j < L ? 4 * j : INT_MIN;
+    }
+    int rowoff = opaque_s(4 * wu * L);  // 4 k L, a running scalar
+    for (int k0 = wu; k0 < H; k0 += 16) {
+#pragma unroll
+      for (int r = 0; r < FI; ++r) {
+        const int k = k0 + kFW * r;
+        if (k < H) {
+          // past L: a negative lane offset, beyond the buffer as unsigned (zero)
+          dma_dword(ubuf, (unsigned)(size_t)&U[k][0], o[r] < 0 ? -1 : rowoff + o[r]);
+        }
+        rowoff += 4 * kFW * L;
+      }
+    }
+  };
+  issue_u(tile0);
+
+  if (cany) {
+    for (int m = cm0; m < cm1; m += 16) {
+      if (m > cm0) carry_load(m);
+      carry_add(m);
+    }
+  }
+  if (!STATE_ONLY) {
+#pragma unroll
+    for (int o = 1; o < NP; o *= 2) {  // the parts (adjacent lanes)
+      h.x += __shfl_xor(h.x, o, 64);
+      h.y += __shfl_xor(h.y, o, 64);
+    }
+    if (cpart == 0) cin_s[cst] = make_float2((float)h.x, (float)h.y);
+  }
+
+  // lane-derived indices, re-derived every tile from an opaque copy of the
+  // lane id so that the compiler forms LDS addresses where they are used
+  // instead of keeping dozens of them live across the tile loop
+  int ln = lane, lq = q, lg = g, a4 = (lane & 15) >> 2;
+  int brow = 16 * a4 + (lane & 3);  // staged row (step) of MFMA tile jt = 0 for this lane
+
+  // out^T[step][i] = sum_k A[i][k] S[k][step] for this wave's 64 rows and the
+  // tile's 64 steps: the fragments of A from L2 (one buffer, the wave's part in
+  // the scalar offset); lane (q, g) gets rows 16 it + q at steps 16 g + 4 jt + r
+  auto fragments = [&](const half8* __restrict__ apk, int M) {
+    const unsigned frag_bytes = (unsigned)(((M + 63) / 64) * 4 * KS * 2 * 64 * 16);
+    const BufRes fb = buf_res_uniform(apk, frag_bytes);
+    const int tb = opaque_s(__builtin_amdgcn_readfirstlane((i0 / 16) * KS * 2 * 64 * 16));
+    return [=](int it, int ks, int hl) {
+      const int so = tb + (it * KS + ks) * 2048 + hl * 1024;
+      const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(fb, 16 * lane, so, 0);
+      return __builtin_bit_cast(half8, r);
+    };
+  };
+  // the products of k step ks with the fragments (fh, fl) of the wave's four
+  // row tiles; the three split products of an accumulator are 16 instructions
+  // apart (a matrix-core result feeding the next product at once would stall)
+  // The staged operand is read one group of JG column tiles ahead of the
+  // products that use it (LDS latency hidden behind the matrix cores); the
+  // three split products of an accumulator are 2 JG kFI instructions apart.
+  constexpr int JG = STATE_ONLY && KS == 8 ? 1 : 2;  // column tiles per group
+  constexpr int NG = 4 / JG;                         // groups per k step
+  typedef half8 BOp[2][JG];                          // [hi, lo][column tile]
+  auto bread = [&](int gi, BOp& bo) {  // group gi = NG ks + j: its staged operands
+    const int ks = gi / NG, j0 = JG * (gi % NG);
+    // chunk 4 ks + g of the lane's staged row, swizzled: 4 (ks ^ a4) + g
+    const int kc = 8 * (4 * (ks ^ a4) + lg);
+#pragma unroll
+    for (int j = 0; j < JG; ++j) {
+      bo[0][j] = *reinterpret_cast<const half8*>(&Sh[brow + 4 * (j0 + j)][kc]);
+      bo[1][j] = *reinterpret_cast<const half8*>(&Sl[brow + 4 * (j0 + j)][kc]);
+    }
+  };
+  auto mgroup = [&](int gi, const BOp& bo, const half8 (&fh)[kFI], const half8 (&fl)[kFI],
+                    v4f (&acc)[4][kFI]) {
+    const int j0 = JG * (gi % NG);
+#pragma unroll
+    for (int j = 0; j < JG; ++j)
+#pragma unroll
+      for (int it = 0; it < kFI; ++it)
+        acc[j0 + j][it] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(bo[0][j], fh[it], acc[j0 + j][it], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < JG; ++j)
+#pragma unroll
+      for (int it = 0; it < kFI; ++it)
+        acc[j0 + j][it] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(bo[0][j], fl[it], acc[j0 + j][it], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < JG; ++j)
+#pragma unroll
+      for (int it = 0; it < kFI; ++it)
+        acc[j0 + j][it] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(bo[1][j], fh[it], acc[j0 + j][it], 0, 0, 0);
+  };
+  // out^T over all k steps: fragment(ks) yields the fragments of k step ks
+  // (loaded one k step ahead by the caller, or held in registers)
+  auto gemm = [&](v4f (&acc)[4][kFI], auto&& kstep_begin, auto&& frags_of) {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+      for (int it = 0; it < kFI; ++it) acc[jt][it] = v4f{0.f, 0.f, 0.f, 0.f};
+    BOp bo[2];
+    bread(0, bo[0]);
+#pragma unroll
+    for (int gi = 0; gi < KS * NG; ++gi) {
+      if (gi % NG == 0) {
+        __builtin_amdgcn_sched_barrier(0);  // one k step's operands (and the next's loads) live at a time
+        kstep_begin(gi / NG);
+      }
+      if (gi + 1 < KS * NG) bread(gi + 1, bo[(gi + 1) & 1]);
+      const auto& fr = frags_of(gi / NG);
+      mgroup(gi, bo[gi & 1], fr.h, fr.l, acc);
+    }
+  };
+  struct Frags {
+    half8 h[kFI], l[kFI];
+  };
+  // Memory loads retire in order: a wait for a fragment also waits for every
+  // memory access issued before it, so the next u tile is issued once the
+  // product's last fragment loads are (after_loads).
+  auto product = [&](const half8* __restrict__ apk, int M, v4f (&acc)[4][kFI],
+                     auto&& after_loads) {
+    const auto frag = fragments(apk, M);
+    Frags fb[2];  // one k step ahead of its products
+#pragma unroll
+    for (int it = 0; it < kFI; ++it) {
+      fb[0].h[it] = frag(it, 0, 0);
+      fb[0].l[it] = frag(it, 0, 1);
+    }
+    gemm(acc,
+         [&](int ks) {
+           if (ks + 1 < KS) {
+#pragma unroll
+             for (int it = 0; it < kFI; ++it) {
+               fb[(ks + 1) & 1].h[it] = frag(it, ks + 1, 0);
+               fb[(ks + 1) & 1].l[it] = frag(it, ks + 1, 1);
+             }
+             if (ks + 2 == KS) after_loads();
+           }
+         },
+         [&](int ks) -> const Frags& { return fb[ks & 1]; });
+  };
+  // the state-only pass keeps the input projection's fragments in registers
+  // (loaded once): its products wait for no memory
+  Frags rf[STATE_ONLY ? KS : 1];
+  if (STATE_ONLY && i0 < M1) {
+    const auto frag = fragments(a.apk_in, M1);
+#pragma unroll
+    for (int ks = 0; ks < (STATE_ONLY ? KS : 1); ++ks)
+#pragma unroll
+      for (int it = 0; it < kFI; ++it) {
+        rf[ks].h[it] = frag(it, ks, 0);
+        rf[ks].l[it] = frag(it, ks, 1);
+      }
+  }
+
+  float2 carry[NS];  // the states entering the tile
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) carry[s2] = make_float2(0.f, 0.f);
+  for (int jb = tile0; jb < tile1; ++jb) {
+    ln = opaque(lane);
+    lq = ln & 15;
+    lg = ln >> 4;
+    a4 = lq >> 2;
+    brow = 16 * a4 + (lq & 3);
+    if (STATE_ONLY || jb == tile0) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's part of the u tile is in LDS
+      __syncthreads();
+      if (!STATE_ONLY && jb == tile0) {
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+          if (pin[s2]) carry[s2] = cin_s[ps[s2]];
+      }
+    }
+    // 1. u into the staged operand: thread (step = lane, wave w) takes rows
+    //    k = 8 (w + W qq) + e, scaled per step
+    {
+      float uv[2 * FI][8];
+      float mx = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < 2 * FI; ++qq)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = 8 * (wu + kFW * qq) + e;
+          uv[qq][e] = k < K1 ? U[k][u_slot(k, ln)] : 0.f;
+          mx = fmaxf(mx, fabsf(uv[qq][e]));
+        }
+      cmax[wu][ln] = mx;
+      __syncthreads();
+      float cm = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kFW; ++w2) cm = fmaxf(cm, cmax[w2][ln]);
+      const int sc = scale_exp(cm);
+      if (wu == 0) cexp[ln] = sc;
+#pragma unroll
+      for (int qq = 0; qq < 2 * FI; ++qq) {
+        half8 hi, lo;
+        split8(uv[qq], hi, lo, sc);
+        const int c = sw_chunk(ln, wu + kFW * qq);
+        *reinterpret_cast<half8*>(&Sh[ln][8 * c]) = hi;
+        *reinterpret_cast<half8*>(&Sl[ln][8 * c]) = lo;
+      }
+    }
+    // D u of this lane's output positions (rows 16 it + q, steps 16 g + 4 jt ..)
+    v4f du[kFI][4];
+    if (!STATE_ONLY) {
+#pragma unroll
+      for (int it = 0; it < kFI; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int i = i0 + 16 * it + lq;  // i % 16 == q
+          du[it][jt] = i < M2 ? dd[it] * *reinterpret_cast<const v4f*>(&U[i][4 * ((4 * lg + jt) ^ lq)])
+                              : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __syncthreads();  // the staged u and its exponents are complete; U may be refilled
+    const bool more = jb + 1 < tile1;
+    if (STATE_ONLY && more) issue_u(jb + 1);
+
+    // 2. v = Bbar u, then the recurrence on the tile (two states per lane)
+    float2 xs[NS][16];
+    if (i0 < M1) {
+      v4f acc[4][kFI];
+      if (STATE_ONLY) {
+        gemm(acc, [](int) {}, [&](int ks) -> const Frags& { return rf[STATE_ONLY ? ks : 0]; });
+      } else {
+        product(a.apk_in, M1, acc, [&] {
+          if (more) issue_u(jb + 1);
+        });
+      }
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int4 ce = *reinterpret_cast<const int4*>(&cexp[16 * lg + 4 * jt]);
+        const int cr[4] = {ce.x, ce.y, ce.z, ce.w};
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            xs[s2][4 * jt + r] =
+                make_float2(__builtin_amdgcn_ldexpf(acc[jt][2 * s2][r], -(rx1[2 * s2] + cr[r])),
+                            __builtin_amdgcn_ldexpf(acc[jt][2 * s2 + 1][r], -(rx1[2 * s2 + 1] + cr[r])));
+      }
+    } else {
+      if (!STATE_ONLY && more) issue_u(jb + 1);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)  // states past P (and waves past the rows) carry zero
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (!pin[s2] || i0 >= M1) xs[s2][j] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2) {
+      float2 x = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x = cmad(lm[s2], x, xs[s2][j]);
+        xs[s2][j] = x;
+      }
+      // the quarters' states from zero: lanes q + 16 k hold quarter k of this state
+      float2 e4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        e4[k] = make_float2(__shfl(x.x, lq + 16 * k, 64), __shfl(x.y, lq + 16 * k, 64));
+      const float2 c0 = carry[s2];
+      float2 ent = c0;  // state entering this lane's quarter
+      if (lg == 1) ent = cmad(l16[s2], c0, e4[0]);
+      if (lg == 2) ent = cmad(l32[s2], c0, cmad(l16[s2], e4[0], e4[1]));
+      if (lg == 3) ent = cmad(l48[s2], c0, cmad(l32[s2], e4[0], cmad(l16[s2], e4[1], e4[2])));
+      carry[s2] = cmad(l64[s2], c0,
+                       cmad(l48[s2], e4[0], cmad(l32[s2], e4[1], cmad(l16[s2], e4[2], e4[3]))));
+      if (!STATE_ONLY) {
+        float2 pw = lm[s2];  // lambda^(j + 1)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          xs[s2][j] = cmad(pw, ent, xs[s2][j]);
+          pw = cmad(pw, lm[s2], make_float2(0.f, 0.f));
+        }
+      }
+    }
+    if (STATE_ONLY) continue;  // the next tile's first barrier orders the reads of the staged u
+
+    // 3. x as the output product's operand: rows k = 2p (Re), 2p + 1 (Im), one
+    //    scale per step from the largest magnitude over all rows
+    {
+      float m16[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float m = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) m = fmaxf(m, fmaxf(fabsf(xs[s2][j].x), fabsf(xs[s2][j].y)));
+        m16[j] = row_max16(m);
+      }
+      float mine = m16[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) mine = lq == j ? m16[j] : mine;
+      cmax[wu][16 * lg + lq] = mine;  // this wave's maximum at step 16 g + q
+    }
+    __syncthreads();  // the maxima are complete; every wave is past its reads of the staged u
+    int sc16[16];
+    {
+      float cm = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kFW; ++w2) cm = fmaxf(cm, cmax[w2][16 * lg + lq]);
+      const int scm = scale_exp(cm);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sc16[j] = __shfl(scm, 16 * lg + j, 64);
+    }
+    if (i0 < M1) {
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const int c = 4 * (NS * wu + s2) + (lq >> 2);  // chunk of k = 2p
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int step = 16 * lg + j;
+          _Float16 hr, lr, hi_, li;
+          split16(__builtin_amdgcn_ldexpf(xs[s2][j].x, sc16[j]), hr, lr);
+          split16(__builtin_amdgcn_ldexpf(xs[s2][j].y, sc16[j]), hi_, li);
+          const int o = 8 * sw_chunk(step, c) + 2 * (lq & 3);
+          half2v vh, vl;
+          vh[0] = hr;
+          vh[1] = hi_;
+          vl[0] = lr;
+          vl[1] = li;
+          *reinterpret_cast<half2v*>(&Sh[step][o]) = vh;
+          *reinterpret_cast<half2v*>(&Sl[step][o]) = vl;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next u tile is in LDS
+    __syncthreads();                     // the staged x is complete (and the next u tile)
+
+    // 4. y = Re(C x) + D u
+    if (i0 < M2) {
+      v4f acc[4][kFI];
+      product(a.apk_out, M2, acc, [] {});
+      const bool vec = (L & 3) == 0;
+#pragma unroll
+      for (int it = 0; it < kFI; ++it) {
+        const int i = i0 + 16 * it + lq;
+        if (i >= M2) continue;
+        float* orow = a.y + ((size_t)b * H + i) * L;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int jj = jb * kFT + 16 * lg + 4 * jt;
+          v4f o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            o[r] = __builtin_amdgcn_ldexpf(acc[jt][it][r], -(rx2[it] + sc16[4 * jt + r])) +
+                   du[it][jt][r];
+          if (vec && jj + 3 < L) {
+            *reinterpret_cast<v4f*>(orow + jj) = o;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (jj + r < L) orow[jj + r] = o[r];
+          }
+        }
+      }
+    }
+  }
+  // the state leaving a segment that is not the last (all its tiles are full)
+  if (STATE_ONLY && g == 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < NS; ++s2)
+      if (pin[s2]) a.sout[((size_t)b * a.nseg + seg) * P + ps[s2]] = carry[s2];
+  }
+}
+
 }  // namespace
 
-S5Layout s5_layout(int B, int H, int P, int L, bool with_spec) {
+S5Layout s5_layout(int B, int H, int P, int L, S5Form form) {
   S5Layout l;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -924,31 +1517,48 @@ S5Layout s5_layout(int B, int H, int P, int L, bool with_spec) {
   auto frag_bytes = [](int M, int K) {
     return (size_t)((M + 63) / 64) * 4 * ((K + 31) / 32) * 2 * 64 * sizeof(half8);
   };
-  l.apk_in = take(frag_bytes(2 * P, H));
-  l.rexp_in = take((size_t)((2 * P + 15) / 16) * 16 * sizeof(int));
-  l.apk_out = take(frag_bytes(H, 2 * P));
+  // the fused form pads both products to the same k steps and may have up to
+  // 32 ceil(P / 16) rows of Bbar (whole 64-row groups)
+  const bool fused = form == kS5Fused;
+  const int kf = fused ? 32 * s5_fused_ks(H, P) : 0;
+  l.apk_in = take(frag_bytes(2 * P, fused ? kf : H));
+  l.rexp_in = take((size_t)((2 * P + 63) / 64) * 64 * sizeof(int));
+  l.apk_out = take(frag_bytes(H, fused ? kf : 2 * P));
   l.rexp_out = take((size_t)((H + 15) / 16) * 16 * sizeof(int));
-  l.v = take((size_t)B * P * 2 * L * sizeof(float));
-  l.x = take((size_t)B * P * 2 * L * sizeof(float));
-  if (with_spec) l.spec = take((size_t)P * 2 * ((size_t)1 << fft_log2m(L)) * sizeof(float2));
+  if (fused) {
+    // the fused form keeps v and x on chip: only the segment states
+    const S5FusedPlan f = s5_fused_plan(B, L);
+    l.sout = take((size_t)B * f.nseg * P * sizeof(float2));
+    l.fconst = take((size_t)P * (2 * sizeof(float4) + f.nseg * sizeof(double2)));
+  } else {
+    l.v = take((size_t)B * P * 2 * L * sizeof(float));
+    l.x = take((size_t)B * P * 2 * L * sizeof(float));
+    if (form == kS5Conv) l.spec = take((size_t)P * 2 * ((size_t)1 << fft_log2m(L)) * sizeof(float2));
+  }
   l.total = off;
   return l;
 }
 
 hipError_t launch_s5_pack(const float* Bbar, const float* C, int H, int P, void* apk_in,
-                          int* rexp_in, void* apk_out, int* rexp_out, hipStream_t st, KEvents ev) {
-  const int tiles = (std::max(2 * P, H) + 15) / 16;
-  const int kmax = std::max(2 * P, H);  // the larger K of the two kinds
+                          int* rexp_in, void* apk_out, int* rexp_out, hipStream_t st, KEvents ev,
+                          bool fused) {
+  // (fused: whole 64-row groups, as a wave of the fused form reads four row tiles)
+  const int m_in = fused ? 64 * ((32 * ((P + 15) / 16) + 63) / 64) : 2 * P;
+  const int tiles = (std::max(m_in, H) + 15) / 16;
+  const int kpad = fused ? s5_fused_ks(H, P) : 0;  // both kinds padded to the same k steps
+  const int kmax = std::max(std::max(2 * P, H), 32 * kpad);
   if (kmax <= kPackLdsK) {
     const int groups = ((kmax + 31) / 32 + kPackKS - 1) / kPackKS;
     launch_k(s5_pack_lds_kernel, dim3((unsigned)tiles, 2, (unsigned)groups), dim3(256), st, ev,
              reinterpret_cast<const float2*>(Bbar), reinterpret_cast<const float2*>(C), H, P,
-             static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out);
+             static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out,
+             fused ? 1 : 0, kpad);
     return hipGetLastError();
   }
   launch_k(s5_pack_kernel, dim3((unsigned)tiles, 2), dim3(256), st, ev,
            reinterpret_cast<const float2*>(Bbar), reinterpret_cast<const float2*>(C), H, P,
-           static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out);
+           static_cast<half8*>(apk_in), rexp_in, static_cast<half8*>(apk_out), rexp_out,
+           fused ? 1 : 0, kpad);
   return hipGetLastError();
 }
 
@@ -1003,6 +1613,77 @@ hipError_t launch_s5_scan_tv(const float* lam_c, const float* delta, const float
                             KEvents ev) {
   launch_k(s5_scan_tv_kernel, dim3((unsigned)(B * P)), dim3(kLanes), st, ev,
            reinterpret_cast<const float2*>(lam_c), delta, step, v, P, L, x);
+  return hipGetLastError();
+}
+
+bool s5_fused_supported(int H, int P, int L) {
+  // a batch row's u within one buffer of 32-bit byte offsets
+  return P <= 128 && H <= kRowsWG && (long)H * L <= (1L << 29);
+}
+
+int s5_fused_ks(int H, int P) {
+  const int ks = (std::max(H, 2 * P) + 31) / 32;
+  return ks <= 2 ? 2 : ks <= 4 ? 4 : 8;
+}
+
+S5FusedPlan s5_fused_plan(int B, int L) {
+  S5FusedPlan f;
+  const int nt = (L + kFT - 1) / kFT;
+  // one workgroup per CU: about 256 segments over the batch rows
+  const int want = std::max(1, (256 + B - 1) / B);
+  f.seg_tiles = std::max(1, (nt + want - 1) / want);
+  f.nseg = (nt + f.seg_tiles - 1) / f.seg_tiles;
+  return f;
+}
+
+hipError_t launch_s5_fused(const void* apk_in, const int* rexp_in, const void* apk_out,
+                           const int* rexp_out, const float* lambda, const float* D,
+                           const float* u, int B, int H, int P, int L, float* y, float2* sout,
+                           void* consts, hipStream_t st, KEvents ev_consts, KEvents ev_state,
+                           KEvents ev_out) {
+  const S5FusedPlan f = s5_fused_plan(B, L);
+  float4* lp = static_cast<float4*>(consts);
+  double2* apow = reinterpret_cast<double2*>(lp + 2 * (size_t)P);
+  {
+    const long n = (long)P * f.nseg + P;
+    launch_k(s5_fused_consts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), st, ev_consts,
+             reinterpret_cast<const float2*>(lambda), P, f.nseg, (double)f.seg_tiles * kFT, lp,
+             apow);
+  }
+  S5FusedArgs a{};
+  a.lp = lp;
+  a.apow = apow;
+  a.apk_in = static_cast<const half8*>(apk_in);
+  a.rexp_in = rexp_in;
+  a.apk_out = static_cast<const half8*>(apk_out);
+  a.rexp_out = rexp_out;
+  a.u = u;
+  a.lam = reinterpret_cast<const float2*>(lambda);
+  a.D = D;
+  a.y = y;
+  a.sout = sout;
+  a.B = B;
+  a.H = H;
+  a.P = P;
+  a.L = L;
+  a.nseg = f.nseg;
+  a.seg_tiles = f.seg_tiles;
+  // 8 waves of 32 rows (the state-only pass with its input fragments in registers)
+  const dim3 grid((unsigned)(B * f.nseg));
+  const int ks = s5_fused_ks(H, P);
+  auto kern = [&](bool state_only) {
+    if (ks == 2) return state_only ? s5_fused_kernel<true, 2, 2> : s5_fused_kernel<false, 2, 2>;
+    if (ks == 4) return state_only ? s5_fused_kernel<true, 4, 2> : s5_fused_kernel<false, 4, 2>;
+    return state_only ? s5_fused_kernel<true, 8, 2> : s5_fused_kernel<false, 8, 2>;
+  };
+  if (f.nseg > 1) {
+    launch_k(kern(true), grid, dim3(512), st, ev_state, a);
+  } else {
+    // one segment: no state to carry (the pass's events are stamped back to back)
+    if (ev_state.start) (void)hipEventRecord(ev_state.start, st);
+    if (ev_state.stop) (void)hipEventRecord(ev_state.stop, st);
+  }
+  launch_k(kern(false), grid, dim3(512), st, ev_out, a);
   return hipGetLastError();
 }
 

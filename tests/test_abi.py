@@ -153,7 +153,7 @@ def _s5ws(B, H, P, L, bi=0, method=bd.S5_SCAN):
     return bd.lib().dssm_s5_workspace_size(ctypes.byref(s), method, ctypes.byref(out)), out.value
 
 
-@pytest.mark.parametrize("method", [bd.S5_SCAN, bd.S5_FFT])
+@pytest.mark.parametrize("method", [bd.S5_SCAN, bd.S5_FFT, bd.S5_FUSED])
 def test_s5_workspace_and_validation(method):
     ws = lambda *a, **k: _s5ws(*a, method=method, **k)
     assert ws(4, 256, 128, 16384)[0] == 0
@@ -164,7 +164,7 @@ def test_s5_workspace_and_validation(method):
     assert ws(1, 2, 5000, 8)[0] == bd.DSSM_ERR_UNSUPPORTED
     assert ws(0, 2, 2, 8) == (0, 0)
     # the generic query with N read as P gives the same sizes
-    op = bd.OP_S5_FFT if method == bd.S5_FFT else bd.OP_S5_SCAN
+    op = {bd.S5_SCAN: bd.OP_S5_SCAN, bd.S5_FFT: bd.OP_S5_FFT, bd.S5_FUSED: bd.OP_S5_FUSED}[method]
     s = bd.Shape(4, 256, 128, 16384, 0)
     out = ctypes.c_size_t(0)
     assert bd.lib().dssm_workspace_size(op, ctypes.byref(s), ctypes.byref(out)) == 0
@@ -182,7 +182,7 @@ def test_s5_workspace_and_validation(method):
     assert call(prm, good, n=64) == bd.DSSM_ERR_WORKSPACE
     assert call(prm, good, ws=FAKE * 4 + 16) == bd.DSSM_ERR_INVALID_ARG
     assert call(prm, bd.S5Shape(2, 3, 4, 32, 1)) == bd.DSSM_ERR_UNSUPPORTED
-    assert call(prm, good, m=2) == bd.DSSM_ERR_INVALID_ARG
+    assert call(prm, good, m=3) == bd.DSSM_ERR_INVALID_ARG
     assert call(prm, good, m=-1) == bd.DSSM_ERR_INVALID_ARG
     assert call(None, bd.S5Shape(0, 3, 4, 32, 0)) == 0
 
@@ -196,7 +196,29 @@ def test_s5_method_limits():
     # the FFT view adds the spectrum table, P x 2M complex values
     n_scan = _s5ws(4, 256, 128, 16384, method=bd.S5_SCAN)[1]
     n_fft = _s5ws(4, 256, 128, 16384, method=bd.S5_FFT)[1]
-    assert n_fft - n_scan >= 128 * 2 * 16384 * 8
+    vx = 2 * 4 * 128 * 16384 * 8  # v and x, complex float32
+    assert n_fft >= vx + 128 * 2 * 16384 * 8
+    assert n_scan >= vx
+    # the fused form keeps v and x on chip: a few MiB of packed projections,
+    # segment states and powers of lambda
+    rc, n_fused = _s5ws(4, 256, 128, 16384, method=bd.S5_FUSED)
+    assert rc == 0 and n_fused < 8 << 20
+    # its limits: P <= 128, H <= 256, H L <= 2^29
+    assert _s5ws(1, 300, 8, 1000, method=bd.S5_FUSED)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _s5ws(1, 8, 130, 1000, method=bd.S5_FUSED)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _s5ws(1, 256, 8, (1 << 21) + 1, method=bd.S5_FUSED)[0] == bd.DSSM_ERR_UNSUPPORTED
+    assert _s5ws(1, 256, 128, 1 << 21, method=bd.S5_FUSED)[0] == 0
+
+
+def test_s5_tv_workspace():
+    fn = bd.lib().dssm_s5_tv_workspace_size
+    out = ctypes.c_size_t(0)
+    s = bd.S5Shape(4, 256, 128, 16384, 0)
+    assert fn(ctypes.byref(s), ctypes.byref(out)) == 0
+    assert out.value >= 2 * 4 * 128 * 16384 * 8  # v and x
+    assert fn(ctypes.byref(s), None) == bd.DSSM_ERR_INVALID_ARG
+    assert fn(ctypes.byref(bd.S5Shape(1, 2, 2, 8, 1)), ctypes.byref(out)) == bd.DSSM_ERR_UNSUPPORTED
+    assert fn(ctypes.byref(bd.S5Shape(0, 2, 2, 8, 0)), ctypes.byref(out)) == 0 and out.value == 0
 
 
 def test_s5_tv_validation():

@@ -13,7 +13,13 @@ from test_gpu_parity import assert_close, say, _torch
 pytestmark = pytest.mark.gpu
 
 
-METHODS = {"scan": bd.S5_SCAN, "fft": bd.S5_FFT}
+METHODS = {"scan": bd.S5_SCAN, "fft": bd.S5_FFT, "fused": bd.S5_FUSED}
+ALL = ["scan", "fft", "fused"]
+
+
+def fused_ok(H, P, L):
+    """The shapes the fused form takes (P <= 128, H <= 256, H L <= 2^29)."""
+    return P <= 128 and H <= 256 and H * L <= 1 << 29
 
 
 def run_s5(x, method="scan"):
@@ -24,7 +30,7 @@ def run_s5(x, method="scan"):
     return y.cpu().numpy()
 
 
-@pytest.mark.parametrize("method", ["scan", "fft"])
+@pytest.mark.parametrize("method", ALL)
 def test_s5_workload_full_size(method):
     c = inputs.config("s5_mimo")
     say("case: s5 workload B=%d H=%d P=%d L=%d method=%s" % (c["B"], c["H"], c["P"], c["L"],
@@ -46,15 +52,29 @@ S5_EDGE = [
     (1, 600, 140, 3001), (2, 72, 300, 515),
     # more than 1024 input channels: the fragments packed without LDS staging
     (1, 1100, 8, 70),
+    # the fused form at its limits (P = 128, H = 256), many segments with a
+    # ragged last tile; one segment per row (B >= 256); odd P and H; P not a
+    # multiple of 32 (a wave's rows past the packed Bbar); just past the fused
+    # limit in P
+    (1, 256, 128, 20000), (2, 256, 127, 4099), (260, 6, 5, 150), (4, 17, 128, 300),
+    (3, 100, 48, 700), (1, 8, 129, 500),
 ]
 
 
-@pytest.mark.parametrize("method", ["scan", "fft"])
+@pytest.mark.parametrize("method", ALL)
 @pytest.mark.parametrize("shape", S5_EDGE, ids=["B%dH%dP%dL%d" % s for s in S5_EDGE])
 def test_s5_edge_shapes(shape, method):
     B, H, P, L = shape
     say("case: s5 edge B=%d H=%d P=%d L=%d method=%s" % (shape + (method,)))
     x = inputs.s5_inputs(B, H, P, L, seed=500 + H + P + L)
+    if method == "fft" and L > 16384:  # past the convolution view's circle
+        with pytest.raises(bd.DSSMError, match="L <= 16384"):
+            run_s5(x, method)
+        return
+    if method == "fused" and not fused_ok(H, P, L):  # past the fused form's limits
+        with pytest.raises(bd.DSSMError, match="fused S5 form needs"):
+            run_s5(x, method)
+        return
     y = run_s5(x, method)
     ref = oracle.s5_recurrence(x["u"], x["lam"], x["Bbar"], x["C"], x["D"])
     assert_close(y, ref, "s5/edge")
@@ -63,7 +83,7 @@ def test_s5_edge_shapes(shape, method):
         assert_close(y, refd, "s5/edge/direct")
 
 
-@pytest.mark.parametrize("method", ["scan", "fft"])
+@pytest.mark.parametrize("method", ALL)
 def test_s5_reduces_to_dlr_bank_on_device(method):
     """P = H, Bbar = I, C = diag(w): the S5 layer equals H scalar DLRs; the
     device S5 path must agree with the device DLR paths on it."""
@@ -87,7 +107,7 @@ def test_s5_reduces_to_dlr_bank_on_device(method):
 S5_MAGS = [("u", -70), ("u", 60), ("BC", 40), ("BC", -40)]
 
 
-@pytest.mark.parametrize("method", ["scan", "fft"])
+@pytest.mark.parametrize("method", ALL)
 @pytest.mark.parametrize("what,k", S5_MAGS, ids=["%s2^%d" % m for m in S5_MAGS])
 def test_s5_magnitudes(what, k, method):
     B, H, P, L = 2, 40, 24, 2000
@@ -106,7 +126,7 @@ def test_s5_magnitudes(what, k, method):
     assert_close(y, ref, "s5/magnitudes")
 
 
-@pytest.mark.parametrize("method", ["scan", "fft"])
+@pytest.mark.parametrize("method", ALL)
 def test_s5_timed_matches_untimed(method):
     torch = _torch()
     x = inputs.s5_inputs(2, 24, 9, 3000, seed=17)
@@ -124,7 +144,7 @@ def test_s5_timed_matches_untimed(method):
     hip.destroy(evs)
 
 
-@pytest.mark.parametrize("method", ["scan", "fft"])
+@pytest.mark.parametrize("method", ALL)
 def test_s5_empty_is_noop(method):
     torch = _torch()
     x = inputs.s5_inputs(1, 3, 2, 8, seed=1)
