@@ -108,22 +108,57 @@ constexpr int kLdsBytes = sizeof(TablesLds) > sizeof(BlockLds) ? sizeof(TablesLd
 // powers (chains of 16 products from lambda^(16 q), q < 4), W lambda^p and the
 // taps K_m = Re sum_n W_n lambda_n^m are float64, each rounded once to float32.
 // Modes n >= N are zero.  Ends with a barrier (the LDS is reused after it).
-__device__ __forceinline__ void build_operands(
+// Parameters of mode `lane` of direction d, channel h (wave 0 only; zero for
+// n >= N and the other waves) and the feed-through D_f + D_b (the first
+// direction's tap 0), read by the caller before anything it leaves in flight:
+// vector memory operations complete in issue order, so the prologue's first
+// wait would otherwise also wait for them.
+struct ModeParams {
+  float re, im;
+  float2 w;
+  float d0, d1;  // D of each direction (workgroup-uniform: scalar loads)
+};
+
+__device__ __forceinline__ ModeParams load_mode_params(
     const float* __restrict__ log_re, const float* __restrict__ log_im,
     const float2* __restrict__ W, const float* __restrict__ D, int ndir, int H, int N, int d,
-    int h, TablesLds& tl, half8* a1, half8* a3, float2& lamT, float2& lam16T, int& eT, int& eW) {
+    int h) {
+  const int t = threadIdx.x, lane = t & 63;
+  ModeParams mp{0.f, 0.f, make_float2(0.f, 0.f), 0.f, 0.f};
+  if (t < 64 && lane < N) {
+    const size_t i = ((size_t)d * H + h) * N + lane;
+    mp.re = log_re[i];
+    mp.im = log_im[i];
+    mp.w = W[i];
+  }
+  if (d == 0) {
+    mp.d0 = D[h];
+    if (ndir == 2) mp.d1 = D[(size_t)H + h];
+  }
+  return mp;
+}
+
+// Marks the mode parameters as arriving here: the caller places it after
+// the loads it leaves in flight, so nothing derived from the parameters is
+// computed (and waited for) before those loads are issued.
+__device__ __forceinline__ void params_here(ModeParams& mp) {
+  asm volatile("" : "+v"(mp.re), "+v"(mp.im), "+v"(mp.w.x), "+v"(mp.w.y));
+}
+
+__device__ __forceinline__ void build_operands(const ModeParams& mp, int N, int d, TablesLds& tl,
+                                               half8* a1, half8* a3, float2& lamT,
+                                               float2& lam16T, int& eT, int& eW) {
   const int t = opaque(threadIdx.x), lane = t & 63, w = t >> 6;
   if (w == 0) {  // lambda_n, W_n (float64, from the exactly promoted parameters)
     const int n = lane;
     double2 lam = make_double2(0.0, 0.0), wv = lam;
     if (n < N) {
-      const size_t i = ((size_t)d * H + h) * N + n;
-      const double re = (double)log_re[i];
+      const double re = (double)mp.re;
       double sn, cs;
-      sincos((double)log_im[i], &sn, &cs);
+      sincos((double)mp.im, &sn, &cs);
       const double m = exp(-re * re);
       lam = make_double2(m * cs, m * sn);
-      wv = make_double2((double)W[i].x, (double)W[i].y);
+      wv = make_double2((double)mp.w.x, (double)mp.w.y);
     }
     tl.lam[n] = lam;
     tl.wv[n] = wv;
@@ -168,8 +203,7 @@ __device__ __forceinline__ void build_operands(
     for (int k = 0; k < 16; ++k) s += tl.KR[16 * q + k][m];
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
-    if (m == 0 && d == 0)
-      for (int dd = 0; dd < ndir; ++dd) s += (double)D[(size_t)dd * H + h];
+    if (t == 0 && d == 0) s += (double)mp.d0 + (double)mp.d1;  // (m = 0: lane 0 of wave 0)
     const float kv = (float)s;
     if (q == 0) tl.ktp[kT + m] = kv;
     if (q == 1) tl.ktp[m] = 0.f;
@@ -311,25 +345,18 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
     auto load_block = [&](int b, int blk, float* v, bool valid = true) {
       const BufRes ub = buf_res(a.u + ((size_t)(valid ? b : 0) * H + h) * L,
                                 valid ? 4u * (unsigned)L : 0u);
-      if (VEC && !rev) {
+      if (VEC) {  // reversed: the four elements sit at descending positions, kept
+                  // in memory order here (one load path for both directions, and no
+                  // register permutation that would wait for the load); the
+                  // staging reads them reversed
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const u32x4 x =
-              __builtin_amdgcn_raw_buffer_load_b128(ub, 4 * pos(blk, 4 * t + 1024 * q), 0, 0);
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+              ub, 4 * pos(blk, 4 * t + 1024 * q + (rev ? 3 : 0)), 0, 0);
           v[4 * q + 0] = __uint_as_float(x.x);
           v[4 * q + 1] = __uint_as_float(x.y);
           v[4 * q + 2] = __uint_as_float(x.z);
           v[4 * q + 3] = __uint_as_float(x.w);
-        }
-      } else if (VEC) {  // reversed: the four elements sit at descending positions
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-              ub, 4 * pos(blk, 4 * t + 1024 * q + 3), 0, 0);
-          v[4 * q + 0] = __uint_as_float(x.w);
-          v[4 * q + 1] = __uint_as_float(x.z);
-          v[4 * q + 2] = __uint_as_float(x.y);
-          v[4 * q + 3] = __uint_as_float(x.x);
         }
       } else {
 #pragma unroll
@@ -339,13 +366,17 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
         }
       }
     };
+    // element c4 of group q is un[4 q + c4], or un[4 q + 3 - c4] for a reversed
+    // 16-byte load
+    const bool swap4 = VEC && rev;
+    ModeParams mp = load_mode_params(a.log_re, a.log_im, a.W, a.D, a.ndir, H, a.N, d, h);
     float un[16];
     load_block(b0, blk0, un);  // in flight while the operands are formed
+    params_here(mp);
     half8 a1[8], a3[12];
     float2 lamT, lam16T;
     int eT, eW;
-    build_operands(a.log_re, a.log_im, a.W, a.D, a.ndir, H, a.N, d, h, tl, a1, a3, lamT, lam16T,
-                   eT, eW);
+    build_operands(mp, a.N, d, tl, a1, a3, lamT, lam16T, eT, eW);
 
     for (int b = b0; b < b1; ++b) {
       const size_t row = (size_t)b * H + h;
@@ -373,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
             _Float16 p, r;
-            split16(__builtin_amdgcn_ldexpf(un[4 * q + c4], sc), p, r);
+            split16(__builtin_amdgcn_ldexpf(un[4 * q + (swap4 ? 3 - c4 : c4)], sc), p, r);
             vh[c4] = p;
             vl[c4] = r;
           }

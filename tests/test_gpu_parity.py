@@ -298,21 +298,22 @@ def test_fft_and_scan_agree_and_are_deterministic():
     assert rel < 2 * REL_L2 and mx < 2 * MAX_VS_RMS
 
 
-@pytest.mark.parametrize("path,nk", [("fft", 2), ("scan", 2)])
-def test_timed_variants_match_and_stamp_each_kernel(path, nk):
+@pytest.mark.parametrize("path,nk,bi", [("fft", 2, 1), ("fft", 2, 0), ("scan", 2, 1)])
+def test_timed_variants_match_and_stamp_each_kernel(path, nk, bi):
     """The timed calls give the untimed calls' bits; each stage's start/stop
     pair is a non-negative duration (the chunked scan's stage 0 has no kernel),
-    the main kernel's is positive, and the pairs are ordered in time."""
+    the main kernel's is positive, and the pairs are ordered in time (both
+    directions, and one: the spectrum's packed even/odd form)."""
     torch = _torch()
-    c = dict(inputs.config("tiny"), B=3, H=8, N=16, L=2000, bidirectional=1)
+    c = dict(inputs.config("tiny"), B=3, H=8, N=16, L=2000, bidirectional=bi)
     x = inputs.inputs_for(c)
     t = dev(x)
     f = bd.forward_fft if path == "fft" else bd.forward_scan
-    y0 = f(t["u"], t["log_re"], t["log_im"], t["W"], t["D"], bidirectional=True)
+    y0 = f(t["u"], t["log_re"], t["log_im"], t["W"], t["D"], bidirectional=bool(bi))
     hip = bd.HipEvents()
     evs = hip.create(2 * nk)
     y1 = bd.forward_timed(path, t["u"], t["log_re"], t["log_im"], t["W"], t["D"], evs,
-                          bidirectional=True)
+                          bidirectional=bool(bi))
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
     for k in range(nk):
