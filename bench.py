@@ -70,19 +70,46 @@ def kernel_sources_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the convolution from the committed counter
-    record, or None when there is none or the kernel sources changed since."""
+def counter_record(name):
+    """The committed counter record `name` of the convolution (a JSON line in
+    the counters profile), or None when there is none or the kernel sources
+    changed since it was taken."""
+    tag = name + "-record: "
     try:
         with open(TRAFFIC_RECORD) as f:
             for ln in f:
-                if ln.startswith("traffic-record: "):
-                    rec = json.loads(ln[len("traffic-record: "):])
+                if ln.startswith(tag):
+                    rec = json.loads(ln[len(tag):])
                     if rec.get("sources_sha256") == kernel_sources_digest():
-                        return rec["fetch_bytes"] + rec["write_bytes"]
-    except (OSError, ValueError, KeyError):
+                        return rec
+    except (OSError, ValueError):
         pass
     return None
+
+
+def measured_traffic():
+    """HBM bytes per launch of the convolution (FETCH_SIZE + WRITE_SIZE,
+    calibrated), from the counter record."""
+    rec = counter_record("traffic")
+    return rec["fetch_bytes"] + rec["write_bytes"] if rec else None
+
+
+def measured_valu():
+    """The convolution's vector-ALU issue against its measured busy cycles
+    (SQ_INSTS_VALU, SQ_WAVES, SQ_BUSY_CU_CYCLES from the counter record): the
+    clock the CUs sustained during the launch, the share of their cycles the
+    vector ALU issues (a wave64 instruction holds its SIMD 4 cycles, and a
+    CU's waves spread over 4 SIMDs), and the launch time the VALU
+    instructions alone need at that clock."""
+    rec = counter_record("valu")
+    if not rec:
+        return None
+    issue = rec["valu_instr_per_wave"] * 4 * rec["waves_per_cu"] / 4  # cycles per SIMD
+    clock = rec["busy_cycles_per_cu"] / (rec["launch_us"] * 1e-6)
+    return {"sustained_clock_ghz": clock / 1e9,
+            "valu_issue_frac": issue / rec["busy_cycles_per_cu"],
+            "valu_floor_ms_at_sustained_clock": issue / clock * 1e3,
+            "source": "counter record (SQ_INSTS_VALU, SQ_WAVES, SQ_BUSY_CU_CYCLES)"}
 
 
 # ---------------------------------------------------------------------------
@@ -694,6 +721,9 @@ def main():
             "alu_alg_flop_per_launch": alg_flop,
             "alu_frac_nonpacked_fp32": tflops / ALU_PEAK_TFLOPS,
             "alu_frac_published_fp32": tflops / FP32_PUBLISHED_TFLOPS,
+            # what actually holds it: vector-ALU issue at the clock the CUs
+            # sustain under this load (below the 2.4 GHz peak)
+            "valu_measured": measured_valu(),
         },
         "extra": {
             "stage_ms_breakdown": {"kernel_spectrum": stages[0], "conv": stages[1]},
