@@ -1,9 +1,12 @@
 """Build libdssm.so in-tree for gfx950 with hipcc (no torch involved).
 
-    python -m long_convolution_sequence_amd.build [--verbose]
+    python -m long_convolution_sequence_amd.build [--verbose] [--phase-stamps]
 
 Steps: generate the twiddle table include, compile every csrc/*.hip to an
-object (in parallel), link the shared library next to this file.
+object (in parallel), link the shared library next to this file.  With
+--phase-stamps the sources are compiled with DSSM_PHASE_STAMPS into a
+separate libdssm_stamps.so (kernels that keep per-phase cycle counts; see
+phase_stamps.py); libdssm.so is not touched.
 """
 import argparse
 import concurrent.futures as cf
@@ -16,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdssm.so")
+BUILD_STAMPS = os.path.join(HERE, "_build_stamps")
+LIB_STAMPS = os.path.join(HERE, "libdssm_stamps.so")
 SOURCES = ["api.hip", "chunk.hip", "eig_gen.hip", "fft.hip", "grad.hip", "scan.hip", "s5.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -42,14 +47,17 @@ def _run(cmd, verbose):
     return "\n".join(lines)
 
 
-def build(verbose=False, resource_usage=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, resource_usage=False, phase_stamps=False):
+    bdir, lib = (BUILD_STAMPS, LIB_STAMPS) if phase_stamps else (BUILD, LIB)
+    os.makedirs(bdir, exist_ok=True)
     inc = os.path.join(CSRC, "twiddle_table.inc")
     subprocess.run([sys.executable, os.path.join(CSRC, "gen_twiddles.py"), inc], check=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    if phase_stamps:
+        extra.append("-DDSSM_PHASE_STAMPS")
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [HIPCC] + FLAGS + extra + ["-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         return obj, _run(cmd, verbose)
 
@@ -59,18 +67,20 @@ def build(verbose=False, resource_usage=False):
     if logs and (verbose or resource_usage):
         print("\n".join(logs))
     objs = [o for o, _ in results]
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="build libdssm_stamps.so with per-phase cycle stamps")
     a = ap.parse_args()
-    print(build(a.verbose, a.resource_usage))
+    print(build(a.verbose, a.resource_usage, a.phase_stamps))
 
 
 if __name__ == "__main__":

@@ -307,6 +307,7 @@ __device__ __forceinline__ double2 lambda64(const ChunkArgs& a, int d, int h, in
 
 template <bool VEC, bool STATE_ONLY, bool CAPTURE>
 __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
+  PhaseClock pc;  // phase stamps (instrumented builds only): slots below
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   TablesLds& tl = *reinterpret_cast<TablesLds*>(lds_raw);
   BlockLds& bl = *reinterpret_cast<BlockLds*>(lds_raw);
@@ -390,8 +391,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
           carry = a.x0[row * a.N + lane];
       }
 
+      pc.mark(0);  // prologue: parameters, operands, first input requested
       for (int blk = blk0; blk < blk1; ++blk) {
         __syncthreads();  // the previous block's readers of U and S are done
+        pc.mark(1);
         // 1. input to LDS, split: element e = 4 t + 1024 q + c4 -> chunk e / 64, step e % 64;
         //    the 16 lanes of a DPP row hold one chunk, scaled by 2^eU[chunk]
 #pragma unroll
@@ -419,7 +422,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
           load_block(same ? b : b + 1, same ? blk + 1 : blk0, un, same || b + 1 < b1);
         }
         __builtin_amdgcn_sched_barrier(0);
+        pc.mark(2);  // input staged, next block requested
         __syncthreads();
+        pc.mark(3);
         // 2. chunk states: S1[c][r] = sum_j A1[r][j] U[j][c]; this wave: rows 32 w .. +31,
         //    in two halves of 32 columns (fewer accumulators live)
 #pragma unroll
@@ -457,7 +462,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
               *reinterpret_cast<f4*>(bl.S1 + c * kS1S + r) = acc[rt][ct];
             }
         }
+        pc.mark(4);  // chunk states (matrix cores)
         __syncthreads();
+        pc.mark(5);
         // 3. chunk recurrence: wave w takes chunks 16 w .. 16 w + 15, lane = mode.  The
         //    wave reads its rows' S1 values before it writes S over them.
         {
@@ -473,7 +480,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
           for (int c = 0; c < 16; ++c) e = cfma(lamT, e, sv[c]);
           bl.E[w][n] = e;
+          pc.mark(6);  // recurrence, first part
           __syncthreads();
+          pc.mark(7);
           float2 cin = carry;  // state entering quarter w
           for (int q = 0; q < w; ++q) cin = cfma(lam16T, cin, bl.E[q][n]);
           float2 cnext = carry;  // state leaving the block (every wave keeps it)
@@ -517,8 +526,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
             *reinterpret_cast<half2v*>(rw + kSLo + 4 * n) = lo;
           }
         }
+        pc.mark(8);  // recurrence, second part (states scaled, split, stored)
         if (STATE_ONLY) continue;  // the segment's end state is all this pass needs
         __syncthreads();
+        pc.mark(9);
         // 4. outputs: Y[i][c] = sum_k A3[i][k] [U; S][k][c]; this wave: rows 16 w .. +15,
         //    in two halves of 32 columns.  The U part (k < T) and the S part are
         //    accumulated apart: each carries its own scale.
@@ -591,6 +602,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
             }
           }
         }
+        pc.mark(10);  // outputs (matrix cores), stored
       }
       // the state leaving a segment that is not the last (all its chunks are real)
       if (a.sout && !last_seg && w == 0 && lane < a.N)
@@ -619,6 +631,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
       __syncthreads();
     }
   }
+  pc.write();
 }
 
 // The state entering each segment from the states the segments leave when
@@ -818,3 +831,10 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
 }
 
 }  // namespace dssm
+
+#ifdef DSSM_PHASE_STAMPS
+// Buffer for the chunked recurrence's phase stamps (instrumented builds only).
+extern "C" int dssm_phase_stamps_chunk(void* buf) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(dssm::g_phase_buf), &buf, sizeof(buf));
+}
+#endif

@@ -39,6 +39,45 @@ constexpr int kMaxLog2M = 14;
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
+// Phase cycle stamps, compiled in only by `build.py --phase-stamps` (which
+// defines DSSM_PHASE_STAMPS and writes libdssm_stamps.so beside the library;
+// the library proper has none).  A kernel reads the shader-clock counter
+// (s_memtime) at its phase boundaries and adds each phase's cycles to a
+// register slot; at its end lane 0 of every wave writes the slots to the
+// buffer set for that source file (dssm_phase_stamps_fft / _chunk):
+//   buf[(workgroup * waves + wave) * kPhaseSlots + slot].
+// Nothing is stored before the end, so the stamps add no memory waits to the
+// phases they time.
+// ---------------------------------------------------------------------------
+constexpr int kPhaseSlots = 16;
+#ifdef DSSM_PHASE_STAMPS
+static __device__ unsigned long long* g_phase_buf = nullptr;
+struct PhaseClock {
+  unsigned long long acc[kPhaseSlots];
+  unsigned long long last;
+  __device__ PhaseClock() : last(__builtin_amdgcn_s_memtime()) {
+    for (int k = 0; k < kPhaseSlots; ++k) acc[k] = 0;
+  }
+  __device__ void mark(int k) {
+    const unsigned long long now = __builtin_amdgcn_s_memtime();
+    acc[k] += now - last;
+    last = now;
+  }
+  __device__ void write() const {
+    if (g_phase_buf && (threadIdx.x & 63) == 0) {
+      const size_t base = ((size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kPhaseSlots;
+      for (int k = 0; k < kPhaseSlots; ++k) g_phase_buf[base + k] = acc[k];
+    }
+  }
+};
+#else
+struct PhaseClock {
+  __device__ void mark(int) {}
+  __device__ void write() const {}
+};
+#endif
+
+// ---------------------------------------------------------------------------
 // Kernel generation (eig_gen.hip)
 // ---------------------------------------------------------------------------
 // K[dh, j] = sum_n W[dh,n] lambda[dh,n]^j for j < L, from the parameters

@@ -779,7 +779,8 @@ __device__ __forceinline__ void conv_rows(const float* __restrict__ r1,
                                           const float* __restrict__ r2, unsigned len1,
                                           unsigned len2, const float2* __restrict__ spec_h,
                                           int lt, float2* lds, const float2* tab,
-                                          float* __restrict__ o1, float* __restrict__ o2) {
+                                          float* __restrict__ o1, float* __restrict__ o2,
+                                          PhaseClock* pc = nullptr) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
   // rows as buffers: element n of register r sits at byte 4 n, n = lt + T(...)
   const BufRes ur1 = buf_res(r1, len1);
@@ -843,6 +844,7 @@ __device__ __forceinline__ void conv_rows(const float* __restrict__ r1,
 #pragma unroll
     for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], tl);
   }
+  if (pc) pc->mark(0);  // entry: twiddle table, input requested
   // pass 0 of both halves (shared twiddles)
   {
     float2 p[16];
@@ -857,11 +859,14 @@ __device__ __forceinline__ void conv_rows(const float* __restrict__ r1,
     lds_read<C, 1>(lds, lt, ve);
     fwd_tail<C, 1>(ve, lds, lt, tab);
   }
+  if (pc) pc->mark(1);  // even half forward
   load_spec(std::integral_constant<int, 0>{}, sv);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) ve[r] = cmul(ve[r], sv[r]);
+  if (pc) pc->mark(2);  // even half: spectrum read, product
   inv_head<C>(ve, lds, lt, tab);
   inverse_finish<C>(ve, lds, lt);
+  if (pc) pc->mark(3);  // even half inverse
   // odd half: its pass-0 positions are disjoint from every other thread's,
   // so it may be written while others still read the even half's
   if constexpr (C::NP > 1) {
@@ -870,11 +875,14 @@ __device__ __forceinline__ void conv_rows(const float* __restrict__ r1,
     lds_read<C, 1>(lds, lt, vo);
     fwd_tail<C, 1>(vo, lds, lt, tab);
   }
+  if (pc) pc->mark(4);  // odd half forward
   load_spec(std::integral_constant<int, 1>{}, sv);
 #pragma unroll
   for (int r = 0; r < C::PT; ++r) vo[r] = cmul(vo[r], sv[r]);
+  if (pc) pc->mark(5);  // odd half: spectrum read, product
   inv_head<C>(vo, lds, lt, tab);
   inverse_finish<C>(vo, lds, lt);
+  if (pc) pc->mark(6);  // odd half inverse
   // The thread index is re-derived here (opaque to the compiler) so the store
   // addresses and t[lt] are recomputed instead of being kept live -- and
   // spilled -- across both transforms.
@@ -893,6 +901,7 @@ __device__ __forceinline__ void conv_rows(const float* __restrict__ r1,
     buf_store_f32(yr1, o, 0, ve[r].x);
     buf_store_f32(yr2, o, 0, ve[r].y);
   }
+  if (pc) pc->mark(7);  // combination, stores issued
 }
 
 // DLR convolution: workgroup problem = (channel h, row pair pr), the batch
@@ -903,6 +912,7 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
     const float* __restrict__ u, const float2* __restrict__ spec, int B, int H, int L, int npairs,
     float* __restrict__ y) {
   using C = Cfg<LOG2M, conv_pt<LOG2M>()>;
+  PhaseClock pc;
   __shared__ float2 lds_all[C::G * C::LDSN];
   __shared__ float2 tab[TwTab<C>::kAlloc];
   twtab_init<C>(tab);  // published by the first barrier, before its first use
@@ -918,7 +928,8 @@ __global__ __launch_bounds__((Cfg<LOG2M, conv_pt<LOG2M>()>::WG)) void conv_kerne
   const size_t o2 = ((size_t)(has2 ? b2 : b1) * H + h) * L;
   conv_rows<LOG2M, false>(u + o1, u + o2, active ? 4u * L : 0u, has2 ? 4u * L : 0u,
                           spec + (size_t)h * 2 * C::M, lt, lds_all + gi * C::LDSN, tab, y + o1,
-                          y + o2);
+                          y + o2, &pc);
+  pc.write();
 }
 
 // S5 convolution view: workgroup problem = one complex row (b, p) of
@@ -1258,3 +1269,10 @@ hipError_t launch_corr(const float* u, const float* dy, int B, int H, int L, int
 }
 
 }  // namespace dssm
+
+#ifdef DSSM_PHASE_STAMPS
+// Buffer for the convolution's phase stamps (instrumented builds only).
+extern "C" int dssm_phase_stamps_fft(void* buf) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(dssm::g_phase_buf), &buf, sizeof(buf));
+}
+#endif

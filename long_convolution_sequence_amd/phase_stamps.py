@@ -1,0 +1,102 @@
+"""Per-phase cycle counts of the FFT convolution and of the chunked recurrence
+on the long-sequence workload (B=4 H=128 N=64 L=16384), from the instrumented
+library libdssm_stamps.so:
+
+    python -m long_convolution_sequence_amd.build --phase-stamps
+    python -m long_convolution_sequence_amd.phase_stamps [--reps 5]
+
+The instrumented kernels read the shader-clock counter at their phase
+boundaries and add each phase's cycles to a register slot, written once at
+the end of the kernel (so the stamps add no memory waits to the phases they
+time).  Printed per kernel: the mean over workgroups and waves of each
+phase's cycles, their sum, the launch time (GPU-stamped events around the
+kernel) and the clock the two imply (every wave of these launches is resident
+from the start of the launch to its end).  The same input set is used on
+every call, so it is partly served from the caches: phases that wait on
+memory read shorter here than in bench.py, which rotates input sets larger
+than the caches.
+"""
+import argparse
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_STAMPS = os.path.join(HERE, "libdssm_stamps.so")
+
+SLOTS = 16
+MAX_WAVES = 4096 * 16  # buffer rows: up to 4096 workgroups of up to 16 waves
+
+CONV_PHASES = ["entry: twiddle table, input requested", "even half forward",
+               "even half: spectrum read, product", "even half inverse", "odd half forward",
+               "odd half: spectrum read, product", "odd half inverse",
+               "combination, stores issued"]
+CHUNK_PHASES = ["prologue: parameters, operands", "block: barrier", "input staged, next requested",
+                "barrier", "chunk states (matrix cores)", "barrier", "recurrence, first part",
+                "barrier", "recurrence, second part", "barrier", "outputs (matrix cores)"]
+
+
+def _phases(buf, nwg, waves, names):
+    d = buf.cpu().numpy().reshape(-1, SLOTS)[: nwg * waves].astype(np.float64)
+    tot = d[:, : len(names)].sum(axis=1)
+    rows = [(nm, d[:, k].mean()) for k, nm in enumerate(names)]
+    return rows, tot.mean()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--reps", type=int, default=5)
+    a = ap.parse_args()
+    if not os.path.exists(LIB_STAMPS):
+        raise SystemExit("%s is missing: python -m long_convolution_sequence_amd.build "
+                         "--phase-stamps" % LIB_STAMPS)
+    import torch
+
+    from long_convolution_sequence_amd import binding as bd
+    from long_convolution_sequence_amd import inputs
+
+    bd.LIB_PATH = LIB_STAMPS
+    lib = bd.lib()
+    for fn in ("dssm_phase_stamps_fft", "dssm_phase_stamps_chunk"):
+        getattr(lib, fn).argtypes = [ctypes.c_void_p]
+        getattr(lib, fn).restype = ctypes.c_int
+
+    c = inputs.config("long_sequence")
+    B, H = c["B"], c["H"]
+    x = inputs.inputs_for(c)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x.items()}
+    args = (t["u"], t["log_re"], t["log_im"], t["W"], t["D"])
+    hip = bd.HipEvents()
+    # (grid of the kernel on this workload, waves per workgroup)
+    kinds = [("fft", "dssm_phase_stamps_fft", "conv_kernel<14>", (H * ((B + 1) // 2), 16),
+              CONV_PHASES, bd.forward_fft),
+             ("scan", "dssm_phase_stamps_chunk", "chunk_kernel", (H * B, 4), CHUNK_PHASES,
+              bd.forward_scan)]
+    for path, setter, kname, (nwg, waves), names, fn in kinds:
+        assert nwg * waves <= MAX_WAVES
+        buf = torch.zeros(MAX_WAVES * SLOTS, dtype=torch.int64, device="cuda")
+        if getattr(lib, setter)(buf.data_ptr()) != 0:
+            raise SystemExit("%s failed" % setter)
+        for _ in range(a.reps):
+            fn(*args)
+        torch.cuda.synchronize()
+        rows, total = _phases(buf, nwg, waves, names)
+        if getattr(lib, setter)(None) != 0:
+            raise SystemExit("%s failed" % setter)
+        evs = [hip.create(4) for _ in range(a.reps + 5)]
+        for e in evs:
+            bd.forward_timed(path, *args, e)
+        torch.cuda.synchronize()
+        ms = sorted(hip.ms(e[2], e[3]) for e in evs[3:])
+        launch_us = 1e3 * ms[len(ms) // 2]
+        for e in evs:
+            hip.destroy(e)
+        print("%s (%d workgroups x %d waves): %.0f cycles per wave, launch %.1f us, "
+              "%.2f GHz" % (kname, nwg, waves, total, launch_us, total / launch_us / 1e3))
+        for nm, v in rows:
+            print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,14 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, name), name
 
 
+def test_library_carries_no_phase_stamps():
+    """The cycle-stamp instrumentation exists only in the separate
+    libdssm_stamps.so (build.py --phase-stamps); libdssm.so has none."""
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in ("dssm_phase_stamps_fft", "dssm_phase_stamps_chunk"):
+        assert not hasattr(lib, name), name
+
+
 def test_version_matches_header():
     m = re.search(r"#define DSSM_VERSION (\d+)", open(HEADER).read())
     assert bd.lib().dssm_version() == int(m.group(1))
