@@ -44,8 +44,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // the library proper has none).  A kernel reads the shader-clock counter
 // (s_memtime) at its phase boundaries and adds each phase's cycles to a
 // register slot; at its end lane 0 of every wave writes the slots to the
-// buffer set for that source file (dssm_phase_stamps_fft / _chunk):
-//   buf[(workgroup * waves + wave) * kPhaseSlots + slot].
+// buffer set for that source file (dssm_phase_stamps_fft / _chunk / _gen):
+//   buf[(workgroup * waves + wave) * kPhaseSlots + slot], workgroups numbered
+//   x fastest.
 // Nothing is stored before the end, so the stamps add no memory waits to the
 // phases they time.
 // ---------------------------------------------------------------------------
@@ -65,7 +66,8 @@ struct PhaseClock {
   }
   __device__ void write() const {
     if (g_phase_buf && (threadIdx.x & 63) == 0) {
-      const size_t base = ((size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kPhaseSlots;
+      const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+      const size_t base = (wg * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kPhaseSlots;
       for (int k = 0; k < kPhaseSlots; ++k) g_phase_buf[base + k] = acc[k];
     }
   }

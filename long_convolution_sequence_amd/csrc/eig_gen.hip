@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
                                                      const float2* __restrict__ W, int N, int L,
                                                      float* __restrict__ K) {
   __shared__ GenLds s;
+  PhaseClock pc;  // phase stamps (instrumented builds only): slots below
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4;
   const int dh = blockIdx.y;
   const int Q = (L + kAnchor - 1) / kAnchor;
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
       s.wv[lane] = wv;
     }
     __syncthreads();
+    pc.mark(0);  // lambda and W (wave 0, float64), barrier
     float am = 0.f;  // largest |A| entry written by this thread
     {
       const int n = lane;
@@ -116,9 +118,11 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
         a = zmul(a, mu);
       }
     }
+    pc.mark(1);  // tables: powers and anchors (float64 chains), split, LDS
     am = wave_max(am);
     if (lane == 0) s.red[w] = am;
     __syncthreads();
+    pc.mark(2);  // largest anchor entry, barrier
     const int eA = scale_exp(fmaxf(fmaxf(s.red[0], s.red[1]), fmaxf(s.red[2], s.red[3])));
 
     // wave w: D[r][q] for r < 64 (4 row tiles) and q = q0 + 16 w + lane % 16
@@ -157,6 +161,7 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
         }
       }
     }
+    pc.mark(3);  // contraction (matrix cores)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -202,6 +207,8 @@ __global__ __launch_bounds__(256, 2) void gen_kernel(const float* __restrict__ l
       }
     }
   }
+  pc.mark(4);  // stores issued
+  pc.write();
 }
 
 }  // namespace
@@ -221,3 +228,10 @@ hipError_t launch_gen(const float* log_re, const float* log_im, const float* W, 
 }
 
 }  // namespace dssm
+
+#ifdef DSSM_PHASE_STAMPS
+// Buffer for the generator's phase stamps (instrumented builds only).
+extern "C" int dssm_phase_stamps_gen(void* buf) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(dssm::g_phase_buf), &buf, sizeof(buf));
+}
+#endif

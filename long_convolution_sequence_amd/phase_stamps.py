@@ -1,6 +1,6 @@
-"""Per-phase cycle counts of the FFT convolution and of the chunked recurrence
-on the long-sequence workload (B=4 H=128 N=64 L=16384), from the instrumented
-library libdssm_stamps.so:
+"""Per-phase cycle counts of the kernel generator, the FFT convolution and the
+chunked recurrence on the long-sequence workload (B=4 H=128 N=64 L=16384),
+from the instrumented library libdssm_stamps.so:
 
     python -m long_convolution_sequence_amd.build --phase-stamps
     python -m long_convolution_sequence_amd.phase_stamps [--reps 5]
@@ -9,12 +9,13 @@ The instrumented kernels read the shader-clock counter at their phase
 boundaries and add each phase's cycles to a register slot, written once at
 the end of the kernel (so the stamps add no memory waits to the phases they
 time).  Printed per kernel: the mean over workgroups and waves of each
-phase's cycles, their sum, the launch time (GPU-stamped events around the
-kernel) and the clock the two imply (every wave of these launches is resident
-from the start of the launch to its end).  The same input set is used on
-every call, so it is partly served from the caches: phases that wait on
-memory read shorter here than in bench.py, which rotates input sets larger
-than the caches.
+phase's cycles, their sum, and for the convolution and the recurrence the
+launch time (GPU-stamped events around the kernel) and the clock the two
+imply (every wave of these launches is resident from the start of the launch
+to its end; the generator shares its stamped stage with the spectrum).  The
+same input set is used on every call, so it is partly served from the
+caches: phases that wait on memory read shorter here than in bench.py, which
+rotates input sets larger than the caches.
 """
 import argparse
 import ctypes
@@ -32,6 +33,8 @@ CONV_PHASES = ["entry: twiddle table, input requested", "even half forward",
                "even half: spectrum read, product", "even half inverse", "odd half forward",
                "odd half: spectrum read, product", "odd half inverse",
                "combination, stores issued"]
+GEN_PHASES = ["lambda and W (wave 0, float64), barrier", "tables (float64 chains), split",
+              "largest anchor entry, barrier", "contraction (matrix cores)", "stores issued"]
 CHUNK_PHASES = ["prologue: parameters, operands", "block: barrier", "input staged, next requested",
                 "barrier", "chunk states (matrix cores)", "barrier", "recurrence, first part",
                 "barrier", "recurrence, second part", "barrier", "outputs (matrix cores)"]
@@ -58,7 +61,7 @@ def main():
 
     bd.LIB_PATH = LIB_STAMPS
     lib = bd.lib()
-    for fn in ("dssm_phase_stamps_fft", "dssm_phase_stamps_chunk"):
+    for fn in ("dssm_phase_stamps_fft", "dssm_phase_stamps_chunk", "dssm_phase_stamps_gen"):
         getattr(lib, fn).argtypes = [ctypes.c_void_p]
         getattr(lib, fn).restype = ctypes.c_int
 
@@ -69,7 +72,10 @@ def main():
     args = (t["u"], t["log_re"], t["log_im"], t["W"], t["D"])
     hip = bd.HipEvents()
     # (grid of the kernel on this workload, waves per workgroup)
-    kinds = [("fft", "dssm_phase_stamps_fft", "conv_kernel<14>", (H * ((B + 1) // 2), 16),
+    L = c["L"]
+    kinds = [(None, "dssm_phase_stamps_gen", "gen_kernel", (H * ((L + 4095) // 4096), 4),
+              GEN_PHASES, bd.forward_fft),
+             ("fft", "dssm_phase_stamps_fft", "conv_kernel<14>", (H * ((B + 1) // 2), 16),
               CONV_PHASES, bd.forward_fft),
              ("scan", "dssm_phase_stamps_chunk", "chunk_kernel", (H * B, 4), CHUNK_PHASES,
               bd.forward_scan)]
@@ -84,6 +90,11 @@ def main():
         rows, total = _phases(buf, nwg, waves, names)
         if getattr(lib, setter)(None) != 0:
             raise SystemExit("%s failed" % setter)
+        if path is None:
+            print("%s (%d workgroups x %d waves): %.0f cycles per wave" % (kname, nwg, waves, total))
+            for nm, v in rows:
+                print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
+            continue
         evs = [hip.create(4) for _ in range(a.reps + 5)]
         for e in evs:
             bd.forward_timed(path, *args, e)
