@@ -305,8 +305,10 @@ __device__ __forceinline__ double2 lambda64(const ChunkArgs& a, int d, int h, in
   return make_double2(m * cs, m * sn);
 }
 
-template <bool VEC, bool STATE_ONLY, bool CAPTURE>
+template <bool VEC, bool STATE_ONLY, bool CAPTURE, int RP = 1>
 __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
+  static_assert(RP == 1 || RP == 2 || RP == 4, "rows per block");
+  static_assert(RP == 1 || (!STATE_ONLY && !CAPTURE), "rows share a block only without state");
   PhaseClock pc;  // phase stamps (instrumented builds only): slots below
   __shared__ __attribute__((aligned(16))) unsigned char lds_raw[kLdsBytes];
   TablesLds& tl = *reinterpret_cast<TablesLds*>(lds_raw);
@@ -330,28 +332,44 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
   const bool last_seg = blk1 == nblk;
   if (STATE_ONLY && last_seg) return;  // (whole workgroup) no later segment needs its state
   unsigned char* srow = reinterpret_cast<unsigned char*>(bl.S1);
+  // RP > 1: rows of one block each (at most 64 / RP chunks; the launch
+  // guarantees it, and no state in or out) share a block, row slot k taking
+  // chunks k CR .. k CR + CR - 1 (CR = 64 / RP: a quarter or a half of the
+  // block, i.e. the chunks of one or two waves' recurrence), their chunk
+  // chains kept apart.
+  constexpr int R = RP;
+  constexpr int lgR = RP == 4 ? 2 : RP == 2 ? 1 : 0;
+  constexpr int lgER = 12 - lgR;  // log2 of the elements per row slot (kCB kT / R)
+  constexpr int lgCR = 6 - lgR;   // log2 of the chunks per row slot
 
   for (int dd = 0; dd < a.ndir_wg; ++dd) {
     const int d = dir0 + dd;
     const bool rev = d == 1;
     const bool add = a.add || dd > 0;
-    // element e of block blk in processing time -> sequence position (out of
-    // range, hence zero on load and dropped on store, beyond the sequence)
+    // element e of block blk in processing time -> sequence position within
+    // its row (out of range, hence zero on load and dropped on store, beyond
+    // the sequence); the row is slot e >> lgER of the block's row group
     auto pos = [&](int blk, int e) {
-      const int q = blk * kCB * kT + e;
+      const int q = blk * kCB * kT + (e & ((1 << lgER) - 1));
       return rev ? Lp - 1 - q : q;
     };
-    // input of block blk of row b: thread t takes elements 4 t + 1024 q + c4 (c4 < 4, q < 4);
-    // !valid: zeros (an empty buffer)
-    auto load_block = [&](int b, int blk, float* v, bool valid = true) {
-      const BufRes ub = buf_res(a.u + ((size_t)(valid ? b : 0) * H + h) * L,
-                                valid ? 4u * (unsigned)L : 0u);
+    // a row of the group starting at row bg, as a buffer (empty beyond the
+    // group's nv valid rows: zeros on load, stores dropped)
+    auto row_buf = [&](const float* base, int bg, int k, int nv) {
+      const bool valid = k < nv;
+      return buf_res(base + ((size_t)(valid ? bg + k : 0) * H + h) * L,
+                     valid ? 4u * (unsigned)L : 0u);
+    };
+    // input of block blk of the row group at bg: thread t takes elements
+    // 4 t + 1024 q + c4 (c4 < 4, q < 4), each group q in one row slot
+    auto load_block = [&](int bg, int blk, float* v, int nv) {
       if (VEC) {  // reversed: the four elements sit at descending positions, kept
                   // in memory order here (one load path for both directions, and no
                   // register permutation that would wait for the load); the
                   // staging reads them reversed
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const BufRes ub = row_buf(a.u, bg, (1024 * q) >> lgER, nv);
           const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
               ub, 4 * pos(blk, 4 * t + 1024 * q + (rev ? 3 : 0)), 0, 0);
           v[4 * q + 0] = __uint_as_float(x.x);
@@ -362,6 +380,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
       } else {
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
+          const BufRes ub = row_buf(a.u, bg, (1024 * (q >> 2)) >> lgER, nv);
           const int e = 4 * t + 1024 * (q >> 2) + (q & 3);
           v[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ub, 4 * pos(blk, e), 0, 0));
         }
@@ -372,16 +391,19 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
     const bool swap4 = VEC && rev;
     ModeParams mp = load_mode_params(a.log_re, a.log_im, a.W, a.D, a.ndir, H, a.N, d, h);
     float un[16];
-    load_block(b0, blk0, un);  // in flight while the operands are formed
+    load_block(b0, blk0, un, min(R, b1 - b0));  // in flight while the operands are formed
     params_here(mp);
     half8 a1[8], a3[12];
     float2 lamT, lam16T;
     int eT, eW;
     build_operands(mp, a.N, d, tl, a1, a3, lamT, lam16T, eT, eW);
 
-    for (int b = b0; b < b1; ++b) {
+    for (int b = b0; b < b1; b += R) {
       const size_t row = (size_t)b * H + h;
-      const BufRes ybuf = buf_res(a.y + row * L, 4u * (unsigned)L);
+      const int nv = min(R, b1 - b);  // rows of this group
+      // (four named buffers, selected below: no array indexed at run time)
+      const BufRes yb0 = row_buf(a.y, b, 0, nv), yb1 = row_buf(a.y, b, 1, nv),
+                   yb2 = row_buf(a.y, b, 2, nv), yb3 = row_buf(a.y, b, 3, nv);
       // the state entering the segment, mode = lane (every wave keeps it)
       float2 carry = make_float2(0.f, 0.f);
       if (lane < a.N) {
@@ -419,7 +441,8 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
         // first block of the next row (zeros beyond the sequence or the rows)
         {
           const bool same = blk + 1 < blk1;
-          load_block(same ? b : b + 1, same ? blk + 1 : blk0, un, same || b + 1 < b1);
+          load_block(same ? b : b + R, same ? blk + 1 : blk0, un,
+                     same ? nv : min(R, b1 - (b + R)));
         }
         __builtin_amdgcn_sched_barrier(0);
         pc.mark(2);  // input staged, next block requested
@@ -483,8 +506,8 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
           pc.mark(6);  // recurrence, first part
           __syncthreads();
           pc.mark(7);
-          float2 cin = carry;  // state entering quarter w
-          for (int q = 0; q < w; ++q) cin = cfma(lam16T, cin, bl.E[q][n]);
+          float2 cin = carry;  // state entering quarter w (from its row slot's first quarter)
+          for (int q = w & ~((4 >> lgR) - 1); q < w; ++q) cin = cfma(lam16T, cin, bl.E[q][n]);
           float2 cnext = carry;  // state leaving the block (every wave keeps it)
 #pragma unroll
           for (int q = 0; q < 4; ++q) cnext = cfma(lam16T, cnext, bl.E[q][n]);
@@ -565,7 +588,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             const int c = 32 * ch + 16 * ct + (lane & 15);
-            const int e0 = (blk * kCB + c) * kT + 16 * w + 4 * (lane >> 4);  // processing time
+            // processing time within the chunk's row (slot (32 ch + 16 ct) >> lgCR)
+            const int e0 = (blk * kCB + (c & ((1 << lgCR) - 1))) * kT + 16 * w + 4 * (lane >> 4);
+            const int slot = (32 * ch + 16 * ct) >> lgCR;
+            const BufRes ybuf = slot == 0 ? yb0 : slot == 1 ? yb1 : slot == 2 ? yb2 : yb3;
             const int xu = -(eT + bl.eU[c]), xs = -(eW + bl.eS[c >> 4]);
             f4 acc;
 #pragma unroll
@@ -727,8 +753,20 @@ void launch_chunk_args(const ChunkArgs& a, hipStream_t st, KEvents ev, int ndir_
     if (vec) launch_k(chunk_kernel<true, false, true>, g, blk, st, ev, a);
     else launch_k(chunk_kernel<false, false, true>, g, blk, st, ev, a);
   } else {
-    if (vec) launch_k(chunk_kernel<true, false, false>, g, blk, st, ev, a);
-    else launch_k(chunk_kernel<false, false, false>, g, blk, st, ev, a);
+    // short stateless rows share blocks: 4 rows of at most 16 chunks, or 2 of
+    // at most 32
+    const int nchunk = (a.L + kT - 1) / kT;
+    const int rp = (a.x0 || a.cin || a.nseg != 1) ? 1 : nchunk <= kCB / 4 ? 4 : nchunk <= kCB / 2 ? 2 : 1;
+    if (rp == 4) {
+      if (vec) launch_k(chunk_kernel<true, false, false, 4>, g, blk, st, ev, a);
+      else launch_k(chunk_kernel<false, false, false, 4>, g, blk, st, ev, a);
+    } else if (rp == 2) {
+      if (vec) launch_k(chunk_kernel<true, false, false, 2>, g, blk, st, ev, a);
+      else launch_k(chunk_kernel<false, false, false, 2>, g, blk, st, ev, a);
+    } else {
+      if (vec) launch_k(chunk_kernel<true, false, false>, g, blk, st, ev, a);
+      else launch_k(chunk_kernel<false, false, false>, g, blk, st, ev, a);
+    }
   }
 }
 

@@ -364,8 +364,11 @@ def test_scan_sequence_split(shape):
     assert_close(y, ref, "scan/split")
 
 
-ROWS = [  # (B, H, N, L, bi): many rows -> several batch rows per workgroup, ragged groups
+ROWS = [  # (B, H, N, L, bi): many rows -> several batch rows per workgroup, ragged groups;
+    # rows of at most 16 chunks (L <= 1024) four to a block, of at most 32 two to a block,
+    # with empty row slots, both directions, and lengths off the 16-byte grid
     (7, 300, 16, 500, 0), (9, 130, 64, 4096, 1), (16, 80, 8, 1000, 1), (5, 230, 64, 70, 0),
+    (7, 160, 32, 2000, 0), (6, 200, 64, 1537, 1),
 ]
 
 
