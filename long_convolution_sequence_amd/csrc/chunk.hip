@@ -652,10 +652,11 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
         }
       }
     }
-    if (dd + 1 < a.ndir_wg) {
-      __threadfence();  // this direction's stores are visible to the next one's sweep
-      __syncthreads();
-    }
+    // this direction's stores are visible to the next one's sweep: both run in
+    // this workgroup, whose vector memory operations stay in order on its CU
+    // (the later direction reads y past the L1); a workgroup barrier orders
+    // them, no agent-scope fence (an L2 write-back and invalidation) needed
+    if (dd + 1 < a.ndir_wg) __syncthreads();
   }
   pc.write();
 }
