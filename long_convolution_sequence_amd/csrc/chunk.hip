@@ -521,14 +521,19 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
             m = fmaxf(m, fmaxf(fabsf(st.x), fabsf(st.y)));
             st = nx;
           }
-          // the state entering the sequence's last chunk, kept for the end state
+          // for the end state: the state entering the sequence's last chunk or,
+          // when L is a whole number of chunks, the state leaving it (the end
+          // state itself: the entering state of the next chunk, or st after the
+          // quarter's last)
           if (CAPTURE && last_seg) {
             const int cloc = cl - blk * kCB - 16 * w;
             if (cloc >= 0 && cloc < 16) {
-              float2 s0 = sv[0];
+              const bool whole = (L % kT) == 0;
+              const int ce = whole ? cloc + 1 : cloc;
+              float2 s0 = st;
 #pragma unroll
-              for (int c = 1; c < 16; ++c)
-                if (c == cloc) s0 = sv[c];
+              for (int c = 0; c < 16; ++c)
+                if (c == ce) s0 = sv[c];
               bl.Xl[n] = s0;
             }
           }
@@ -638,7 +643,9 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
       // holds the last chunk), advanced in float64 by one wave, lane = mode
       if (CAPTURE && last_seg) {
         __syncthreads();  // Xl written by the wave that held the last chunk
-        if (w == 0) {
+        if (w == 0 && (L % kT) == 0) {  // Xl is the state after step L - 1
+          if (lane < a.N) a.xend[row * a.N + lane] = bl.Xl[lane];
+        } else if (w == 0) {  // a partial last chunk: its real steps from Xl, in float64
           const int c = cl - (nblk - 1) * kCB;  // the last chunk's index in its block
           const double2 lam = lambda64(a, d, h, lane);
           const float2 s0 = bl.Xl[lane];

@@ -79,6 +79,10 @@ def main():
               CONV_PHASES, bd.forward_fft),
              ("scan", "dssm_phase_stamps_chunk", "chunk_kernel", (H * B, 4), CHUNK_PHASES,
               bd.forward_scan)]
+    # the streaming call (state in, end state out) from a random state
+    x0 = torch.from_numpy(inputs.dlr_state(B, H, c["N"], seed=3)).cuda()
+    kinds.append((None, "dssm_phase_stamps_chunk", "chunk_kernel, streaming", (H * B, 4),
+                  CHUNK_PHASES, lambda *a_: bd.forward_scan_state(*a_, x0.clone())))
     for path, setter, kname, (nwg, waves), names, fn in kinds:
         assert nwg * waves <= MAX_WAVES
         buf = torch.zeros(MAX_WAVES * SLOTS, dtype=torch.int64, device="cuda")
