@@ -369,7 +369,9 @@ def dlr_config(name, steps, hip):
 
         ms = wall_ms(call, steps, 3)
         dist = step_distribution(call, max(100, steps), hip)
-        st = stage_times(call_timed, 2, max(20, steps // 2), hip)
+        # (the chunked form for N <= 64 is one kernel: its first stage has none)
+        chunked = path == "scan" and N <= 64
+        st = stage_times(call_timed, 2, max(20, steps // 2), hip, only=1 if chunked else None)
         gbs, frac = hbm(elems, ms)
         kgbs, kfrac = hbm(elems, st[1])
         call(0)
@@ -378,7 +380,7 @@ def dlr_config(name, steps, hip):
         p = {"ms_per_forward": ms, "elements_per_s": elems / (ms * 1e-3),
              "layer_hbm_gbs": gbs, "layer_hbm_frac": frac, "step_distribution": dist,
              "stage_ms": ({"kernel_spectrum": st[0], "conv": st[1]} if path == "fft"
-                          else {"consts": st[0], "scan": st[1]}),
+                          else {"scan": st[1]} if chunked else {"consts": st[0], "scan": st[1]}),
              "kernel_hbm_gbs": kgbs, "kernel_hbm_frac": kfrac,
              "vs_oracle_sampled_channels": errors_vs(y, ref)}
         if path == "fft":

@@ -147,8 +147,9 @@ __device__ __forceinline__ void params_here(ModeParams& mp) {
 
 __device__ __forceinline__ void build_operands(const ModeParams& mp, int N, int d, TablesLds& tl,
                                                half8* a1, half8* a3, float2& lamT,
-                                               float2& lam16T, int& eT, int& eW) {
+                                               float2& lam16T, int& eT, int& eW, PhaseClock& pc) {
   const int t = opaque(threadIdx.x), lane = t & 63, w = t >> 6;
+  pc.mark(11);
   if (w == 0) {  // lambda_n, W_n (float64, from the exactly promoted parameters)
     const int n = lane;
     double2 lam = make_double2(0.0, 0.0), wv = lam;
@@ -164,6 +165,7 @@ __device__ __forceinline__ void build_operands(const ModeParams& mp, int N, int 
     tl.wv[n] = wv;
   }
   __syncthreads();
+  pc.mark(12);
   float2 pw[16];  // lambda^p of this thread's 16 powers, kept for the planes
   float qm = 0.f;  // largest |Q| entry written by this thread
   {  // mode n = lane, powers p = 16 w .. 16 w + 15
@@ -196,6 +198,7 @@ __device__ __forceinline__ void build_operands(const ModeParams& mp, int N, int 
   qm = wave_max(qm);
   if (lane == 0) tl.red[w] = qm;
   __syncthreads();
+  pc.mark(13);
   {  // taps: wave w sums taps 16 w .. +15, a quarter of the modes per 16 lanes
     const int m = 16 * w + (lane & 15), q = lane >> 4;
     double s = 0.0;
@@ -211,6 +214,7 @@ __device__ __forceinline__ void build_operands(const ModeParams& mp, int N, int 
     if (lane == 0) tl.red[4 + w] = km;
   }
   __syncthreads();  // KR read: its space takes the power planes
+  pc.mark(14);
   eW = scale_exp(fmaxf(fmaxf(tl.red[0], tl.red[1]), fmaxf(tl.red[2], tl.red[3])));
   eT = scale_exp(fmaxf(fmaxf(tl.red[4], tl.red[5]), fmaxf(tl.red[6], tl.red[7])));
   {
@@ -224,6 +228,7 @@ __device__ __forceinline__ void build_operands(const ModeParams& mp, int N, int 
     }
   }
   __syncthreads();
+  pc.mark(15);
   const int g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
     half8 a1[8], a3[12];
     float2 lamT, lam16T;
     int eT, eW;
-    build_operands(mp, a.N, d, tl, a1, a3, lamT, lam16T, eT, eW);
+    build_operands(mp, a.N, d, tl, a1, a3, lamT, lam16T, eT, eW, pc);
 
     for (int b = b0; b < b1; b += R) {
       const size_t row = (size_t)b * H + h;
@@ -413,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
           carry = a.x0[row * a.N + lane];
       }
 
-      pc.mark(0);  // prologue: parameters, operands, first input requested
+      pc.mark(0);  // prologue's end: operand fragments, barrier, the entering state
       for (int blk = blk0; blk < blk1; ++blk) {
         __syncthreads();  // the previous block's readers of U and S are done
         pc.mark(1);

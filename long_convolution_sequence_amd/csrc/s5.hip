@@ -1038,6 +1038,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
   constexpr int kFI = FI;
   constexpr int kFR = 16 * FI;  // rows per wave
   constexpr int NS = FI / 2;    // states per lane
+  PhaseClock pc;  // phase stamps (instrumented builds only): slots below
   __shared__ __attribute__((aligned(16))) _Float16 Sh[kFT][kBTS];  // staged operand, hi
   __shared__ __attribute__((aligned(16))) _Float16 Sl[kFT][kBTS];  // staged operand, lo
   __shared__ __attribute__((aligned(16))) float U[kRowsWG][kFT];   // u tile, fp32
@@ -1166,6 +1167,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
     }
     if (cpart == 0) cin_s[cst] = make_float2((float)h.x, (float)h.y);
   }
+  pc.mark(0);  // prologue: parameters, the entering state joined, first u tile requested
 
   // lane-derived indices, re-derived every tile from an opaque copy of the
   // lane id so that the compiler forms LDS addresses where they are used
@@ -1307,6 +1309,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
           if (pin[s2]) carry[s2] = cin_s[ps[s2]];
       }
     }
+    pc.mark(1);  // u tile in LDS (first tile; every tile of the state-only pass), barrier
     // 1. u into the staged operand: thread (step = lane, wave w) takes rows
     //    k = 8 (w + W qq) + e, scaled per step
     {
@@ -1349,6 +1352,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
         }
     }
     __syncthreads();  // the staged u and its exponents are complete; U may be refilled
+    pc.mark(2);  // u scaled, split and staged, D u (two barriers)
     const bool more = jb + 1 < tile1;
     if (STATE_ONLY && more) issue_u(jb + 1);
 
@@ -1378,6 +1382,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
     } else {
       if (!STATE_ONLY && more) issue_u(jb + 1);
     }
+    pc.mark(3);  // input projection v = Bbar u (matrix cores), next u tile requested
 #pragma unroll
     for (int s2 = 0; s2 < NS; ++s2)  // states past P (and waves past the rows) carry zero
 #pragma unroll
@@ -1412,6 +1417,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
         }
       }
     }
+    pc.mark(4);  // recurrence on the tile
     if (STATE_ONLY) continue;  // the next tile's first barrier orders the reads of the staged u
 
     // 3. x as the output product's operand: rows k = 2p (Re), 2p + 1 (Im), one
@@ -1461,8 +1467,10 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
         }
       }
     }
+    pc.mark(5);  // x: per-step maximum (barrier), scaled, split and staged
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next u tile is in LDS
     __syncthreads();                     // the staged x is complete (and the next u tile)
+    pc.mark(6);  // next u tile in LDS, barrier
 
     // 4. y = Re(C x) + D u
     if (i0 < M2) {
@@ -1492,6 +1500,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
         }
       }
     }
+    pc.mark(7);  // output projection y = Re(C x) + D u (matrix cores), stores issued
   }
   // the state leaving a segment that is not the last (all its tiles are full)
   if (STATE_ONLY && g == 0) {
@@ -1499,6 +1508,7 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
     for (int s2 = 0; s2 < NS; ++s2)
       if (pin[s2]) a.sout[((size_t)b * a.nseg + seg) * P + ps[s2]] = carry[s2];
   }
+  pc.write();
 }
 
 }  // namespace
@@ -1695,3 +1705,10 @@ hipError_t launch_s5_proj_out(const void* apk_out, const int* rexp_out, const fl
 }
 
 }  // namespace dssm
+
+#ifdef DSSM_PHASE_STAMPS
+// Buffer for the fused S5 kernel's phase stamps (instrumented builds only).
+extern "C" int dssm_phase_stamps_s5(void* buf) {
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(dssm::g_phase_buf), &buf, sizeof(buf));
+}
+#endif

@@ -1,6 +1,7 @@
 """Per-phase cycle counts of the kernel generator, the FFT convolution and the
 chunked recurrence on the long-sequence workload (B=4 H=128 N=64 L=16384),
-from the instrumented library libdssm_stamps.so:
+and of the fused S5 form's output pass on the S5 workload (B=4 H=256 P=128
+L=16384), from the instrumented library libdssm_stamps.so:
 
     python -m long_convolution_sequence_amd.build --phase-stamps
     python -m long_convolution_sequence_amd.phase_stamps [--reps 5]
@@ -35,9 +36,17 @@ CONV_PHASES = ["entry: twiddle table, input requested", "even half forward",
                "combination, stores issued"]
 GEN_PHASES = ["lambda and W (wave 0, float64), barrier", "tables (float64 chains), split",
               "largest anchor entry, barrier", "contraction (matrix cores)", "stores issued"]
-CHUNK_PHASES = ["prologue: parameters, operands", "block: barrier", "input staged, next requested",
+CHUNK_PHASES = ["prologue: fragments, barrier", "block: barrier", "input staged, next requested",
                 "barrier", "chunk states (matrix cores)", "barrier", "recurrence, first part",
-                "barrier", "recurrence, second part", "barrier", "outputs (matrix cores)"]
+                "barrier", "recurrence, second part", "barrier", "outputs (matrix cores)",
+                "prologue: entry, loads issued", "prologue: lambda (float64), barrier",
+                "prologue: powers, Q and KR tables, barrier", "prologue: taps, barrier",
+                "prologue: power planes, barrier"]
+S5_PHASES = ["prologue: parameters, entering state, first u tile requested",
+             "u tile in LDS (first tile), barrier", "u scaled, split, staged; D u (2 barriers)",
+             "input projection (matrix cores)", "recurrence on the tile",
+             "x maximum (barrier), scaled, split, staged", "next u tile in LDS, barrier",
+             "output projection (matrix cores), stores issued"]
 
 
 def _phases(buf, nwg, waves, names):
@@ -61,7 +70,8 @@ def main():
 
     bd.LIB_PATH = LIB_STAMPS
     lib = bd.lib()
-    for fn in ("dssm_phase_stamps_fft", "dssm_phase_stamps_chunk", "dssm_phase_stamps_gen"):
+    for fn in ("dssm_phase_stamps_fft", "dssm_phase_stamps_chunk", "dssm_phase_stamps_gen",
+               "dssm_phase_stamps_s5"):
         getattr(lib, fn).argtypes = [ctypes.c_void_p]
         getattr(lib, fn).restype = ctypes.c_int
 
@@ -111,6 +121,40 @@ def main():
               "%.2f GHz" % (kname, nwg, waves, total, launch_us, total / launch_us / 1e3))
         for nm, v in rows:
             print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
+
+    # the fused S5 form: its output pass is the last launch to write the stamps
+    c5 = inputs.config("s5_mimo")
+    x5 = inputs.inputs_for(c5)
+    t5 = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x5.items()}
+    ws = torch.empty(bd.s5_workspace_size(c5["B"], c5["H"], c5["P"], c5["L"], bd.S5_FUSED),
+                     dtype=torch.uint8, device="cuda")
+
+    def s5(evs=None):
+        bd.s5_forward(t5["u"], t5["lam"], t5["Bbar"], t5["C"], t5["D"], workspace=ws,
+                      method=bd.S5_FUSED, events=evs)
+
+    buf = torch.zeros(MAX_WAVES * SLOTS, dtype=torch.int64, device="cuda")
+    if lib.dssm_phase_stamps_s5(buf.data_ptr()) != 0:
+        raise SystemExit("dssm_phase_stamps_s5 failed")
+    for _ in range(a.reps):
+        s5()
+    torch.cuda.synchronize()
+    nwg, waves = 256, 8  # the output pass's grid on this workload
+    rows, total = _phases(buf, nwg, waves, S5_PHASES)
+    if lib.dssm_phase_stamps_s5(None) != 0:
+        raise SystemExit("dssm_phase_stamps_s5 failed")
+    evs = [hip.create(8) for _ in range(a.reps + 5)]
+    for e in evs:
+        s5(e)
+    torch.cuda.synchronize()
+    ms = sorted(hip.ms(e[6], e[7]) for e in evs[3:])  # stage 3: the output pass
+    launch_us = 1e3 * ms[len(ms) // 2]
+    for e in evs:
+        hip.destroy(e)
+    print("s5_fused_kernel, output pass (%d workgroups x %d waves): %.0f cycles per wave, "
+          "launch %.1f us, %.2f GHz" % (nwg, waves, total, launch_us, total / launch_us / 1e3))
+    for nm, v in rows:
+        print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
 
 
 if __name__ == "__main__":
