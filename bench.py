@@ -397,10 +397,12 @@ def dlr_config(name, steps, hip):
 def scan_split(hip, reps=5):
     """The recurrence view when rows are few and the sequence long (B=1, H=4,
     N=64, L=2^20, one and two directions): the sequence cut into segments
-    (state-only pass, carry chain, output pass) against the walk of one
-    workgroup per row it replaces.  That walk is estimated from one row's
-    kernel time at one block (4096 steps) and at one chunk (64 steps): the
-    operand prologue plus blocks times the per-block time."""
+    (a state-only pass, the join of the segments' states into the state each
+    one enters, the output pass) against the walk of one workgroup per row it
+    replaces.  That walk is bounded from below by kernel times of whole rows:
+    one row of one block alone, and 512 rows (one workgroup each, two to a
+    CU) of one and of two blocks, whose difference is the CU time of two
+    blocks -- a block of a lone workgroup takes at least half of it."""
     import numpy as np
     import torch
 
@@ -423,20 +425,23 @@ def scan_split(hip, reps=5):
 
     out = {}
     L = 1 << 20
-    one_blk = kernel_ms(1, 1, 64, 4096, False, 51)
-    one_chunk = kernel_ms(1, 1, 64, 64, False, 52)
-    per_blk = max(one_blk - one_chunk, 0.0)
+    one_row = kernel_ms(1, 1, 64, 4096, False, 51)
+    rows1 = kernel_ms(1, 512, 64, 4096, False, 52)
+    rows2 = kernel_ms(1, 512, 64, 8192, False, 52)
+    blk_lone_min = max(rows2 - rows1, 0.0) / 2
     for bi in (False, True):
         ms = kernel_ms(1, 4, 64, L, bi, 53)
         ndir = 2 if bi else 1
-        walk = ndir * (one_chunk + (L // 4096) * per_blk)
+        walk = ndir * (one_row + (L // 4096 - 1) * blk_lone_min)
         out["bidirectional" if bi else "unidirectional"] = {
             "B": 1, "H": 4, "N": 64, "L": L, "kernels_ms": ms,
             "elements_per_s": 4 * L / (ms * 1e-3),
-            "one_workgroup_per_row_walk_ms_estimate": walk,
-            "speedup_over_walk": walk / ms,
+            "one_workgroup_per_row_walk_ms_lower_bound": walk,
+            "speedup_over_walk_at_least": walk / ms,
         }
-    out["walk_estimate_from"] = {"one_row_one_block_ms": one_blk, "one_row_one_chunk_ms": one_chunk}
+    out["walk_bound_from"] = {"one_row_one_block_ms": one_row,
+                              "rows512_one_block_ms": rows1, "rows512_two_blocks_ms": rows2,
+                              "lone_block_ms_at_least": blk_lone_min}
     return out
 
 

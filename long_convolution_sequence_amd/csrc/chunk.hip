@@ -674,82 +674,90 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
 }
 
 // The state entering each segment from the states the segments leave when
-// started from zero: cin[s] = A cin[s-1] + sout[s-1] with A = lambda^S (S =
-// the segment's length in steps), cin[0] = x0 or zero, in float64.  A
-// parallel scan over the segments of one (direction, row, channel, mode):
-// thread j of a group of P2 lanes takes segments 16 j .. 16 j + 15 (its 16
-// loads issued together), forms their aggregate from zero, the lanes combine
-// the aggregates by a Hillis-Steele scan with the multipliers A^(16 2^k),
-// and each thread
-// replays its segments from the state entering its first one.  A is formed
-// from the float64 logarithm; its powers A^(16 2^k) by squaring.
-constexpr int kSegPerThread = 16;
+// started from zero (sout, a state-only pass's) and the caller's state x0
+// (direction 0; zero without it):
+//   cin[s] = A^s x0 + sum_{m < s} A^(s - 1 - m) sout[m],  A = lambda^S,
+// S the steps of a segment, in float64, rounded once.  One workgroup per
+// (direction, row, segment), lane = mode: wave w takes a quarter of the
+// segments m < s by Horner's rule (the state leaving its last one from its
+// terms alone), advanced by A^(s - its end) to the segment's start; the four
+// partial states meet in LDS.  Every load is unconditional (buffers: lanes
+// past N, and x0 when absent, read zero), so a wave's loads issue together.
+// A is formed from the float64 logarithm, its powers A^k by squaring (at
+// most 9 squarings for 512 segments: a relative error of a few hundred
+// float64 ulp).
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ double2 zfma(double2 m, double2 x, double2 c) {  // m x + c
   return make_double2(fma(m.x, x.x, fma(-m.y, x.y, c.x)), fma(m.x, x.y, fma(m.y, x.x, c.y)));
 }
 
-__global__ __launch_bounds__(256) void chunk_carry_kernel(ChunkArgs a, int seg_len, int p2,
-                                                          float2* __restrict__ cin) {
-  const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long pairs = (long)a.ndir * a.B * a.H * a.N;
-  const long pr = g / p2;  // (direction, row, channel, mode)
-  const int j = (int)(g % p2);
-  const bool active = pr < pairs;
-  const long pc = active ? pr : 0;
-  const int n = (int)(pc % a.N);
-  const long r = pc / a.N;  // (d, b, h)
-  const int h = (int)(r % a.H);
-  const int b = (int)((r / a.H) % a.B);
-  const int d = (int)(r / ((long)a.H * a.B));
-  const size_t i_par = ((size_t)d * a.H + h) * a.N + n;
-  const double re = (double)a.log_re[i_par], im = (double)a.log_im[i_par];
-  // lambda^m = exp(m log lambda), log lambda = -re^2 + i im
-  auto lpow = [&](double m) {
-    double sn, cs;
-    sincos(fmod(im * m, 2.0 * M_PI), &sn, &cs);  // (a small argument: the fast reduction)
-    const double mag = exp(-re * re * m);
-    return make_double2(mag * cs, mag * sn);
+__global__ __launch_bounds__(256) void chunk_join_kernel(const ChunkArgs a,
+                                                         float2* __restrict__ cin) {
+  __shared__ double2 part[256];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int seg = blockIdx.x % a.nseg;
+  const int r = blockIdx.x / a.nseg;  // (d, b, h)
+  const int h = r % a.H, b = (r / a.H) % a.B, d = r / (a.H * a.B);
+  const bool live = lane < a.N;
+  const size_t row = ((size_t)d * a.B + b) * a.H + h;
+  const int lo = live ? 8 * lane : 1 << 30;  // (past every buffer: zero)
+  auto load2 = [&](BufRes rs, int off) {
+    const v2u v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+    return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
   };
-  const double2 A = lpow((double)seg_len);
-  // A^16 and its powers A^(16 2^k) by squaring (relative error ~2^k ulp of
-  // float64 after k squarings, k <= 9 here)
-  auto zsq = [](double2 z) { return make_double2(z.x * z.x - z.y * z.y, 2.0 * z.x * z.y); };
-  double2 A16 = zsq(zsq(zsq(zsq(A))));
-  const size_t base = ((((size_t)d * a.B + b) * a.H + h) * a.nseg) * a.N + n;
-  const int s0 = kSegPerThread * j;
-  float2 o[kSegPerThread];
-#pragma unroll
-  for (int k = 0; k < kSegPerThread; ++k) {  // segment s0 + k leaves o[k] (the last one: unused)
-    const int sg = s0 + k;
-    o[k] = (active && sg < a.nseg - 1) ? a.sout[base + (size_t)sg * a.N] : make_float2(0.f, 0.f);
+  const bool with_x0 = a.x0 && d == 0;
+  const BufRes xr = buf_res_uniform(with_x0 ? a.x0 + ((size_t)b * a.H + h) * a.N : a.sout,
+                                    with_x0 ? 8u * (unsigned)a.N : 0u);
+  const float2 x0 = load2(xr, lo);
+  float2* out = cin + (row * a.nseg + seg) * a.N;
+  if (seg == 0) {  // (the whole workgroup)
+    if (w == 0 && live) out[lane] = x0;
+    return;
   }
-  double2 agg = make_double2(0.0, 0.0);  // the state leaving segment s0 + 15 from zero at s0
+  const BufRes sr = buf_res_uniform(a.sout + row * a.nseg * a.N, 8u * (unsigned)(a.nseg * a.N));
+  const int q = (seg + 3) / 4;
+  const int m0 = min(seg, w * q), m1 = min(seg, m0 + q);
+  const size_t ip = ((size_t)d * a.H + h) * a.N + (live ? lane : 0);
+  const float fre = a.log_re[ip], fim = a.log_im[ip];
+  constexpr int kJ = 32;  // terms requested at once, in flight while A is formed
+  float2 v[kJ];
 #pragma unroll
-  for (int k = 0; k < kSegPerThread; ++k)
-    agg = zfma(A, agg, make_double2((double)o[k].x, (double)o[k].y));
-  double2 x0 = make_double2(0.0, 0.0);
-  if (active && a.x0 && d == 0) {
-    const float2 v = a.x0[((size_t)b * a.H + h) * a.N + n];
-    x0 = make_double2((double)v.x, (double)v.y);
+  for (int e = 0; e < kJ; ++e) v[e] = load2(sr, lo + 8 * a.N * min(m0 + e, seg - 1));  // (past m1: unused)
+  const double re = (double)fre, im = (double)fim;
+  const double S = (double)a.seg_blocks * kCB * kT;
+  double sn, cs;
+  sincos(fmod(im * S, 2.0 * M_PI), &sn, &cs);  // (reduced exactly: the small-argument path)
+  const double mag = exp(-re * re * S);
+  const double2 A = make_double2(mag * cs, mag * sn);
+  double2 F = make_double2(1.0, 0.0), p2 = A;
+  for (int k = seg - m1; k; k >>= 1) {
+    if (k & 1) F = zmul(F, p2);
+    p2 = zmul(p2, p2);
   }
-  // inclusive scan over j of v_j = A^16 v_{j-1} + agg_j, v_{-1} = x0
-  double2 v = j == 0 ? zfma(A16, x0, agg) : agg;
-  double2 m = A16;  // A^(16 2^k)
-  for (int k = 0; (1 << k) < p2; ++k) {
-    const int off = 1 << k;
-    const double2 up = make_double2(__shfl_up(v.x, off, p2), __shfl_up(v.y, off, p2));
-    if (j >= off) v = zfma(m, up, v);
-    m = zsq(m);
-  }
-  // the state entering segment s0
-  const double2 prev = make_double2(__shfl_up(v.x, 1, p2), __shfl_up(v.y, 1, p2));
-  double2 c = j == 0 ? x0 : prev;
+  double2 c = w == 0 ? make_double2((double)x0.x, (double)x0.y) : make_double2(0.0, 0.0);
+  const int n0 = min(kJ, m1 - m0);  // (wave-uniform)
 #pragma unroll
-  for (int k = 0; k < kSegPerThread; ++k) {
-    const int sg = s0 + k;
-    if (active && sg < a.nseg) cin[base + (size_t)sg * a.N] = make_float2((float)c.x, (float)c.y);
-    c = zfma(A, c, make_double2((double)o[k].x, (double)o[k].y));
+  for (int e = 0; e < kJ; ++e)
+    if (e < n0) c = zfma(A, c, make_double2((double)v[e].x, (double)v[e].y));
+  // (more than kJ segments per quarter, at most 512 segments: further groups)
+  for (int m = m0 + kJ; m < m1; m += kJ) {
+    float2 u[kJ];
+#pragma unroll
+    for (int e = 0; e < kJ; ++e) u[e] = load2(sr, lo + 8 * a.N * min(m + e, seg - 1));
+    const int nm = min(kJ, m1 - m);
+#pragma unroll
+    for (int e = 0; e < kJ; ++e)
+      if (e < nm) c = zfma(A, c, make_double2((double)u[e].x, (double)u[e].y));
+  }
+  part[t] = zmul(F, c);
+  __syncthreads();
+  if (w == 0) {
+    double2 x = part[lane];
+#pragma unroll
+    for (int k = 1; k < 4; ++k)
+      x = make_double2(x.x + part[64 * k + lane].x, x.y + part[64 * k + lane].y);
+    if (live) out[lane] = make_float2((float)x.x, (float)x.y);
   }
 }
 
@@ -844,8 +852,9 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
     return hipGetLastError();
   }
   // segments: (1) the state each segment leaves from zero, (2) the state each
-  // one enters, (3) the outputs from those states, one direction per launch
-  // (the reversed one adding into y)
+  // one enters (a workgroup per segment joining the earlier ones' and x0),
+  // (3) the outputs from those states, one direction per launch (the reversed
+  // one adding into y)
   const size_t part = align_up((size_t)ndir * B * H * p.nseg * N * sizeof(float2), 256);
   float2* sout = static_cast<float2*>(ws);
   float2* cin = reinterpret_cast<float2*>(static_cast<char*>(ws) + part);
@@ -856,18 +865,13 @@ hipError_t launch_chunk(const float* u, const float* log_re, const float* log_im
   s1.dir_in_grid = 1;  // the directions side by side (no outputs to share)
   s1.state_only = 1;
   s1.sout = sout;
-  s1.x0 = nullptr;  // every segment from zero here; x0 enters through the carries
+  s1.x0 = nullptr;  // every segment from zero here; x0 enters through the join
   s1.xend = nullptr;
   launch_chunk_args(s1, st, e_first, ndir);
-  // lanes per (direction, row, channel, mode): a power of two covering the
-  // segments in groups of kSegPerThread (nseg <= 512, so at most 32)
-  int p2 = 1;
-  while (p2 * kSegPerThread < p.nseg) p2 *= 2;
-  const long threads = (long)ndir * B * H * N * p2;
   ChunkArgs s2 = a;
   s2.sout = sout;
-  launch_k(chunk_carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), st,
-           KEvents{}, s2, p.seg_blocks * kCB * kT, p2, cin);
+  launch_k(chunk_join_kernel, dim3((unsigned)((long)ndir * B * H * p.nseg)), dim3(256), st,
+           KEvents{}, s2, cin);
   for (int d = 0; d < ndir; ++d) {
     ChunkArgs s3 = a;
     s3.dir0 = d;

@@ -341,8 +341,8 @@ def test_empty_inputs_are_noops():
 
 # ----------------------------------------------------------------------------
 # The recurrence view's work split: several batch rows per workgroup (many
-# rows), and the sequence cut into segments whose entering states come from a
-# state-only pass and a carry combination (few rows, long sequences).
+# rows), and the sequence cut into segments whose entering states are joined
+# from a state-only pass's segment states (few rows, long sequences).
 # ----------------------------------------------------------------------------
 
 SPLIT = [  # (B, H, N, L, bi, re_scale): few rows -> segments
