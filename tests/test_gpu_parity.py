@@ -351,6 +351,8 @@ SPLIT = [  # (B, H, N, L, bi, re_scale): few rows -> segments
     (2, 3, 33, 5 * 4096 * 3 + 77, 1, 1.0),  # ragged last chunk and block, one block per segment
     (1, 1, 16, 4096 * 2 + 1, 0, 1.0),    # the last segment holds one step
     (3, 2, 64, 3 * 4096, 0, 0.1),        # length a whole number of blocks
+    (1, 1, 16, 1 << 20, 0, 0.1),         # 256 segments: a join quarter over 32 terms
+    (1, 1, 8, 600000, 1, 1.0),           # 147 segments, both directions, ragged
 ]
 
 
