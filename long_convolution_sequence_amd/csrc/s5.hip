@@ -416,6 +416,7 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
     const half8* __restrict__ apk, const int* __restrict__ rexp, const float* __restrict__ Bm,
     int M, int K, int L, int B, const float* __restrict__ D, const float* __restrict__ u,
     float* __restrict__ out) {
+  PhaseClock pc;  // phase stamps (instrumented builds only): slots below
   __shared__ __attribute__((aligned(16))) _Float16 Bh[2][kColsWG][kBTS];
   __shared__ __attribute__((aligned(16))) _Float16 Bl[2][kColsWG][kBTS];
   __shared__ float cmax[kPW][kColsWG];
@@ -493,11 +494,13 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
     load_tile(tt);
     stage(0);
   }
+  pc.mark(0);  // prologue: fragments, first tile loaded and staged
   const bool vec = (L & 3) == 0;
   for (int sl = 0; tt < ntiles; tt += gridDim.x, sl ^= 1) {
     const int tn = tt + gridDim.x;
     const bool has_next = tn < ntiles;  // the same in the whole workgroup
     load_tile(has_next ? tn : tt);      // unconditional: no load under a branch
+    pc.mark(1);  // next tile requested
 
     v4f acc[4][2];
 #pragma unroll
@@ -519,6 +522,7 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
           }
         }
       }
+      pc.mark(2);  // product (matrix cores)
       // acc[jt][it][c]: column 64 jb + 16 jt + 4 g + c, row i0 + 16 it + lane % 16
       const int b = tt / njb, jb = tt - b * njb;
       float* ob = out + (size_t)b * M * L;
@@ -549,8 +553,11 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
         }
       }
     }
+    pc.mark(3);  // outputs scaled (D u added), stores issued
     if (has_next) stage(sl ^ 1);
+    pc.mark(4);  // next tile received, scaled, split, staged (two barriers)
   }
+  pc.write();
 }
 
 constexpr int kSeg = 16;       // steps per lane

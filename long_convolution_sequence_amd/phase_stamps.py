@@ -42,6 +42,9 @@ CHUNK_PHASES = ["prologue: fragments, barrier", "block: barrier", "input staged,
                 "prologue: entry, loads issued", "prologue: lambda (float64), barrier",
                 "prologue: powers, Q and KR tables, barrier", "prologue: taps, barrier",
                 "prologue: power planes, barrier"]
+S5_PIPE_PHASES = ["prologue: fragments, first tile loaded and staged", "next tile requested",
+                  "product (matrix cores)", "outputs scaled (+ D u), stores issued",
+                  "next tile received, split, staged (2 barriers)"]
 S5_PHASES = ["prologue: parameters, entering state, first u tile requested",
              "u tile in LDS (first tile), barrier", "u scaled, split, staged; D u (2 barriers)",
              "input projection (matrix cores)", "recurrence on the tile",
@@ -121,6 +124,27 @@ def main():
               "%.2f GHz" % (kname, nwg, waves, total, launch_us, total / launch_us / 1e3))
         for nm, v in rows:
             print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
+
+    # the S5 scan method: its output projection is the last launch to write the stamps
+    c5 = inputs.config("s5_mimo")
+    x5 = inputs.inputs_for(c5)
+    t5 = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in x5.items()}
+    ws5 = torch.empty(bd.s5_workspace_size(c5["B"], c5["H"], c5["P"], c5["L"], bd.S5_SCAN),
+                      dtype=torch.uint8, device="cuda")
+    buf = torch.zeros(MAX_WAVES * SLOTS, dtype=torch.int64, device="cuda")
+    if lib.dssm_phase_stamps_s5(buf.data_ptr()) != 0:
+        raise SystemExit("dssm_phase_stamps_s5 failed")
+    for _ in range(a.reps):
+        bd.s5_forward(t5["u"], t5["lam"], t5["Bbar"], t5["C"], t5["D"], workspace=ws5,
+                      method=bd.S5_SCAN)
+    torch.cuda.synchronize()
+    rows, total = _phases(buf, 256, 8, S5_PIPE_PHASES)
+    if lib.dssm_phase_stamps_s5(None) != 0:
+        raise SystemExit("dssm_phase_stamps_s5 failed")
+    print("s5_gemm_pipe_kernel<true>, output projection (256 workgroups x 8 waves): "
+          "%.0f cycles per wave" % total)
+    for nm, v in rows:
+        print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
 
     # the fused S5 form: its output pass is the last launch to write the stamps
     c5 = inputs.config("s5_mimo")
