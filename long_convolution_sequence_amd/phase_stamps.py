@@ -1,7 +1,8 @@
 """Per-phase cycle counts of the kernel generator, the FFT convolution and the
 chunked recurrence on the long-sequence workload (B=4 H=128 N=64 L=16384),
-and of the fused S5 form's output pass on the S5 workload (B=4 H=256 P=128
-L=16384), from the instrumented library libdssm_stamps.so:
+and of the S5 scan method's output projection and the fused S5 form's output
+pass on the S5 workload (B=4 H=256 P=128 L=16384), from the instrumented
+library libdssm_stamps.so:
 
     python -m long_convolution_sequence_amd.build --phase-stamps
     python -m long_convolution_sequence_amd.phase_stamps [--reps 5]
