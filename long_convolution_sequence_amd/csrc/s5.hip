@@ -1037,6 +1037,10 @@ __device__ __forceinline__ int opaque_s(int x) {  // a scalar the optimiser reco
   return x;
 }
 
+#ifdef DSSM_PHASE_STAMPS
+constexpr size_t kStateRows = 4096;  // stamp rows of the fused output pass before the state pass's
+#endif
+
 // KS: k steps (of 32) of both products, the fragments zero-padded to 32 KS;
 // FI: 16-row tiles per wave of each product (2: 8 waves, 4: 4 waves)
 template <bool STATE_ONLY, int KS, int FI>
@@ -1515,7 +1519,19 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
     for (int s2 = 0; s2 < NS; ++s2)
       if (pin[s2]) a.sout[((size_t)b * a.nseg + seg) * P + ps[s2]] = carry[s2];
   }
+#ifdef DSSM_PHASE_STAMPS
+  // (the state-only pass writes its stamps past the output pass's: rows from
+  // kStateRows on, so one forward leaves both)
+  if (STATE_ONLY && g_phase_buf && (threadIdx.x & 63) == 0) {
+    const size_t base = (kStateRows + (size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) *
+                        kPhaseSlots;
+    for (int k = 0; k < kPhaseSlots; ++k) g_phase_buf[base + k] = pc.acc[k];
+  } else {
+    pc.write();
+  }
+#else
   pc.write();
+#endif
 }
 
 }  // namespace

@@ -166,6 +166,12 @@ def main():
     torch.cuda.synchronize()
     nwg, waves = 256, 8  # the output pass's grid on this workload
     rows, total = _phases(buf, nwg, waves, S5_PHASES)
+    # the state-only pass: its stamps from row 4096 on (its last segments'
+    # workgroups return at once and leave none)
+    d = buf.cpu().numpy().reshape(-1, SLOTS)[4096: 4096 + nwg * waves].astype(np.float64)
+    d = d[d[:, : len(S5_PHASES)].sum(axis=1) > 0]
+    st_rows = [(nm, d[:, k].mean()) for k, nm in enumerate(S5_PHASES)]
+    st_total = d[:, : len(S5_PHASES)].sum(axis=1).mean()
     if lib.dssm_phase_stamps_s5(None) != 0:
         raise SystemExit("dssm_phase_stamps_s5 failed")
     evs = [hip.create(8) for _ in range(a.reps + 5)]
@@ -180,6 +186,10 @@ def main():
           "launch %.1f us, %.2f GHz" % (nwg, waves, total, launch_us, total / launch_us / 1e3))
     for nm, v in rows:
         print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
+    print("s5_fused_kernel, state-only pass (%d waves with stamps): %.0f cycles per wave"
+          % (len(d), st_total))
+    for nm, v in st_rows:
+        print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / st_total))
 
 
 if __name__ == "__main__":
