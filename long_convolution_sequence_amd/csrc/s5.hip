@@ -1199,13 +1199,14 @@ __global__ __launch_bounds__(1024 / FI, 1) void s5_fused_kernel(const S5FusedArg
       return __builtin_bit_cast(half8, r);
     };
   };
-  // the products of k step ks with the fragments (fh, fl) of the wave's four
-  // row tiles; the three split products of an accumulator are 16 instructions
-  // apart (a matrix-core result feeding the next product at once would stall)
-  // The staged operand is read one group of JG column tiles ahead of the
-  // products that use it (LDS latency hidden behind the matrix cores); the
-  // three split products of an accumulator are 2 JG kFI instructions apart.
-  constexpr int JG = STATE_ONLY && KS == 8 ? 1 : 2;  // column tiles per group
+  // the products of k step ks with the fragments (fh, fl) of the wave's row
+  // tiles.  The staged operand is read one group of JG column tiles ahead of
+  // the products that use it (LDS latency hidden behind the matrix cores); the
+  // three split products of an accumulator are 2 JG kFI instructions apart (a
+  // matrix-core result feeding the next product at once would stall).  Two
+  // column tiles per group in both passes (the state-only pass with one: 8%
+  // slower, the register need the same).
+  constexpr int JG = 2;  // column tiles per group
   constexpr int NG = 4 / JG;                         // groups per k step
   typedef half8 BOp[2][JG];                          // [hi, lo][column tile]
   auto bread = [&](int gi, BOp& bo) {  // group gi = NG ks + j: its staged operands
