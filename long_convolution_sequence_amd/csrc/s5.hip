@@ -401,6 +401,10 @@ __global__ __launch_bounds__(256, 2) void s5_gemm_kernel(const half8* __restrict
   }
 }
 
+#ifdef DSSM_PHASE_STAMPS
+constexpr size_t kProjInRows = 8192;  // stamp rows of the output projection before the input's
+#endif
+
 // Persistent form for K <= 256 (one k chunk).  A workgroup of 8 waves owns
 // 256 rows (32 per wave: its split A^T fragments stay in registers for the
 // whole kernel, read from L2 once) and walks the column tiles t = blockIdx.x,
@@ -557,7 +561,19 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
     if (has_next) stage(sl ^ 1);
     pc.mark(4);  // next tile received, scaled, split, staged (two barriers)
   }
+#ifdef DSSM_PHASE_STAMPS
+  // (the input projection writes its stamps past the output projection's:
+  // rows from kProjInRows on, so one forward leaves both)
+  if (!kAddDu && g_phase_buf && (threadIdx.x & 63) == 0) {
+    const size_t wgl = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const size_t base = (kProjInRows + wgl * (blockDim.x >> 6) + (threadIdx.x >> 6)) * kPhaseSlots;
+    for (int k = 0; k < kPhaseSlots; ++k) g_phase_buf[base + k] = pc.acc[k];
+  } else {
+    pc.write();
+  }
+#else
   pc.write();
+#endif
 }
 
 constexpr int kSeg = 16;       // steps per lane

@@ -140,12 +140,16 @@ def main():
                       method=bd.S5_SCAN)
     torch.cuda.synchronize()
     rows, total = _phases(buf, 256, 8, S5_PIPE_PHASES)
+    dp = buf.cpu().numpy().reshape(-1, SLOTS)[8192: 8192 + 256 * 8].astype(np.float64)
+    in_rows = [(nm, dp[:, k].mean()) for k, nm in enumerate(S5_PIPE_PHASES)]
+    in_total = dp[:, : len(S5_PIPE_PHASES)].sum(axis=1).mean()
     if lib.dssm_phase_stamps_s5(None) != 0:
         raise SystemExit("dssm_phase_stamps_s5 failed")
-    print("s5_gemm_pipe_kernel<true>, output projection (256 workgroups x 8 waves): "
-          "%.0f cycles per wave" % total)
-    for nm, v in rows:
-        print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / total))
+    for kname, tot, rws in (("s5_gemm_pipe_kernel<false>, input projection", in_total, in_rows),
+                            ("s5_gemm_pipe_kernel<true>, output projection", total, rows)):
+        print("%s (256 workgroups x 8 waves): %.0f cycles per wave" % (kname, tot))
+        for nm, v in rws:
+            print("  %-42s %8.0f  %5.1f%%" % (nm, v, 100.0 * v / tot))
 
     # the fused S5 form: its output pass is the last launch to write the stamps
     c5 = inputs.config("s5_mimo")
