@@ -409,22 +409,25 @@ constexpr size_t kProjInRows = 8192;  // stamp rows of the output projection bef
 // 256 rows (32 per wave: its split A^T fragments stay in registers for the
 // whole kernel, read from L2 once) and walks the column tiles t = blockIdx.x,
 // blockIdx.x + gridDim.x, ... over all batch rows.  The right-hand tile of the
-// next column tile is loaded into registers while the current one is
-// multiplied from the other half of a double-buffered LDS tile; the products
-// read only LDS and registers, so the in-order completion of memory
-// operations never makes them wait for the prefetch.
+// next column tile is loaded straight into LDS (buffer-to-LDS loads, no
+// registers) while the current one is multiplied from the split tile; the
+// u of the current tile's D u terms (output projection) is requested before
+// it, so that wait -- memory loads retiring in issue order -- never holds for
+// the next tile.
 constexpr int kPW = 8;  // waves per workgroup of the persistent form
 
-template <bool kAddDu>
+// VEC: L % 4 == 0 (16-byte accesses along the sequence)
+template <bool kAddDu, bool VEC>
 __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
     const half8* __restrict__ apk, const int* __restrict__ rexp, const float* __restrict__ Bm,
     int M, int K, int L, int B, const float* __restrict__ D, const float* __restrict__ u,
     float* __restrict__ out) {
   PhaseClock pc;  // phase stamps (instrumented builds only): slots below
-  __shared__ __attribute__((aligned(16))) _Float16 Bh[2][kColsWG][kBTS];
-  __shared__ __attribute__((aligned(16))) _Float16 Bl[2][kColsWG][kBTS];
+  __shared__ __attribute__((aligned(16))) _Float16 Bh[kColsWG][kBTS];
+  __shared__ __attribute__((aligned(16))) _Float16 Bl[kColsWG][kBTS];
+  __shared__ __attribute__((aligned(16))) float Braw[kKC][kColsWG];  // the next tile, fp32
   __shared__ float cmax[kPW][kColsWG];
-  __shared__ __attribute__((aligned(16))) int cexp[2][kColsWG];
+  __shared__ __attribute__((aligned(16))) int cexp[kColsWG];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int i0 = blockIdx.y * kRowsWG + 32 * w;  // this wave's first row
@@ -451,44 +454,68 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
     }
   }
 
-  // right-hand tile tt = (b, jb): thread (column lane, wave w) loads rows
-  // k = 8 (w + 8 q) + e through a raw buffer over each row (wave-uniform):
-  // columns past L read zero, a row past K has an empty range
-  float v[4][8];
+  // right-hand tile tt = (b, jb) into Braw[k][column]: wave w requests rows
+  // k = 8 (w + 8 q) + e (q < 4, e < 8), the rows its own threads read back in
+  // stage().  VEC: four rows per load, 16 bytes (four columns) per lane,
+  // through one raw buffer over the batch row's K x L floats (rows past K read
+  // zero; columns past L read the next row's, or zero, and only feed outputs
+  // past L, which are not stored); else one row per load, a dword per lane,
+  // through a buffer over that row (columns past L read zero).
   auto load_tile = [&](int tt) {
     const int b = tt / njb, jb = tt - b * njb;
     const float* Bb = Bm + (size_t)b * K * L;
-    const unsigned jbyte = 4u * (unsigned)(jb * kColsWG + lane);
+    if (VEC) {
+      const BufRes all = buf_res_uniform(Bb, 4u * (unsigned)K * (unsigned)L);
+      const int rl = lane >> 4, cl = 4 * (lane & 15);  // row within the four, first column
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = 8 * (wu + kPW * q) + e;
-        const BufRes row =
-            buf_res_uniform(Bb + (size_t)min(k, K - 1) * L, k < K ? 4u * (unsigned)L : 0u);
-        v[q][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(row, jbyte, 0, 0));
-      }
+        for (int e4 = 0; e4 < 2; ++e4) {
+          const int k = 8 * (wu + kPW * q) + 4 * e4;  // first of four rows
+          const unsigned off = 4u * ((unsigned)(k + rl) * (unsigned)L + (unsigned)(jb * kColsWG + cl));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              all, (__attribute__((address_space(3))) void*)&Braw[k][0], 16, off, 0, 0, 0);
+        }
+    } else {
+      const unsigned jbyte = 4u * (unsigned)(jb * kColsWG + lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = 8 * (wu + kPW * q) + e;
+          const BufRes row =
+              buf_res_uniform(Bb + (size_t)min(k, K - 1) * L, k < K ? 4u * (unsigned)L : 0u);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              row, (__attribute__((address_space(3))) void*)&Braw[k][0], 4, jbyte, 0, 0, 0);
+        }
+    }
   };
-  // split the loaded tile into LDS half sl, each column scaled by 2^cexp
-  auto stage = [&](int sl) {
+  // the requested tile, scaled per column by 2^cexp and split into Bh / Bl
+  // (after every wave's product has read the previous tile: the first barrier)
+  auto stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows are in Braw
+    float v[4][8];
     float m = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[q][e]));
+      for (int e = 0; e < 8; ++e) {
+        v[q][e] = Braw[8 * (w + kPW * q) + e][lane];
+        m = fmaxf(m, fabsf(v[q][e]));
+      }
     cmax[w][lane] = m;
     __syncthreads();
     float cm = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < kPW; ++w2) cm = fmaxf(cm, cmax[w2][lane]);
     const int sc = scale_exp(cm);
-    if (w == 0) cexp[sl][lane] = sc;
+    if (w == 0) cexp[lane] = sc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       half8 hi, lo;
       split8(v[q], hi, lo, sc);
-      *reinterpret_cast<half8*>(&Bh[sl][lane][8 * (w + kPW * q)]) = hi;
-      *reinterpret_cast<half8*>(&Bl[sl][lane][8 * (w + kPW * q)]) = lo;
+      *reinterpret_cast<half8*>(&Bh[lane][8 * (w + kPW * q)]) = hi;
+      *reinterpret_cast<half8*>(&Bl[lane][8 * (w + kPW * q)]) = lo;
     }
     __syncthreads();
   };
@@ -496,15 +523,40 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
   int tt = blockIdx.x;
   if (tt < ntiles) {
     load_tile(tt);
-    stage(0);
+    stage();
   }
   pc.mark(0);  // prologue: fragments, first tile loaded and staged
-  const bool vec = (L & 3) == 0;
-  for (int sl = 0; tt < ntiles; tt += gridDim.x, sl ^= 1) {
+  for (; tt < ntiles; tt += gridDim.x) {
     const int tn = tt + gridDim.x;
     const bool has_next = tn < ntiles;  // the same in the whole workgroup
-    load_tile(has_next ? tn : tt);      // unconditional: no load under a branch
-    pc.mark(1);  // next tile requested
+    const int b = tt / njb, jb = tt - b * njb;
+    // u of this lane's outputs (for D u), requested before the next tile: every
+    // load unconditional, at a clamped address (positions past L masked in the
+    // epilogue), and nothing computed from them before the product
+    v4f du[2][4];
+    float dv[2];
+    if (kAddDu) {
+      const float* ub = u + (size_t)b * M * L;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int i = min(i0 + 16 * it + (lane & 15), M - 1);
+        dv[it] = D[i];
+        const float* urow = ub + (size_t)i * L;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          const int jj = jb * kColsWG + 16 * jt + 4 * g;
+          if (VEC) {
+            du[it][jt] = *reinterpret_cast<const v4f*>(urow + min(jj, L - 4));
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) du[it][jt][c] = urow[min(jj + c, L - 1)];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // (the u loads stay ahead of the tile's)
+    load_tile(has_next ? tn : tt);  // unconditional: no load under a branch
+    pc.mark(1);  // D u and the next tile requested
 
     v4f acc[4][2];
 #pragma unroll
@@ -516,8 +568,8 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
         const int kk = 32 * ks + 8 * g;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          const half8 bh = *reinterpret_cast<const half8*>(&Bh[sl][16 * jt + (lane & 15)][kk]);
-          const half8 bl = *reinterpret_cast<const half8*>(&Bl[sl][16 * jt + (lane & 15)][kk]);
+          const half8 bh = *reinterpret_cast<const half8*>(&Bh[16 * jt + (lane & 15)][kk]);
+          const half8 bl = *reinterpret_cast<const half8*>(&Bl[16 * jt + (lane & 15)][kk]);
 #pragma unroll
           for (int it = 0; it < 2; ++it) {
             acc[jt][it] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bh, ah[it][ks], acc[jt][it], 0, 0, 0);
@@ -527,38 +579,49 @@ __global__ __launch_bounds__(512, 1) void s5_gemm_pipe_kernel(
         }
       }
       pc.mark(2);  // product (matrix cores)
+    }
+    if (kAddDu) {  // the D u terms arrive here, after the product (in every wave: no
+                   // branch the compiler could sink their loads into)
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        asm volatile("" : "+v"(dv[it]));
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) asm volatile("" : "+v"(du[it][jt]));
+      }
+    }
+    if (rows_here) {
       // acc[jt][it][c]: column 64 jb + 16 jt + 4 g + c, row i0 + 16 it + lane % 16
-      const int b = tt / njb, jb = tt - b * njb;
       float* ob = out + (size_t)b * M * L;
-      const float* ub = kAddDu ? u + (size_t)b * M * L : nullptr;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const int i = i0 + 16 * it + (lane & 15);
         if (i >= M) continue;
-        const float d = kAddDu ? D[i] : 0.f;
         float* orow = ob + (size_t)i * L;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
           const int jj = jb * kColsWG + 16 * jt + 4 * g;
-          const int4 ce = *reinterpret_cast<const int4*>(&cexp[sl][16 * jt + 4 * g]);
+          const int4 ce = *reinterpret_cast<const int4*>(&cexp[16 * jt + 4 * g]);
           v4f o;
           o[0] = __builtin_amdgcn_ldexpf(acc[jt][it][0], -(rx[it] + ce.x));
           o[1] = __builtin_amdgcn_ldexpf(acc[jt][it][1], -(rx[it] + ce.y));
           o[2] = __builtin_amdgcn_ldexpf(acc[jt][it][2], -(rx[it] + ce.z));
           o[3] = __builtin_amdgcn_ldexpf(acc[jt][it][3], -(rx[it] + ce.w));
-          if (vec && jj + 3 < L) {
-            if (kAddDu) o += d * *reinterpret_cast<const v4f*>(ub + (size_t)i * L + jj);
+          if (kAddDu) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o[c] += jj + c < L ? dv[it] * du[it][jt][c] : 0.f;
+          }
+          if (VEC && jj + 3 < L) {
             *reinterpret_cast<v4f*>(orow + jj) = o;
           } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-              if (jj + c < L) orow[jj + c] = kAddDu ? o[c] + d * ub[(size_t)i * L + jj + c] : o[c];
+              if (jj + c < L) orow[jj + c] = o[c];
           }
         }
       }
     }
     pc.mark(3);  // outputs scaled (D u added), stores issued
-    if (has_next) stage(sl ^ 1);
+    if (has_next) stage();
     pc.mark(4);  // next tile received, scaled, split, staged (two barriers)
   }
 #ifdef DSSM_PHASE_STAMPS
@@ -1636,8 +1699,13 @@ void launch_gemm(const void* apk, const int* rexp, const float* Bm, int M, int K
     const long ntiles = (long)B * ((L + kColsWG - 1) / kColsWG);
     const long per = std::max(1, cu_count() / nrb);
     const dim3 grid((unsigned)std::min(ntiles, per), (unsigned)nrb);
-    launch_k(s5_gemm_pipe_kernel<kAddDu>, grid, dim3(64 * kPW), st, ev, a, rexp, Bm, M, K, L, B,
-             D, u, out);
+    // (16-byte tile loads need L % 4 == 0 and a batch row's K x L floats under 2 GB)
+    if ((L & 3) == 0 && (size_t)4 * K * L < ((size_t)1 << 31))
+      launch_k(s5_gemm_pipe_kernel<kAddDu, true>, grid, dim3(64 * kPW), st, ev, a, rexp, Bm, M, K,
+               L, B, D, u, out);
+    else
+      launch_k(s5_gemm_pipe_kernel<kAddDu, false>, grid, dim3(64 * kPW), st, ev, a, rexp, Bm, M, K,
+               L, B, D, u, out);
     return;
   }
   const dim3 grid((unsigned)((L + kColsWG - 1) / kColsWG), (unsigned)nrb, (unsigned)B);
