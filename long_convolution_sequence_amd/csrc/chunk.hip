@@ -456,7 +456,10 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
         // 2. chunk states: S1[c][r] = sum_j A1[r][j] U[j][c]; this wave: rows 32 w .. +31,
         //    in two halves of 32 columns (fewer accumulators live).  The output
         //    product's U part (the Toeplitz taps, rows 16 w .. +15) takes the same U
-        //    fragments here: U is read from LDS once for both products
+        //    fragments here: U is read from LDS once for both products.  Not in the
+        //    streaming form: its end-state capture leaves no room for the 16
+        //    accumulators held across the recurrence (they would spill to scratch)
+        constexpr bool kFuseU = !CAPTURE;
         f4 accU[2][2];  // [column half][column tile]
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
                 acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc[rt][ct], 0, 0, 0);
                 acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc[rt][ct], 0, 0, 0);
               }
-              if (!STATE_ONLY) {
+              if (!STATE_ONLY && kFuseU) {
                 f4& au = accU[ch][ct];
                 if (ks == 0) au = f4{0.f, 0.f, 0.f, 0.f};
                 const half8 th = a3[ks * 2], tlo = a3[ks * 2 + 1];
@@ -579,23 +582,51 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
         //    accumulated apart: each carries its own scale.
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-          f4 accS[2];
+          f4 accS[2], accUo[2];
           accS[0] = accS[1] = f4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (kFuseU) {
 #pragma unroll
-          for (int ks = 2; ks < 6; ++ks) {  // (the U part, k < T: formed with the chunk states)
-            __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
-            const half8 ah = a3[ks * 2], al = a3[ks * 2 + 1];
+            for (int ks = 2; ks < 6; ++ks) {  // (the U part, k < T: formed with the chunk states)
+              __builtin_amdgcn_sched_barrier(0);  // one k step's operands live at a time
+              const half8 ah = a3[ks * 2], al = a3[ks * 2 + 1];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              const int c = 32 * ch + 16 * ct + (lane & 15);
-              const int k = 32 * (ks - 2) + 8 * (lane >> 4);
-              const unsigned char* rw = srow + c * kSRow;
-              const half8 bh = *reinterpret_cast<const half8*>(rw + 2 * k);
-              const half8 blo = *reinterpret_cast<const half8*>(rw + kSLo + 2 * k);
-              f4& acc = accS[ct];
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+              for (int ct = 0; ct < 2; ++ct) {
+                const int c = 32 * ch + 16 * ct + (lane & 15);
+                const int k = 32 * (ks - 2) + 8 * (lane >> 4);
+                const unsigned char* rw = srow + c * kSRow;
+                const half8 bh = *reinterpret_cast<const half8*>(rw + 2 * k);
+                const half8 blo = *reinterpret_cast<const half8*>(rw + kSLo + 2 * k);
+                f4& acc = accS[ct];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+              }
+            }
+          } else {
+            accUo[0] = accUo[1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 6; ++ks) {  // the U part (k < T), then the S part
+              __builtin_amdgcn_sched_barrier(0);
+              const half8 ah = a3[ks * 2], al = a3[ks * 2 + 1];
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) {
+                const int c = 32 * ch + 16 * ct + (lane & 15);
+                half8 bh, blo;
+                if (ks < 2) {
+                  const int k = 32 * ks + 8 * (lane >> 4);
+                  bh = *reinterpret_cast<const half8*>(bl.Uh + c * kUS + k);
+                  blo = *reinterpret_cast<const half8*>(bl.Ul + c * kUS + k);
+                } else {
+                  const int k = 32 * (ks - 2) + 8 * (lane >> 4);
+                  const unsigned char* rw = srow + c * kSRow;
+                  bh = *reinterpret_cast<const half8*>(rw + 2 * k);
+                  blo = *reinterpret_cast<const half8*>(rw + kSLo + 2 * k);
+                }
+                f4& acc = ks < 2 ? accUo[ct] : accS[ct];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, acc, 0, 0, 0);
+              }
             }
           }
           // acc*[ct][v]: step i = 16 w + 4 (lane / 16) + v of chunk c = 32 ch + 16 ct + lane % 16
@@ -610,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void chunk_kernel(const ChunkArgs a) {
             f4 acc;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4)
-              acc[v4] = __builtin_amdgcn_ldexpf(accU[ch][ct][v4], xu) +
+              acc[v4] = __builtin_amdgcn_ldexpf(kFuseU ? accU[ch][ct][v4] : accUo[ct][v4], xu) +
                         __builtin_amdgcn_ldexpf(accS[ct][v4], xs);
             if (VEC) {
               // four consecutive processing times: one 16-byte group (ascending
